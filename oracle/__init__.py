@@ -1,0 +1,27 @@
+"""Plain fp64 CPU oracle for absorbed MLA decode over a paged latent cache.
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE. Only the test suite, the smoke check in
+``__graft_entry__`` and the benchmark's CPU-baseline leg may import this
+package. The product path (the HIP library and its Python binding) never
+imports it, and it imports nothing from the product.
+
+Everything is float64 numpy, written from the definitions on the pages:
+  * the naive ("path A") and absorbed ("path B") score formulas of the MLA
+    operator-teardown page (jh158.com), section 4;
+  * the per-token latent row of 512 c_KV + 64 k_R values and the 64-token
+    page of the same page, sections 1 and 3;
+  * the split scan plus log-sum-exp reduction structure of the MI355X Kimi K3
+    time-share study (jinnpan.com), "Inside the blocks" (stage 1 KV scan,
+    stage 2 KV-split reduction).
+
+Each function is pinned by tests under ``tests/test_oracle*.py`` against
+closed forms, brute-force loops, the pages' storage arithmetic and the
+naive/absorbed identity. The pages' printed bf16 error magnitudes for their
+absorption script are not reproducible and are not used as a pin.
+"""
+from .mla_oracle import (  # noqa: F401
+    as_f64, bf16_bits_to_f64, default_scale, gather_rows, absorb, visible_len,
+    scores_absorbed, softmax_rows, attend_absorbed, decode_absorbed,
+    decode_naive, up_proj, split_ranges, decode_split, combine, decode_rows,
+    latent_row_elems, latent_row_bytes, mha_kv_bytes_per_token_layer,
+)

@@ -1,0 +1,293 @@
+"""fp64 reference for absorbed MLA decode (test infrastructure only).
+
+Notation (MLA operator-teardown page, sections 1, 3, 4):
+  H heads, d_hc = 128 content dims per head, d_c = 512 latent dims,
+  d_R = 64 decoupled-RoPE dims, page = 64 tokens.
+  A cache row holds c_KV (d_c values) followed by k_R (d_R values).
+  Path A (naive): K_h = c_KV . W_UK[h]^T, score = q_c . K_h + q_R . k_R.
+  Path B (absorbed): q_abs[h] = q_c[h] . W_UK[h], score = q_abs . c_KV + q_R . k_R.
+  Both scores are multiplied by 1/sqrt(d_hc + d_R).
+
+Readings taken where the pages are silent (each also listed in the design notes):
+  * W_UV has the layout of W_UK, [H, d_hc, d_c]; out[h, d] = sum_c o_lat[h, c] W_UV[h, d, c].
+  * q_R and k_R arrive already rotated; no rotation happens here.
+  * with s_q new tokens per sequence, query i (0-based) sees cache tokens
+    t <= L_b - s_q + i (the chunk's own latents are already in the cache).
+  * LSE is the natural log of the sum of exp(scaled score).
+  * an empty key range yields o = 0 and LSE = -inf.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+# --------------------------------------------------------------------------
+# bf16 decoding and storage arithmetic
+# --------------------------------------------------------------------------
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact value of bf16 bit patterns: the top 16 bits of an IEEE float32."""
+    u32 = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u32.view(np.float32).astype(np.float64)
+
+
+def as_f64(x) -> np.ndarray:
+    """Exact float64 copy of a torch tensor or numpy array (bf16 via its bits)."""
+    try:
+        import torch
+    except ImportError:  # pragma: no cover
+        torch = None
+    if torch is not None and isinstance(x, torch.Tensor):
+        x = x.detach().cpu()
+        if x.dtype == torch.bfloat16:
+            return bf16_bits_to_f64(x.contiguous().view(torch.int16).numpy().view(np.uint16))
+        return x.to(torch.float64).numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def latent_row_elems(d_c: int = 512, d_r: int = 64) -> int:
+    """Values stored per token and layer: the latent plus the shared RoPE key."""
+    return d_c + d_r
+
+
+def latent_row_bytes(d_c: int = 512, d_r: int = 64, elem_bytes: int = 2) -> int:
+    return latent_row_elems(d_c, d_r) * elem_bytes
+
+
+def mha_kv_bytes_per_token_layer(h: int = 128, d_head: int = 128, elem_bytes: int = 2) -> int:
+    """Uncompressed multi-head K and V for one token and layer."""
+    return 2 * h * d_head * elem_bytes
+
+
+def default_scale(d_hc: int = 128, d_r: int = 64) -> float:
+    """Softmax scale 1/sqrt(d_hc + d_R) (teardown page, section 4 script)."""
+    return 1.0 / math.sqrt(d_hc + d_r)
+
+
+# --------------------------------------------------------------------------
+# paged gather
+# --------------------------------------------------------------------------
+
+
+def gather_rows(kv_cache: np.ndarray, block_table_row: np.ndarray, n_tokens: int) -> np.ndarray:
+    """Logical rows 0..n_tokens-1 of one sequence.
+
+    Token t lives in physical page block_table_row[t // page] at row t % page.
+    Only the entries the sequence needs are read; they must be valid page ids.
+    """
+    kv = np.asarray(kv_cache)
+    page = kv.shape[1]
+    n_pages = -(-int(n_tokens) // page)
+    ids = np.asarray(block_table_row[:n_pages], dtype=np.int64)
+    if n_pages and (ids.min() < 0 or ids.max() >= kv.shape[0]):
+        raise ValueError("block table entry out of range")
+    rows = kv[ids].reshape(n_pages * page, kv.shape[2])
+    return rows[:n_tokens]
+
+
+# --------------------------------------------------------------------------
+# absorbed path (path B)
+# --------------------------------------------------------------------------
+
+
+def absorb(q_c: np.ndarray, w_uk: np.ndarray) -> np.ndarray:
+    """q_abs[..., h, c] = sum_d q_c[..., h, d] * W_UK[h, d, c]."""
+    return np.einsum("...hd,hdc->...hc", np.asarray(q_c, np.float64), np.asarray(w_uk, np.float64))
+
+
+def visible_len(L_b: int, s_q: int, i: int) -> int:
+    """Keys visible to query i of an s_q-token chunk whose latents end the cache."""
+    return int(L_b) - int(s_q) + int(i) + 1
+
+
+def scores_absorbed(qa: np.ndarray, qr: np.ndarray, C: np.ndarray, R: np.ndarray,
+                    scale: float) -> np.ndarray:
+    """[H, L] scaled scores (q_abs . c_KV + q_R . k_R) * scale."""
+    return (qa @ C.T + qr @ R.T) * scale
+
+
+def softmax_rows(s: np.ndarray):
+    """Row softmax with max subtraction; returns (P, m, l) with P = exp(s-m)/l."""
+    m = s.max(axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    l = e.sum(axis=-1, keepdims=True)
+    return e / l, m[..., 0], l[..., 0]
+
+
+def attend_absorbed(qa: np.ndarray, qr: np.ndarray, C: np.ndarray, R: np.ndarray, scale: float):
+    """One query token, all heads: (o_lat [H, d_c], lse [H]) over keys C, R."""
+    Hn, d_c = qa.shape
+    if C.shape[0] == 0:
+        return np.zeros((Hn, d_c)), np.full((Hn,), -np.inf)
+    s = scores_absorbed(qa, qr, C, R, scale)
+    P, m, l = softmax_rows(s)
+    return P @ C, m + np.log(l)
+
+
+def _split_row(row: np.ndarray, d_c: int):
+    return row[:, :d_c], row[:, d_c:]
+
+
+def decode_absorbed(q_abs, q_r, kv_cache, block_table, seqlens, scale: float):
+    """Latent attention output o_lat [B, s_q, H, d_c] and lse [B, s_q, H]."""
+    q_abs = np.asarray(q_abs, np.float64)
+    q_r = np.asarray(q_r, np.float64)
+    B, s_q, Hn, d_c = q_abs.shape
+    o = np.zeros((B, s_q, Hn, d_c))
+    lse = np.zeros((B, s_q, Hn))
+    for b in range(B):
+        L = int(seqlens[b])
+        rows = gather_rows(kv_cache, block_table[b], max(L, 0))
+        C, R = _split_row(np.asarray(rows, np.float64), d_c)
+        for i in range(s_q):
+            n = max(visible_len(L, s_q, i), 0)
+            o[b, i], lse[b, i] = attend_absorbed(q_abs[b, i], q_r[b, i], C[:n], R[:n], scale)
+    return o, lse
+
+
+# --------------------------------------------------------------------------
+# naive path (path A): decompress per-head keys and values
+# --------------------------------------------------------------------------
+
+
+def decode_naive(q_c, q_r, kv_cache, block_table, seqlens, w_uk, w_uv, scale: float):
+    """Final output out [B, s_q, H, d_hc] and lse [B, s_q, H] without absorption.
+
+    K_h[t, d] = sum_c c_KV[t, c] W_UK[h, d, c];  V_h[t, d] = sum_c c_KV[t, c] W_UV[h, d, c].
+    """
+    q_c = np.asarray(q_c, np.float64)
+    q_r = np.asarray(q_r, np.float64)
+    w_uk = np.asarray(w_uk, np.float64)
+    w_uv = np.asarray(w_uv, np.float64)
+    B, s_q, Hn, d_hc = q_c.shape
+    d_c = w_uk.shape[2]
+    out = np.zeros((B, s_q, Hn, w_uv.shape[1]))
+    lse = np.zeros((B, s_q, Hn))
+    for b in range(B):
+        L = int(seqlens[b])
+        rows = np.asarray(gather_rows(kv_cache, block_table[b], max(L, 0)), np.float64)
+        C, R = _split_row(rows, d_c)
+        for h in range(Hn):
+            K = C @ w_uk[h].T          # [L, d_hc]
+            V = C @ w_uv[h].T          # [L, d_hc]
+            for i in range(s_q):
+                n = max(visible_len(L, s_q, i), 0)
+                if n == 0:
+                    out[b, i, h] = 0.0
+                    lse[b, i, h] = -np.inf
+                    continue
+                s = (K[:n] @ q_c[b, i, h] + R[:n] @ q_r[b, i, h]) * scale
+                m = s.max()
+                e = np.exp(s - m)
+                l = e.sum()
+                out[b, i, h] = (e @ V[:n]) / l
+                lse[b, i, h] = m + np.log(l)
+    return out, lse
+
+
+# --------------------------------------------------------------------------
+# up-projection
+# --------------------------------------------------------------------------
+
+
+def up_proj(o_lat, w_uv) -> np.ndarray:
+    """out[..., h, d] = sum_c o_lat[..., h, c] * W_UV[h, d, c]."""
+    return np.einsum("...hc,hdc->...hd", np.asarray(o_lat, np.float64), np.asarray(w_uv, np.float64))
+
+
+# --------------------------------------------------------------------------
+# split scan + log-sum-exp combine (stage 1 / stage 2)
+# --------------------------------------------------------------------------
+
+
+def split_ranges(n_pages: int, num_splits: int):
+    """Page ranges of a split plan: split s covers [s*q, min((s+1)*q, n)), q = ceil(n/S).
+
+    Trailing splits may be empty. This is the plan the library documents for
+    its partial outputs; the combined result does not depend on it.
+    """
+    q = -(-int(n_pages) // int(num_splits)) if n_pages > 0 else 0
+    out = []
+    for s in range(num_splits):
+        p0 = min(s * q, n_pages)
+        p1 = min((s + 1) * q, n_pages)
+        out.append((p0, p1))
+    return out
+
+
+def decode_split(q_abs, q_r, kv_cache, block_table, seqlens, scale: float, num_splits: int):
+    """Per-split partials: o_part [B, s_q, H, S, d_c] (each normalised), lse_part [B, s_q, H, S]."""
+    q_abs = np.asarray(q_abs, np.float64)
+    q_r = np.asarray(q_r, np.float64)
+    B, s_q, Hn, d_c = q_abs.shape
+    page = np.asarray(kv_cache).shape[1]
+    o = np.zeros((B, s_q, Hn, num_splits, d_c))
+    lse = np.full((B, s_q, Hn, num_splits), -np.inf)
+    for b in range(B):
+        L = int(seqlens[b])
+        rows = np.asarray(gather_rows(kv_cache, block_table[b], max(L, 0)), np.float64)
+        C, R = _split_row(rows, d_c)
+        for i in range(s_q):
+            n = max(visible_len(L, s_q, i), 0)
+            n_pages = -(-n // page)
+            for s, (p0, p1) in enumerate(split_ranges(n_pages, num_splits)):
+                t0, t1 = p0 * page, min(p1 * page, n)
+                if t1 <= t0:
+                    continue
+                o[b, i, :, s], lse[b, i, :, s] = attend_absorbed(
+                    q_abs[b, i], q_r[b, i], C[t0:t1], R[t0:t1], scale)
+    return o, lse
+
+
+def combine(o_part, lse_part):
+    """Merge normalised split outputs by their log-sum-exp weights.
+
+    LSE = M + ln sum_s exp(lse_s - M), M = max_s lse_s;  o = sum_s exp(lse_s - LSE) o_s.
+    Rows whose splits are all empty give o = 0, LSE = -inf.
+    """
+    o_part = np.asarray(o_part, np.float64)
+    lse_part = np.asarray(lse_part, np.float64)
+    M = lse_part.max(axis=-1)
+    finite = np.isfinite(M)
+    Ms = np.where(finite, M, 0.0)
+    w = np.where(np.isfinite(lse_part), np.exp(lse_part - Ms[..., None]), 0.0)
+    tot = w.sum(axis=-1)
+    LSE = np.where(finite, Ms + np.log(np.where(finite, tot, 1.0)), -np.inf)
+    wn = np.where(finite[..., None], w / np.where(finite, tot, 1.0)[..., None], 0.0)
+    o = np.einsum("...s,...sc->...c", wn, o_part)
+    return o, LSE
+
+
+# --------------------------------------------------------------------------
+# sampled rows for large workloads
+# --------------------------------------------------------------------------
+
+
+def decode_rows(q_abs, q_r, kv_cache, block_table, seqlens, scale: float, picks):
+    """o_lat and lse for selected (b, i, h) rows only; picks is a list of triples.
+
+    Gathers each needed sequence once; cost is linear in the rows requested.
+    """
+    q_abs = np.asarray(q_abs)
+    q_r = np.asarray(q_r)
+    s_q = q_abs.shape[1]
+    d_c = q_abs.shape[-1]
+    out_o = np.zeros((len(picks), d_c))
+    out_l = np.zeros((len(picks),))
+    by_b: dict[int, list[int]] = {}
+    for k, (b, _, _) in enumerate(picks):
+        by_b.setdefault(int(b), []).append(k)
+    for b, ks in by_b.items():
+        L = int(seqlens[b])
+        rows = np.asarray(gather_rows(kv_cache, block_table[b], max(L, 0)), np.float64)
+        C, R = _split_row(rows, d_c)
+        for k in ks:
+            _, i, h = picks[k]
+            n = max(visible_len(L, s_q, int(i)), 0)
+            qa = np.asarray(q_abs[b, i, h], np.float64)[None]
+            qr = np.asarray(q_r[b, i, h], np.float64)[None]
+            o, l = attend_absorbed(qa, qr, C[:n], R[:n], scale)
+            out_o[k], out_l[k] = o[0], l[0]
+    return out_o, out_l

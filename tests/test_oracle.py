@@ -1,0 +1,368 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+None of these re-types an oracle formula: each check is a closed form, a
+brute-force loop in plain Python floats, a value printed on the pages, or an
+identity between two independently written paths (naive vs absorbed).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from mla_inputs import make_inputs, tiny_inputs, CONFIGS, make_structure
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# --------------------------------------------------------------------------
+# storage arithmetic printed on the teardown page (sections 1 and 3)
+# --------------------------------------------------------------------------
+
+def test_storage_arithmetic_matches_teardown_page():
+    g = _golden("teardown_storage.json")
+    d_c, d_r = g["latent_kv_dim"], g["rope_dim"]
+    assert O.latent_row_elems(d_c, d_r) == g["elements_per_token_layer"]
+    assert O.latent_row_bytes(d_c, d_r) / 1024 == g["bf16_kb_per_token_layer"]
+    mha = O.mha_kv_bytes_per_token_layer(g["heads"], g["head_dim_content"])
+    assert mha / 1024 == g["mha_kb_per_token_layer"]
+    assert round(100 * (1 - O.latent_row_bytes(d_c, d_r) / mha), 2) == g["compression_percent"]
+    assert 16 * O.latent_row_bytes(d_c, d_r) / 1024 == g["page16_kb"]
+    assert 64 * O.latent_row_bytes(d_c, d_r) / 1024 == pytest.approx(g["page64_kb_approx"], rel=0.01)
+    assert O.default_scale(g["head_dim_content"], g["rope_dim"]) == 1.0 / math.sqrt(g["softmax_scale_denominator_sqrt_of"])
+
+
+def test_k3_byte_count_per_token():
+    g = _golden("k3_mla_bytes.json")
+    per_tok = g["mla_layers"] * O.latent_row_bytes()
+    assert per_tok / 1024 == pytest.approx(g["kib_per_token_all_layers"], abs=0.05)
+    # "1M context" read as 2^20 tokens: 28.99 GB vs the printed 28.96 GB (0.1%)
+    assert per_tok * 2**20 / 1e9 == pytest.approx(g["gb_per_step_at_1M"], rel=2e-3)
+    bw = g["gb_per_step_at_1M"] / (g["scan_ms_at_1M"] * 1e-3) / 1e3
+    assert bw == pytest.approx(g["scan_tb_per_s"], abs=0.01)
+    assert 100 * bw / g["peak_tb_per_s"] == pytest.approx(g["scan_fraction_of_peak_percent"], abs=0.05)
+
+
+# --------------------------------------------------------------------------
+# bf16 decoding: against IEEE bit patterns and torch's own conversion
+# --------------------------------------------------------------------------
+
+def test_bf16_decoding():
+    bits = np.array([0x3F80, 0xC000, 0x7F80, 0xFF80, 0x0001, 0x4049, 0x0000, 0x8000], dtype=np.uint16)
+    v = O.bf16_bits_to_f64(bits)
+    assert v[0] == 1.0 and v[1] == -2.0
+    assert v[2] == np.inf and v[3] == -np.inf
+    assert v[4] == 2.0 ** -133
+    assert v[5] == 3.140625
+    assert v[6] == 0.0 and np.signbit(v[7])
+    x = torch.randn(4096, dtype=torch.float32).to(torch.bfloat16)
+    assert np.array_equal(O.as_f64(x), x.to(torch.float64).numpy())
+
+
+# --------------------------------------------------------------------------
+# brute force in plain Python floats (tiny dims, several pages, ragged, causal)
+# --------------------------------------------------------------------------
+
+def _brute_naive(inp, scale):
+    """Path A written as explicit loops over Python floats."""
+    q_c, q_r = inp["q_c"].tolist(), inp["q_r"].tolist()
+    w_uk, w_uv = inp["w_uk"].tolist(), inp["w_uv"].tolist()
+    kv, bt, seqlens = inp["kv_cache"].tolist(), inp["block_table"].tolist(), inp["seqlens"].tolist()
+    B, s_q, Hn, d_hc = inp["q_c"].shape
+    d_c = inp["w_uk"].shape[2]
+    page = inp["kv_cache"].shape[1]
+    out = [[[None] * Hn for _ in range(s_q)] for _ in range(B)]
+    lse = [[[None] * Hn for _ in range(s_q)] for _ in range(B)]
+    for b in range(B):
+        L = seqlens[b]
+        rows = []
+        for t in range(L):
+            rows.append(kv[bt[b][t // page]][t % page])
+        for i in range(s_q):
+            last = L - s_q + i  # last visible key index
+            for h in range(Hn):
+                scores, vals = [], []
+                for t in range(last + 1):
+                    row = rows[t]
+                    k = [sum(row[c] * w_uk[h][d][c] for c in range(d_c)) for d in range(d_hc)]
+                    v = [sum(row[c] * w_uv[h][d][c] for c in range(d_c)) for d in range(d_hc)]
+                    s = sum(q_c[b][i][h][d] * k[d] for d in range(d_hc))
+                    s += sum(q_r[b][i][h][j] * row[d_c + j] for j in range(len(q_r[b][i][h])))
+                    scores.append(s * scale)
+                    vals.append(v)
+                mx = max(scores)
+                ex = [math.exp(s - mx) for s in scores]
+                tot = sum(ex)
+                out[b][i][h] = [sum(ex[t] * vals[t][d] for t in range(len(ex))) / tot for d in range(d_hc)]
+                lse[b][i][h] = mx + math.log(tot)
+    return np.array(out), np.array(lse)
+
+
+def _brute_absorbed(inp, q_abs, scale):
+    """o_lat and lse over the latent rows, as explicit loops."""
+    q_r = inp["q_r"].tolist()
+    kv, bt, seqlens = inp["kv_cache"].tolist(), inp["block_table"].tolist(), inp["seqlens"].tolist()
+    qa = np.asarray(q_abs).tolist()
+    B, s_q, Hn, d_c = np.asarray(q_abs).shape
+    page = inp["kv_cache"].shape[1]
+    o = np.zeros((B, s_q, Hn, d_c))
+    l = np.zeros((B, s_q, Hn))
+    for b in range(B):
+        L = seqlens[b]
+        for i in range(s_q):
+            n = L - s_q + i + 1
+            for h in range(Hn):
+                sc = []
+                for t in range(n):
+                    row = kv[bt[b][t // page]][t % page]
+                    s = sum(qa[b][i][h][c] * row[c] for c in range(d_c))
+                    s += sum(q_r[b][i][h][j] * row[d_c + j] for j in range(len(row) - d_c))
+                    sc.append(s * scale)
+                mx = max(sc)
+                ex = [math.exp(s - mx) for s in sc]
+                tot = sum(ex)
+                for c in range(d_c):
+                    o[b, i, h, c] = sum(ex[t] * kv[bt[b][t // page]][t % page][c] for t in range(n)) / tot
+                l[b, i, h] = mx + math.log(tot)
+    return o, l
+
+
+@pytest.mark.parametrize("seqlens,s_q", [([7, 10], 3), ([4, 1, 9], 1), ([13], 5)])
+def test_brute_force_tiny(seqlens, s_q):
+    inp = tiny_inputs(B=len(seqlens), s_q=s_q, seqlens=seqlens, h=2, d_hc=3, d_c=5, d_r=2, page=4)
+    n = {k: v.numpy() for k, v in inp.items()}
+    scale = 1.0 / math.sqrt(3 + 2)
+    ref_out, ref_lse = _brute_naive(inp, scale)
+    out_a, lse_a = O.decode_naive(n["q_c"], n["q_r"], n["kv_cache"], n["block_table"], n["seqlens"],
+                                  n["w_uk"], n["w_uv"], scale)
+    np.testing.assert_allclose(out_a, ref_out, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse_a, ref_lse, rtol=1e-12, atol=1e-13)
+    q_abs = O.absorb(n["q_c"], n["w_uk"])
+    o_lat, lse_b = O.decode_absorbed(q_abs, n["q_r"], n["kv_cache"], n["block_table"], n["seqlens"], scale)
+    ref_o, ref_l = _brute_absorbed(inp, q_abs, scale)
+    np.testing.assert_allclose(o_lat, ref_o, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse_b, ref_l, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(O.up_proj(o_lat, n["w_uv"]), ref_out, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(lse_b, ref_lse, rtol=1e-12, atol=1e-13)
+
+
+def test_absorb_brute_force():
+    g = np.random.default_rng(3)
+    q = g.standard_normal((2, 3, 4, 5))
+    w = g.standard_normal((4, 5, 6))
+    ref = np.zeros((2, 3, 4, 6))
+    for a in range(2):
+        for b in range(3):
+            for h in range(4):
+                for c in range(6):
+                    ref[a, b, h, c] = sum(q[a, b, h, d] * w[h, d, c] for d in range(5))
+    np.testing.assert_allclose(O.absorb(q, w), ref, rtol=1e-13, atol=1e-14)
+
+
+def test_up_proj_brute_force():
+    g = np.random.default_rng(4)
+    o = g.standard_normal((3, 4, 7))
+    w = g.standard_normal((4, 5, 7))
+    ref = np.zeros((3, 4, 5))
+    for t in range(3):
+        for h in range(4):
+            for d in range(5):
+                ref[t, h, d] = sum(o[t, h, c] * w[h, d, c] for c in range(7))
+    np.testing.assert_allclose(O.up_proj(o, w), ref, rtol=1e-13, atol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# the teardown page's equivalence (section 4) at real dims, in fp64
+# --------------------------------------------------------------------------
+
+def test_naive_equals_absorbed_real_dims():
+    inp = make_inputs("single")
+    f = {k: O.as_f64(getattr(inp, k)) for k in ("q_c", "q_r", "w_uk", "kv_cache", "w_uv")}
+    bt, L = inp.block_table.numpy(), inp.seqlens.numpy()
+    scale = O.default_scale()
+    out_a, lse_a = O.decode_naive(f["q_c"], f["q_r"], f["kv_cache"], bt, L, f["w_uk"], f["w_uv"], scale)
+    q_abs = O.absorb(f["q_c"], f["w_uk"])
+    o_lat, lse_b = O.decode_absorbed(q_abs, f["q_r"], f["kv_cache"], bt, L, scale)
+    out_b = O.up_proj(o_lat, f["w_uv"])
+    assert np.abs(out_a - out_b).max() <= 1e-11 * np.abs(out_a).max()
+    assert np.abs(lse_a - lse_b).max() <= 1e-11
+
+
+def test_score_variance_with_documented_weight_scale():
+    """W ~ N(0, 1/512) with unit inputs makes the scaled score variance 1."""
+    inp = make_inputs("single")
+    q_abs = O.absorb(O.as_f64(inp.q_c), O.as_f64(inp.w_uk))
+    kv = O.as_f64(inp.kv_cache).reshape(-1, 576)
+    s = O.scores_absorbed(q_abs[0, 0], O.as_f64(inp.q_r)[0, 0], kv[:, :512], kv[:, 512:], O.default_scale())
+    assert 0.9 < s.std() < 1.1
+
+
+# --------------------------------------------------------------------------
+# softmax and closed forms
+# --------------------------------------------------------------------------
+
+def test_softmax_rows_sum_to_one():
+    g = np.random.default_rng(5)
+    s = g.standard_normal((64, 1000)) * 7
+    P, m, l = O.softmax_rows(s)
+    np.testing.assert_allclose(P.sum(-1), 1.0, atol=1e-12)
+    assert (P >= 0).all()
+    np.testing.assert_array_equal(m, s.max(-1))
+
+
+def _single_row_inputs(L, seed=11):
+    g = torch.Generator().manual_seed(seed)
+    kv = torch.randn((-(-L // 64), 64, 576), generator=g).to(torch.bfloat16)
+    return O.as_f64(kv), np.arange(kv.shape[0])[None].astype(np.int32)
+
+
+def test_closed_form_single_key():
+    kv, bt = _single_row_inputs(1)
+    g = np.random.default_rng(6)
+    qa, qr = g.standard_normal((1, 1, 128, 512)), g.standard_normal((1, 1, 128, 64))
+    o, lse = O.decode_absorbed(qa, qr, kv, bt, [1], O.default_scale())
+    assert np.array_equal(o[0, 0], np.broadcast_to(kv[0, 0, :512], (128, 512)))
+    s0 = (qa[0, 0] @ kv[0, 0, :512] + qr[0, 0] @ kv[0, 0, 512:]) * O.default_scale()
+    np.testing.assert_allclose(lse[0, 0], s0, rtol=1e-14, atol=1e-14)
+
+
+def test_closed_form_zero_query_is_mean():
+    L = 300
+    kv, bt = _single_row_inputs(L)
+    qa, qr = np.zeros((1, 1, 4, 512)), np.zeros((1, 1, 4, 64))
+    o, lse = O.decode_absorbed(qa, qr, kv, bt, [L], O.default_scale())
+    mean = kv.reshape(-1, 576)[:L, :512].mean(0)
+    np.testing.assert_allclose(o[0, 0], np.broadcast_to(mean, (4, 512)), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse[0, 0], math.log(L), rtol=1e-14)
+
+
+def test_closed_form_one_hot_selects_row():
+    L, tstar = 200, 137
+    kv, bt = _single_row_inputs(L)
+    kv = kv.copy()
+    kv[..., 512:] = 0.0
+    kv.reshape(-1, 576)[tstar, 512] = 1.0
+    qa = np.zeros((1, 1, 2, 512))
+    qr = np.zeros((1, 1, 2, 64))
+    qr[..., 0] = 2000.0
+    o, lse = O.decode_absorbed(qa, qr, kv, bt, [L], O.default_scale())
+    row = kv.reshape(-1, 576)[tstar, :512]
+    np.testing.assert_allclose(o[0, 0], np.broadcast_to(row, (2, 512)), rtol=1e-15, atol=1e-50)
+    np.testing.assert_allclose(lse[0, 0], 2000.0 * O.default_scale(), rtol=1e-14)
+
+
+def test_empty_range_convention():
+    kv, bt = _single_row_inputs(64)
+    o, lse = O.decode_absorbed(np.ones((1, 1, 3, 512)), np.ones((1, 1, 3, 64)), kv, bt, [0], 0.1)
+    assert (o == 0).all() and np.isneginf(lse).all()
+
+
+# --------------------------------------------------------------------------
+# paged gather
+# --------------------------------------------------------------------------
+
+def test_gather_matches_token_loop_and_rejects_bad_ids():
+    st = make_structure(CONFIGS["ragged"], seed=5)
+    pool = st.num_pages
+    kv = np.arange(pool * 64 * 3, dtype=np.float64).reshape(pool, 64, 3)
+    for b in (0, 17, 63):
+        L = int(st.seqlens[b])
+        rows = O.gather_rows(kv, st.block_table[b].numpy(), L)
+        bt = st.block_table[b].tolist()
+        ref = np.array([kv[bt[t // 64], t % 64] for t in range(L)])
+        assert np.array_equal(rows, ref)
+    bad = st.block_table[0].numpy().copy()
+    bad[0] = pool
+    with pytest.raises(ValueError):
+        O.gather_rows(kv, bad, 10)
+
+
+def test_page_permutation_invariance():
+    inp = tiny_inputs(B=2, s_q=2, seqlens=[150, 70], h=3, d_hc=4, d_c=8, d_r=2, page=16, seed=9)
+    n = {k: v.numpy() for k, v in inp.items()}
+    qa = O.absorb(n["q_c"], n["w_uk"])
+    o1, l1 = O.decode_absorbed(qa, n["q_r"], n["kv_cache"], n["block_table"], n["seqlens"], 0.3)
+    perm = np.random.default_rng(1).permutation(n["kv_cache"].shape[0])
+    inv = np.argsort(perm)
+    kv2 = n["kv_cache"][perm]          # new physical page p holds old page perm[p]
+    bt2 = np.where(n["block_table"] >= 0, inv[np.maximum(n["block_table"], 0)], -1)
+    o2, l2 = O.decode_absorbed(qa, n["q_r"], kv2, bt2, n["seqlens"], 0.3)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+# --------------------------------------------------------------------------
+# split scan + combine
+# --------------------------------------------------------------------------
+
+def test_split_ranges_cover_pages():
+    for n in (0, 1, 5, 64, 1023):
+        for S in (1, 2, 7, 16, 64):
+            r = O.split_ranges(n, S)
+            assert len(r) == S
+            covered = [p for a, b in r for p in range(a, b)]
+            assert covered == list(range(n))
+
+
+@pytest.mark.parametrize("num_splits", [1, 2, 7, 20])
+def test_split_invariance(num_splits):
+    inp = tiny_inputs(B=3, s_q=2, seqlens=[300, 64, 129], h=4, d_hc=8, d_c=32, d_r=8, page=16, seed=12)
+    n = {k: v.numpy() for k, v in inp.items()}
+    qa = O.absorb(n["q_c"], n["w_uk"])
+    ref_o, ref_l = O.decode_absorbed(qa, n["q_r"], n["kv_cache"], n["block_table"], n["seqlens"], 0.25)
+    op, lp = O.decode_split(qa, n["q_r"], n["kv_cache"], n["block_table"], n["seqlens"], 0.25, num_splits)
+    o, l = O.combine(op, lp)
+    np.testing.assert_allclose(o, ref_o, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(l, ref_l, rtol=1e-13, atol=1e-13)
+
+
+def test_combine_closed_forms():
+    g = np.random.default_rng(8)
+    o = g.standard_normal((5, 3, 16))
+    # one split: identity
+    oc, lc = O.combine(o[:, :1], np.array([[0.7]] * 5))
+    np.testing.assert_array_equal(oc, o[:, 0])
+    np.testing.assert_allclose(lc, 0.7)
+    # equal lse over 3 splits: average, lse + ln 3
+    oc, lc = O.combine(o, np.full((5, 3), -1.5))
+    np.testing.assert_allclose(oc, o.mean(1), rtol=1e-14)
+    np.testing.assert_allclose(lc, -1.5 + math.log(3), rtol=1e-14)
+    # an empty split is ignored; all-empty gives zero / -inf
+    lp = np.array([[0.2, -np.inf, 0.2]] * 5)
+    oc, lc = O.combine(o, lp)
+    np.testing.assert_allclose(oc, (o[:, 0] + o[:, 2]) / 2, rtol=1e-14)
+    oc, lc = O.combine(o, np.full((5, 3), -np.inf))
+    assert (oc == 0).all() and np.isneginf(lc).all()
+
+
+def test_causal_chunk_reduces_to_single_queries():
+    inp = tiny_inputs(B=2, s_q=4, seqlens=[40, 9], h=2, d_hc=4, d_c=8, d_r=2, page=8, seed=21)
+    n = {k: v.numpy() for k, v in inp.items()}
+    qa = O.absorb(n["q_c"], n["w_uk"])
+    o, l = O.decode_absorbed(qa, n["q_r"], n["kv_cache"], n["block_table"], n["seqlens"], 0.5)
+    for b in range(2):
+        for i in range(4):
+            Lv = int(n["seqlens"][b]) - 4 + i + 1
+            o1, l1 = O.decode_absorbed(qa[b:b + 1, i:i + 1], n["q_r"][b:b + 1, i:i + 1], n["kv_cache"],
+                                       n["block_table"][b:b + 1], [Lv], 0.5)
+            assert np.array_equal(o1[0, 0], o[b, i]) and np.array_equal(l1[0, 0], l[b, i])
+
+
+def test_decode_rows_matches_full():
+    inp = tiny_inputs(B=2, s_q=3, seqlens=[100, 33], h=4, d_hc=4, d_c=16, d_r=4, page=8, seed=2)
+    n = {k: v.numpy() for k, v in inp.items()}
+    qa = O.absorb(n["q_c"], n["w_uk"])
+    o, l = O.decode_absorbed(qa, n["q_r"], n["kv_cache"], n["block_table"], n["seqlens"], 0.4)
+    picks = [(0, 0, 1), (1, 2, 3), (0, 2, 0)]
+    ro, rl = O.decode_rows(qa, n["q_r"], n["kv_cache"], n["block_table"], n["seqlens"], 0.4, picks)
+    for k, (b, i, h) in enumerate(picks):
+        # one-row and many-row BLAS products round differently in the last ulp
+        np.testing.assert_allclose(ro[k], o[b, i, h], rtol=1e-13, atol=1e-15)
+        np.testing.assert_allclose(rl[k], l[b, i, h], rtol=1e-14)

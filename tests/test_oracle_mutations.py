@@ -1,0 +1,92 @@
+"""Planted mistakes in the oracle (CPU only) must each be caught by a pin.
+
+Every mutant replaces one oracle function with a plausible wrong version
+(a dropped term, an off-by-one, a wrong weight) for the duration of one test,
+then re-runs the pins that should notice and expects at least one to fail.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+import oracle.mla_oracle as M
+import tests.test_oracle as pins
+
+
+def _patch(monkeypatch, name, fn):
+    monkeypatch.setattr(M, name, fn)
+    monkeypatch.setattr(O, name, fn)
+
+
+def _expect_fail(*checks):
+    failed = 0
+    for chk in checks:
+        try:
+            chk()
+        except (AssertionError, ValueError, IndexError):
+            failed += 1
+    assert failed > 0, "no pin noticed the planted mistake"
+
+
+def test_dropped_rope_term_is_caught(monkeypatch):
+    _patch(monkeypatch, "scores_absorbed", lambda qa, qr, C, R, scale: (qa @ C.T) * scale)
+    _expect_fail(pins.test_naive_equals_absorbed_real_dims,
+                 lambda: pins.test_brute_force_tiny([7, 10], 3))
+
+
+def test_wrong_scale_is_caught(monkeypatch):
+    real = M.scores_absorbed
+    _patch(monkeypatch, "scores_absorbed", lambda qa, qr, C, R, scale: real(qa, qr, C, R, scale) * 1.01)
+    _expect_fail(pins.test_closed_form_one_hot_selects_row,
+                 lambda: pins.test_brute_force_tiny([4, 1, 9], 1))
+
+
+def test_causal_off_by_one_is_caught(monkeypatch):
+    _patch(monkeypatch, "visible_len", lambda L, s_q, i: int(L) - int(s_q) + int(i))
+    _expect_fail(lambda: pins.test_brute_force_tiny([7, 10], 3))
+
+
+def test_split_plan_losing_last_page_is_caught(monkeypatch):
+    real = M.split_ranges
+
+    def lossy(n, S):
+        r = real(n, S)
+        return [(a, min(b, max(n - 1, 0))) for a, b in r]
+    _patch(monkeypatch, "split_ranges", lossy)
+    _expect_fail(lambda: pins.test_split_invariance(2), pins.test_split_ranges_cover_pages)
+
+
+def test_gather_ignoring_block_table_is_caught(monkeypatch):
+    def naive_gather(kv, bt_row, n):
+        kv = np.asarray(kv)
+        return kv.reshape(-1, kv.shape[2])[:n]
+    _patch(monkeypatch, "gather_rows", naive_gather)
+    _expect_fail(pins.test_gather_matches_token_loop_and_rejects_bad_ids,
+                 pins.test_page_permutation_invariance,
+                 lambda: pins.test_brute_force_tiny([7, 10], 3))
+
+
+def test_combine_without_lse_weights_is_caught(monkeypatch):
+    def plain_mean(o_part, lse_part):
+        o_part = np.asarray(o_part, np.float64)
+        return o_part.mean(axis=-2), np.asarray(lse_part).max(axis=-1)
+    _patch(monkeypatch, "combine", plain_mean)
+    _expect_fail(pins.test_combine_closed_forms, lambda: pins.test_split_invariance(7))
+
+
+def test_transposed_up_proj_is_caught(monkeypatch):
+    def wrong(o_lat, w_uv):
+        w = np.asarray(w_uv, np.float64)
+        # contracts the right index but reads heads in reverse order
+        return np.einsum("...hc,hdc->...hd", np.asarray(o_lat, np.float64), w[::-1])
+    _patch(monkeypatch, "up_proj", wrong)
+    _expect_fail(pins.test_up_proj_brute_force, lambda: pins.test_brute_force_tiny([4, 1, 9], 1))
+
+
+def test_softmax_without_max_subtraction_bias_is_caught(monkeypatch):
+    def biased(s):
+        m = s.max(axis=-1, keepdims=True)
+        e = np.exp(s - m)
+        l = e.sum(axis=-1, keepdims=True) + 1e-3
+        return e / l, m[..., 0], l[..., 0]
+    _patch(monkeypatch, "softmax_rows", biased)
+    _expect_fail(pins.test_softmax_rows_sum_to_one, pins.test_closed_form_zero_query_is_mean)
