@@ -1,0 +1,159 @@
+/*
+ * mla.h -- C ABI of the absorbed Multi-Head Latent Attention (MLA) decode
+ * library for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (MLA operator-teardown page, jh158.com, sections 1, 3, 4):
+ *   per token and layer the cache holds a 512-wide latent c_KV followed by a
+ *   64-wide decoupled RoPE key k_R (576 bf16 values). W_UK is absorbed into
+ *   the query (q_abs = q_c . W_UK per head), so each score is
+ *       s[h, t] = (q_abs[h] . c_KV[t] + q_R[h] . k_R[t]) / sqrt(128 + 64)
+ *   and the latent output o_lat[h] = softmax(s[h]) . c_KV is up-projected
+ *   per head through W_UV. The per-head 16384-wide keys never exist.
+ * Long contexts are scanned in page-aligned splits whose partial results are
+ *   merged by their log-sum-exp (stage 1 scan and stage 2 reduction of the
+ *   MI355X Kimi K3 time-share study, jinnpan.com, "Inside the blocks").
+ *
+ * Conventions for every function below:
+ *   - Pointers are DEVICE pointers unless stated otherwise, must be non-NULL
+ *     and 16-byte aligned. Tensors are dense, row-major, innermost last.
+ *   - bf16 is IEEE bfloat16 stored as uint16; fp32 is IEEE float.
+ *   - The caller owns every buffer. The library allocates nothing, keeps no
+ *     state besides cached device properties, and is safe to call from
+ *     several host threads.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     with no host synchronisation. Results are valid once the caller has
+ *     synchronised with that stream.
+ *   - Arguments are validated on the host before any launch. A non-OK status
+ *     means nothing was enqueued, except MLA_ERR_HIP, which reports a launch
+ *     failure. Device faults surface at the caller's next synchronisation.
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef MLA_H
+#define MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Problem constants (teardown page, section 3: 128 heads, content head dim
+ * 128, latent 512, RoPE 64, page size 64). */
+enum {
+  MLA_HEADS = 128, /* attention heads H */
+  MLA_D_HC = 128,  /* content dims per head of q_c, W_UK and W_UV rows */
+  MLA_D_C = 512,   /* latent dims of c_KV */
+  MLA_D_R = 64,    /* decoupled RoPE dims of q_R and k_R */
+  MLA_ROW = 576,   /* bf16 values stored per token and layer */
+  MLA_PAGE = 64    /* tokens per cache page */
+};
+
+typedef enum mla_status {
+  MLA_OK = 0,
+  MLA_ERR_NULL = 1,      /* a required pointer is NULL */
+  MLA_ERR_SHAPE = 2,     /* a size argument is out of range */
+  MLA_ERR_ALIGN = 3,     /* a pointer is not 16-byte aligned */
+  MLA_ERR_WORKSPACE = 4, /* a caller buffer is too small for the request */
+  MLA_ERR_HIP = 5        /* the HIP runtime reported an error */
+} mla_status;
+
+/* Static, never-NULL name of a status code ("MLA_OK", ...). Unknown codes
+ * give "MLA_ERR_UNKNOWN". */
+const char* mla_status_string(int status);
+
+/* Human-readable detail of the most recent non-OK status returned on the
+ * calling host thread (which argument failed and why). Static per-thread
+ * storage; never NULL; "" if nothing failed yet. */
+const char* mla_last_error(void);
+
+/* Absorb W_UK into the query (teardown page, section 4, absorbed path):
+ *     q_abs[t, h, c] = sum_d q_c[t, h, d] * W_UK[h, d, c]
+ * fp32 accumulation, result rounded to bf16 (round-to-nearest-even).
+ *   q_c   bf16 [T, H, 128]   (T = batch * new tokens, any order)
+ *   w_uk  bf16 [H, 128, 512] (the page's w_uk layout (nh, dhc, dc))
+ *   q_abs bf16 [T, H, 512]   output
+ *   T >= 1, H == MLA_HEADS. */
+mla_status mla_absorb_q(const void* q_c, const void* w_uk, void* q_abs,
+                        int64_t T, int H, void* stream);
+
+/* Bytes of o_part plus lse_part for mla_decode_paged with these sizes
+ * (B * s_q * H * num_splits * (512 + 1) * 4). Host-only, no validation;
+ * returns 0 for non-positive arguments. */
+size_t mla_decode_workspace_bytes(int B, int s_q, int H, int num_splits);
+
+/* A split count for mla_decode_paged that fills the GPU for these sizes
+ * (host-only heuristic; max_len is the longest sequence in tokens). The
+ * result is in [1, ceil(max_len / 64)] (1 if max_len < 1). */
+int mla_recommended_splits(int B, int s_q, int max_len, int num_cus);
+
+/* Stage 1: split scan of the paged latent cache, absorbed scores, online
+ * softmax, P . c_KV on matrix cores (teardown page, section 4 absorbed
+ * scores; K3 study "Inside the blocks" stage 1).
+ *   q_abs       bf16 [B, s_q, H, 512]   absorbed queries
+ *   q_r         bf16 [B, s_q, H, 64]    rotated RoPE queries
+ *   kv_cache    bf16 [num_pages, 64, 576]; row = c_KV (0..511), k_R (512..575)
+ *   block_table int32 [B, max_pages]: logical page p of sequence b lives in
+ *               physical page block_table[b, p]. Only the first
+ *               ceil(L_b / 64) entries are read; they must lie in
+ *               [0, num_pages). Others (e.g. -1) are never read. Entries out
+ *               of range are clamped into [0, num_pages) so no access leaves
+ *               the cache; the affected rows' results are then unspecified.
+ *   seqlens     int32 [B]: L_b = tokens in the cache for sequence b,
+ *               including the s_q new ones. Values are clamped to
+ *               [0, max_pages * 64].
+ *   softmax_scale  multiplies q_abs.c_KV + q_R.k_R (1/sqrt(192) for DeepSeek).
+ *   num_splits  in [1, max_pages]; query i of sequence b sees tokens
+ *               t <= L_b - s_q + i, i.e. n = ceil((L_b - s_q + i + 1) / 64)
+ *               pages, and split s scans pages [s*q, min((s+1)*q, n)) with
+ *               q = ceil(n / num_splits). Empty splits are allowed.
+ *   o_part      fp32 [B, s_q, H, num_splits, 512] output: each split's
+ *               softmax-normalised latent output (zeros for an empty split)
+ *   lse_part    fp32 [B, s_q, H, num_splits] output: natural-log
+ *               log-sum-exp of the split's scaled scores (-inf if empty)
+ * B >= 1, 1 <= s_q <= 4096, H == MLA_HEADS, 1 <= max_pages,
+ * num_pages >= 1. */
+mla_status mla_decode_paged(const void* q_abs, const void* q_r,
+                            const void* kv_cache, int64_t num_pages,
+                            const int32_t* block_table, int max_pages,
+                            const int32_t* seqlens, int B, int s_q, int H,
+                            float softmax_scale, int num_splits,
+                            float* o_part, float* lse_part, void* stream);
+
+/* Stage 2: merge split partials by their log-sum-exp (K3 study, "Inside the
+ * blocks", KV-split reduction):
+ *     LSE = M + ln sum_s exp(lse_s - M),  M = max_s lse_s
+ *     o   = sum_s exp(lse_s - LSE) * o_s
+ * A row whose splits are all empty gives o = 0 and LSE = -inf.
+ *   o_part   fp32 [B, s_q, H, num_splits, 512], lse_part fp32 [B, s_q, H, num_splits]
+ *   o_lat    fp32 [B, s_q, H, 512] output,  lse fp32 [B, s_q, H] output
+ * B >= 1, s_q >= 1, H == MLA_HEADS, num_splits >= 1. */
+mla_status mla_combine_splits(const float* o_part, const float* lse_part,
+                              int B, int s_q, int H, int num_splits,
+                              float* o_lat, float* lse, void* stream);
+
+/* Per-head up-projection of the latent output (W_UV has W_UK's layout):
+ *     out[t, h, d] = sum_c o_lat[t, h, c] * W_UV[h, d, c]
+ * o_lat is split into a bf16 high part and a bf16 remainder so the fp32
+ * input keeps ~16 significant bits on bf16 matrix cores; fp32 accumulation;
+ * result rounded to bf16.
+ *   o_lat fp32 [T, H, 512], w_uv bf16 [H, 128, 512], out bf16 [T, H, 128]
+ *   T >= 1, H == MLA_HEADS. */
+mla_status mla_up_proj(const float* o_lat, const void* w_uv, void* out,
+                       int64_t T, int H, void* stream);
+
+/* Test and debug aid: gather the logical cache rows of each sequence through
+ * the block table with the same address arithmetic as mla_decode_paged.
+ *   out bf16 [B, max_len, 576]: row t of sequence b is the cache row of token
+ *   t for t < min(L_b, max_len) and zero otherwise.
+ * Same argument rules as mla_decode_paged; max_len >= 1. */
+mla_status mla_debug_gather(const void* kv_cache, int64_t num_pages,
+                            const int32_t* block_table, int max_pages,
+                            const int32_t* seqlens, int B, int max_len,
+                            void* out, void* stream);
+
+#ifdef __cplusplus
+} /* extern "C" */
+#endif
+
+#endif /* MLA_H */

@@ -1,0 +1,182 @@
+"""Absorbed MLA decode over a paged latent cache on MI355X (gfx950).
+
+Python binding of libmla (include/mla.h). Each function has the name of the
+C entry point it calls; it only checks and marshals arguments (dtype, shape,
+device, contiguity, the current torch stream) and allocates outputs through
+torch when none are given. All computation runs in the HIP kernels.
+
+Shapes (H = 128 heads, content dim 128, latent 512, RoPE 64, page 64):
+  q_c      bf16 [B, s_q, H, 128]          w_uk, w_uv  bf16 [H, 128, 512]
+  q_abs    bf16 [B, s_q, H, 512]          q_r         bf16 [B, s_q, H, 64]
+  kv_cache bf16 [num_pages, 64, 576]      block_table int32 [B, max_pages]
+  seqlens  int32 [B] (tokens in cache incl. the s_q new ones)
+  o_part   fp32 [B, s_q, H, S, 512]       lse_part    fp32 [B, s_q, H, S]
+  o_lat    fp32 [B, s_q, H, 512]          lse         fp32 [B, s_q, H]
+  out      bf16 [B, s_q, H, 128]
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import _lib
+
+H, D_HC, D_C, D_R, ROW, PAGE = 128, 128, 512, 64, 576, 64
+DEFAULT_SCALE = 1.0 / math.sqrt(D_HC + D_R)
+
+STATUS_NAMES = {0: "MLA_OK", 1: "MLA_ERR_NULL", 2: "MLA_ERR_SHAPE", 3: "MLA_ERR_ALIGN",
+                4: "MLA_ERR_WORKSPACE", 5: "MLA_ERR_HIP"}
+
+
+class MlaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        name = _lib.LIB.mla_status_string(status).decode()
+        detail = _lib.LIB.mla_last_error().decode()
+        super().__init__(f"{where}: {name}: {detail}")
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise MlaError(status, where)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on a GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _ptr(t: torch.Tensor) -> int:
+    return t.data_ptr()
+
+
+def num_cus(device=None) -> int:
+    return torch.cuda.get_device_properties(device or torch.cuda.current_device()).multi_processor_count
+
+
+def mla_recommended_splits(B: int, s_q: int, max_len: int, cus: int | None = None) -> int:
+    return int(_lib.LIB.mla_recommended_splits(int(B), int(s_q), int(max_len), int(cus or num_cus())))
+
+
+def mla_decode_workspace_bytes(B: int, s_q: int, num_splits: int, heads: int = H) -> int:
+    return int(_lib.LIB.mla_decode_workspace_bytes(int(B), int(s_q), int(heads), int(num_splits)))
+
+
+def mla_absorb_q(q_c: torch.Tensor, w_uk: torch.Tensor, q_abs: torch.Tensor | None = None, stream=None):
+    """q_abs[..., h, :] = q_c[..., h, :] @ W_UK[h]; q_c [..., H, 128] -> q_abs [..., H, 512]."""
+    lead = tuple(q_c.shape[:-2])
+    T = math.prod(lead) if lead else 1
+    _need(q_c, "q_c", torch.bfloat16, lead + (H, D_HC))
+    _need(w_uk, "w_uk", torch.bfloat16, (H, D_HC, D_C))
+    if q_abs is None:
+        q_abs = torch.empty(lead + (H, D_C), dtype=torch.bfloat16, device=q_c.device)
+    _need(q_abs, "q_abs", torch.bfloat16, lead + (H, D_C))
+    _check(_lib.LIB.mla_absorb_q(_ptr(q_c), _ptr(w_uk), _ptr(q_abs), T, H, _stream(stream)), "mla_absorb_q")
+    return q_abs
+
+
+def mla_decode_paged(q_abs, q_r, kv_cache, block_table, seqlens, num_splits: int,
+                     softmax_scale: float = DEFAULT_SCALE, o_part=None, lse_part=None, stream=None):
+    """Split scan; returns (o_part [B,s_q,H,S,512] fp32, lse_part [B,s_q,H,S] fp32)."""
+    B, s_q = q_abs.shape[0], q_abs.shape[1]
+    _need(q_abs, "q_abs", torch.bfloat16, (B, s_q, H, D_C))
+    _need(q_r, "q_r", torch.bfloat16, (B, s_q, H, D_R))
+    if kv_cache.dim() != 3 or kv_cache.shape[1:] != (PAGE, ROW):
+        raise ValueError(f"kv_cache must be [num_pages, 64, 576], got {tuple(kv_cache.shape)}")
+    _need(kv_cache, "kv_cache", torch.bfloat16)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError(f"block_table must be [B, max_pages], got {tuple(block_table.shape)}")
+    _need(block_table, "block_table", torch.int32)
+    _need(seqlens, "seqlens", torch.int32, (B,))
+    S = int(num_splits)
+    if o_part is None:
+        o_part = torch.empty((B, s_q, H, S, D_C), dtype=torch.float32, device=q_abs.device)
+    if lse_part is None:
+        lse_part = torch.empty((B, s_q, H, S), dtype=torch.float32, device=q_abs.device)
+    _need(o_part, "o_part", torch.float32, (B, s_q, H, S, D_C))
+    _need(lse_part, "lse_part", torch.float32, (B, s_q, H, S))
+    _check(_lib.LIB.mla_decode_paged(
+        _ptr(q_abs), _ptr(q_r), _ptr(kv_cache), kv_cache.shape[0], _ptr(block_table), block_table.shape[1],
+        _ptr(seqlens), B, s_q, H, float(softmax_scale), S, _ptr(o_part), _ptr(lse_part), _stream(stream)),
+        "mla_decode_paged")
+    return o_part, lse_part
+
+
+def mla_combine_splits(o_part, lse_part, o_lat=None, lse=None, stream=None):
+    """LSE-weighted merge; returns (o_lat [B,s_q,H,512] fp32, lse [B,s_q,H] fp32)."""
+    B, s_q, _, S = lse_part.shape
+    _need(o_part, "o_part", torch.float32, (B, s_q, H, S, D_C))
+    _need(lse_part, "lse_part", torch.float32, (B, s_q, H, S))
+    if o_lat is None:
+        o_lat = torch.empty((B, s_q, H, D_C), dtype=torch.float32, device=o_part.device)
+    if lse is None:
+        lse = torch.empty((B, s_q, H), dtype=torch.float32, device=o_part.device)
+    _need(o_lat, "o_lat", torch.float32, (B, s_q, H, D_C))
+    _need(lse, "lse", torch.float32, (B, s_q, H))
+    _check(_lib.LIB.mla_combine_splits(_ptr(o_part), _ptr(lse_part), B, s_q, H, S, _ptr(o_lat), _ptr(lse),
+                                       _stream(stream)), "mla_combine_splits")
+    return o_lat, lse
+
+
+def mla_up_proj(o_lat, w_uv, out=None, stream=None):
+    """out[..., h, :] = W_UV[h] @ o_lat[..., h, :]; o_lat [..., H, 512] fp32 -> out [..., H, 128] bf16."""
+    lead = tuple(o_lat.shape[:-2])
+    T = math.prod(lead) if lead else 1
+    _need(o_lat, "o_lat", torch.float32, lead + (H, D_C))
+    _need(w_uv, "w_uv", torch.bfloat16, (H, D_HC, D_C))
+    if out is None:
+        out = torch.empty(lead + (H, D_HC), dtype=torch.bfloat16, device=o_lat.device)
+    _need(out, "out", torch.bfloat16, lead + (H, D_HC))
+    _check(_lib.LIB.mla_up_proj(_ptr(o_lat), _ptr(w_uv), _ptr(out), T, H, _stream(stream)), "mla_up_proj")
+    return out
+
+
+def mla_debug_gather(kv_cache, block_table, seqlens, max_len: int, out=None, stream=None):
+    """Logical rows [B, max_len, 576] gathered through the block table (zeros past L_b)."""
+    B = block_table.shape[0]
+    _need(kv_cache, "kv_cache", torch.bfloat16)
+    _need(block_table, "block_table", torch.int32)
+    _need(seqlens, "seqlens", torch.int32, (B,))
+    if out is None:
+        out = torch.empty((B, max_len, ROW), dtype=torch.bfloat16, device=kv_cache.device)
+    _need(out, "out", torch.bfloat16, (B, max_len, ROW))
+    _check(_lib.LIB.mla_debug_gather(_ptr(kv_cache), kv_cache.shape[0], _ptr(block_table), block_table.shape[1],
+                                     _ptr(seqlens), B, int(max_len), _ptr(out), _stream(stream)),
+           "mla_debug_gather")
+    return out
+
+
+def decode_layer(q_c, q_r, kv_cache, block_table, seqlens, w_uk, w_uv, num_splits: int | None = None,
+                 softmax_scale: float = DEFAULT_SCALE, max_len: int | None = None, stream=None):
+    """The whole hot path for one layer: absorb -> split scan -> combine -> up-projection.
+
+    Returns a dict with every intermediate (q_abs, o_part, lse_part, o_lat, lse, out).
+    ``max_len`` (longest sequence, host int) only feeds the split heuristic.
+    """
+    B, s_q = q_c.shape[0], q_c.shape[1]
+    if num_splits is None:
+        ml = int(max_len) if max_len is not None else block_table.shape[1] * PAGE
+        num_splits = mla_recommended_splits(B, s_q, ml)
+    q_abs = mla_absorb_q(q_c, w_uk, stream=stream)
+    o_part, lse_part = mla_decode_paged(q_abs, q_r, kv_cache, block_table, seqlens, num_splits,
+                                        softmax_scale, stream=stream)
+    o_lat, lse = mla_combine_splits(o_part, lse_part, stream=stream)
+    out = mla_up_proj(o_lat, w_uv, stream=stream)
+    return dict(q_abs=q_abs, o_part=o_part, lse_part=lse_part, o_lat=o_lat, lse=lse, out=out)

@@ -1,0 +1,74 @@
+// Stage 2 of absorbed MLA decode: merge the split partials of each
+// (sequence, query, head) row by their log-sum-exp (KV-split reduction of the
+// K3 time-share study, "Inside the blocks").
+//
+// One wave per row: every lane reads the row's split LSEs to form the weights,
+// then owns 8 of the 512 latent columns and streams the n_split partial rows
+// with 32-byte loads (2 KiB contiguous per split across the wave).
+#include "mla_device.hpp"
+#include "decode.hpp"
+
+namespace mla {
+
+namespace {
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o_part,
+                                                      const float* __restrict__ lse_part, int rows,
+                                                      int num_splits, float* __restrict__ o_lat,
+                                                      float* __restrict__ lse) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const float* lp = lse_part + (int64_t)row * num_splits;
+  float* orow = o_lat + (int64_t)row * kDc + 8 * lane;
+
+  float M = -INFINITY;
+  for (int s = lane; s < num_splits; s += 64) M = fmaxf(M, lp[s]);
+  M = wave_max(M);
+  if (M == -INFINITY) {  // every split empty
+    *reinterpret_cast<f32x4*>(orow) = f32x4{};
+    *reinterpret_cast<f32x4*>(orow + 4) = f32x4{};
+    if (lane == 0) lse[row] = -INFINITY;
+    return;
+  }
+  float tot = 0.f;
+  for (int s = lane; s < num_splits; s += 64) tot += expf(lp[s] - M);
+  tot = wave_sum(tot);
+  const float L = M + logf(tot);
+
+  f32x4 a0 = f32x4{}, a1 = f32x4{};
+  const float* op = o_part + (int64_t)row * num_splits * kDc + 8 * lane;
+  for (int s = 0; s < num_splits; ++s) {
+    const float w = expf(lp[s] - L);  // 0 for an empty split (lse = -inf)
+    const f32x4 v0 = *reinterpret_cast<const f32x4*>(op + (int64_t)s * kDc);
+    const f32x4 v1 = *reinterpret_cast<const f32x4*>(op + (int64_t)s * kDc + 4);
+    a0 += w * v0;
+    a1 += w * v1;
+  }
+  *reinterpret_cast<f32x4*>(orow) = a0;
+  *reinterpret_cast<f32x4*>(orow + 4) = a1;
+  if (lane == 0) lse[row] = L;
+}
+
+hipError_t launch_combine(const float* o_part, const float* lse_part, int rows, int num_splits,
+                          float* o_lat, float* lse, hipStream_t stream) {
+  const int blocks = (rows + 3) / 4;
+  hipLaunchKernelGGL(combine_kernel, dim3(blocks), dim3(256), 0, stream, o_part, lse_part, rows, num_splits,
+                     o_lat, lse);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,39 @@
+// Launch interfaces of the MLA kernels (host side of each .hip file).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace mla {
+
+struct DecodeParams {
+  const __bf16* q_abs;        // [B, s_q, 128, 512]
+  const __bf16* q_r;          // [B, s_q, 128, 64]
+  const char* kv;             // [num_pages, 64, 576] bf16
+  int64_t num_pages;
+  const int32_t* block_table; // [B, max_pages]
+  int max_pages;
+  const int32_t* seqlens;     // [B]
+  int B;
+  int s_q;
+  int num_splits;
+  float scale_log2;           // softmax_scale * log2(e)
+  float* o_part;              // [B, s_q, 128, num_splits, 512]
+  float* lse_part;            // [B, s_q, 128, num_splits]
+  int items;                  // B * s_q * num_splits
+  int items_per_xcd;          // ceil(items / 8)
+};
+
+hipError_t launch_decode_paged(const DecodeParams& p, hipStream_t stream);
+
+hipError_t launch_combine(const float* o_part, const float* lse_part, int rows, int num_splits,
+                          float* o_lat, float* lse, hipStream_t stream);
+
+hipError_t launch_absorb(const __bf16* q_c, const __bf16* w_uk, __bf16* q_abs, int T, hipStream_t stream);
+
+hipError_t launch_up_proj(const float* o_lat, const __bf16* w_uv, __bf16* out, int T, hipStream_t stream);
+
+hipError_t launch_gather(const char* kv, int64_t num_pages, const int32_t* block_table, int max_pages,
+                         const int32_t* seqlens, int B, int max_len, __bf16* out, hipStream_t stream);
+
+}  // namespace mla

@@ -1,0 +1,116 @@
+// extern "C" entry points of libmla: host-side validation, launch-parameter
+// setup and kernel launches. Everything is enqueued on the caller's stream;
+// nothing here synchronises or allocates.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <string>
+
+#include "../../include/mla.h"
+#include "decode.hpp"
+#include "validate.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+mla_status report(const mla::Check& c) {
+  if (!c.ok()) g_last_error = c.detail;
+  return c.status;
+}
+
+mla_status report_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MLA_OK;
+  g_last_error = std::string(what) + ": " + hipGetErrorString(e);
+  return MLA_ERR_HIP;
+}
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(int status) {
+  switch (status) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_NULL: return "MLA_ERR_NULL";
+    case MLA_ERR_SHAPE: return "MLA_ERR_SHAPE";
+    case MLA_ERR_ALIGN: return "MLA_ERR_ALIGN";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP";
+    default: return "MLA_ERR_UNKNOWN";
+  }
+}
+
+const char* mla_last_error(void) { return g_last_error.c_str(); }
+
+size_t mla_decode_workspace_bytes(int B, int s_q, int H, int num_splits) {
+  return mla::workspace_bytes(B, s_q, H, num_splits);
+}
+
+int mla_recommended_splits(int B, int s_q, int max_len, int num_cus) {
+  return mla::recommended_splits(B, s_q, max_len, num_cus);
+}
+
+mla_status mla_absorb_q(const void* q_c, const void* w_uk, void* q_abs, int64_t T, int H, void* stream) {
+  const mla::Check c = mla::check_absorb(q_c, w_uk, q_abs, T, H);
+  if (!c.ok()) return report(c);
+  return report_hip(mla::launch_absorb(static_cast<const __bf16*>(q_c), static_cast<const __bf16*>(w_uk),
+                                       static_cast<__bf16*>(q_abs), (int)T, as_stream(stream)),
+                    "mla_absorb_q launch");
+}
+
+mla_status mla_decode_paged(const void* q_abs, const void* q_r, const void* kv_cache, int64_t num_pages,
+                            const int32_t* block_table, int max_pages, const int32_t* seqlens, int B, int s_q,
+                            int H, float softmax_scale, int num_splits, float* o_part, float* lse_part,
+                            void* stream) {
+  const mla::Check c = mla::check_decode(q_abs, q_r, kv_cache, num_pages, block_table, max_pages, seqlens, B, s_q, H,
+                                         softmax_scale, num_splits, o_part, lse_part);
+  if (!c.ok()) return report(c);
+  mla::DecodeParams p{};
+  p.q_abs = static_cast<const __bf16*>(q_abs);
+  p.q_r = static_cast<const __bf16*>(q_r);
+  p.kv = static_cast<const char*>(kv_cache);
+  p.num_pages = num_pages;
+  p.block_table = block_table;
+  p.max_pages = max_pages;
+  p.seqlens = seqlens;
+  p.B = B;
+  p.s_q = s_q;
+  p.num_splits = num_splits;
+  p.scale_log2 = softmax_scale * 1.44269504088896340736f;
+  p.o_part = o_part;
+  p.lse_part = lse_part;
+  p.items = B * s_q * num_splits;
+  p.items_per_xcd = (p.items + 7) / 8;
+  return report_hip(mla::launch_decode_paged(p, as_stream(stream)), "mla_decode_paged launch");
+}
+
+mla_status mla_combine_splits(const float* o_part, const float* lse_part, int B, int s_q, int H, int num_splits,
+                              float* o_lat, float* lse, void* stream) {
+  const mla::Check c = mla::check_combine(o_part, lse_part, B, s_q, H, num_splits, o_lat, lse);
+  if (!c.ok()) return report(c);
+  return report_hip(mla::launch_combine(o_part, lse_part, B * s_q * H, num_splits, o_lat, lse, as_stream(stream)),
+                    "mla_combine_splits launch");
+}
+
+mla_status mla_up_proj(const float* o_lat, const void* w_uv, void* out, int64_t T, int H, void* stream) {
+  const mla::Check c = mla::check_up_proj(o_lat, w_uv, out, T, H);
+  if (!c.ok()) return report(c);
+  return report_hip(mla::launch_up_proj(o_lat, static_cast<const __bf16*>(w_uv), static_cast<__bf16*>(out), (int)T,
+                                        as_stream(stream)),
+                    "mla_up_proj launch");
+}
+
+mla_status mla_debug_gather(const void* kv_cache, int64_t num_pages, const int32_t* block_table, int max_pages,
+                            const int32_t* seqlens, int B, int max_len, void* out, void* stream) {
+  const mla::Check c = mla::check_gather(kv_cache, num_pages, block_table, max_pages, seqlens, B, max_len, out);
+  if (!c.ok()) return report(c);
+  return report_hip(mla::launch_gather(static_cast<const char*>(kv_cache), num_pages, block_table, max_pages, seqlens,
+                                       B, max_len, static_cast<__bf16*>(out), as_stream(stream)),
+                    "mla_debug_gather launch");
+}
+
+}  // extern "C"

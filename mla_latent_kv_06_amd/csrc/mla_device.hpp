@@ -1,0 +1,57 @@
+// Device-side types and paged-cache addressing shared by the MLA kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace mla {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
+
+constexpr int kH = 128;
+constexpr int kDhc = 128;
+constexpr int kDc = 512;
+constexpr int kDr = 64;
+constexpr int kRowElems = 576;
+constexpr int kRowBytes = kRowElems * 2;      // 1152
+constexpr int kPage = 64;
+constexpr int kPageBytes = kPage * kRowBytes;  // 73728
+
+// Tokens of sequence b that the cache can hold: L clamped to [0, max_pages*64].
+__device__ __forceinline__ int clamp_len(int L, int max_pages) {
+  const int cap = max_pages * kPage;
+  return L < 0 ? 0 : (L > cap ? cap : L);
+}
+
+// Physical page of logical page p of sequence b, clamped into the cache so
+// that a bad table entry can never address memory outside it.
+__device__ __forceinline__ int64_t physical_page(const int32_t* __restrict__ block_table, int max_pages,
+                                                 int b, int p, int64_t num_pages) {
+  int64_t id = block_table[(int64_t)b * max_pages + p];
+  if (id < 0) id = 0;
+  if (id >= num_pages) id = num_pages - 1;
+  return id;
+}
+
+// Byte address of token t (logical) of sequence b in the paged cache.
+__device__ __forceinline__ const char* token_row(const char* __restrict__ kv, const int32_t* __restrict__ block_table,
+                                                 int max_pages, int b, int t, int64_t num_pages) {
+  const int64_t page = physical_page(block_table, max_pages, b, t >> 6, num_pages);
+  return kv + page * kPageBytes + (int64_t)(t & (kPage - 1)) * kRowBytes;
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4] = 7, lgkmcnt [11:8] = 15).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+}  // namespace mla

@@ -33,6 +33,11 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     return u32.view(np.float32).astype(np.float64)
 
 
+def bf16_bits(x) -> np.ndarray:
+    """Zero-copy uint16 view of a CPU torch bf16 tensor (its bit patterns)."""
+    return x.detach().cpu().contiguous().view(__import__("torch").int16).numpy().view(np.uint16)
+
+
 def as_f64(x) -> np.ndarray:
     """Exact float64 copy of a torch tensor or numpy array (bf16 via its bits)."""
     try:
@@ -76,6 +81,8 @@ def gather_rows(kv_cache: np.ndarray, block_table_row: np.ndarray, n_tokens: int
 
     Token t lives in physical page block_table_row[t // page] at row t % page.
     Only the entries the sequence needs are read; they must be valid page ids.
+    A uint16 cache is taken as bf16 bit patterns and decoded exactly after the
+    gather (so a large cache never has to exist in float64).
     """
     kv = np.asarray(kv_cache)
     page = kv.shape[1]
@@ -83,8 +90,10 @@ def gather_rows(kv_cache: np.ndarray, block_table_row: np.ndarray, n_tokens: int
     ids = np.asarray(block_table_row[:n_pages], dtype=np.int64)
     if n_pages and (ids.min() < 0 or ids.max() >= kv.shape[0]):
         raise ValueError("block table entry out of range")
-    rows = kv[ids].reshape(n_pages * page, kv.shape[2])
-    return rows[:n_tokens]
+    rows = kv[ids].reshape(n_pages * page, kv.shape[2])[:n_tokens]
+    if rows.dtype == np.uint16:
+        return bf16_bits_to_f64(rows)
+    return rows
 
 
 # --------------------------------------------------------------------------
@@ -93,8 +102,13 @@ def gather_rows(kv_cache: np.ndarray, block_table_row: np.ndarray, n_tokens: int
 
 
 def absorb(q_c: np.ndarray, w_uk: np.ndarray) -> np.ndarray:
-    """q_abs[..., h, c] = sum_d q_c[..., h, d] * W_UK[h, d, c]."""
-    return np.einsum("...hd,hdc->...hc", np.asarray(q_c, np.float64), np.asarray(w_uk, np.float64))
+    """q_abs[..., h, c] = sum_d q_c[..., h, d] * W_UK[h, d, c] (one matmul per head)."""
+    q = np.asarray(q_c, np.float64)
+    w = np.asarray(w_uk, np.float64)
+    lead = q.shape[:-2]
+    qh = q.reshape(-1, q.shape[-2], q.shape[-1]).transpose(1, 0, 2)   # [H, T, d]
+    out = np.matmul(qh, w)                                             # [H, T, c]
+    return out.transpose(1, 0, 2).reshape(lead + (w.shape[0], w.shape[2]))
 
 
 def visible_len(L_b: int, s_q: int, i: int) -> int:
@@ -193,8 +207,13 @@ def decode_naive(q_c, q_r, kv_cache, block_table, seqlens, w_uk, w_uv, scale: fl
 
 
 def up_proj(o_lat, w_uv) -> np.ndarray:
-    """out[..., h, d] = sum_c o_lat[..., h, c] * W_UV[h, d, c]."""
-    return np.einsum("...hc,hdc->...hd", np.asarray(o_lat, np.float64), np.asarray(w_uv, np.float64))
+    """out[..., h, d] = sum_c o_lat[..., h, c] * W_UV[h, d, c] (one matmul per head)."""
+    o = np.asarray(o_lat, np.float64)
+    w = np.asarray(w_uv, np.float64)
+    lead = o.shape[:-2]
+    oh = o.reshape(-1, o.shape[-2], o.shape[-1]).transpose(1, 0, 2)   # [H, T, c]
+    out = np.matmul(oh, w.transpose(0, 2, 1))                          # [H, T, d]
+    return out.transpose(1, 0, 2).reshape(lead + (w.shape[0], w.shape[1]))
 
 
 # --------------------------------------------------------------------------

@@ -1,0 +1,92 @@
+"""The C ABI on the CPU: the library loads, exports what include/mla.h
+declares, the header is valid C99, and host-side validation rejects bad
+arguments before any launch (these calls never reach the GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from mla_latent_kv_06_amd import _lib
+    return _lib.LIB
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert len(names) == 9, names
+    out = subprocess.run(["nm", "-D", "--defined-only", os.path.join(ROOT, "mla_latent_kv_06_amd", "libmla.so")],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (mla_[a-z_]+)\b", out))
+    assert set(names) <= exported, set(names) - exported
+    for n in names:
+        assert getattr(lib, n) is not None
+
+
+def test_header_is_c99():
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-x", "c", HEADER], check=True)
+
+
+def test_status_strings(lib):
+    assert lib.mla_status_string(0) == b"MLA_OK"
+    assert lib.mla_status_string(4) == b"MLA_ERR_WORKSPACE"
+    assert lib.mla_status_string(99) == b"MLA_ERR_UNKNOWN"
+
+
+A = 1 << 20  # an aligned, never-dereferenced fake address
+MIS = A + 8
+
+
+def _decode(lib, **kw):
+    a = dict(q_abs=A, q_r=A, kv=A, num_pages=10, bt=A, max_pages=4, seqlens=A, B=2, s_q=1, H=128,
+             scale=0.07, S=2, o_part=A, lse_part=A)
+    a.update(kw)
+    return lib.mla_decode_paged(a["q_abs"], a["q_r"], a["kv"], a["num_pages"], a["bt"], a["max_pages"],
+                                a["seqlens"], a["B"], a["s_q"], a["H"], a["scale"], a["S"], a["o_part"],
+                                a["lse_part"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q_abs=None), 1), (dict(lse_part=None), 1), (dict(kv=MIS), 3), (dict(o_part=MIS), 3),
+    (dict(H=64), 2), (dict(B=0), 2), (dict(s_q=0), 2), (dict(s_q=5000), 2), (dict(S=0), 2),
+    (dict(S=5), 2), (dict(max_pages=0), 2), (dict(num_pages=0), 2), (dict(scale=float("nan")), 2),
+    (dict(scale=float("inf")), 2),
+])
+def test_decode_validation(lib, kw, status):
+    assert _decode(lib, **kw) == status
+    assert lib.mla_last_error() != b""
+
+
+def test_other_entry_validation(lib):
+    assert lib.mla_absorb_q(None, A, A, 4, 128, None) == 1
+    assert lib.mla_absorb_q(A, A, A, 0, 128, None) == 2
+    assert lib.mla_absorb_q(A, MIS, A, 4, 128, None) == 3
+    assert lib.mla_up_proj(A, A, A, 4, 127, None) == 2
+    assert lib.mla_combine_splits(A, A, 1, 1, 128, 0, A, A, None) == 2
+    assert lib.mla_combine_splits(A, A, 1, 1, 128, 2, MIS, A, None) == 3
+    assert lib.mla_debug_gather(A, 3, A, 1, A, 1, 0, A, None) == 2
+
+
+def test_host_helpers(lib):
+    assert lib.mla_decode_workspace_bytes(16, 1, 128, 16) == 16 * 128 * 16 * 513 * 4
+    assert lib.mla_decode_workspace_bytes(0, 1, 128, 16) == 0
+    # fills ~one work item per CU but keeps splits >= 8 pages
+    assert lib.mla_recommended_splits(16, 1, 65536, 256) == 16
+    assert lib.mla_recommended_splits(1, 1, 2048, 256) == 4
+    assert lib.mla_recommended_splits(4, 256, 16640, 256) == 1
+    assert lib.mla_recommended_splits(1, 1, 0, 256) == 1
+    for B, L in [(3, 100), (64, 32768), (1, 10 ** 6)]:
+        s = lib.mla_recommended_splits(B, 1, L, 256)
+        assert 1 <= s <= -(-L // 64)

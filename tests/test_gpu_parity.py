@@ -1,0 +1,332 @@
+"""GPU parity of every C-ABI entry point against the fp64 oracle.
+
+Each function is judged on exactly the inputs it received (the GPU's own bf16
+q_abs for the decode, its own fp32 o_lat for the up-projection), so a bar
+measures that function's own error. Large workloads are checked on sampled
+rows that the oracle computes one by one. Integer work (the paged gather) and
+placement invariance are bit-exact.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from mla_inputs import CONFIGS, Config, make_inputs, make_structure
+from tests._bars import assert_bar, assert_lse
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+SCALE = 1.0 / math.sqrt(192)
+
+
+@pytest.fixture(scope="module")
+def M():
+    import mla_latent_kv_06_amd as mod
+    return mod
+
+
+def _say(msg):
+    print(f"[gpu] {msg}", flush=True)
+
+
+def _to(inp):
+    d = {k: getattr(inp, k).to(DEV) for k in ("q_c", "q_r", "w_uk", "kv_cache", "w_uv", "block_table", "seqlens")}
+    return d
+
+
+def _random_case(seqlens, s_q, seed, pool_extra=5, nan_tail=False):
+    """Small random inputs with real dims, arbitrary lengths and a permuted pool."""
+    g = torch.Generator().manual_seed(seed)
+    need = [-(-int(L) // 64) for L in seqlens]
+    pool = sum(need) + pool_extra
+    order = torch.randperm(pool, generator=g)
+    maxp = max(max(need), 1) + 1
+    bt = torch.full((len(seqlens), maxp), -1, dtype=torch.int32)
+    off = 0
+    for b, n in enumerate(need):
+        bt[b, :n] = order[off:off + n].to(torch.int32)
+        off += n
+    B = len(seqlens)
+    q_abs = torch.randn((B, s_q, 128, 512), generator=g).to(torch.bfloat16)
+    q_r = torch.randn((B, s_q, 128, 64), generator=g).to(torch.bfloat16)
+    kv = torch.randn((pool, 64, 576), generator=g).to(torch.bfloat16)
+    if nan_tail:
+        for b, L in enumerate(seqlens):
+            if L % 64:
+                kv[int(bt[b, L // 64]), L % 64:, :] = float("nan")
+    return q_abs, q_r, kv, bt, torch.tensor(seqlens, dtype=torch.int32)
+
+
+def _decode_check(M, q_abs, q_r, kv, bt, sl, num_splits, what, check_parts=True):
+    _say(f"{what}: B={q_abs.shape[0]} s_q={q_abs.shape[1]} lens={sl.tolist()[:6]} splits={num_splits}")
+    o_part, lse_part = M.mla_decode_paged(q_abs.to(DEV), q_r.to(DEV), kv.to(DEV), bt.to(DEV), sl.to(DEV),
+                                          num_splits, SCALE)
+    o_lat, lse = M.mla_combine_splits(o_part, lse_part)
+    torch.cuda.synchronize()
+    kvb = O.bf16_bits(kv)
+    ref_o, ref_l = O.decode_absorbed(O.as_f64(q_abs), O.as_f64(q_r), kvb, bt.numpy(), sl.numpy(), SCALE)
+    assert_bar(o_lat.cpu().numpy(), ref_o, f"{what} o_lat")
+    assert_lse(lse.cpu().numpy(), ref_l, f"{what} lse")
+    if check_parts:
+        rp_o, rp_l = O.decode_split(O.as_f64(q_abs), O.as_f64(q_r), kvb, bt.numpy(), sl.numpy(), SCALE, num_splits)
+        assert_lse(lse_part.cpu().numpy(), rp_l, f"{what} lse_part")
+        assert_bar(o_part.cpu().numpy(), rp_o, f"{what} o_part")
+    return o_lat, lse
+
+
+# ---------------------------------------------------------------------------
+# paged gather: bit-exact
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cfg", ["single", "uniform"])
+def test_gather_bit_exact(M, cfg):
+    inp = make_inputs(cfg)
+    max_len = int(inp.seqlens.max()) + 17
+    _say(f"gather {cfg} max_len={max_len}")
+    out = M.mla_debug_gather(inp.kv_cache.to(DEV), inp.block_table.to(DEV), inp.seqlens.to(DEV), max_len)
+    torch.cuda.synchronize()
+    got = out.cpu().view(torch.int16).numpy()
+    bits = O.bf16_bits(inp.kv_cache)
+    for b in range(inp.cfg.B):
+        L = int(inp.seqlens[b])
+        ref = np.zeros((max_len, 576), np.uint16)
+        ref[:L] = bits[inp.block_table[b, :(L + 63) // 64].numpy().astype(np.int64)].reshape(-1, 576)[:L]
+        assert np.array_equal(got[b].view(np.uint16), ref), f"sequence {b}"
+
+
+def test_gather_ragged_lengths_bit_exact(M):
+    lens = [0, 1, 63, 64, 65, 127, 129, 300]
+    _, _, kv, bt, sl = _random_case(lens, 1, seed=5)
+    out = M.mla_debug_gather(kv.to(DEV), bt.to(DEV), sl.to(DEV), 320)
+    torch.cuda.synchronize()
+    got = out.cpu().view(torch.int16).numpy().view(np.uint16)
+    bits = O.bf16_bits(kv)
+    for b, L in enumerate(lens):
+        ref = np.zeros((320, 576), np.uint16)
+        if L:
+            ref[:L] = bits[bt[b, :(L + 63) // 64].numpy().astype(np.int64)].reshape(-1, 576)[:L]
+        assert np.array_equal(got[b], ref), f"L={L}"
+
+
+# ---------------------------------------------------------------------------
+# absorb and up-projection
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T", [1, 16, 45, 1024])
+def test_absorb_parity(M, T):
+    g = torch.Generator().manual_seed(100 + T)
+    q_c = torch.randn((T, 128, 128), generator=g).to(torch.bfloat16)
+    w_uk = (torch.randn((128, 128, 512), generator=g) / math.sqrt(512)).to(torch.bfloat16)
+    _say(f"absorb T={T}")
+    q_abs = M.mla_absorb_q(q_c.to(DEV), w_uk.to(DEV))
+    torch.cuda.synchronize()
+    ref = O.absorb(O.as_f64(q_c), O.as_f64(w_uk))
+    assert_bar(O.as_f64(q_abs.cpu()), ref, f"absorb T={T}")
+
+
+@pytest.mark.parametrize("T", [1, 16, 45, 1024])
+def test_up_proj_parity(M, T):
+    g = torch.Generator().manual_seed(200 + T)
+    o_lat = torch.randn((T, 128, 512), generator=g, dtype=torch.float32)
+    w_uv = (torch.randn((128, 128, 512), generator=g) / math.sqrt(512)).to(torch.bfloat16)
+    _say(f"up_proj T={T}")
+    out = M.mla_up_proj(o_lat.to(DEV), w_uv.to(DEV))
+    torch.cuda.synchronize()
+    ref = O.up_proj(o_lat.double().numpy(), O.as_f64(w_uv))
+    assert_bar(O.as_f64(out.cpu()), ref, f"up_proj T={T}")
+
+
+# ---------------------------------------------------------------------------
+# combine
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("S", [1, 3, 16, 70])
+def test_combine_parity(M, S):
+    g = torch.Generator().manual_seed(300 + S)
+    B, s_q = 3, 2
+    o_part = torch.randn((B, s_q, 128, S, 512), generator=g)
+    lse_part = torch.randn((B, s_q, 128, S), generator=g) * 5
+    if S > 1:
+        lse_part[0, 0, :, -1] = float("-inf")   # an empty split
+    lse_part[2, 1, 5, :] = float("-inf")        # a row with no keys at all
+    o_part[2, 1, 5] = 0
+    _say(f"combine S={S}")
+    o_lat, lse = M.mla_combine_splits(o_part.to(DEV), lse_part.to(DEV))
+    torch.cuda.synchronize()
+    ref_o, ref_l = O.combine(o_part.double().numpy(), lse_part.double().numpy())
+    assert_bar(o_lat.cpu().numpy(), ref_o, f"combine S={S}")
+    assert_lse(lse.cpu().numpy(), ref_l, f"combine S={S}")
+
+
+# ---------------------------------------------------------------------------
+# decode (+ combine): workloads, edge lengths, causal chunks, split plans
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("num_splits", [1, 2, 7, 32])
+def test_decode_single_config(M, num_splits):
+    inp = make_inputs("single")
+    d = _to(inp)
+    q_abs = M.mla_absorb_q(d["q_c"], d["w_uk"]).cpu()
+    _decode_check(M, q_abs, inp.q_r, inp.kv_cache, inp.block_table, inp.seqlens, num_splits, "single")
+
+
+def test_decode_uniform_config(M):
+    inp = make_inputs("uniform")
+    d = _to(inp)
+    S = M.mla_recommended_splits(16, 1, 4096)
+    q_abs = M.mla_absorb_q(d["q_c"], d["w_uk"]).cpu()
+    _decode_check(M, q_abs, inp.q_r, inp.kv_cache, inp.block_table, inp.seqlens, S, "uniform", check_parts=False)
+
+
+@pytest.mark.parametrize("lens,s_q,S", [
+    ([1, 31, 32, 33, 63], 1, 1),
+    ([64, 65, 127, 129, 2047], 1, 3),
+    ([5, 300, 1000], 1, 17),      # more splits than pages of short rows: empty splits
+    ([300, 77], 2, 2),
+    ([100, 400], 37, 3),          # causal chunk
+])
+def test_decode_edge_lengths(M, lens, s_q, S):
+    q_abs, q_r, kv, bt, sl = _random_case(lens, s_q, seed=sum(lens) + s_q)
+    _decode_check(M, q_abs, q_r, kv, bt, sl, S, f"edge lens={lens} s_q={s_q}")
+
+
+def test_decode_zero_length_rows(M):
+    q_abs, q_r, kv, bt, sl = _random_case([0, 70], 1, seed=9)
+    o_lat, lse = _decode_check(M, q_abs, q_r, kv, bt, sl, 2, "zero length", check_parts=True)
+    assert (o_lat[0].cpu() == 0).all() and torch.isneginf(lse[0].cpu()).all()
+
+
+def test_decode_nan_in_unused_tail_rows(M):
+    q_abs, q_r, kv, bt, sl = _random_case([100, 33, 130], 1, seed=10, nan_tail=True)
+    _decode_check(M, q_abs, q_r, kv, bt, sl, 2, "NaN past the end")
+
+
+def test_decode_score_jump_triggers_exact_rescan(M):
+    """A key scoring 2^208 above the first tile's reference forces the rescan path."""
+    L, tstar = 2048, 1500
+    g = torch.Generator().manual_seed(11)
+    kv = torch.randn((32, 64, 576), generator=g).to(torch.bfloat16)
+    kv[..., 512:] = 0
+    kv.view(-1, 576)[tstar, 512] = 1.0
+    q_abs = torch.zeros((1, 1, 128, 512), dtype=torch.bfloat16)
+    q_r = torch.zeros((1, 1, 128, 64), dtype=torch.bfloat16)
+    q_r[..., 0] = 2000.0
+    bt = torch.arange(32, dtype=torch.int32)[None]
+    sl = torch.tensor([L], dtype=torch.int32)
+    o_lat, lse = _decode_check(M, q_abs, q_r, kv, bt, sl, 1, "rescan one-hot")
+    row = kv.view(-1, 576)[tstar, :512].float()
+    assert torch.equal(o_lat[0, 0].cpu(), row.expand(128, 512)), "one-hot row must be reproduced exactly"
+
+
+def test_decode_rising_scores_within_headroom(M):
+    """Scores that climb by ~40 (log2) over the sequence stay on the single-pass path."""
+    L = 1024
+    g = torch.Generator().manual_seed(12)
+    kv = torch.randn((16, 64, 576), generator=g).to(torch.bfloat16)
+    ramp = torch.linspace(0, 1, L)
+    kv.view(-1, 576)[:L, 512] = ramp.to(torch.bfloat16)
+    kv.view(-1, 576)[:L, 513:] = 0
+    q_abs = (torch.randn((1, 1, 128, 512), generator=g) * 0.1).to(torch.bfloat16)
+    q_r = torch.zeros((1, 1, 128, 64), dtype=torch.bfloat16)
+    q_r[..., 0] = 384.0
+    bt = torch.randperm(16, generator=g).to(torch.int32)[None]
+    _decode_check(M, q_abs, q_r, kv, bt, torch.tensor([L], dtype=torch.int32), 1, "rising scores")
+
+
+# ---------------------------------------------------------------------------
+# bit-exact invariances
+# ---------------------------------------------------------------------------
+
+def test_page_placement_and_batch_independence_bit_exact(M):
+    q_abs, q_r, kv, bt, sl = _random_case([700, 64, 1500], 1, seed=13)
+    S = 4
+    o1, l1 = M.mla_decode_paged(q_abs.to(DEV), q_r.to(DEV), kv.to(DEV), bt.to(DEV), sl.to(DEV), S, SCALE)
+    # same logical rows at other physical pages
+    perm = torch.randperm(kv.shape[0], generator=torch.Generator().manual_seed(1))
+    inv = torch.argsort(perm)
+    kv2 = kv[perm]
+    bt2 = torch.where(bt >= 0, inv[bt.clamp(min=0).long()].to(torch.int32), bt)
+    o2, l2 = M.mla_decode_paged(q_abs.to(DEV), q_r.to(DEV), kv2.to(DEV), bt2.to(DEV), sl.to(DEV), S, SCALE)
+    # sequence 2 alone
+    o3, l3 = M.mla_decode_paged(q_abs[2:].contiguous().to(DEV), q_r[2:].contiguous().to(DEV), kv.to(DEV),
+                                bt[2:].contiguous().to(DEV), sl[2:].contiguous().to(DEV), S, SCALE)
+    # and a rerun: deterministic
+    o4, l4 = M.mla_decode_paged(q_abs.to(DEV), q_r.to(DEV), kv.to(DEV), bt.to(DEV), sl.to(DEV), S, SCALE)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2), "physical placement changed the result"
+    assert torch.equal(o1[2:], o3) and torch.equal(l1[2:], l3), "batch neighbours changed the result"
+    assert torch.equal(o1, o4) and torch.equal(l1, l4), "rerun is not bit-identical"
+
+
+# ---------------------------------------------------------------------------
+# whole chain on the teardown page's size: vs the naive (path A) oracle
+# ---------------------------------------------------------------------------
+
+def test_chain_single_vs_naive(M):
+    inp = make_inputs("single")
+    d = _to(inp)
+    _say("chain single: absorb -> decode -> combine -> up_proj vs naive path")
+    r = M.decode_layer(d["q_c"], d["q_r"], d["kv_cache"], d["block_table"], d["seqlens"], d["w_uk"], d["w_uv"],
+                       num_splits=4)
+    torch.cuda.synchronize()
+    f = {k: O.as_f64(getattr(inp, k)) for k in ("q_c", "q_r", "w_uk", "w_uv")}
+    ref_out, ref_lse = O.decode_naive(f["q_c"], f["q_r"], O.bf16_bits(inp.kv_cache), inp.block_table.numpy(),
+                                      inp.seqlens.numpy(), f["w_uk"], f["w_uv"], SCALE)
+    # per-function bars on each function's own inputs
+    assert_bar(O.as_f64(r["q_abs"].cpu()), O.absorb(f["q_c"], f["w_uk"]), "chain absorb")
+    assert_bar(O.as_f64(r["out"].cpu()), O.up_proj(r["o_lat"].cpu().double().numpy(), f["w_uv"]), "chain up_proj")
+    # end to end: the bf16 rounding of q_abs and P compounds; max bar holds, mean reported
+    mx, l1 = assert_bar(O.as_f64(r["out"].cpu()), ref_out, "chain end-to-end", l1_rel=5e-3)
+    assert_lse(r["lse"].cpu().numpy(), ref_lse, "chain lse")
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads on sampled rows, in the launch configuration the bench uses
+# ---------------------------------------------------------------------------
+
+def _sampled_check(M, inp, picks, what, num_splits=None):
+    d = _to(inp)
+    B, s_q = inp.cfg.B, inp.cfg.s_q
+    S = num_splits or M.mla_recommended_splits(B, s_q, int(inp.seqlens.max()))
+    _say(f"{what}: B={B} s_q={s_q} pages={inp.kv_cache.shape[0]} splits={S} rows={len(picks)}")
+    r = M.decode_layer(d["q_c"], d["q_r"], d["kv_cache"], d["block_table"], d["seqlens"], d["w_uk"], d["w_uv"],
+                       num_splits=S)
+    torch.cuda.synchronize()
+    q_abs = r["q_abs"].cpu()
+    ro, rl = O.decode_rows(O.as_f64(q_abs), O.as_f64(inp.q_r), O.bf16_bits(inp.kv_cache), inp.block_table.numpy(),
+                           inp.seqlens.numpy(), SCALE, picks)
+    o_lat = r["o_lat"].cpu()
+    lse = r["lse"].cpu()
+    go = np.stack([o_lat[b, i, h].double().numpy() for b, i, h in picks])
+    gl = np.array([float(lse[b, i, h]) for b, i, h in picks])
+    assert_bar(go, ro, f"{what} o_lat rows")
+    assert_lse(gl, rl, f"{what} lse rows")
+    # absorb and up-projection on their own inputs, full tensors
+    assert_bar(O.as_f64(q_abs), O.absorb(O.as_f64(inp.q_c), O.as_f64(inp.w_uk)), f"{what} absorb")
+    sel = slice(0, min(B, 4))
+    assert_bar(O.as_f64(r["out"][sel].cpu()), O.up_proj(r["o_lat"][sel].cpu().double().numpy(), O.as_f64(inp.w_uv)),
+               f"{what} up_proj")
+
+
+def test_ragged_config_sampled(M):
+    inp = make_inputs("ragged")
+    rng = np.random.default_rng(0)
+    picks = [(b, 0, int(h)) for b in range(inp.cfg.B) for h in rng.choice(128, 3, replace=False)]
+    _sampled_check(M, inp, picks, "ragged")
+
+
+def test_long_config_sampled(M):
+    inp = make_inputs("long")
+    rng = np.random.default_rng(1)
+    picks = [(b, 0, int(h)) for b in range(inp.cfg.B) for h in rng.choice(128, 2, replace=False)]
+    _sampled_check(M, inp, picks, "long 64K")
+
+
+def test_prefill_config_sampled(M):
+    inp = make_inputs("prefill")
+    rng = np.random.default_rng(2)
+    picks = [(b, i, int(rng.integers(128))) for b in range(inp.cfg.B) for i in (0, 1, 100, 254, 255)]
+    _sampled_check(M, inp, picks, "prefill 256 over 16K")

@@ -366,3 +366,14 @@ def test_decode_rows_matches_full():
         # one-row and many-row BLAS products round differently in the last ulp
         np.testing.assert_allclose(ro[k], o[b, i, h], rtol=1e-13, atol=1e-15)
         np.testing.assert_allclose(rl[k], l[b, i, h], rtol=1e-14)
+
+
+def test_gather_of_bf16_bits_decodes_exactly():
+    g = torch.Generator().manual_seed(3)
+    kv = torch.randn((5, 64, 576), generator=g).to(torch.bfloat16)
+    bt = np.array([3, 0, 4], dtype=np.int32)
+    rows_bits = O.gather_rows(O.bf16_bits(kv), bt, 150)
+    rows_f64 = O.gather_rows(O.as_f64(kv), bt, 150)
+    assert rows_bits.dtype == np.float64 and np.array_equal(rows_bits, rows_f64)
+    ref = kv.to(torch.float64)[[3, 0, 4]].reshape(-1, 576)[:150].numpy()
+    assert np.array_equal(rows_bits, ref)
