@@ -1,0 +1,247 @@
+"""Benchmark: absorbed MLA decode over a paged latent cache on one MI355X.
+
+A step is one pass of the whole hot path for one layer: mla_absorb_q ->
+mla_decode_paged -> mla_combine_splits -> mla_up_proj. The default workload is
+B=16 sequences of 65536 cached tokens with 60 layers of latent cache resident
+(72.5 GB); step k uses layer k mod 60, so every step reads its 1.2 GB of cache
+from HBM (it cannot be served by the 256 MB last-level cache).
+
+Prints one JSON line (rank 0):
+  value            whole-step throughput, algorithmic TFLOP/s
+  roofline         the dominant kernel (mla_decode_paged) against HBM
+  cpu_baseline     the fp64 CPU oracle on a bounded sample of the workload
+plus effective KV GB/s and per-kernel times.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+FLOP_PER_PAIR = 128 * 2 * (576 + 512)  # all heads, one (query, key) pair: QK over 576 + PV over 512
+KV_BYTES_PER_TOKEN = 576 * 2
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_paged_long_hbm_traffic.json")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=60)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="long", choices=["single", "uniform", "ragged", "long", "prefill"])
+    p.add_argument("--layers", type=int, default=0, help="resident cache layers (0: workload default)")
+    p.add_argument("--splits", type=int, default=0, help="num_splits (0: library recommendation)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle time for the baseline")
+    return p.parse_args()
+
+
+def visible_pairs(seqlens, s_q):
+    """(query, key) pairs the causal rule admits: query i sees L - s_q + i + 1 keys."""
+    tot = 0
+    for L in seqlens:
+        for i in range(s_q):
+            tot += max(L - s_q + i + 1, 0)
+    return tot
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    for f in ("decode.hip", "mla_device.hpp", "decode.hpp"):
+        with open(os.path.join(ROOT, "mla_latent_kv_06_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, splits):
+    """HBM bytes per decode launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source and launch configuration."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_digest") != kernel_source_digest() or t.get("workload") != workload or t.get("splits") != splits:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp_cpu, q_abs_cpu, target_s):
+    """fp64 oracle (absorbed path) on whole sequences of the workload until ~target_s."""
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    kvb = O.bf16_bits(inp_cpu["kv_cache"])
+    bt = inp_cpu["block_table"].numpy()
+    sl = inp_cpu["seqlens"].numpy()
+    qa = O.as_f64(q_abs_cpu)
+    qr = O.as_f64(inp_cpu["q_r"])
+    s_q = qa.shape[1]
+    scale = 1.0 / math.sqrt(192)
+    t0 = time.perf_counter()
+    done, flop = 0, 0.0
+    while time.perf_counter() - t0 < target_s:
+        b = done % qa.shape[0]
+        O.decode_absorbed(qa[b:b + 1], qr[b:b + 1], kvb, bt[b:b + 1], sl[b:b + 1], scale)
+        flop += visible_pairs([int(sl[b])], s_q) * FLOP_PER_PAIR
+        done += 1
+    dt = time.perf_counter() - t0
+    return {
+        "value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+        "sample": f"fp64 numpy absorbed path (gather, scores, softmax, P.c_KV) over {done} whole sequences "
+                  f"(cycling through the {qa.shape[0]} of layer 0), all 128 heads, {dt:.1f} s; "
+                  f"host logical CPUs {os.cpu_count()}, "
+                  f"affinity {len(os.sched_getaffinity(0))}",
+        "seconds": dt,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); the split-KV decode is measured on one "
+              "MI355X and multi-GPU sharding is not built", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mla_latent_kv_06_amd as M
+    from mla_inputs import CONFIGS, make_inputs, make_structure, make_cache_on_device
+
+    cfg = CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---- inputs resident in HBM before timing
+    inp = make_inputs(cfg, seed=42, with_cache=False)
+    st0 = make_structure(cfg, seed=42)
+    layer_bytes = st0.num_pages * 64 * 576 * 2
+    layers = args.layers or max(cfg.layers, math.ceil(2 * 2**30 / layer_bytes))
+    print(f"[bench] workload={cfg.name} B={cfg.B} s_q={cfg.s_q} layers={layers} "
+          f"cache={layers * layer_bytes / 1e9:.1f} GB", file=sys.stderr, flush=True)
+    kv = make_cache_on_device(st0.num_pages, layers, seed=1234, device=dev)
+    tables = torch.stack([make_structure(cfg, seed=42 + l).block_table for l in range(layers)]).to(dev)
+    seqlens = st0.seqlens.to(dev)
+    q_c, q_r = inp.q_c.to(dev), inp.q_r.to(dev)
+    w_uk, w_uv = inp.w_uk.to(dev), inp.w_uv.to(dev)
+    lens = [int(x) for x in st0.seqlens]
+    S = args.splits or M.mla_recommended_splits(cfg.B, cfg.s_q, max(lens))
+    B, s_q = cfg.B, cfg.s_q
+    T = B * s_q
+
+    # preallocated outputs: the timed loop allocates nothing
+    q_abs = torch.empty((B, s_q, 128, 512), dtype=torch.bfloat16, device=dev)
+    o_part = torch.empty((B, s_q, 128, S, 512), dtype=torch.float32, device=dev)
+    lse_part = torch.empty((B, s_q, 128, S), dtype=torch.float32, device=dev)
+    o_lat = torch.empty((B, s_q, 128, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, s_q, 128), dtype=torch.float32, device=dev)
+    out = torch.empty((B, s_q, 128, 128), dtype=torch.bfloat16, device=dev)
+
+    stream = torch.cuda.current_stream()
+    nev = 5
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+
+    def step(k, ev=None):
+        layer = k % layers
+        if ev: ev[0].record(stream)
+        M.mla_absorb_q(q_c, w_uk, q_abs)
+        if ev: ev[1].record(stream)
+        M.mla_decode_paged(q_abs, q_r, kv[layer], tables[layer], seqlens, S, o_part=o_part, lse_part=lse_part)
+        if ev: ev[2].record(stream)
+        M.mla_combine_splits(o_part, lse_part, o_lat, lse)
+        if ev: ev[3].record(stream)
+        M.mla_up_proj(o_lat, w_uv, out)
+        if ev: ev[4].record(stream)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup {args.warmup} done; timing {args.steps} steps (splits={S})", file=sys.stderr, flush=True)
+
+    # wall-clock over exactly K steps (no events inside, so nothing is added between kernels)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(args.warmup + k)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # the same K steps again with HIP events around each kernel (same stream)
+    for k in range(args.steps):
+        step(args.warmup + k, events[k])
+    torch.cuda.synchronize()
+    per = [[events[k][j].elapsed_time(events[k][j + 1]) for k in range(args.steps)] for j in range(nev - 1)]
+    avg = [sum(x) / len(x) for x in per]
+    names = ["mla_absorb_q", "mla_decode_paged", "mla_combine_splits", "mla_up_proj"]
+
+    pairs = visible_pairs(lens, s_q)
+    flop_attn = pairs * FLOP_PER_PAIR
+    flop_proj = 2 * (2 * T * 128 * 128 * 512)
+    flop_step = flop_attn + flop_proj
+    kv_bytes = sum(lens) * KV_BYTES_PER_TOKEN
+    q_bytes = T * 128 * 576 * 2
+    olat_bytes = T * 128 * (512 + 1) * 4
+    decode_bytes = kv_bytes + q_bytes + olat_bytes        # algorithmic bytes of the attention itself
+    step_bytes = decode_bytes + 2 * (128 * 128 * 512 * 2) + T * 128 * 128 * 2 * 2
+    ms_step = wall / args.steps * 1e3
+    dec_ms = avg[1]
+    achieved_gbs = decode_bytes / (dec_ms * 1e-3) / 1e9
+    t_roof = max(flop_step / (MFMA_BF16_PEAK_TFLOPS * 1e12), step_bytes / (HBM_PEAK_GBS * 1e9))
+    traffic = measured_traffic(cfg.name, S)
+
+    result = {
+        "metric": "MLA decode TFLOP/s + effective KV GB/s, B=16 ctx 64K, % of MI355X roofline",
+        "value": round(flop_step / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 cache and activations, N(0,1/512) weights)",
+        "config": {"workload": f"{cfg.name}: {cfg.notes}", "B": B, "s_q": s_q, "ctx": max(lens),
+                   "heads": 128, "d_c": 512, "d_R": 64, "page": 64, "num_splits": S,
+                   "resident_layers": layers, "cache_gb": round(layers * layer_bytes / 1e9, 2)},
+        "kv_gbps": round(kv_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "step_roofline_frac": round(t_roof / (ms_step * 1e-3), 4),
+        "kernels_ms": {n: round(a, 4) for n, a in zip(names, avg)},
+        "roofline": {
+            "kernel": "mla_decode_paged",
+            "bound": "hbm",
+            "achieved": round(achieved_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": decode_bytes,
+            "decode_tflops": round(flop_attn / (dec_ms * 1e-3) / 1e12, 1),
+            "mfma_frac": round(flop_attn / (dec_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (fp64 oracle on host cores)", file=sys.stderr, flush=True)
+        layer0 = {"kv_cache": kv[0].cpu(), "block_table": tables[0].cpu(), "seqlens": st0.seqlens,
+                  "q_r": inp.q_r}
+        M.mla_absorb_q(q_c, w_uk, q_abs)
+        torch.cuda.synchronize()
+        result["cpu_baseline"] = cpu_baseline(layer0, q_abs.cpu(), args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -6,31 +6,34 @@
 // operator-teardown page, section 4; split scan of the K3 time-share study,
 // "Inside the blocks").
 //
-// Layout of the work:
-//   * 4 waves; wave w owns heads 32w..32w+31.
-//   * the cache streams through a ring of 4 LDS stages of 32 tokens (36 KiB
-//     each, half a page); three stages are in flight while one is consumed.
-//     Stages are filled with 16-byte direct-to-LDS loads, 9 per thread.
-//   * S^T = K . Q^T on v_mfma_f32_32x32x16_bf16: A = 32 cache rows x 16 dims
-//     read from LDS, B = the wave's 32 queries (held in 144 VGPRs for all
-//     576 dims). Each lane ends up owning one head and 16 of the tile's
-//     tokens; its partner lane (lane ^ 32) owns the other 16.
+// Work split inside the workgroup (4 waves, one per SIMD):
+//   * QK: wave w owns heads 32w..32w+31. S^T = K . Q^T on
+//     v_mfma_f32_32x32x16_bf16 with A = 32 cache rows x 16 dims read from LDS
+//     and B = the wave's queries, held in 144 VGPRs for all 576 dims. A lane
+//     ends up owning one head and 16 of the tile's 32 tokens.
 //   * softmax in the exp2 domain against a per-head reference max taken from
 //     the split's first tile; P = exp2(x - ref) may grow to 2^64, which bf16
 //     and the fp32 accumulators hold without loss, so the accumulator is
 //     never rescaled. Each lane also tracks the true running max; if any
 //     score exceeded its reference by more than 64, the workgroup rescans
-//     the split once with the exact max as reference (only adversarial
-//     score ranges trigger it; a second rescan is impossible).
-//   * O^T += V^T . P^T on the same MFMA: the S accumulator registers are
-//     already the P^T operand layout, and V^T is read from the row-major
-//     tile with ds_read_b64_tr_b16 (each 16-lane group turns a 4-row x
-//     16-column block into 4 consecutive tokens per lane). O^T (512 x 32
-//     per wave) lives in the accumulation registers.
+//     the split once with the exact max as reference.
+//   * PV: wave w owns latent columns 128w..128w+127 for ALL heads. Every
+//     wave publishes its P^T tile (bf16, already in MFMA operand layout) to
+//     LDS, and each wave reads V^T only for its own columns with
+//     ds_read_b64_tr_b16. This reads each V element from LDS once instead of
+//     once per head group (transposed reads run at about half the rate of
+//     plain 16-byte reads).
+//   * software pipeline: iteration i runs QK(i), then softmax(i) interleaved
+//     with PV(i-1), so the softmax VALU work overlaps matrix-core work and
+//     P(i) is published in a double-buffered slot that the next iteration's
+//     barrier makes visible.
+//   * the cache streams through a ring of 4 LDS stages of 32 tokens (36 KiB,
+//     half a page) filled with 16-byte direct-to-LDS loads; two stages are in
+//     flight while one is consumed by QK and one by PV.
 //   * LDS rows are 72 chunks of 16 bytes; the low 3 bits of a chunk index are
-//     XOR-swizzled with ((t&3)<<1) ^ ((t>>2)&7) of the row t, which keeps both
-//     the 16-byte row reads of QK and the transposed 8-byte reads of PV free
-//     of bank conflicts.
+//     XOR-swizzled with ((t&3)<<1) ^ ((t>>2)&7) of the row t, which keeps the
+//     16-byte row reads of QK and the transposed 8-byte reads of PV free of
+//     bank conflicts.
 #include "mla_device.hpp"
 #include "decode.hpp"
 
@@ -43,8 +46,11 @@ constexpr int kStages = 4;                        // LDS ring depth
 constexpr int kStageBytes = kTok * kRowBytes;     // 36864
 constexpr int kThreads = 256;
 constexpr int kDmaPerThread = kStageBytes / (kThreads * 16);  // 9
+constexpr int kPBytes = 2 * 4 * 2 * 1024;         // [slot][wave][k-step][64 lanes x 16 B]
+constexpr int kLdsBytes = kStages * kStageBytes + kPBytes;   // 163840 = all of it
 constexpr float kRefSlack = 64.0f;                // log2 headroom above the reference max
 static_assert(kDmaPerThread * kThreads * 16 == kStageBytes, "stage must split into 16-byte loads");
+static_assert(kLdsBytes <= 163840, "LDS budget");
 
 __device__ __forceinline__ int swz(int t) { return ((t & 3) << 1) ^ ((t >> 2) & 7); }
 
@@ -66,14 +72,20 @@ __device__ __forceinline__ void mfma_result_fence(f32x16& d) {
   asm("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(d));
 }
 
+__device__ __forceinline__ bf16x8 cat8(const i16x4& v0, const i16x4& v1) {
+  const bf16x4 b0 = __builtin_bit_cast(bf16x4, v0);
+  const bf16x4 b1 = __builtin_bit_cast(bf16x4, v1);
+  return bf16x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+}
+
 }  // namespace
 
 __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
     const __bf16* __restrict__ q_abs, const __bf16* __restrict__ q_r, const char* __restrict__ kv,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seqlens,
     float* __restrict__ o_part, float* __restrict__ lse_part, DecodeParams a) {
-  __shared__ __attribute__((aligned(1024))) char lds[kStages * kStageBytes];
-  __shared__ int rescan_flag;
+  __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
+  char* const pbuf = lds + kStages * kStageBytes;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -103,17 +115,14 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
   const int tile0 = t_begin / kTok;
   const int n_tiles = t_end > t_begin ? (t_end - t_begin + kTok - 1) / kTok : 0;
 
-  const int h = wave * 32 + lo;
-  const int64_t qrow = (int64_t)(b * a.s_q + i) * kH + h;
-  const int64_t orow = qrow * a.num_splits + split;
+  const int h_own = wave * 32 + lo;                       // head this lane owns in QK/softmax
+  const int64_t qbase = (int64_t)(b * a.s_q + i) * kH;    // row of head 0 of this query
 
-  if (tid == 0) rescan_flag = 0;
-
-  // queries: B operand of S^T = K . Q^T; lane (g, lo) holds dims 16kk+8g..+7 of head h
+  // queries: B operand of S^T = K . Q^T; lane (g, lo) holds dims 16kk+8g..+7 of head h_own
   bf16x8 qf[36];
   if (n_tiles > 0) {
-    const bf16x8* qa = reinterpret_cast<const bf16x8*>(q_abs + qrow * kDc);
-    const bf16x8* qr = reinterpret_cast<const bf16x8*>(q_r + qrow * kDr);
+    const bf16x8* qa = reinterpret_cast<const bf16x8*>(q_abs + (qbase + h_own) * kDc);
+    const bf16x8* qr = reinterpret_cast<const bf16x8*>(q_r + (qbase + h_own) * kDr);
 #pragma unroll
     for (int kk = 0; kk < 32; ++kk) qf[kk] = qa[2 * kk + g];
 #pragma unroll
@@ -124,9 +133,10 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
   int qk_off[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) qk_off[r] = lo * kRowBytes + (((2 * r + g) ^ swz(lo)) << 4);
-  // PV A operand (V^T) through transposed reads; group G = lane>>4, ii = lane&15
-  // fetches row 4(G>>1) + (ii>>2) (+8 half, +16 ks), columns 16(G&1) + 4(ii&3)..+3
-  int pv_off[2][2][2];  // [ct&1][half][ks]
+  // PV A operand (V^T) for this wave's columns 128w + 32c' through transposed
+  // reads; group G = lane>>4, ii = lane&15 fetches row 4(G>>1) + (ii>>2)
+  // (+8 half, +16 k-step), columns 16(G&1) + 4(ii&3)..+3 of the 32-column tile.
+  int pv_off[2][2][2];  // [c'&1][half][k-step]; add (c'>>1)*128
   {
     const int G = lane >> 4, ii = lane & 15;
     const int t_lane = 4 * (G >> 1) + (ii >> 2);
@@ -139,10 +149,9 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
         for (int ks = 0; ks < 2; ++ks) {
           const int t = t_lane + 8 * hf + 16 * ks;
           const int j = 4 * cp + jl;
-          pv_off[cp][hf][ks] = t * kRowBytes + ((j ^ swz(t)) << 4) + (ii & 1) * 8;
+          pv_off[cp][hf][ks] = t * kRowBytes + ((j ^ swz(t)) << 4) + (ii & 1) * 8 + wave * 256;
         }
   }
-
   // DMA: thread tid fills chunk slot q = k*256 + tid of a stage; the matching
   // source chunk of the 32-row half page is (row q/72, chunk (q%72) ^ swz(row))
   unsigned dma_off[kDmaPerThread];
@@ -168,136 +177,159 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
   };
 
   const float c_log2 = a.scale_log2;
-  f32x16 O[16];
-  float m_ref = -INFINITY;   // reference max of this head (log2 units)
-  float m_seen = -INFINITY;  // true running max of this head
+  f32x16 O[4][4];            // O^T tiles [column tile c'][head tile ht]
+  float m_ref = -INFINITY;   // reference max of head h_own (log2 units)
+  float m_seen = -INFINITY;  // true running max of head h_own
   float l_run = 0.f;         // this lane's share of sum exp2(x - m_ref)
+
+  // QK(t) + softmax(t): publish P^T(t) into slot (t & 1)
+  auto qk_softmax = [&](int it, bool& over) {
+    const char* tb = lds + (it & (kStages - 1)) * kStageBytes;
+    const int valid = t_end - (tile0 + it) * kTok;  // >= 1; >= 32 means a full tile
+    f32x16 S;
+    mfma_qk_first(S, *reinterpret_cast<const bf16x8*>(tb + qk_off[0]), qf[0]);
+#pragma unroll
+    for (int kk = 1; kk < 36; ++kk)
+      mfma_qk(S, *reinterpret_cast<const bf16x8*>(tb + qk_off[kk & 3] + (kk >> 2) * 128), qf[kk]);
+    mfma_result_fence(S);
+    // lane owns head h_own, tokens 8(r>>2) + 4g + (r&3) of the tile
+    float xs[16];
+    const int vlim = valid - 4 * g;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float v = S[r] * c_log2;
+      xs[r] = (8 * (r >> 2) + (r & 3)) < vlim ? v : -INFINITY;
+    }
+    float mx = xs[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, xs[r]);
+    mx = fmaxf(mx, shfl_xor32(mx));
+    m_seen = fmaxf(m_seen, mx);
+    m_ref = m_ref == -INFINITY ? mx : m_ref;  // first tile of the first pass
+    over |= mx > m_ref + kRefSlack;
+    bf16x8 pb[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = __builtin_amdgcn_exp2f(xs[r] - m_ref);
+      l_run += p;
+      pb[r >> 3][r & 7] = (__bf16)p;
+    }
+    char* ps = pbuf + ((it & 1) * 8 + wave * 2) * 1024 + lane * 16;
+    *reinterpret_cast<bf16x8*>(ps) = pb[0];
+    *reinterpret_cast<bf16x8*>(ps + 1024) = pb[1];
+  };
+
+  // PV(t): O^T[c', ht] += V^T(t)[c', tokens] . P^T(t)[tokens, ht]
+  auto pv = [&](int it) {
+    const char* tb = lds + (it & (kStages - 1)) * kStageBytes;
+    const char* ps = pbuf + (it & 1) * 8 * 1024 + lane * 16;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 pf[4];
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht) pf[ht] = *reinterpret_cast<const bf16x8*>(ps + (ht * 2 + ks) * 1024);
+#pragma unroll
+      for (int cp = 0; cp < 4; ++cp) {
+        const int base = (cp >> 1) * 128;
+        const bf16x8 va = cat8(
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(tb + pv_off[cp & 1][0][ks] + base)),
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(tb + pv_off[cp & 1][1][ks] + base)));
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht)
+          O[cp][ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[ht], O[cp][ht], 0, 0, 0);
+      }
+    }
+  };
+
+  // rows past the visible length may hold anything (even NaN); P is 0 there,
+  // so make those rows exactly 0 as well before PV reads them
+  auto zero_tail = [&](int it) {
+    const int valid = t_end - (tile0 + it) * kTok;
+    if (valid < kTok) {
+      char* tb = lds + (it & (kStages - 1)) * kStageBytes;
+      for (int q = tid; q < (kTok - valid) * (kRowBytes / 16); q += kThreads)
+        *reinterpret_cast<f32x4*>(tb + valid * kRowBytes + q * 16) = f32x4{};
+    }
+  };
+
+  float* const lbuf = reinterpret_cast<float*>(pbuf);   // end-of-pass exchange (reuses the P slots)
+  int* const flag = reinterpret_cast<int*>(pbuf + 1024);
 
   for (int pass = 0; pass < 2; ++pass) {
     // O^T = 0 through the matrix core, so O is only ever defined by MFMAs
     {
       const bf16x8 z = bf16x8{};
 #pragma unroll
-      for (int ct = 0; ct < 16; ++ct) O[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(z, z, f32x16{}, 0, 0, 0);
+      for (int cp = 0; cp < 4; ++cp)
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht) O[cp][ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(z, z, f32x16{}, 0, 0, 0);
     }
     l_run = 0.f;
     bool over = false;
 
-    const int pre = n_tiles < kStages - 1 ? n_tiles : kStages - 1;
-    for (int s = 0; s < pre; ++s) issue(tile0 + s, s);
-
-    for (int it = 0; it < n_tiles; ++it) {
-      const int ahead = n_tiles - 1 - it;
-      if (ahead >= 2)
-        wait_vmcnt<2 * kDmaPerThread>();
-      else if (ahead == 1)
-        wait_vmcnt<kDmaPerThread>();
-      else
-        wait_vmcnt<0>();
+    if (n_tiles > 0) {
+      issue(tile0, 0);
+      if (n_tiles > 1) issue(tile0 + 1, 1);
+      // tile 0: QK + softmax only
+      if (n_tiles > 1) wait_vmcnt<kDmaPerThread>(); else wait_vmcnt<0>();
       __syncthreads();
-      if (it + kStages - 1 < n_tiles) issue(tile0 + it + kStages - 1, (it + kStages - 1) & (kStages - 1));
-
-      char* tb = lds + (it & (kStages - 1)) * kStageBytes;
-      const int valid = t_end - (tile0 + it) * kTok;  // >= 1; >= 32 means a full tile
-      if (valid < kTok) {
-        // rows past the visible length may hold anything (even NaN); P is 0
-        // there, so make those rows exactly 0 as well
-        for (int q = tid; q < (kTok - valid) * (kRowBytes / 16); q += kThreads)
-          *reinterpret_cast<f32x4*>(tb + valid * kRowBytes + q * 16) = f32x4{};
+      if (n_tiles > 2) issue(tile0 + 2, 2);
+      zero_tail(0);
+      qk_softmax(0, over);
+      // steady state: QK(it) + softmax(it) overlapped with PV(it - 1)
+      for (int it = 1; it < n_tiles; ++it) {
+        if (it + 1 < n_tiles) wait_vmcnt<kDmaPerThread>(); else wait_vmcnt<0>();
         __syncthreads();
+        if (it + 2 < n_tiles) issue(tile0 + it + 2, (it + 2) & (kStages - 1));
+        zero_tail(it);
+        qk_softmax(it, over);
+        pv(it - 1);
       }
-
-      // ---- S^T[token, head] over 576 dims
-      f32x16 S;
-      mfma_qk_first(S, *reinterpret_cast<const bf16x8*>(tb + qk_off[0]), qf[0]);
-#pragma unroll
-      for (int kk = 1; kk < 36; ++kk)
-        mfma_qk(S, *reinterpret_cast<const bf16x8*>(tb + qk_off[kk & 3] + (kk >> 2) * 128), qf[kk]);
-      mfma_result_fence(S);
-
-      // ---- softmax numerators (lane owns head h, tokens 8(r>>2) + 4g + (r&3))
-      float xs[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) xs[r] = S[r] * c_log2;
-      if (valid < kTok) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int tok = 8 * (r >> 2) + 4 * g + (r & 3);
-          if (tok >= valid) xs[r] = -INFINITY;
-        }
-      }
-      float mx = xs[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, xs[r]);
-      mx = fmaxf(mx, shfl_xor32(mx));
-      m_seen = fmaxf(m_seen, mx);
-      if (m_ref == -INFINITY) m_ref = mx;  // first tile of the first pass
-      over |= mx > m_ref + kRefSlack;
-      bf16x8 pb[2];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(xs[r] - m_ref);
-        l_run += p;
-        pb[r >> 3][r & 7] = (__bf16)p;
-      }
-
-      // ---- O^T[c, head] += V^T[c, token] . P^T[token, head]
-      // 32 MFMAs n = 2ct + ks; the V^T fragments are read 3 MFMAs ahead
-      auto vfrag = [&](int n) {
-        const int ct = n >> 1, ks = n & 1;
-        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4_t*)(tb + pv_off[ct & 1][0][ks] + (ct >> 1) * 128));
-        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4_t*)(tb + pv_off[ct & 1][1][ks] + (ct >> 1) * 128));
-        const bf16x4 b0 = __builtin_bit_cast(bf16x4, v0);
-        const bf16x4 b1 = __builtin_bit_cast(bf16x4, v1);
-        return bf16x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-      };
-      bf16x8 vq[4];
-      vq[0] = vfrag(0);
-      vq[1] = vfrag(1);
-      vq[2] = vfrag(2);
-#pragma unroll
-      for (int n = 0; n < 32; ++n) {
-        if (n + 3 < 32) vq[(n + 3) & 3] = vfrag(n + 3);
-        O[n >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vq[n & 3], pb[n & 1], O[n >> 1], 0, 0, 0);
-      }
-      // schedule: the first three fragments (6 reads), then per MFMA the reads
-      // of the fragment three MFMAs ahead
-      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-#pragma unroll
-      for (int n = 0; n < 29; ++n) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+      __syncthreads();
+      pv(n_tiles - 1);
     }
 
-    // rescan once with the exact max if some score outgrew its reference
-    if (__any(over) && lane == 0) rescan_flag = 1;
+    // end of pass: publish per-head sums and whether any score outgrew its reference
+    __syncthreads();                        // all P slot reads are done
+    if (tid == 0) *flag = 0;
     __syncthreads();
-    const bool again = rescan_flag != 0;
+    const float l_tot = l_run + shfl_xor32(l_run);
+    if (g == 0) lbuf[h_own] = l_tot;
+    if (__any(over) && lane == 0) *flag = 1;
+    __syncthreads();
+    const bool again = *flag != 0;
     if (!again || pass == 1) break;
-    __syncthreads();
-    m_ref = m_seen;
+    m_ref = m_seen;                          // exact max: a second rescan is impossible
+    __syncthreads();                         // everyone has read the flag and lbuf
   }
 
-  // ---- epilogue: normalise, write this split's partial row and its LSE
-  const float l_tot = l_run + shfl_xor32(l_run);
-  const bool empty = !(l_tot > 0.f);
-  const float inv = empty ? 0.f : 1.0f / l_tot;
-  float* orow_ptr = o_part + orow * kDc;
+  // ---- epilogue: normalise, write this split's partial rows and their LSEs
+  float inv[4];
+  bool empty[4];
 #pragma unroll
-  for (int ct = 0; ct < 16; ++ct)
+  for (int ht = 0; ht < 4; ++ht) {
+    const float l = lbuf[ht * 32 + lo];
+    empty[ht] = !(l > 0.f);
+    inv[ht] = empty[ht] ? 0.f : 1.0f / l;
+  }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      f32x4 v;
+  for (int ht = 0; ht < 4; ++ht) {
+    float* orow = o_part + ((qbase + ht * 32 + lo) * a.num_splits + split) * kDc + wave * 128;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = empty ? 0.f : O[ct][4 * q + e] * inv;
-      *reinterpret_cast<f32x4*>(orow_ptr + 32 * ct + 8 * q + 4 * g) = v;
-    }
-  if (g == 0)
-    lse_part[orow] = empty ? -INFINITY : (m_ref + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994530942f;
+    for (int cp = 0; cp < 4; ++cp)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = empty[ht] ? 0.f : O[cp][ht][4 * q + e] * inv[ht];
+        *reinterpret_cast<f32x4*>(orow + 32 * cp + 8 * q + 4 * g) = v;
+      }
+  }
+  if (g == 0) {
+    const float l = lbuf[h_own];
+    lse_part[(qbase + h_own) * a.num_splits + split] =
+        l > 0.f ? (m_ref + __builtin_amdgcn_logf(l)) * 0.69314718055994530942f : -INFINITY;
+  }
 }
 
 hipError_t launch_decode_paged(const DecodeParams& p, hipStream_t stream) {
