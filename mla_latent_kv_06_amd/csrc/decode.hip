@@ -72,6 +72,38 @@ __device__ __forceinline__ void mfma_result_fence(f32x16& d) {
   asm("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(d));
 }
 
+// scheduling hint: one MFMA followed by up to N VALU/transcendental ops, four times
+template <int N>
+__device__ __forceinline__ void interleave() {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x402, N, 0);
+  }
+}
+
+// Workgroup barrier for the tile pipeline: this wave's LDS writes are done
+// (lgkmcnt 0) and the wave has already waited for its own direct-to-LDS loads
+// of the tile with an explicit vmcnt. Unlike __syncthreads() it does not
+// drain every outstanding global load (its release fence would wait for the
+// whole prefetch window). The memory clobber keeps the compiler from moving
+// memory operations across it.
+__device__ __forceinline__ void tile_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// One 16-byte-per-lane direct-to-LDS load: lane l's 16 bytes from
+// sbase + voff land at LDS byte address lds_addr + 16*l. Written as asm so the
+// compiler does not treat every later LDS read as possibly overlapping it
+// (which would make it drain all outstanding loads); completion is tracked
+// with explicit vmcnt waits before the tile is read. An SALU write of M0
+// needs one wait state before an LDS-DMA instruction reads it.
+__device__ __forceinline__ void dma16(const char* sbase, unsigned voff, unsigned lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+               "s"(lds_addr)
+               : "memory", "m0");
+}
+
 __device__ __forceinline__ bf16x8 cat8(const i16x4& v0, const i16x4& v1) {
   const bf16x4 b0 = __builtin_bit_cast(bf16x4, v0);
   const bf16x4 b1 = __builtin_bit_cast(bf16x4, v1);
@@ -165,14 +197,27 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
   auto issue = [&](int tile, int stage) {
     const int64_t page = physical_page(block_table, a.max_pages, b, tile >> 1, a.num_pages);
     const char* src = kv + page * kPageBytes + (tile & 1) * kStageBytes;
-    char* dst = lds + stage * kStageBytes + wave * 1024;
+    const unsigned dst = (unsigned)(uintptr_t)(lds_void_t*)(lds + stage * kStageBytes + wave * 1024);
 #pragma unroll
-    for (int k = 0; k < kDmaPerThread; ++k) {
-      // keep the 32-bit offset opaque inside the loop so that the address is
-      // formed as uniform base + 32-bit lane offset (no 64-bit copies hoisted)
-      unsigned off = dma_off[k];
-      asm volatile("" : "+v"(off));
-      __builtin_amdgcn_global_load_lds(src + off, (lds_void_t*)(dst + k * (kThreads * 16)), 16, 0, 0);
+    for (int k = 0; k < kDmaPerThread; ++k) dma16(src, dma_off[k], dst + k * (kThreads * 16));
+  };
+
+  // L2 / last-level-cache prefetch of a half page two tiles beyond the DMA
+  // front: one dword load per 64-byte segment (3 per thread; the spare loads
+  // repeat the first segments), landing in loop-carried dummy registers that
+  // are tied through every prefetch so no late return can clobber live data.
+  // Tiles past the split re-prefetch its last tile, so every iteration issues
+  // exactly 3 of these per wave and the vmcnt arithmetic below is fixed.
+  unsigned pf_sink[3] = {0u, 0u, 0u};
+  auto prefetch = [&](int t) {
+    const int tile = t < n_tiles ? tile0 + t : tile0 + n_tiles - 1;
+    const int64_t page = physical_page(block_table, a.max_pages, b, tile >> 1, a.num_pages);
+    const char* src = kv + page * kPageBytes + (tile & 1) * kStageBytes;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const unsigned q = k * kThreads + tid;
+      const unsigned off = (q < kStageBytes / 64 ? q : q - kStageBytes / 64) * 64u;
+      asm volatile("global_load_dword %0, %1, %2" : "+v"(pf_sink[k]) : "v"(off), "s"(src) : "memory");
     }
   };
 
@@ -182,62 +227,136 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
   float m_seen = -INFINITY;  // true running max of head h_own
   float l_run = 0.f;         // this lane's share of sum exp2(x - m_ref)
 
-  // QK(t) + softmax(t): publish P^T(t) into slot (t & 1)
-  auto qk_softmax = [&](int it, bool& over) {
+  // ---- phase A: S^T[token, head] = K(it) . Q^T over 576 dims, pinned in
+  // program order: the K fragment for MFMA kk+3 is read right after MFMA kk,
+  // so three LDS reads are always in flight.
+  auto qk = [&](int it) -> f32x16 {
     const char* tb = lds + (it & (kStages - 1)) * kStageBytes;
-    const int valid = t_end - (tile0 + it) * kTok;  // >= 1; >= 32 means a full tile
     f32x16 S;
-    mfma_qk_first(S, *reinterpret_cast<const bf16x8*>(tb + qk_off[0]), qf[0]);
+    bf16x8 kf[4];
 #pragma unroll
-    for (int kk = 1; kk < 36; ++kk)
-      mfma_qk(S, *reinterpret_cast<const bf16x8*>(tb + qk_off[kk & 3] + (kk >> 2) * 128), qf[kk]);
+    for (int kk = 0; kk < 3; ++kk) kf[kk] = *reinterpret_cast<const bf16x8*>(tb + qk_off[kk]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < 36; ++kk) {
+      if (kk == 0)
+        mfma_qk_first(S, kf[0], qf[0]);
+      else
+        mfma_qk(S, kf[kk & 3], qf[kk]);
+      if (kk + 3 < 36)
+        kf[(kk + 3) & 3] = *reinterpret_cast<const bf16x8*>(tb + qk_off[(kk + 3) & 3] + ((kk + 3) >> 2) * 128);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     mfma_result_fence(S);
-    // lane owns head h_own, tokens 8(r>>2) + 4g + (r&3) of the tile
-    float xs[16];
-    const int vlim = valid - 4 * g;
+    __builtin_amdgcn_sched_barrier(0);
+    return S;
+  };
+
+  // ---- softmax numerators in chunks (lane owns head h_own and tokens
+  // 8(r>>2) + 4g + (r&3) of the tile); chunks are interleaved with PV below
+  float xs[16];
+  float mx = 0.f, mx_other = 0.f;
+  bf16x8 pb[2];
+  auto sm_scale = [&](const f32x16& S, int it) {
+    const int vlim = t_end - (tile0 + it) * kTok - 4 * g;  // tokens < vlim are visible
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const float v = S[r] * c_log2;
       xs[r] = (8 * (r >> 2) + (r & 3)) < vlim ? v : -INFINITY;
     }
-    float mx = xs[0];
+  };
+  auto sm_localmax = [&]() {
+    mx = xs[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, xs[r]);
-    mx = fmaxf(mx, shfl_xor32(mx));
+    mx_other = shfl_xor32(mx);
+  };
+  auto sm_ref = [&](bool& over) {
+    mx = fmaxf(mx, mx_other);
     m_seen = fmaxf(m_seen, mx);
     m_ref = m_ref == -INFINITY ? mx : m_ref;  // first tile of the first pass
     over |= mx > m_ref + kRefSlack;
-    bf16x8 pb[2];
+  };
+  auto sm_exp = [&](int r0) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = __builtin_amdgcn_exp2f(xs[r] - m_ref);
-      l_run += p;
-      pb[r >> 3][r & 7] = (__bf16)p;
+    for (int r = r0; r < r0 + 8; ++r) {
+      xs[r] = __builtin_amdgcn_exp2f(xs[r] - m_ref);
+      l_run += xs[r];
     }
+  };
+  auto sm_pack = [&]() {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pb[r >> 3][r & 7] = (__bf16)xs[r];
+  };
+  auto sm_publish = [&](int it) {
     char* ps = pbuf + ((it & 1) * 8 + wave * 2) * 1024 + lane * 16;
     *reinterpret_cast<bf16x8*>(ps) = pb[0];
     *reinterpret_cast<bf16x8*>(ps + 1024) = pb[1];
   };
 
-  // PV(t): O^T[c', ht] += V^T(t)[c', tokens] . P^T(t)[tokens, ht]
-  auto pv = [&](int it) {
-    const char* tb = lds + (it & (kStages - 1)) * kStageBytes;
-    const char* ps = pbuf + (it & 1) * 8 * 1024 + lane * 16;
+  // ---- PV pieces: V^T fragment (k-step ks, column tile c') and P^T fragment
+  // (k-step ks, head tile ht) of tile ip, and the 4 MFMAs of one (ks, c')
+  auto vfrag = [&](int ip, int ks, int cp) -> bf16x8 {
+    const char* tv = lds + (ip & (kStages - 1)) * kStageBytes + (cp >> 1) * 128;
+    return cat8(__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(tv + pv_off[cp & 1][0][ks])),
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(tv + pv_off[cp & 1][1][ks])));
+  };
+  auto pfrag = [&](int ip, int ks, int ht) -> bf16x8 {
+    return *reinterpret_cast<const bf16x8*>(pbuf + (ip & 1) * 8 * 1024 + (ht * 2 + ks) * 1024 + lane * 16);
+  };
+  auto mm4 = [&](int cp, const bf16x8& va, const bf16x8* pf) {
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht)
+      O[cp][ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[ht], O[cp][ht], 0, 0, 0);
+  };
+#define MLA_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+  // tile `it` without PV (first tile of a pass)
+  auto softmax_only = [&](int it, bool& over) {
+    const f32x16 S = qk(it);
+    sm_scale(S, it);
+    sm_localmax();
+    sm_ref(over);
+    sm_exp(0);
+    sm_exp(8);
+    sm_pack();
+    sm_publish(it);
+    MLA_FENCE();
+  };
+
+  // tile `it`: QK(it), then softmax(it) chunks interleaved with PV(it-1)
+  auto softmax_pv = [&](int it, bool& over) {
+    const int ip = it - 1;
+    const f32x16 S = qk(it);
+    bf16x8 pf[4], va[3];
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) pf[ht] = pfrag(ip, 0, ht);
+    va[0] = vfrag(ip, 0, 0);
+    va[1] = vfrag(ip, 0, 1);
+    MLA_FENCE();
+    sm_scale(S, it);       mm4(0, va[0], pf); va[2] = vfrag(ip, 0, 2); interleave<8>(); MLA_FENCE();
+    sm_localmax();         mm4(1, va[1], pf); va[0] = vfrag(ip, 0, 3); interleave<4>(); MLA_FENCE();
+    sm_ref(over);          mm4(2, va[2], pf); va[1] = vfrag(ip, 1, 0); interleave<2>(); MLA_FENCE();
+    sm_exp(0);             mm4(3, va[0], pf); interleave<4>(); MLA_FENCE();
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) pf[ht] = pfrag(ip, 1, ht);
+    va[2] = vfrag(ip, 1, 1);
+    MLA_FENCE();
+    sm_exp(8);             mm4(0, va[1], pf); va[0] = vfrag(ip, 1, 2); interleave<4>(); MLA_FENCE();
+    sm_pack();             mm4(1, va[2], pf); va[1] = vfrag(ip, 1, 3); interleave<2>(); MLA_FENCE();
+    sm_publish(it);        mm4(2, va[0], pf); MLA_FENCE();
+    mm4(3, va[1], pf);     MLA_FENCE();
+  };
+
+  // PV(t) alone (the last tile of a pass)
+  auto pv_only = [&](int ip) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       bf16x8 pf[4];
 #pragma unroll
-      for (int ht = 0; ht < 4; ++ht) pf[ht] = *reinterpret_cast<const bf16x8*>(ps + (ht * 2 + ks) * 1024);
+      for (int ht = 0; ht < 4; ++ht) pf[ht] = pfrag(ip, ks, ht);
 #pragma unroll
-      for (int cp = 0; cp < 4; ++cp) {
-        const int base = (cp >> 1) * 128;
-        const bf16x8 va = cat8(
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(tb + pv_off[cp & 1][0][ks] + base)),
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(tb + pv_off[cp & 1][1][ks] + base)));
-#pragma unroll
-        for (int ht = 0; ht < 4; ++ht)
-          O[cp][ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[ht], O[cp][ht], 0, 0, 0);
-      }
+      for (int cp = 0; cp < 4; ++cp) mm4(cp, vfrag(ip, ks, cp), pf);
     }
   };
 
@@ -268,25 +387,37 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
     bool over = false;
 
     if (n_tiles > 0) {
+      // Iteration j issues DMA(j+2) (9 loads per thread, only for tiles that
+      // exist) and then prefetch(j+4) (3 loads, always). Both go out at the END
+      // of the iteration, after its LDS reads: a direct-to-LDS load in flight
+      // ahead of LDS reads makes the compiler wait for all LDS reads at every
+      // use. Stage (j+2)&3 was last read by PV(j-2) in iteration j-1.
+      // At the top of iteration it the loads issued after DMA(it) are
+      // prefetch(it+2), DMA(it+1) if it exists, and prefetch(it+3).
       issue(tile0, 0);
+      prefetch(2);
       if (n_tiles > 1) issue(tile0 + 1, 1);
+      prefetch(3);
       // tile 0: QK + softmax only
-      if (n_tiles > 1) wait_vmcnt<kDmaPerThread>(); else wait_vmcnt<0>();
-      __syncthreads();
-      if (n_tiles > 2) issue(tile0 + 2, 2);
+      if (n_tiles > 1) wait_vmcnt<kDmaPerThread + 6>(); else wait_vmcnt<6>();
+      tile_barrier();
       zero_tail(0);
-      qk_softmax(0, over);
+      softmax_only(0, over);
+      if (n_tiles > 2) issue(tile0 + 2, 2);
+      prefetch(4);
       // steady state: QK(it) + softmax(it) overlapped with PV(it - 1)
       for (int it = 1; it < n_tiles; ++it) {
-        if (it + 1 < n_tiles) wait_vmcnt<kDmaPerThread>(); else wait_vmcnt<0>();
-        __syncthreads();
-        if (it + 2 < n_tiles) issue(tile0 + it + 2, (it + 2) & (kStages - 1));
+        if (it + 1 < n_tiles) wait_vmcnt<kDmaPerThread + 6>(); else wait_vmcnt<6>();
+        tile_barrier();
         zero_tail(it);
-        qk_softmax(it, over);
-        pv(it - 1);
+        softmax_pv(it, over);
+        if (it + 2 < n_tiles) issue(tile0 + it + 2, (it + 2) & (kStages - 1));
+        prefetch(it + 4);
       }
-      __syncthreads();
-      pv(n_tiles - 1);
+      tile_barrier();
+      pv_only(n_tiles - 1);
+      wait_vmcnt<0>();  // outstanding prefetches land before their sink registers can be reused
+      asm volatile("" ::"v"(pf_sink[0]), "v"(pf_sink[1]), "v"(pf_sink[2]));
     }
 
     // end of pass: publish per-head sums and whether any score outgrew its reference
