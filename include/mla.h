@@ -102,7 +102,8 @@ int mla_recommended_splits(int B, int s_q, int max_len, int num_cus);
  *   seqlens     int32 [B]: L_b = tokens in the cache for sequence b,
  *               including the s_q new ones. Values are clamped to
  *               [0, max_pages * 64].
- *   softmax_scale  multiplies q_abs.c_KV + q_R.k_R (1/sqrt(192) for DeepSeek).
+ *   softmax_scale  multiplies q_abs.c_KV + q_R.k_R (1/sqrt(192) for DeepSeek);
+ *               must be positive and finite.
  *   num_splits  in [1, max_pages]; query i of sequence b sees tokens
  *               t <= L_b - s_q + i, i.e. n = ceil((L_b - s_q + i + 1) / 64)
  *               pages, and split s scans pages [s*q, min((s+1)*q, n)) with

@@ -28,12 +28,15 @@
 //     P(i) is published in a double-buffered slot that the next iteration's
 //     barrier makes visible.
 //   * the cache streams through a ring of 4 LDS stages of 32 tokens (36 KiB,
-//     half a page) filled with 16-byte direct-to-LDS loads; two stages are in
-//     flight while one is consumed by QK and one by PV.
+//     half a page) filled with 16-byte direct-to-LDS loads; while one stage
+//     is read by QK and one by PV, the next tile is landing and the one after
+//     is issued, spread between the QK MFMAs.
 //   * LDS rows are 72 chunks of 16 bytes; the low 3 bits of a chunk index are
 //     XOR-swizzled with ((t&3)<<1) ^ ((t>>2)&7) of the row t, which keeps the
 //     16-byte row reads of QK and the transposed 8-byte reads of PV free of
 //     bank conflicts.
+#include <type_traits>
+
 #include "mla_device.hpp"
 #include "decode.hpp"
 
@@ -159,6 +162,9 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
     for (int kk = 0; kk < 32; ++kk) qf[kk] = qa[2 * kk + g];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) qf[32 + kk] = qr[2 * kk + g];
+    // land the queries before the tile loop: otherwise the compiler re-waits
+    // for them inside the loop, where the wait would also drain cache DMA
+    wait_vmcnt<0>();
   }
 
   // QK A operand: row lo, chunk 2kk+g; kk = 4a + r -> offset qk_off[r] + 128a
@@ -194,31 +200,22 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
     const unsigned p = q - t * 72u;
     dma_off[k] = t * kRowBytes + ((p ^ swz(t)) << 4);
   }
-  auto issue = [&](int tile, int stage) {
-    const int64_t page = physical_page(block_table, a.max_pages, b, tile >> 1, a.num_pages);
-    const char* src = kv + page * kPageBytes + (tile & 1) * kStageBytes;
-    const unsigned dst = (unsigned)(uintptr_t)(lds_void_t*)(lds + stage * kStageBytes + wave * 1024);
-#pragma unroll
-    for (int k = 0; k < kDmaPerThread; ++k) dma16(src, dma_off[k], dst + k * (kThreads * 16));
+  // DMA of one 32-token tile (half a page) into an LDS stage, 9 loads per
+  // thread; issue_part(k) issues load k so the loads can be spread between
+  // the MFMAs of the QK phase.
+  struct DmaTarget {
+    const char* src;
+    unsigned dst;
   };
-
-  // L2 / last-level-cache prefetch of a half page two tiles beyond the DMA
-  // front: one dword load per 64-byte segment (3 per thread; the spare loads
-  // repeat the first segments), landing in loop-carried dummy registers that
-  // are tied through every prefetch so no late return can clobber live data.
-  // Tiles past the split re-prefetch its last tile, so every iteration issues
-  // exactly 3 of these per wave and the vmcnt arithmetic below is fixed.
-  unsigned pf_sink[3] = {0u, 0u, 0u};
-  auto prefetch = [&](int t) {
-    const int tile = t < n_tiles ? tile0 + t : tile0 + n_tiles - 1;
+  auto dma_target = [&](int tile, int stage) -> DmaTarget {
     const int64_t page = physical_page(block_table, a.max_pages, b, tile >> 1, a.num_pages);
-    const char* src = kv + page * kPageBytes + (tile & 1) * kStageBytes;
+    return DmaTarget{kv + page * kPageBytes + (tile & 1) * kStageBytes,
+                     (unsigned)(uintptr_t)(lds_void_t*)(lds + stage * kStageBytes + wave * 1024)};
+  };
+  auto issue = [&](int tile, int stage) {
+    const DmaTarget t = dma_target(tile, stage);
 #pragma unroll
-    for (int k = 0; k < 3; ++k) {
-      const unsigned q = k * kThreads + tid;
-      const unsigned off = (q < kStageBytes / 64 ? q : q - kStageBytes / 64) * 64u;
-      asm volatile("global_load_dword %0, %1, %2" : "+v"(pf_sink[k]) : "v"(off), "s"(src) : "memory");
-    }
+    for (int k = 0; k < kDmaPerThread; ++k) dma16(t.src, dma_off[k], t.dst + k * (kThreads * 16));
   };
 
   const float c_log2 = a.scale_log2;
@@ -230,8 +227,14 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
   // ---- phase A: S^T[token, head] = K(it) . Q^T over 576 dims, pinned in
   // program order: the K fragment for MFMA kk+3 is read right after MFMA kk,
   // so three LDS reads are always in flight.
-  auto qk = [&](int it) -> f32x16 {
+  // The next tile's DMA (if any) is issued inside the QK phase, one load
+  // after every fourth MFMA, so the issue cost hides under matrix-core work.
+  // dma_tag is std::true_type / std::false_type: whether to issue DMA(it+2).
+  auto qk = [&](int it, auto dma_tag) -> f32x16 {
+    constexpr bool dma = decltype(dma_tag)::value;
     const char* tb = lds + (it & (kStages - 1)) * kStageBytes;
+    DmaTarget t{nullptr, 0u};
+    if constexpr (dma) t = dma_target(tile0 + it + 2, (it + 2) & (kStages - 1));
     f32x16 S;
     bf16x8 kf[4];
 #pragma unroll
@@ -245,6 +248,9 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
         mfma_qk(S, kf[kk & 3], qf[kk]);
       if (kk + 3 < 36)
         kf[(kk + 3) & 3] = *reinterpret_cast<const bf16x8*>(tb + qk_off[(kk + 3) & 3] + ((kk + 3) >> 2) * 128);
+      if constexpr (dma) {
+        if ((kk & 3) == 1) dma16(t.src, dma_off[kk >> 2], t.dst + (kk >> 2) * (kThreads * 16));
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     mfma_result_fence(S);
@@ -257,30 +263,38 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
   float xs[16];
   float mx = 0.f, mx_other = 0.f;
   bf16x8 pb[2];
+  // xs = raw scores; the tail tile masks tokens past the visible length
   auto sm_scale = [&](const f32x16& S, int it) {
-    const int vlim = t_end - (tile0 + it) * kTok - 4 * g;  // tokens < vlim are visible
+    const int valid = t_end - (tile0 + it) * kTok;  // uniform; >= 32 for full tiles
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float v = S[r] * c_log2;
-      xs[r] = (8 * (r >> 2) + (r & 3)) < vlim ? v : -INFINITY;
+    for (int r = 0; r < 16; ++r) xs[r] = S[r];
+    if (valid < kTok) {
+      const int vlim = valid - 4 * g;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xs[r] = (8 * (r >> 2) + (r & 3)) < vlim ? xs[r] : -INFINITY;
     }
   };
   auto sm_localmax = [&]() {
-    mx = xs[0];
+    mx = fmaxf(fmaxf(xs[0], xs[1]), xs[2]);
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, xs[r]);
+    for (int r = 3; r < 15; r += 2) mx = fmaxf(fmaxf(mx, xs[r]), xs[r + 1]);
+    mx = fmaxf(mx, xs[15]);
     mx_other = shfl_xor32(mx);
   };
+  // reference and running max in log2 units (softmax_scale > 0, so the max of
+  // the scaled scores is the scaled max)
   auto sm_ref = [&](bool& over) {
-    mx = fmaxf(mx, mx_other);
+    mx = fmaxf(mx, mx_other) * c_log2;
     m_seen = fmaxf(m_seen, mx);
     m_ref = m_ref == -INFINITY ? mx : m_ref;  // first tile of the first pass
     over |= mx > m_ref + kRefSlack;
   };
+  // exp2(x*c - m_ref) in one fma: the exact product is used, so the weight of
+  // the maximum itself is 2^e with |e| <= 2^-24 |m_ref| rather than exactly 1
   auto sm_exp = [&](int r0) {
 #pragma unroll
     for (int r = r0; r < r0 + 8; ++r) {
-      xs[r] = __builtin_amdgcn_exp2f(xs[r] - m_ref);
+      xs[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(xs[r], c_log2, -m_ref));
       l_run += xs[r];
     }
   };
@@ -312,8 +326,8 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
 #define MLA_FENCE() __builtin_amdgcn_sched_barrier(0)
 
   // tile `it` without PV (first tile of a pass)
-  auto softmax_only = [&](int it, bool& over) {
-    const f32x16 S = qk(it);
+  auto softmax_only = [&](int it, bool& over, auto dma_tag) {
+    const f32x16 S = qk(it, dma_tag);
     sm_scale(S, it);
     sm_localmax();
     sm_ref(over);
@@ -325,9 +339,9 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
   };
 
   // tile `it`: QK(it), then softmax(it) chunks interleaved with PV(it-1)
-  auto softmax_pv = [&](int it, bool& over) {
+  auto softmax_pv = [&](int it, bool& over, auto dma_tag) {
     const int ip = it - 1;
-    const f32x16 S = qk(it);
+    const f32x16 S = qk(it, dma_tag);
     bf16x8 pf[4], va[3];
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht) pf[ht] = pfrag(ip, 0, ht);
@@ -387,37 +401,37 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
     bool over = false;
 
     if (n_tiles > 0) {
-      // Iteration j issues DMA(j+2) (9 loads per thread, only for tiles that
-      // exist) and then prefetch(j+4) (3 loads, always). Both go out at the END
-      // of the iteration, after its LDS reads: a direct-to-LDS load in flight
-      // ahead of LDS reads makes the compiler wait for all LDS reads at every
-      // use. Stage (j+2)&3 was last read by PV(j-2) in iteration j-1.
-      // At the top of iteration it the loads issued after DMA(it) are
-      // prefetch(it+2), DMA(it+1) if it exists, and prefetch(it+3).
+      // Iteration j issues DMA(j+2) inside its QK phase (only for tiles that
+      // exist); stage (j+2)&3 was last read by PV(j-2) in iteration j-1. At
+      // the top of iteration it the only loads issued after DMA(it) are those
+      // of DMA(it+1).
       issue(tile0, 0);
-      prefetch(2);
       if (n_tiles > 1) issue(tile0 + 1, 1);
-      prefetch(3);
       // tile 0: QK + softmax only
-      if (n_tiles > 1) wait_vmcnt<kDmaPerThread + 6>(); else wait_vmcnt<6>();
+      if (n_tiles > 1) wait_vmcnt<kDmaPerThread>(); else wait_vmcnt<0>();
       tile_barrier();
       zero_tail(0);
-      softmax_only(0, over);
-      if (n_tiles > 2) issue(tile0 + 2, 2);
-      prefetch(4);
-      // steady state: QK(it) + softmax(it) overlapped with PV(it - 1)
-      for (int it = 1; it < n_tiles; ++it) {
-        if (it + 1 < n_tiles) wait_vmcnt<kDmaPerThread + 6>(); else wait_vmcnt<6>();
+      if (n_tiles > 2)
+        softmax_only(0, over, std::true_type{});
+      else
+        softmax_only(0, over, std::false_type{});
+      // steady state: QK(it) + softmax(it) overlapped with PV(it - 1); the
+      // last two tiles issue no further DMA
+      int it = 1;
+      for (; it + 2 < n_tiles; ++it) {
+        wait_vmcnt<kDmaPerThread>();
         tile_barrier();
         zero_tail(it);
-        softmax_pv(it, over);
-        if (it + 2 < n_tiles) issue(tile0 + it + 2, (it + 2) & (kStages - 1));
-        prefetch(it + 4);
+        softmax_pv(it, over, std::true_type{});
+      }
+      for (; it < n_tiles; ++it) {
+        if (it + 1 < n_tiles) wait_vmcnt<kDmaPerThread>(); else wait_vmcnt<0>();
+        tile_barrier();
+        zero_tail(it);
+        softmax_pv(it, over, std::false_type{});
       }
       tile_barrier();
       pv_only(n_tiles - 1);
-      wait_vmcnt<0>();  // outstanding prefetches land before their sink registers can be reused
-      asm volatile("" ::"v"(pf_sink[0]), "v"(pf_sink[1]), "v"(pf_sink[2]));
     }
 
     // end of pass: publish per-head sums and whether any score outgrew its reference

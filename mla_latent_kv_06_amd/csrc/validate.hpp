@@ -88,8 +88,8 @@ inline Check check_decode(const void* q_abs, const void* q_r, const void* kv, in
   MLA_TRY(need_range(s_q, 1, kMaxSq, "s_q"));
   MLA_TRY(need_range(H, MLA_HEADS, MLA_HEADS, "H"));
   MLA_TRY(need_range(num_splits, 1, max_pages, "num_splits"));
-  if (!(scale == scale) || scale > 3.0e38f || scale < -3.0e38f)
-    return fail(MLA_ERR_SHAPE, "softmax_scale is not finite%s", "");
+  if (!(scale > 0.0f) || scale > 3.0e38f)
+    return fail(MLA_ERR_SHAPE, "softmax_scale must be positive and finite%s", "");
   // grid size: work items are (b, i, split); keep well inside 32-bit counts
   long long items = (long long)B * s_q * num_splits;
   MLA_TRY(need_range(items, 1, (1LL << 30), "B * s_q * num_splits"));

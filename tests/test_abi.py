@@ -62,7 +62,7 @@ def _decode(lib, **kw):
     (dict(q_abs=None), 1), (dict(lse_part=None), 1), (dict(kv=MIS), 3), (dict(o_part=MIS), 3),
     (dict(H=64), 2), (dict(B=0), 2), (dict(s_q=0), 2), (dict(s_q=5000), 2), (dict(S=0), 2),
     (dict(S=5), 2), (dict(max_pages=0), 2), (dict(num_pages=0), 2), (dict(scale=float("nan")), 2),
-    (dict(scale=float("inf")), 2),
+    (dict(scale=float("inf")), 2), (dict(scale=0.0), 2), (dict(scale=-0.5), 2),
 ])
 def test_decode_validation(lib, kw, status):
     assert _decode(lib, **kw) == status
