@@ -2,9 +2,11 @@
 // (sequence, query, head) row by their log-sum-exp (KV-split reduction of the
 // K3 time-share study, "Inside the blocks").
 //
-// One wave per row: every lane reads the row's split LSEs to form the weights,
-// then owns 8 of the 512 latent columns and streams the n_split partial rows
-// with 32-byte loads (2 KiB contiguous per split across the wave).
+// One wave per row: the row's split LSEs are wave-uniform (scalar loads);
+// every lane owns 8 of the 512 latent columns and streams the partial rows
+// with 32-byte loads (2 KiB contiguous per split across the wave). The loads
+// of up to 16 splits are issued before the LSE arithmetic so that their
+// latency overlaps it.
 #include "mla_device.hpp"
 #include "decode.hpp"
 
@@ -25,15 +27,30 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 }  // namespace
 
+constexpr int kCombineChunk = 16;  // splits whose loads are in flight together
+
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o_part,
                                                       const float* __restrict__ lse_part, int rows,
                                                       int num_splits, float* __restrict__ o_lat,
                                                       float* __restrict__ lse) {
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int row = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
   if (row >= rows) return;
   const float* lp = lse_part + (int64_t)row * num_splits;
+  const float* op = o_part + (int64_t)row * num_splits * kDc + 8 * lane;
   float* orow = o_lat + (int64_t)row * kDc + 8 * lane;
+
+  f32x4 v0[kCombineChunk], v1[kCombineChunk];
+  auto load_chunk = [&](int s0) {
+#pragma unroll
+    for (int k = 0; k < kCombineChunk; ++k) {
+      if (s0 + k < num_splits) {
+        v0[k] = *reinterpret_cast<const f32x4*>(op + (int64_t)(s0 + k) * kDc);
+        v1[k] = *reinterpret_cast<const f32x4*>(op + (int64_t)(s0 + k) * kDc + 4);
+      }
+    }
+  };
+  load_chunk(0);
 
   float M = -INFINITY;
   for (int s = lane; s < num_splits; s += 64) M = fmaxf(M, lp[s]);
@@ -49,14 +66,21 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   tot = wave_sum(tot);
   const float L = M + logf(tot);
 
+  // lane k holds the weight of split c0 + k of the current 64-split block;
+  // each split's weight is then broadcast with readlane
   f32x4 a0 = f32x4{}, a1 = f32x4{};
-  const float* op = o_part + (int64_t)row * num_splits * kDc + 8 * lane;
-  for (int s = 0; s < num_splits; ++s) {
-    const float w = expf(lp[s] - L);  // 0 for an empty split (lse = -inf)
-    const f32x4 v0 = *reinterpret_cast<const f32x4*>(op + (int64_t)s * kDc);
-    const f32x4 v1 = *reinterpret_cast<const f32x4*>(op + (int64_t)s * kDc + 4);
-    a0 += w * v0;
-    a1 += w * v1;
+  float wl = 0.f;
+  for (int s0 = 0; s0 < num_splits; s0 += kCombineChunk) {
+    if ((s0 & 63) == 0) wl = s0 + lane < num_splits ? expf(lp[s0 + lane] - L) : 0.f;  // 0 for lse = -inf
+    if (s0 > 0) load_chunk(s0);
+#pragma unroll
+    for (int k = 0; k < kCombineChunk; ++k) {
+      if (s0 + k < num_splits) {
+        const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), (s0 & 63) + k));
+        a0 += w * v0[k];
+        a1 += w * v1[k];
+      }
+    }
   }
   *reinterpret_cast<f32x4*>(orow) = a0;
   *reinterpret_cast<f32x4*>(orow + 4) = a1;

@@ -26,7 +26,9 @@
 //   * software pipeline: iteration i runs QK(i), then softmax(i) interleaved
 //     with PV(i-1), so the softmax VALU work overlaps matrix-core work and
 //     P(i) is published in a double-buffered slot that the next iteration's
-//     barrier makes visible.
+//     barrier makes visible. The last quarter of PV(i-1) waits until after
+//     the next barrier, where its MFMAs hide the latency of the first K reads,
+//     and the first PV(i-1) operands are read during the last QK(i) MFMAs.
 //   * the cache streams through a ring of 4 LDS stages of 32 tokens (36 KiB,
 //     half a page) filled with 16-byte direct-to-LDS loads; while one stage
 //     is read by QK and one by PV, the next tile is landing and the one after
@@ -224,14 +226,36 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
   float m_seen = -INFINITY;  // true running max of head h_own
   float l_run = 0.f;         // this lane's share of sum exp2(x - m_ref)
 
+  // ---- PV pieces: V^T fragment (k-step ks, column tile c') and P^T fragment
+  // (k-step ks, head tile ht) of tile ip, and the 4 MFMAs of one (ks, c')
+  auto vfrag = [&](int ip, int ks, int cp) -> bf16x8 {
+    const char* tv = lds + (ip & (kStages - 1)) * kStageBytes + (cp >> 1) * 128;
+    return cat8(__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(tv + pv_off[cp & 1][0][ks])),
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(tv + pv_off[cp & 1][1][ks])));
+  };
+  auto pfrag = [&](int ip, int ks, int ht) -> bf16x8 {
+    return *reinterpret_cast<const bf16x8*>(pbuf + (ip & 1) * 8 * 1024 + (ht * 2 + ks) * 1024 + lane * 16);
+  };
+  auto mm4 = [&](int cp, const bf16x8& va, const bf16x8* pf) {
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht)
+      O[cp][ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[ht], O[cp][ht], 0, 0, 0);
+  };
+  // PV operands, carried across iterations: PV(i) leaves its last four
+  // MFMAs (k-step 1, column tile 3) to run right after the next tile
+  // barrier, where they cover the latency of the first K reads of QK(i+2);
+  // zero operands (a no-op MFMA) when there is no earlier tile
+  bf16x8 pf[4], va[3];
+
   // ---- phase A: S^T[token, head] = K(it) . Q^T over 576 dims, pinned in
   // program order: the K fragment for MFMA kk+3 is read right after MFMA kk,
   // so three LDS reads are always in flight.
   // The next tile's DMA (if any) is issued inside the QK phase, one load
   // after every fourth MFMA, so the issue cost hides under matrix-core work.
   // dma_tag is std::true_type / std::false_type: whether to issue DMA(it+2).
-  auto qk = [&](int it, auto dma_tag) -> f32x16 {
+  auto qk = [&](int it, auto dma_tag, auto pv_tag) -> f32x16 {
     constexpr bool dma = decltype(dma_tag)::value;
+    constexpr bool pv = decltype(pv_tag)::value;  // prefetch PV(it-1) operands
     const char* tb = lds + (it & (kStages - 1)) * kStageBytes;
     DmaTarget t{nullptr, 0u};
     if constexpr (dma) t = dma_target(tile0 + it + 2, (it + 2) & (kStages - 1));
@@ -240,14 +264,22 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
 #pragma unroll
     for (int kk = 0; kk < 3; ++kk) kf[kk] = *reinterpret_cast<const bf16x8*>(tb + qk_off[kk]);
     __builtin_amdgcn_sched_barrier(0);
+    mm4(3, va[1], pf);  // deferred tail of the previous PV
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kk = 0; kk < 36; ++kk) {
       if (kk == 0)
         mfma_qk_first(S, kf[0], qf[0]);
       else
         mfma_qk(S, kf[kk & 3], qf[kk]);
-      if (kk + 3 < 36)
+      if (kk + 3 < 36) {
         kf[(kk + 3) & 3] = *reinterpret_cast<const bf16x8*>(tb + qk_off[(kk + 3) & 3] + ((kk + 3) >> 2) * 128);
+      } else if constexpr (pv) {
+        // the K reads are done: fetch the first PV(it-1) operands instead
+        if (kk == 33) { pf[0] = pfrag(it - 1, 0, 0); pf[1] = pfrag(it - 1, 0, 1); }
+        if (kk == 34) { pf[2] = pfrag(it - 1, 0, 2); pf[3] = pfrag(it - 1, 0, 3); }
+        if (kk == 35) { va[0] = vfrag(it - 1, 0, 0); va[1] = vfrag(it - 1, 0, 1); }
+      }
       if constexpr (dma) {
         if ((kk & 3) == 1) dma16(t.src, dma_off[kk >> 2], t.dst + (kk >> 2) * (kThreads * 16));
       }
@@ -308,26 +340,11 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
     *reinterpret_cast<bf16x8*>(ps + 1024) = pb[1];
   };
 
-  // ---- PV pieces: V^T fragment (k-step ks, column tile c') and P^T fragment
-  // (k-step ks, head tile ht) of tile ip, and the 4 MFMAs of one (ks, c')
-  auto vfrag = [&](int ip, int ks, int cp) -> bf16x8 {
-    const char* tv = lds + (ip & (kStages - 1)) * kStageBytes + (cp >> 1) * 128;
-    return cat8(__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(tv + pv_off[cp & 1][0][ks])),
-                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(tv + pv_off[cp & 1][1][ks])));
-  };
-  auto pfrag = [&](int ip, int ks, int ht) -> bf16x8 {
-    return *reinterpret_cast<const bf16x8*>(pbuf + (ip & 1) * 8 * 1024 + (ht * 2 + ks) * 1024 + lane * 16);
-  };
-  auto mm4 = [&](int cp, const bf16x8& va, const bf16x8* pf) {
-#pragma unroll
-    for (int ht = 0; ht < 4; ++ht)
-      O[cp][ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[ht], O[cp][ht], 0, 0, 0);
-  };
 #define MLA_FENCE() __builtin_amdgcn_sched_barrier(0)
 
   // tile `it` without PV (first tile of a pass)
   auto softmax_only = [&](int it, bool& over, auto dma_tag) {
-    const f32x16 S = qk(it, dma_tag);
+    const f32x16 S = qk(it, dma_tag, std::false_type{});
     sm_scale(S, it);
     sm_localmax();
     sm_ref(over);
@@ -338,16 +355,11 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
     MLA_FENCE();
   };
 
-  // tile `it`: QK(it), then softmax(it) chunks interleaved with PV(it-1)
+  // tile `it`: QK(it), then softmax(it) chunks interleaved with PV(it-1),
+  // whose first operands QK(it) has already fetched
   auto softmax_pv = [&](int it, bool& over, auto dma_tag) {
     const int ip = it - 1;
-    const f32x16 S = qk(it, dma_tag);
-    bf16x8 pf[4], va[3];
-#pragma unroll
-    for (int ht = 0; ht < 4; ++ht) pf[ht] = pfrag(ip, 0, ht);
-    va[0] = vfrag(ip, 0, 0);
-    va[1] = vfrag(ip, 0, 1);
-    MLA_FENCE();
+    const f32x16 S = qk(it, dma_tag, std::true_type{});
     sm_scale(S, it);       mm4(0, va[0], pf); va[2] = vfrag(ip, 0, 2); interleave<8>(); MLA_FENCE();
     sm_localmax();         mm4(1, va[1], pf); va[0] = vfrag(ip, 0, 3); interleave<4>(); MLA_FENCE();
     sm_ref(over);          mm4(2, va[2], pf); va[1] = vfrag(ip, 1, 0); interleave<2>(); MLA_FENCE();
@@ -359,7 +371,7 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
     sm_exp(8);             mm4(0, va[1], pf); va[0] = vfrag(ip, 1, 2); interleave<4>(); MLA_FENCE();
     sm_pack();             mm4(1, va[2], pf); va[1] = vfrag(ip, 1, 3); interleave<2>(); MLA_FENCE();
     sm_publish(it);        mm4(2, va[0], pf); MLA_FENCE();
-    mm4(3, va[1], pf);     MLA_FENCE();
+    // mm4(3, va[1], pf) of PV(ip) runs at the start of the next QK
   };
 
   // PV(t) alone (the last tile of a pass)
@@ -399,6 +411,10 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
     }
     l_run = 0.f;
     bool over = false;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) pf[k] = bf16x8{};
+#pragma unroll
+    for (int k = 0; k < 3; ++k) va[k] = bf16x8{};
 
     if (n_tiles > 0) {
       // Iteration j issues DMA(j+2) inside its QK phase (only for tiles that
@@ -431,6 +447,7 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
         softmax_pv(it, over, std::false_type{});
       }
       tile_barrier();
+      mm4(3, va[1], pf);  // deferred tail of PV(n_tiles - 2)
       pv_only(n_tiles - 1);
     }
 

@@ -32,14 +32,31 @@ __global__ __launch_bounds__(256) void absorb_kernel(const __bf16* __restrict__ 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, lo = lane & 31;
 
+  // B operand (q_c^T: dims d = 16ks + 8g + 0..7 of token t0 + lo) of a token
+  // tile; the first tile is requested before the weights so both latencies
+  // overlap
+  bf16x8 bq[8];
+  auto load_q = [&](int t0) {
+    const int t = t0 + lo;
+    const bool tv = t < T;
+    const bf16x8* qrow = reinterpret_cast<const bf16x8*>(q_c + ((int64_t)(tv ? t : 0) * kH + h) * kDhc);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) bq[ks] = tv ? qrow[2 * ks + g] : bf16x8{};
+  };
+  load_q(0);
+
   // stage W rows d = 0..127, columns cb*128 .. +128 (256 bytes per row)
   const char* wsrc = reinterpret_cast<const char*>(w_uk + ((int64_t)h * kDhc) * kDc + cb * kAbsCols);
+  f32x4 wv[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const int q = k * 256 + tid;        // 16-byte chunk: row q/16, chunk q%16
-    const int d = q >> 4, ch = q & 15;
-    const f32x4 v = *reinterpret_cast<const f32x4*>(wsrc + (int64_t)d * kDc * 2 + ch * 16);
-    *reinterpret_cast<f32x4*>(lds + d * kAbsLdsStride + ch * 16) = v;
+    wv[k] = *reinterpret_cast<const f32x4*>(wsrc + (int64_t)(q >> 4) * kDc * 2 + (q & 15) * 16);
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int q = k * 256 + tid;
+    *reinterpret_cast<f32x4*>(lds + (q >> 4) * kAbsLdsStride + (q & 15) * 16) = wv[k];
   }
   __syncthreads();
 
@@ -62,16 +79,12 @@ __global__ __launch_bounds__(256) void absorb_kernel(const __bf16* __restrict__ 
 
   const int c0 = cb * kAbsCols + wave * 32;
   for (int t0 = 0; t0 < T; t0 += 32) {
-    const int t = t0 + lo;
-    const bool tv = t < T;
-    const bf16x8* qrow = reinterpret_cast<const bf16x8*>(q_c + ((int64_t)(tv ? t : 0) * kH + h) * kDhc);
     f32x16 acc = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const bf16x8 bq = tv ? qrow[2 * ks + g] : bf16x8{};
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], bq, acc, 0, 0, 0);
-    }
-    if (tv) {
+    for (int ks = 0; ks < 8; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], bq[ks], acc, 0, 0, 0);
+    if (t0 + 32 < T) load_q(t0 + 32);
+    const int t = t0 + lo;
+    if (t < T) {
       __bf16* orow = q_abs + ((int64_t)t * kH + h) * kDc + c0;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -82,49 +95,63 @@ __global__ __launch_bounds__(256) void absorb_kernel(const __bf16* __restrict__ 
   }
 }
 
-// Workgroup = (head h, 64-row half of d), 2 waves of 32 rows d each, looping
-// over token tiles. A = W_UV[h][d][c] rows (contiguous 16-byte reads);
-// B = o_lat^T split into bf16 high part and bf16 remainder (two MFMAs per step).
-__global__ __launch_bounds__(128) void up_proj_kernel(const float* __restrict__ o_lat, const __bf16* __restrict__ w_uv,
-                                                      __bf16* __restrict__ out, int T) {
-  const int h = blockIdx.x >> 1;
-  const int half = blockIdx.x & 1;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// Workgroup = (head h, block of 32 rows d), split-K over its 4 waves: wave w
+// covers latent columns c in [128w, 128w + 128) and all 32 rows, then the
+// four partial tiles are added in LDS in a fixed order. Within a k-step, lane
+// group g holds c = 128w + 64g + 8ks + 0..7 for both operands (any common
+// permutation of the reduction index gives the same sum), so every lane reads
+// 128 contiguous bytes of W_UV and 256 of o_lat, all issued up front.
+// A = W_UV[h][d][c] rows; B = o_lat^T split into a bf16 high part and a bf16
+// remainder (two MFMAs per step).
+__global__ __launch_bounds__(256) void up_proj_kernel(const float* __restrict__ o_lat, const __bf16* __restrict__ w_uv,
+                                                      __bf16* __restrict__ out, int T, int wg_per_xcd) {
+  __shared__ f32x4 red[4][4][64];  // [wave][register quad][lane]
+  // blockIdx -> (h, row block) with the 4 row blocks of a head on one XCD,
+  // so they share its o_lat rows in L2
+  const int x = blockIdx.x;
+  const int id = (x & 7) * wg_per_xcd + (x >> 3);
+  if (id >= kH * 4) return;
+  const int h = id >> 2;
+  const int db = id & 3;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, lo = lane & 31;
-  const int d0 = half * 64 + wave * 32;
+  const int kc = 128 * wave + 64 * g;  // first latent column of this lane's slice
 
-  const bf16x8* wrow = reinterpret_cast<const bf16x8*>(w_uv + ((int64_t)h * kDhc + d0 + lo) * kDc);
+  const bf16x8* wp = reinterpret_cast<const bf16x8*>(w_uv + ((int64_t)h * kDhc + db * 32 + lo) * kDc + kc);
+  bf16x8 a[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) a[ks] = wp[ks];
+
   for (int t0 = 0; t0 < T; t0 += 32) {
     const int t = t0 + lo;
     const bool tv = t < T;
-    const float* orow = o_lat + ((int64_t)(tv ? t : 0) * kH + h) * kDc;
+    const f32x4* xp = reinterpret_cast<const f32x4*>(o_lat + ((int64_t)(tv ? t : 0) * kH + h) * kDc + kc);
+    f32x4 xv[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) xv[k] = tv ? xp[k] : f32x4{};
     f32x16 acc = f32x16{};
-#pragma unroll 4
-    for (int ks = 0; ks < 32; ++ks) {
-      const bf16x8 a = wrow[2 * ks + g];
-      f32x4 x0 = f32x4{}, x1 = f32x4{};
-      if (tv) {
-        x0 = *reinterpret_cast<const f32x4*>(orow + 16 * ks + 8 * g);
-        x1 = *reinterpret_cast<const f32x4*>(orow + 16 * ks + 8 * g + 4);
-      }
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
       bf16x8 hi, lw;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        hi[j] = (__bf16)x0[j];
-        hi[4 + j] = (__bf16)x1[j];
-        lw[j] = (__bf16)(x0[j] - (float)hi[j]);
-        lw[4 + j] = (__bf16)(x1[j] - (float)hi[4 + j]);
+      for (int j = 0; j < 8; ++j) {
+        const float v = xv[2 * ks + (j >> 2)][j & 3];
+        hi[j] = (__bf16)v;
+        lw[j] = (__bf16)(v - (float)hi[j]);
       }
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, hi, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, lw, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], hi, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], lw, acc, 0, 0, 0);
     }
-    if (tv) {
-      __bf16* op = out + ((int64_t)t * kH + h) * kDhc + d0;
+    if (t0 > 0) __syncthreads();  // the previous tile's sums have been read
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const bf16x4 o = {(__bf16)acc[4 * q], (__bf16)acc[4 * q + 1], (__bf16)acc[4 * q + 2], (__bf16)acc[4 * q + 3]};
-        *reinterpret_cast<bf16x4*>(op + 8 * q + 4 * g) = o;
-      }
+    for (int q = 0; q < 4; ++q) red[wave][q][lane] = f32x4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+    __syncthreads();
+    // wave w finishes register quad w: rows d = 32db + 8w + 4g + 0..3 of token t
+    const f32x4 r = ((red[0][wave][lane] + red[1][wave][lane]) + red[2][wave][lane]) + red[3][wave][lane];
+    if (tv) {
+      const bf16x4 o = {(__bf16)r[0], (__bf16)r[1], (__bf16)r[2], (__bf16)r[3]};
+      *reinterpret_cast<bf16x4*>(out + ((int64_t)t * kH + h) * kDhc + db * 32 + 8 * wave + 4 * g) = o;
     }
   }
 }
@@ -135,7 +162,9 @@ hipError_t launch_absorb(const __bf16* q_c, const __bf16* w_uk, __bf16* q_abs, i
 }
 
 hipError_t launch_up_proj(const float* o_lat, const __bf16* w_uv, __bf16* out, int T, hipStream_t stream) {
-  hipLaunchKernelGGL(up_proj_kernel, dim3(kH * 2), dim3(128), 0, stream, o_lat, w_uv, out, T);
+  constexpr int kWg = kH * 4;
+  constexpr int kPerXcd = kWg / 8;
+  hipLaunchKernelGGL(up_proj_kernel, dim3(kWg), dim3(256), 0, stream, o_lat, w_uv, out, T, kPerXcd);
   return hipGetLastError();
 }
 
