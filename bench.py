@@ -35,8 +35,11 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_paged_long_hbm_traffic.jso
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=60)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--steps", type=int, default=100)
+    # the board's power controller overshoots during the first ~15 ms of
+    # sustained load (decode slows by up to 40%, then recovers); 100 warmup
+    # steps (~30 ms) start the timed region in the settled state
+    p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--workload", default="long", choices=["single", "uniform", "ragged", "long", "prefill"])
     p.add_argument("--layers", type=int, default=0, help="resident cache layers (0: workload default)")
     p.add_argument("--splits", type=int, default=0, help="num_splits (0: library recommendation)")
