@@ -155,20 +155,6 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
   const int h_own = wave * 32 + lo;                       // head this lane owns in QK/softmax
   const int64_t qbase = (int64_t)(b * a.s_q + i) * kH;    // row of head 0 of this query
 
-  // queries: B operand of S^T = K . Q^T; lane (g, lo) holds dims 16kk+8g..+7 of head h_own
-  bf16x8 qf[36];
-  if (n_tiles > 0) {
-    const bf16x8* qa = reinterpret_cast<const bf16x8*>(q_abs + (qbase + h_own) * kDc);
-    const bf16x8* qr = reinterpret_cast<const bf16x8*>(q_r + (qbase + h_own) * kDr);
-#pragma unroll
-    for (int kk = 0; kk < 32; ++kk) qf[kk] = qa[2 * kk + g];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) qf[32 + kk] = qr[2 * kk + g];
-    // land the queries before the tile loop: otherwise the compiler re-waits
-    // for them inside the loop, where the wait would also drain cache DMA
-    wait_vmcnt<0>();
-  }
-
   // QK A operand: row lo, chunk 2kk+g; kk = 4a + r -> offset qk_off[r] + 128a
   int qk_off[4];
 #pragma unroll
@@ -219,6 +205,24 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
 #pragma unroll
     for (int k = 0; k < kDmaPerThread; ++k) dma16(t.src, dma_off[k], t.dst + k * (kThreads * 16));
   };
+
+  // The first two tiles are requested before the queries so that the cache
+  // latency and the query loads overlap; all of them land before the tile loop
+  // (otherwise the compiler re-waits for the queries inside the loop, where the
+  // wait would also drain cache DMA).
+  if (n_tiles > 0) issue(tile0, 0);
+  if (n_tiles > 1) issue(tile0 + 1, 1);
+  // queries: B operand of S^T = K . Q^T; lane (g, lo) holds dims 16kk+8g..+7 of head h_own
+  bf16x8 qf[36];
+  if (n_tiles > 0) {
+    const bf16x8* qa = reinterpret_cast<const bf16x8*>(q_abs + (qbase + h_own) * kDc);
+    const bf16x8* qr = reinterpret_cast<const bf16x8*>(q_r + (qbase + h_own) * kDr);
+#pragma unroll
+    for (int kk = 0; kk < 32; ++kk) qf[kk] = qa[2 * kk + g];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) qf[32 + kk] = qr[2 * kk + g];
+    wait_vmcnt<0>();
+  }
 
   const float c_log2 = a.scale_log2;
   f32x16 O[4][4];            // O^T tiles [column tile c'][head tile ht]
@@ -421,8 +425,10 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
       // exist); stage (j+2)&3 was last read by PV(j-2) in iteration j-1. At
       // the top of iteration it the only loads issued after DMA(it) are those
       // of DMA(it+1).
-      issue(tile0, 0);
-      if (n_tiles > 1) issue(tile0 + 1, 1);
+      if (pass > 0) {  // the first pass's two tiles were issued with the queries
+        issue(tile0, 0);
+        if (n_tiles > 1) issue(tile0 + 1, 1);
+      }
       // tile 0: QK + softmax only
       if (n_tiles > 1) wait_vmcnt<kDmaPerThread>(); else wait_vmcnt<0>();
       tile_barrier();
@@ -465,7 +471,15 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
     __syncthreads();                         // everyone has read the flag and lbuf
   }
 
-  // ---- epilogue: normalise, write this split's partial rows and their LSEs
+  // ---- epilogue: normalise, write this split's partial rows and their LSEs.
+  // A lane holds 16-byte pieces of one head row, so storing straight from the
+  // accumulators would write 32 bytes of 32 different rows per instruction and
+  // leave partly written lines behind. Instead each wave stages 32 head rows of
+  // its 128-column slice in its own LDS region (the stage ring is idle now) and
+  // stores whole 512-byte row slices, two rows per instruction. LDS operations
+  // of one wave complete in order, so no barrier is needed between the two.
+  constexpr int kEpiStride = 128 * 4 + 16;  // staged row: 512 bytes + 16 of padding against bank conflicts
+  char* const ebuf = lds + wave * (32 * kEpiStride);
   float inv[4];
   bool empty[4];
 #pragma unroll
@@ -476,7 +490,6 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
   }
 #pragma unroll
   for (int ht = 0; ht < 4; ++ht) {
-    float* orow = o_part + ((qbase + ht * 32 + lo) * a.num_splits + split) * kDc + wave * 128;
 #pragma unroll
     for (int cp = 0; cp < 4; ++cp)
 #pragma unroll
@@ -484,8 +497,17 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
         f32x4 v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = empty[ht] ? 0.f : O[cp][ht][4 * q + e] * inv[ht];
-        *reinterpret_cast<f32x4*>(orow + 32 * cp + 8 * q + 4 * g) = v;
+        *reinterpret_cast<f32x4*>(ebuf + lo * kEpiStride + (32 * cp + 8 * q + 4 * g) * 4) = v;
       }
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int r = 2 * j + g;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(ebuf + r * kEpiStride + lo * 16);
+      float* orow = o_part + ((qbase + ht * 32 + r) * a.num_splits + split) * kDc + wave * 128 + lo * 4;
+      *reinterpret_cast<f32x4*>(orow) = v;
+    }
+    asm volatile("" ::: "memory");
   }
   if (g == 0) {
     const float l = lbuf[h_own];
