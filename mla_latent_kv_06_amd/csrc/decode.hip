@@ -61,6 +61,20 @@ __device__ __forceinline__ int swz(int t) { return ((t & 3) << 1) ^ ((t >> 2) & 
 
 __device__ __forceinline__ float shfl_xor32(float v) { return __shfl_xor(v, 32, 64); }
 
+// max(v[l], v[l ^ 32]) in every lane, on the VALU: v_permlane32_swap exchanges
+// the upper half-wave of one register with the lower half of another (a
+// copy of v), so each lane then holds both values of its pair. Unlike a
+// cross-half shuffle it does not go through LDS, whose counter would also
+// make the wait cover the LDS reads in flight. Written as asm with the wait
+// states for its operands (the builtin loses its second result with this
+// compiler).
+__device__ __forceinline__ float pair_max32(float v) {
+  float w = v;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1\n\tv_max_f32 %0, %0, %1"
+               : "+v"(v), "+v"(w));
+  return v;
+}
+
 // S^T accumulation kept in VGPRs (the softmax reads it with VALU) while the
 // 256 AGPRs hold O^T. Only this MFMA is written as asm: a chain whose srcC is
 // exactly the previous destination needs no wait states.
@@ -297,7 +311,7 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
   // ---- softmax numerators in chunks (lane owns head h_own and tokens
   // 8(r>>2) + 4g + (r&3) of the tile); chunks are interleaved with PV below
   float xs[16];
-  float mx = 0.f, mx_other = 0.f;
+  float mx = 0.f;
   bf16x8 pb[2];
   // xs = raw scores; the tail tile masks tokens past the visible length
   auto sm_scale = [&](const f32x16& S, int it) {
@@ -315,12 +329,12 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
 #pragma unroll
     for (int r = 3; r < 15; r += 2) mx = fmaxf(fmaxf(mx, xs[r]), xs[r + 1]);
     mx = fmaxf(mx, xs[15]);
-    mx_other = shfl_xor32(mx);
+    mx = pair_max32(mx);
   };
   // reference and running max in log2 units (softmax_scale > 0, so the max of
   // the scaled scores is the scaled max)
   auto sm_ref = [&](bool& over) {
-    mx = fmaxf(mx, mx_other) * c_log2;
+    mx = mx * c_log2;
     m_seen = fmaxf(m_seen, mx);
     m_ref = m_ref == -INFINITY ? mx : m_ref;  // first tile of the first pass
     over |= mx > m_ref + kRefSlack;
@@ -332,6 +346,13 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
     for (int r = r0; r < r0 + 8; ++r) {
       xs[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(xs[r], c_log2, -m_ref));
       l_run += xs[r];
+    }
+  };
+  auto sm_exp2 = [&](int r) {  // scores r, r+1
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      xs[r + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(xs[r + e], c_log2, -m_ref));
+      l_run += xs[r + e];
     }
   };
   auto sm_pack = [&]() {
