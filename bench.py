@@ -140,7 +140,7 @@ def main():
     q_c, q_r = inp.q_c.to(dev), inp.q_r.to(dev)
     w_uk, w_uv = inp.w_uk.to(dev), inp.w_uv.to(dev)
     lens = [int(x) for x in st0.seqlens]
-    S = args.splits or M.mla_recommended_splits(cfg.B, cfg.s_q, max(lens))
+    S = args.splits or M.mla_plan_splits(lens, tables.shape[2], cfg.s_q)
     B, s_q = cfg.B, cfg.s_q
     T = B * s_q
 

@@ -82,10 +82,21 @@ mla_status mla_absorb_q(const void* q_c, const void* w_uk, void* q_abs,
  * returns 0 for non-positive arguments. */
 size_t mla_decode_workspace_bytes(int B, int s_q, int H, int num_splits);
 
-/* A split count for mla_decode_paged that fills the GPU for these sizes
- * (host-only heuristic; max_len is the longest sequence in tokens). The
- * result is in [1, ceil(max_len / 64)] (1 if max_len < 1). */
+/* A split count for mla_decode_paged (host-only heuristic; max_len is the
+ * longest sequence in tokens, num_cus the GPU's compute units, 256 if <= 0):
+ * mla_plan_splits for B sequences of max_len tokens and a block table just
+ * wide enough for them. The result is in [1, min(ceil(max_len / 64), 256)]
+ * (1 if max_len < 1). */
 int mla_recommended_splits(int B, int s_q, int max_len, int num_cus);
+
+/* Split count for a batch whose lengths are known on the host
+ * (seqlens_host: HOST pointer to B int32 lengths, clamped as
+ * mla_decode_paged clamps them): the smallest S whose scan plan minimises a
+ * time model of the launch (the slowest workgroup's pages and row pieces,
+ * plus writing and re-reading every partial). Returns 1 for NULL or
+ * non-positive sizes and for B * s_q above 2^22; otherwise a value in
+ * [1, min(max_pages, 256)]. */
+int mla_plan_splits(const int32_t* seqlens_host, int B, int s_q, int max_pages, int num_cus);
 
 /* Stage 1: split scan of the paged latent cache, absorbed scores, online
  * softmax, P . c_KV on matrix cores (teardown page, section 4 absorbed
@@ -104,12 +115,25 @@ int mla_recommended_splits(int B, int s_q, int max_len, int num_cus);
  *               [0, max_pages * 64].
  *   softmax_scale  multiplies q_abs.c_KV + q_R.k_R (1/sqrt(192) for DeepSeek);
  *               must be positive and finite.
- *   num_splits  in [1, max_pages]; query i of sequence b sees tokens
- *               t <= L_b - s_q + i, i.e. n = ceil((L_b - s_q + i + 1) / 64)
- *               pages, and split s scans pages [s*q, min((s+1)*q, n)) with
- *               q = ceil(n / num_splits). Empty splits are allowed.
- *   o_part      fp32 [B, s_q, H, num_splits, 512] output: each split's
- *               softmax-normalised latent output (zeros for an empty split)
+ *   num_splits  S in [1, max_pages]: the partial slots per row. Query i of
+ *               sequence b sees tokens t <= L_b - s_q + i, i.e. row (b, i)
+ *               has n = ceil((L_b - s_q + i + 1) / 64) pages. The scan
+ *               concatenates the pages of all rows in (b, i) order (P_tot in
+ *               all, row r starting at page P_r) and gives each of 256
+ *               workgroups an equal range of W pages, so ragged batches are
+ *               balanced:
+ *                 S > 1: W = max(ceil(P_tot / 256), ceil((n_max - 1)/(S - 1)), 1);
+ *                        the piece of row r inside range k (pages
+ *                        [kW, (k+1)W)) goes to slot k - floor(P_r / W);
+ *                 S = 1: W = ceil(P_tot / 256); rows are not cut, each goes
+ *                        to slot 0.
+ *               Slots a row does not use are empty. The plan depends on the
+ *               lengths of the whole batch (not on any other input); see
+ *               mla_plan_splits for choosing S. B * s_q * max_pages must be
+ *               below 2^31.
+ *   o_part      fp32 [B, s_q, H, num_splits, 512] output: each non-empty
+ *               split's softmax-normalised latent output; the rows of an
+ *               empty split are not written
  *   lse_part    fp32 [B, s_q, H, num_splits] output: natural-log
  *               log-sum-exp of the split's scaled scores (-inf if empty)
  * B >= 1, 1 <= s_q <= 4096, H == MLA_HEADS, 1 <= max_pages,
@@ -125,7 +149,9 @@ mla_status mla_decode_paged(const void* q_abs, const void* q_r,
  * blocks", KV-split reduction):
  *     LSE = M + ln sum_s exp(lse_s - M),  M = max_s lse_s
  *     o   = sum_s exp(lse_s - LSE) * o_s
- * A row whose splits are all empty gives o = 0 and LSE = -inf.
+ * A split with lse_s = -inf is empty: its o_part row is never read (it may
+ * hold anything). A row whose splits are all empty gives o = 0 and
+ * LSE = -inf.
  *   o_part   fp32 [B, s_q, H, num_splits, 512], lse_part fp32 [B, s_q, H, num_splits]
  *   o_lat    fp32 [B, s_q, H, 512] output,  lse fp32 [B, s_q, H] output
  * B >= 1, s_q >= 1, H == MLA_HEADS, num_splits >= 1. */

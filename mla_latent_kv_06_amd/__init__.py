@@ -75,6 +75,15 @@ def mla_recommended_splits(B: int, s_q: int, max_len: int, cus: int | None = Non
     return int(_lib.LIB.mla_recommended_splits(int(B), int(s_q), int(max_len), int(cus or num_cus())))
 
 
+def mla_plan_splits(seqlens, max_pages: int, s_q: int = 1, cus: int | None = None) -> int:
+    """Split count for host-known lengths (a sequence of ints or a CPU int tensor)."""
+    lens = torch.as_tensor(seqlens, dtype=torch.int32, device="cpu").contiguous()
+    if lens.dim() != 1 or lens.numel() < 1:
+        raise ValueError("seqlens must be a non-empty 1-D sequence of lengths")
+    return int(_lib.LIB.mla_plan_splits(lens.data_ptr(), int(lens.numel()), int(s_q), int(max_pages),
+                                        int(cus or num_cus())))
+
+
 def mla_decode_workspace_bytes(B: int, s_q: int, num_splits: int, heads: int = H) -> int:
     return int(_lib.LIB.mla_decode_workspace_bytes(int(B), int(s_q), int(heads), int(num_splits)))
 

@@ -2,11 +2,12 @@
 // (sequence, query, head) row by their log-sum-exp (KV-split reduction of the
 // K3 time-share study, "Inside the blocks").
 //
-// One wave per row: the row's split LSEs are wave-uniform (scalar loads);
-// every lane owns 8 of the 512 latent columns and streams the partial rows
-// with 32-byte loads (2 KiB contiguous per split across the wave). The loads
-// of up to 16 splits are issued before the LSE arithmetic so that their
-// latency overlaps it.
+// One wave per row: lane k holds the LSE of split k (of each block of 64),
+// max and sum come from wave reductions, and each split's weight is
+// broadcast with readlane. Every lane owns 8 of the 512 latent columns and
+// streams the partial rows with 32-byte loads (2 KiB contiguous per split
+// across the wave), up to 16 splits' loads in flight. Splits with LSE = -inf
+// are empty; their partial rows were never written and are not read.
 #include "mla_device.hpp"
 #include "decode.hpp"
 
@@ -40,18 +41,6 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const float* op = o_part + (int64_t)row * num_splits * kDc + 8 * lane;
   float* orow = o_lat + (int64_t)row * kDc + 8 * lane;
 
-  f32x4 v0[kCombineChunk], v1[kCombineChunk];
-  auto load_chunk = [&](int s0) {
-#pragma unroll
-    for (int k = 0; k < kCombineChunk; ++k) {
-      if (s0 + k < num_splits) {
-        v0[k] = *reinterpret_cast<const f32x4*>(op + (int64_t)(s0 + k) * kDc);
-        v1[k] = *reinterpret_cast<const f32x4*>(op + (int64_t)(s0 + k) * kDc + 4);
-      }
-    }
-  };
-  load_chunk(0);
-
   float M = -INFINITY;
   for (int s = lane; s < num_splits; s += 64) M = fmaxf(M, lp[s]);
   M = wave_max(M);
@@ -66,19 +55,29 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   tot = wave_sum(tot);
   const float L = M + logf(tot);
 
-  // lane k holds the weight of split c0 + k of the current 64-split block;
-  // each split's weight is then broadcast with readlane
   f32x4 a0 = f32x4{}, a1 = f32x4{};
-  float wl = 0.f;
+  f32x4 v0[kCombineChunk], v1[kCombineChunk];
+  float wl = 0.f;  // lane k: weight of split (s0 & ~63) + k
+  auto weight = [&](int s) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), s & 63));
+  };
   for (int s0 = 0; s0 < num_splits; s0 += kCombineChunk) {
-    if ((s0 & 63) == 0) wl = s0 + lane < num_splits ? expf(lp[s0 + lane] - L) : 0.f;  // 0 for lse = -inf
-    if (s0 > 0) load_chunk(s0);
+    if ((s0 & 63) == 0) wl = s0 + lane < num_splits ? expf(lp[s0 + lane] - L) : 0.f;  // 0 when lse = -inf
+#pragma unroll
+    for (int k = 0; k < kCombineChunk; ++k) {
+      if (s0 + k < num_splits && weight(s0 + k) > 0.f) {
+        v0[k] = *reinterpret_cast<const f32x4*>(op + (int64_t)(s0 + k) * kDc);
+        v1[k] = *reinterpret_cast<const f32x4*>(op + (int64_t)(s0 + k) * kDc + 4);
+      }
+    }
 #pragma unroll
     for (int k = 0; k < kCombineChunk; ++k) {
       if (s0 + k < num_splits) {
-        const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), (s0 & 63) + k));
-        a0 += w * v0[k];
-        a1 += w * v1[k];
+        const float w = weight(s0 + k);
+        if (w > 0.f) {
+          a0 += w * v0[k];
+          a1 += w * v1[k];
+        }
       }
     }
   }

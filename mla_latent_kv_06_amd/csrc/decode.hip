@@ -54,6 +54,7 @@ constexpr int kDmaPerThread = kStageBytes / (kThreads * 16);  // 9
 constexpr int kPBytes = 2 * 4 * 2 * 1024;         // [slot][wave][k-step][64 lanes x 16 B]
 constexpr int kLdsBytes = kStages * kStageBytes + kPBytes;   // 163840 = all of it
 constexpr float kRefSlack = 64.0f;                // log2 headroom above the reference max
+constexpr int kScanGroups = 256;                  // workgroups of a scan (one per MI355X CU)
 static_assert(kDmaPerThread * kThreads * 16 == kStageBytes, "stage must split into 16-byte loads");
 static_assert(kLdsBytes <= 163840, "LDS budget");
 
@@ -129,6 +130,38 @@ __device__ __forceinline__ bf16x8 cat8(const i16x4& v0, const i16x4& v1) {
   return bf16x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
 }
 
+// Split-plan arithmetic counts pages in 32 bits: the host rejects launches
+// with B * s_q * max_pages >= 2^31, which bounds every sum below.
+// Pages of keys 1..x summed over rows: sum_{v=1..x} ceil(v / 64) (0 for x <= 0).
+__device__ __forceinline__ int pages_prefix(int x) {
+  if (x <= 0) return 0;
+  const int q = x >> 6, r = x & (kPage - 1);
+  return kPage * q * (q + 1) / 2 + r * (q + 1);
+}
+// Pages of the first i query rows of a sequence holding L tokens: row i' sees
+// L - s_q + i' + 1 keys.
+__device__ __forceinline__ int rows_pages(int L, int s_q, int i) {
+  return pages_prefix(L - s_q + i) - pages_prefix(L - s_q);
+}
+__device__ __forceinline__ int wave_sum32(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return __builtin_amdgcn_readfirstlane(v);
+}
+__device__ __forceinline__ int wave_max32(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
+  return __builtin_amdgcn_readfirstlane(v);
+}
+__device__ __forceinline__ int wave_incl_scan32(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o, 64);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
 }  // namespace
 
 __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
@@ -144,30 +177,89 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
   const int lo = lane & 31;
   const int g = lane >> 5;
 
-  // blockIdx -> work item, contiguous per XCD (workgroups are dealt to the 8
-  // XCDs round-robin), so neighbouring items share an L2.
-  const int x = blockIdx.x;
-  const int item = (x & 7) * a.items_per_xcd + (x >> 3);
-  if (item >= a.items) return;
-  const int i = item % a.s_q;
-  const int rest = item / a.s_q;
-  const int split = rest % a.num_splits;
-  const int b = rest / a.num_splits;
+  // ---- split plan: the pages of all rows (b, i), concatenated in order, are
+  // cut into kScanGroups equal ranges of W pages; workgroup k scans range k
+  // and writes one partial for every row piece in it, into slot
+  // k - floor(P_r / W) of row r (P_r = the row's first page in the
+  // concatenation). W is at least ceil((n_max - 1) / (num_splits - 1)), so a
+  // row never needs more than num_splits slots; with num_splits = 1 rows are
+  // not cut and each row goes whole to the range holding its first page.
+  const int S = a.num_splits;
+  // the first 64 sequences stay in registers (lane = sequence); larger
+  // batches are read in further blocks of 64
+  const int L0 = lane < a.B ? clamp_len(seqlens[lane], a.max_pages) : 0;
+  const int T0 = lane < a.B ? rows_pages(L0, a.s_q, a.s_q) : 0;
+  int p_tot = wave_sum32(T0);
+  int n_max = wave_max32((L0 + kPage - 1) / kPage);
+  bool any_empty_row = __any(lane < a.B && L0 < a.s_q);
+  for (int b0 = 64; b0 < a.B; b0 += 64) {
+    const int bb = b0 + lane;
+    const int L = bb < a.B ? clamp_len(seqlens[bb], a.max_pages) : 0;
+    p_tot += wave_sum32(bb < a.B ? rows_pages(L, a.s_q, a.s_q) : 0);
+    n_max = max(n_max, wave_max32((L + kPage - 1) / kPage));
+    any_empty_row |= __any(bb < a.B && L < a.s_q);
+  }
+  int W = (p_tot + kScanGroups - 1) / kScanGroups;
+  if (S > 1) W = max(W, (n_max - 1 + S - 2) / (S - 1));
+  if (W < 1) W = 1;
+  // the ceil(p_tot / W) non-empty ranges are dealt contiguously over all 8
+  // XCDs (workgroups go to the XCDs round-robin), so a sequence's pieces
+  // share an L2 for its queries and every XCD's bandwidth is used
+  const int n_ranges = (p_tot + W - 1) / W;
+  const int per_xcd = (n_ranges + 7) / 8;
+  const bool has_range = (int)(blockIdx.x >> 3) < per_xcd;
+  const int k = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  const int r_lo = has_range ? k * W : p_tot;  // k * W < p_tot + W <= 2^31
+  const int r_hi = min(r_lo + W, p_tot);
 
-  const int L = clamp_len(seqlens[b], a.max_pages);
-  int Lv = L - a.s_q + i + 1;  // keys visible to query i
-  if (Lv < 0) Lv = 0;
-  const int n_pages = (Lv + kPage - 1) / kPage;
-  const int per = (n_pages + a.num_splits - 1) / a.num_splits;
-  const int p0 = min(split * per, n_pages);
-  const int p1 = min(p0 + per, n_pages);
-  const int t_begin = p0 * kPage;
-  const int t_end = min(p1 * kPage, Lv);
-  const int tile0 = t_begin / kTok;
-  const int n_tiles = t_end > t_begin ? (t_end - t_begin + kTok - 1) / kTok : 0;
+  // rows that see no key at all: every slot's LSE is -inf; row r is written
+  // by workgroup (blockIdx) r mod kScanGroups
+  if (any_empty_row) {
+    for (int bb = 0; bb < a.B; ++bb) {
+      const int L = clamp_len(seqlens[bb], a.max_pages);
+      for (int ii = 0; ii < a.s_q - L; ++ii) {
+        const int64_t r = (int64_t)bb * a.s_q + ii;
+        if (r % kScanGroups != (int)blockIdx.x) continue;
+        for (int q = tid; q < kH * S; q += kThreads) lse_part[r * kH * S + q] = -INFINITY;
+      }
+    }
+  }
+  if (r_lo >= r_hi) return;
 
+  // first row touching the range: the sequence whose pages end past r_lo, then
+  // (binary search) its last query row starting at or before r_lo
+  int cb = 0, cL = 0;
+  int cp = 0;  // first page of sequence cb
+  for (int b0 = 0; b0 < a.B; b0 += 64) {
+    const int bb = b0 + lane;
+    const int L = b0 == 0 ? L0 : (bb < a.B ? clamp_len(seqlens[bb], a.max_pages) : 0);
+    const int t = b0 == 0 ? T0 : (bb < a.B ? rows_pages(L, a.s_q, a.s_q) : 0);
+    const int incl = wave_incl_scan32(t, lane);
+    const uint64_t hit = __ballot(cp + incl > r_lo);
+    if (hit) {
+      const int f = __builtin_ctzll(hit);
+      cb = b0 + f;
+      cL = __builtin_amdgcn_readlane(L, f);
+      cp += __builtin_amdgcn_readlane(incl - t, f);
+      break;
+    }
+    cp += __builtin_amdgcn_readlane(incl, 63);
+  }
+  int ci = 0;
+  {
+    int lo_i = 0, hi_i = a.s_q - 1;  // largest i with cp + rows_pages(cL, s_q, i) <= r_lo
+    while (lo_i < hi_i) {
+      const int mid = (lo_i + hi_i + 1) >> 1;
+      if (cp + rows_pages(cL, a.s_q, mid) <= r_lo) lo_i = mid; else hi_i = mid - 1;
+    }
+    ci = lo_i;
+    cp += rows_pages(cL, a.s_q, ci);
+  }
+
+  // per-piece state, set by the piece loop at the end of the kernel
+  int b = 0, i = 0, split = 0, tile0 = 0, t_end = 0, n_tiles = 0;
+  int64_t qbase = 0;  // row of head 0 of the piece's query
   const int h_own = wave * 32 + lo;                       // head this lane owns in QK/softmax
-  const int64_t qbase = (int64_t)(b * a.s_q + i) * kH;    // row of head 0 of this query
 
   // QK A operand: row lo, chunk 2kk+g; kk = 4a + r -> offset qk_off[r] + 128a
   int qk_off[4];
@@ -220,23 +312,7 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
     for (int k = 0; k < kDmaPerThread; ++k) dma16(t.src, dma_off[k], t.dst + k * (kThreads * 16));
   };
 
-  // The first two tiles are requested before the queries so that the cache
-  // latency and the query loads overlap; all of them land before the tile loop
-  // (otherwise the compiler re-waits for the queries inside the loop, where the
-  // wait would also drain cache DMA).
-  if (n_tiles > 0) issue(tile0, 0);
-  if (n_tiles > 1) issue(tile0 + 1, 1);
-  // queries: B operand of S^T = K . Q^T; lane (g, lo) holds dims 16kk+8g..+7 of head h_own
-  bf16x8 qf[36];
-  if (n_tiles > 0) {
-    const bf16x8* qa = reinterpret_cast<const bf16x8*>(q_abs + (qbase + h_own) * kDc);
-    const bf16x8* qr = reinterpret_cast<const bf16x8*>(q_r + (qbase + h_own) * kDr);
-#pragma unroll
-    for (int kk = 0; kk < 32; ++kk) qf[kk] = qa[2 * kk + g];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) qf[32 + kk] = qr[2 * kk + g];
-    wait_vmcnt<0>();
-  }
+  bf16x8 qf[36];  // queries of the current piece
 
   const float c_log2 = a.scale_log2;
   f32x16 O[4][4];            // O^T tiles [column tile c'][head tile ht]
@@ -425,121 +501,171 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
   float* const lbuf = reinterpret_cast<float*>(pbuf);   // end-of-pass exchange (reuses the P slots)
   int* const flag = reinterpret_cast<int*>(pbuf + 1024);
 
-  for (int pass = 0; pass < 2; ++pass) {
-    // O^T = 0 through the matrix core, so O is only ever defined by MFMAs
-    {
-      const bf16x8 z = bf16x8{};
-#pragma unroll
-      for (int cp = 0; cp < 4; ++cp)
-#pragma unroll
-        for (int ht = 0; ht < 4; ++ht) O[cp][ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(z, z, f32x16{}, 0, 0, 0);
-    }
-    l_run = 0.f;
-    bool over = false;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) pf[k] = bf16x8{};
-#pragma unroll
-    for (int k = 0; k < 3; ++k) va[k] = bf16x8{};
+  // ---- piece loop: rows touching [r_lo, r_hi), in order
+  while (cb < a.B && cp < r_hi) {
+    const int v = cL - a.s_q + ci + 1;          // keys visible to query ci
+    const int n_row = v > 0 ? (v + kPage - 1) / kPage : 0;
+    const bool mine = n_row > 0 && (S > 1 ? cp + n_row > r_lo : cp >= r_lo);
+    if (mine) {
+      const int pa = S > 1 ? max(r_lo, cp) - cp : 0;
+      const int pe = S > 1 ? min(r_hi, cp + n_row) - cp : n_row;
+      b = cb;
+      i = ci;
+      split = S > 1 ? k - cp / W : 0;
+      qbase = ((int64_t)b * a.s_q + i) * kH;
+      const int t_begin = pa * kPage;
+      t_end = min(pe * kPage, v);
+      tile0 = t_begin / kTok;
+      n_tiles = (t_end - t_begin + kTok - 1) / kTok;
+      m_ref = -INFINITY;
+      m_seen = -INFINITY;
 
-    if (n_tiles > 0) {
-      // Iteration j issues DMA(j+2) inside its QK phase (only for tiles that
-      // exist); stage (j+2)&3 was last read by PV(j-2) in iteration j-1. At
-      // the top of iteration it the only loads issued after DMA(it) are those
-      // of DMA(it+1).
-      if (pass > 0) {  // the first pass's two tiles were issued with the queries
-        issue(tile0, 0);
-        if (n_tiles > 1) issue(tile0 + 1, 1);
+      // The first two tiles are requested before the queries so that the cache
+      // latency and the query loads overlap; all of them land before the tile loop
+      // (otherwise the compiler re-waits for the queries inside the loop, where the
+      // wait would also drain cache DMA).
+      if (n_tiles > 0) issue(tile0, 0);
+      if (n_tiles > 1) issue(tile0 + 1, 1);
+      // queries: B operand of S^T = K . Q^T; lane (g, lo) holds dims 16kk+8g..+7 of head h_own
+      if (n_tiles > 0) {
+        const bf16x8* qa = reinterpret_cast<const bf16x8*>(q_abs + (qbase + h_own) * kDc);
+        const bf16x8* qr = reinterpret_cast<const bf16x8*>(q_r + (qbase + h_own) * kDr);
+    #pragma unroll
+        for (int kk = 0; kk < 32; ++kk) qf[kk] = qa[2 * kk + g];
+    #pragma unroll
+        for (int kk = 0; kk < 4; ++kk) qf[32 + kk] = qr[2 * kk + g];
+        wait_vmcnt<0>();
       }
-      // tile 0: QK + softmax only
-      if (n_tiles > 1) wait_vmcnt<kDmaPerThread>(); else wait_vmcnt<0>();
-      tile_barrier();
-      zero_tail(0);
-      if (n_tiles > 2)
-        softmax_only(0, over, std::true_type{});
-      else
-        softmax_only(0, over, std::false_type{});
-      // steady state: QK(it) + softmax(it) overlapped with PV(it - 1); the
-      // last two tiles issue no further DMA
-      int it = 1;
-      for (; it + 2 < n_tiles; ++it) {
-        wait_vmcnt<kDmaPerThread>();
-        tile_barrier();
-        zero_tail(it);
-        softmax_pv(it, over, std::true_type{});
-      }
-      for (; it < n_tiles; ++it) {
-        if (it + 1 < n_tiles) wait_vmcnt<kDmaPerThread>(); else wait_vmcnt<0>();
-        tile_barrier();
-        zero_tail(it);
-        softmax_pv(it, over, std::false_type{});
-      }
-      tile_barrier();
-      mm4(3, va[1], pf);  // deferred tail of PV(n_tiles - 2)
-      pv_only(n_tiles - 1);
-    }
 
-    // end of pass: publish per-head sums and whether any score outgrew its reference
-    __syncthreads();                        // all P slot reads are done
-    if (tid == 0) *flag = 0;
-    __syncthreads();
-    const float l_tot = l_run + shfl_xor32(l_run);
-    if (g == 0) lbuf[h_own] = l_tot;
-    if (__any(over) && lane == 0) *flag = 1;
-    __syncthreads();
-    const bool again = *flag != 0;
-    if (!again || pass == 1) break;
-    m_ref = m_seen;                          // exact max: a second rescan is impossible
-    __syncthreads();                         // everyone has read the flag and lbuf
-  }
+      for (int pass = 0; pass < 2; ++pass) {
+        // O^T = 0 through the matrix core, so O is only ever defined by MFMAs
+        {
+          const bf16x8 z = bf16x8{};
+    #pragma unroll
+          for (int cp = 0; cp < 4; ++cp)
+    #pragma unroll
+            for (int ht = 0; ht < 4; ++ht) O[cp][ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(z, z, f32x16{}, 0, 0, 0);
+        }
+        l_run = 0.f;
+        bool over = false;
+    #pragma unroll
+        for (int k = 0; k < 4; ++k) pf[k] = bf16x8{};
+    #pragma unroll
+        for (int k = 0; k < 3; ++k) va[k] = bf16x8{};
 
-  // ---- epilogue: normalise, write this split's partial rows and their LSEs.
-  // A lane holds 16-byte pieces of one head row, so storing straight from the
-  // accumulators would write 32 bytes of 32 different rows per instruction and
-  // leave partly written lines behind. Instead each wave stages 32 head rows of
-  // its 128-column slice in its own LDS region (the stage ring is idle now) and
-  // stores whole 512-byte row slices, two rows per instruction. LDS operations
-  // of one wave complete in order, so no barrier is needed between the two.
-  constexpr int kEpiStride = 128 * 4 + 16;  // staged row: 512 bytes + 16 of padding against bank conflicts
-  char* const ebuf = lds + wave * (32 * kEpiStride);
-  float inv[4];
-  bool empty[4];
-#pragma unroll
-  for (int ht = 0; ht < 4; ++ht) {
-    const float l = lbuf[ht * 32 + lo];
-    empty[ht] = !(l > 0.f);
-    inv[ht] = empty[ht] ? 0.f : 1.0f / l;
-  }
-#pragma unroll
-  for (int ht = 0; ht < 4; ++ht) {
-#pragma unroll
-    for (int cp = 0; cp < 4; ++cp)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        f32x4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = empty[ht] ? 0.f : O[cp][ht][4 * q + e] * inv[ht];
-        *reinterpret_cast<f32x4*>(ebuf + lo * kEpiStride + (32 * cp + 8 * q + 4 * g) * 4) = v;
+        if (n_tiles > 0) {
+          // Iteration j issues DMA(j+2) inside its QK phase (only for tiles that
+          // exist); stage (j+2)&3 was last read by PV(j-2) in iteration j-1. At
+          // the top of iteration it the only loads issued after DMA(it) are those
+          // of DMA(it+1).
+          if (pass > 0) {  // the first pass's two tiles were issued with the queries
+            issue(tile0, 0);
+            if (n_tiles > 1) issue(tile0 + 1, 1);
+          }
+          // tile 0: QK + softmax only
+          if (n_tiles > 1) wait_vmcnt<kDmaPerThread>(); else wait_vmcnt<0>();
+          tile_barrier();
+          zero_tail(0);
+          if (n_tiles > 2)
+            softmax_only(0, over, std::true_type{});
+          else
+            softmax_only(0, over, std::false_type{});
+          // steady state: QK(it) + softmax(it) overlapped with PV(it - 1); the
+          // last two tiles issue no further DMA
+          int it = 1;
+          for (; it + 2 < n_tiles; ++it) {
+            wait_vmcnt<kDmaPerThread>();
+            tile_barrier();
+            zero_tail(it);
+            softmax_pv(it, over, std::true_type{});
+          }
+          for (; it < n_tiles; ++it) {
+            if (it + 1 < n_tiles) wait_vmcnt<kDmaPerThread>(); else wait_vmcnt<0>();
+            tile_barrier();
+            zero_tail(it);
+            softmax_pv(it, over, std::false_type{});
+          }
+          tile_barrier();
+          mm4(3, va[1], pf);  // deferred tail of PV(n_tiles - 2)
+          pv_only(n_tiles - 1);
+        }
+
+        // end of pass: publish per-head sums and whether any score outgrew its reference
+        __syncthreads();                        // all P slot reads are done
+        if (tid == 0) *flag = 0;
+        __syncthreads();
+        const float l_tot = l_run + shfl_xor32(l_run);
+        if (g == 0) lbuf[h_own] = l_tot;
+        if (__any(over) && lane == 0) *flag = 1;
+        __syncthreads();
+        const bool again = *flag != 0;
+        if (!again || pass == 1) break;
+        m_ref = m_seen;                          // exact max: a second rescan is impossible
+        __syncthreads();                         // everyone has read the flag and lbuf
       }
-    asm volatile("" ::: "memory");
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int r = 2 * j + g;
-      const f32x4 v = *reinterpret_cast<const f32x4*>(ebuf + r * kEpiStride + lo * 16);
-      float* orow = o_part + ((qbase + ht * 32 + r) * a.num_splits + split) * kDc + wave * 128 + lo * 4;
-      *reinterpret_cast<f32x4*>(orow) = v;
+
+      // ---- epilogue: normalise, write this split's partial rows and their LSEs.
+      // A lane holds 16-byte pieces of one head row, so storing straight from the
+      // accumulators would write 32 bytes of 32 different rows per instruction and
+      // leave partly written lines behind. Instead each wave stages 32 head rows of
+      // its 128-column slice in its own LDS region (the stage ring is idle now) and
+      // stores whole 512-byte row slices, two rows per instruction. LDS operations
+      // of one wave complete in order, so no barrier is needed between the two.
+      constexpr int kEpiStride = 128 * 4 + 16;  // staged row: 512 bytes + 16 of padding against bank conflicts
+      char* const ebuf = lds + wave * (32 * kEpiStride);
+      float inv[4];
+      bool empty[4];
+    #pragma unroll
+      for (int ht = 0; ht < 4; ++ht) {
+        const float l = lbuf[ht * 32 + lo];
+        empty[ht] = !(l > 0.f);
+        inv[ht] = empty[ht] ? 0.f : 1.0f / l;
+      }
+    #pragma unroll
+      for (int ht = 0; ht < 4; ++ht) {
+    #pragma unroll
+        for (int cp = 0; cp < 4; ++cp)
+    #pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            f32x4 v;
+    #pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = empty[ht] ? 0.f : O[cp][ht][4 * q + e] * inv[ht];
+            *reinterpret_cast<f32x4*>(ebuf + lo * kEpiStride + (32 * cp + 8 * q + 4 * g) * 4) = v;
+          }
+        asm volatile("" ::: "memory");
+    #pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int r = 2 * j + g;
+          const f32x4 v = *reinterpret_cast<const f32x4*>(ebuf + r * kEpiStride + lo * 16);
+          float* orow = o_part + ((qbase + ht * 32 + r) * a.num_splits + split) * kDc + wave * 128 + lo * 4;
+          *reinterpret_cast<f32x4*>(orow) = v;
+        }
+        asm volatile("" ::: "memory");
+      }
+      if (g == 0) {
+        const float l = lbuf[h_own];
+        lse_part[(qbase + h_own) * a.num_splits + split] =
+            l > 0.f ? (m_ref + __builtin_amdgcn_logf(l)) * 0.69314718055994530942f : -INFINITY;
+      }
+
+      // slots past this row's last piece stay empty
+      if (S > 1 && cp + n_row <= r_hi) {
+        const int rest = S - 1 - split;
+        for (int q = tid; q < kH * rest; q += kThreads)
+          lse_part[(qbase + q / rest) * S + split + 1 + q % rest] = -INFINITY;
+      }
+      __syncthreads();  // the next piece reuses the LDS stages and buffers
     }
-    asm volatile("" ::: "memory");
-  }
-  if (g == 0) {
-    const float l = lbuf[h_own];
-    lse_part[(qbase + h_own) * a.num_splits + split] =
-        l > 0.f ? (m_ref + __builtin_amdgcn_logf(l)) * 0.69314718055994530942f : -INFINITY;
+    cp += n_row;
+    if (++ci == a.s_q) {
+      ci = 0;
+      if (++cb < a.B) cL = clamp_len(seqlens[cb], a.max_pages);
+    }
   }
 }
 
 hipError_t launch_decode_paged(const DecodeParams& p, hipStream_t stream) {
-  const int blocks = 8 * p.items_per_xcd;
-  hipLaunchKernelGGL(decode_paged_kernel, dim3(blocks), dim3(kThreads), 0, stream, p.q_abs, p.q_r, p.kv,
+  hipLaunchKernelGGL(decode_paged_kernel, dim3(kScanGroups), dim3(kThreads), 0, stream, p.q_abs, p.q_r, p.kv,
                      p.block_table, p.seqlens, p.o_part, p.lse_part, p);
   return hipGetLastError();
 }

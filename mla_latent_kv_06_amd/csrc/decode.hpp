@@ -20,8 +20,6 @@ struct DecodeParams {
   float scale_log2;           // softmax_scale * log2(e)
   float* o_part;              // [B, s_q, 128, num_splits, 512]
   float* lse_part;            // [B, s_q, 128, num_splits]
-  int items;                  // B * s_q * num_splits
-  int items_per_xcd;          // ceil(items / 8)
 };
 
 hipError_t launch_decode_paged(const DecodeParams& p, hipStream_t stream);

@@ -54,6 +54,10 @@ int mla_recommended_splits(int B, int s_q, int max_len, int num_cus) {
   return mla::recommended_splits(B, s_q, max_len, num_cus);
 }
 
+int mla_plan_splits(const int32_t* seqlens_host, int B, int s_q, int max_pages, int num_cus) {
+  return mla::plan_splits(seqlens_host, B, s_q, max_pages, num_cus);
+}
+
 mla_status mla_absorb_q(const void* q_c, const void* w_uk, void* q_abs, int64_t T, int H, void* stream) {
   const mla::Check c = mla::check_absorb(q_c, w_uk, q_abs, T, H);
   if (!c.ok()) return report(c);
@@ -83,8 +87,6 @@ mla_status mla_decode_paged(const void* q_abs, const void* q_r, const void* kv_c
   p.scale_log2 = softmax_scale * 1.44269504088896340736f;
   p.o_part = o_part;
   p.lse_part = lse_part;
-  p.items = B * s_q * num_splits;
-  p.items_per_xcd = (p.items + 7) / 8;
   return report_hip(mla::launch_decode_paged(p, as_stream(stream)), "mla_decode_paged launch");
 }
 

@@ -7,6 +7,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <string>
+#include <vector>
 
 #include "../../include/mla.h"
 
@@ -93,6 +94,8 @@ inline Check check_decode(const void* q_abs, const void* q_r, const void* kv, in
   // grid size: work items are (b, i, split); keep well inside 32-bit counts
   long long items = (long long)B * s_q * num_splits;
   MLA_TRY(need_range(items, 1, (1LL << 30), "B * s_q * num_splits"));
+  // the split plan counts the pages of all rows in 32 bits
+  MLA_TRY(need_range((long long)B * s_q * max_pages, 1, (1LL << 31) - 1, "B * s_q * max_pages"));
   // partial rows index o_part with 64-bit offsets; nothing more to check here
   return Check{};
 }
@@ -129,23 +132,113 @@ inline size_t workspace_bytes(int B, int s_q, int H, int num_splits) {
   return (size_t)B * s_q * H * num_splits * (MLA_D_C + 1) * sizeof(float);
 }
 
-// Split count: enough (b, i, split) work items for about two per compute
-// unit, but never splits shorter than kMinSplitPages pages, because each
-// split writes a 256 KiB partial that costs as much HBM time as reading
-// ~3.5 pages of cache.
+// ---- split planning -------------------------------------------------------
+// mla_decode_paged concatenates the pages of all rows (b, i) in order and
+// gives workgroup k of kScanGroups the page range [kW, (k+1)W). With
+// num_splits S > 1 rows are cut at range borders and
+//     W = max(ceil(P_tot / kScanGroups), ceil((n_max - 1) / (S - 1)), 1),
+// which bounds any row to S pieces; with S = 1 rows are not cut, W is
+// ceil(P_tot / kScanGroups) and a row goes whole to the range holding its
+// first page. The planner below evaluates that plan for every distinct W.
+constexpr int kScanGroups = 256;
+
+// Visible pages of every row (b, i), lengths clamped like the kernel does.
+inline std::vector<int64_t> row_pages(const int32_t* seqlens, int B, int s_q, int max_pages) {
+  std::vector<int64_t> n;
+  n.reserve((size_t)B * s_q);
+  const long long cap = (long long)max_pages * MLA_PAGE;
+  for (int b = 0; b < B; ++b) {
+    long long L = seqlens[b];
+    L = L < 0 ? 0 : (L > cap ? cap : L);
+    for (int i = 0; i < s_q; ++i) {
+      const long long v = L - s_q + i + 1;
+      n.push_back(v > 0 ? (v + MLA_PAGE - 1) / MLA_PAGE : 0);
+    }
+  }
+  return n;
+}
+
+// Time model of one scan, in units of ~0.105 us on MI355X: the slowest
+// workgroup (2.8 us per page, ~10.5 us per row piece for its query loads,
+// pipeline start and partial write), times the rounds needed when the GPU has
+// fewer than kScanGroups CUs, plus writing and re-reading every partial.
+inline long long scan_cost(const std::vector<int64_t>& n, int64_t W, bool cut, long long cus) {
+  constexpr long long kPageCost = 27, kPieceCost = 100;
+  long long pages[kScanGroups] = {}, pieces[kScanGroups] = {};
+  long long total = 0;
+  int64_t P = 0;
+  for (const int64_t nr : n) {
+    if (nr > 0) {
+      if (cut) {
+        const int64_t k0 = P / W, k1 = (P + nr - 1) / W;
+        for (int64_t k = k0; k <= k1; ++k) {
+          const int64_t a = P > k * W ? P : k * W;
+          const int64_t e = P + nr < (k + 1) * W ? P + nr : (k + 1) * W;
+          pages[k] += e - a;
+          ++pieces[k];
+        }
+        total += k1 - k0 + 1;
+      } else {
+        pages[P / W] += nr;
+        ++pieces[P / W];
+        ++total;
+      }
+    }
+    P += nr;
+  }
+  long long span = 0;
+  for (int k = 0; k < kScanGroups; ++k) {
+    const long long t = kPageCost * pages[k] + kPieceCost * pieces[k];
+    if (t > span) span = t;
+  }
+  const long long rounds = (kScanGroups + cus - 1) / cus;
+  return span * rounds + total;
+}
+
+// Smallest S whose plan has the lowest modelled time.
+inline int plan_rows(const std::vector<int64_t>& n, int max_pages, int num_cus) {
+  const long long cus = num_cus > 0 ? num_cus : kScanGroups;
+  int64_t p_tot = 0, n_max = 0;
+  for (const int64_t nr : n) {
+    p_tot += nr;
+    if (nr > n_max) n_max = nr;
+  }
+  if (p_tot == 0) return 1;
+  const int64_t w_base = (p_tot + kScanGroups - 1) / kScanGroups;
+  int best_s = 1;
+  long long best = scan_cost(n, w_base, false, cus);
+  const int s_max = max_pages < 256 ? max_pages : 256;
+  int64_t w_prev = -1;
+  for (int S = 2; S <= s_max; ++S) {
+    int64_t W = (n_max - 1 + S - 2) / (S - 1);
+    if (W < w_base) W = w_base;
+    if (W < 1) W = 1;
+    if (W == w_prev) continue;  // the same plan with more slots
+    w_prev = W;
+    const long long c = scan_cost(n, W, true, cus);
+    if (c < best) {
+      best = c;
+      best_s = S;
+    }
+  }
+  return best_s;
+}
+
+// Split count for host-known lengths.
+inline int plan_splits(const int32_t* seqlens, int B, int s_q, int max_pages, int num_cus) {
+  if (seqlens == nullptr || B < 1 || s_q < 1 || max_pages < 1) return 1;
+  if ((long long)B * s_q > (1LL << 22)) return 1;  // huge batches fill the GPU unsplit
+  return plan_rows(row_pages(seqlens, B, s_q, max_pages), max_pages, num_cus);
+}
+
+// Split count when only the longest length is known: the plan for B
+// sequences of max_len tokens and a block table just wide enough for them.
 inline int recommended_splits(int B, int s_q, int max_len, int num_cus) {
-  constexpr int kMinSplitPages = 8;
   if (max_len < 1 || B < 1 || s_q < 1) return 1;
-  long long pages = (max_len + MLA_PAGE - 1) / MLA_PAGE;
-  long long items = (long long)B * s_q;
-  long long cus = num_cus > 0 ? num_cus : 256;
-  long long want = (cus + items - 1) / items;  // one work item per CU
-  long long cap = pages / kMinSplitPages;
-  if (cap < 1) cap = 1;
-  if (want > cap) want = cap;
-  if (want > pages) want = pages;
-  if (want < 1) want = 1;
-  return (int)want;
+  const long long pages = ((long long)max_len + MLA_PAGE - 1) / MLA_PAGE;
+  if (pages > (1 << 24)) return 1;
+  std::vector<int32_t> lens((size_t)B, max_len);
+  return plan_splits(lens.data(), B, s_q, (int)pages, num_cus);
 }
 
 }  // namespace mla

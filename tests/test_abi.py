@@ -26,7 +26,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     out = subprocess.run(["nm", "-D", "--defined-only", os.path.join(ROOT, "mla_latent_kv_06_amd", "libmla.so")],
                          capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\bT (mla_[a-z_]+)\b", out))
@@ -82,11 +82,34 @@ def test_other_entry_validation(lib):
 def test_host_helpers(lib):
     assert lib.mla_decode_workspace_bytes(16, 1, 128, 16) == 16 * 128 * 16 * 513 * 4
     assert lib.mla_decode_workspace_bytes(0, 1, 128, 16) == 0
-    # fills ~one work item per CU but keeps splits >= 8 pages
-    assert lib.mla_recommended_splits(16, 1, 65536, 256) == 16
-    assert lib.mla_recommended_splits(1, 1, 2048, 256) == 4
-    assert lib.mla_recommended_splits(4, 256, 16640, 256) == 1
-    assert lib.mla_recommended_splits(1, 1, 0, 256) == 1
-    for B, L in [(3, 100), (64, 32768), (1, 10 ** 6)]:
-        s = lib.mla_recommended_splits(B, 1, L, 256)
-        assert 1 <= s <= -(-L // 64)
+    # time model of the balanced scan: more splits for a single short sequence,
+    # few for a batch that fills the GPU
+    assert lib.mla_recommended_splits(1, 1, 2048, 256) == 32
+    assert lib.mla_recommended_splits(4, 256, 16640, 256) in (1, 2)
+    assert lib.mla_recommended_splits(16, 1, 4096, 256) in (8, 9, 11)
+
+
+def test_plan_splits(lib):
+    import ctypes
+    from mla_inputs import CONFIGS, make_structure
+
+    def plan(lens, width, s_q=1):
+        arr = (ctypes.c_int32 * len(lens))(*lens)
+        return lib.mla_plan_splits(ctypes.cast(arr, ctypes.c_void_p), len(lens), s_q, width, 256)
+    # equal lengths: the same choice as the max-length model
+    for B, L in [(16, 65536), (16, 4096), (1, 2048)]:
+        assert plan([L] * B, -(-L // 64)) == lib.mla_recommended_splits(B, 1, L, 256)
+    # 16 x 1024 pages: ranges of exactly 64 pages need S >= 17 (any row alignment)
+    assert lib.mla_recommended_splits(16, 1, 65536, 256) == 17
+    assert plan([16640] * 4, 260, s_q=256) in (1, 2)
+    # a ragged batch: the chosen plan's ranges stay close to the balanced width
+    st = make_structure(CONFIGS["ragged"], 42)
+    lens = [int(x) for x in st.seqlens]
+    S = plan(lens, st.block_table.shape[1])
+    pages = [-(-L // 64) for L in lens]
+    p_tot = sum(pages)
+    W = max(-(-p_tot // 256), -(-(max(pages) - 1) // (S - 1)) if S > 1 else 0)
+    assert S > 1 and W <= 1.25 * -(-p_tot // 256), (S, W)
+    # degenerate inputs
+    assert lib.mla_plan_splits(None, 4, 1, 8, 256) == 1
+    assert plan([0, 0], 4) == 1

@@ -73,7 +73,9 @@ def _decode_check(M, q_abs, q_r, kv, bt, sl, num_splits, what, check_parts=True)
     if check_parts:
         rp_o, rp_l = O.decode_split(O.as_f64(q_abs), O.as_f64(q_r), kvb, bt.numpy(), sl.numpy(), SCALE, num_splits)
         assert_lse(lse_part.cpu().numpy(), rp_l, f"{what} lse_part")
-        assert_bar(o_part.cpu().numpy(), rp_o, f"{what} o_part")
+        # rows of empty splits are not written: compare the others only
+        live = np.isfinite(rp_l)
+        assert_bar(o_part.cpu().numpy()[live], rp_o[live], f"{what} o_part")
     return o_lat, lse
 
 
@@ -199,6 +201,35 @@ def test_decode_zero_length_rows(M):
     assert (o_lat[0].cpu() == 0).all() and torch.isneginf(lse[0].cpu()).all()
 
 
+def test_decode_ragged_plan_leaves_empty_splits_unwritten_and_unread(M):
+    """Balanced plan on a ragged batch: rows use only the slots of their pieces; the
+    unused ones get lse = -inf, their o_part rows are never written (a NaN fill
+    survives) and the combine never reads them."""
+    lens = [5000, 1000, 64, 30, 2047]
+    q_abs, q_r, kv, bt, sl = _random_case(lens, 1, seed=15)
+    S = 8
+    B = len(lens)
+    o_part = torch.full((B, 1, 128, S, 512), float("nan"), dtype=torch.float32, device=DEV)
+    lse_part = torch.empty((B, 1, 128, S), dtype=torch.float32, device=DEV)
+    M.mla_decode_paged(q_abs.to(DEV), q_r.to(DEV), kv.to(DEV), bt.to(DEV), sl.to(DEV), S, SCALE,
+                       o_part=o_part, lse_part=lse_part)
+    o_lat, lse = M.mla_combine_splits(o_part, lse_part)
+    torch.cuda.synchronize()
+    kvb = O.bf16_bits(kv)
+    ref_o, ref_l = O.decode_absorbed(O.as_f64(q_abs), O.as_f64(q_r), kvb, bt.numpy(), sl.numpy(), SCALE)
+    assert_bar(o_lat.cpu().numpy(), ref_o, "ragged plan o_lat")
+    assert_lse(lse.cpu().numpy(), ref_l, "ragged plan lse")
+    rp_o, rp_l = O.decode_split(O.as_f64(q_abs), O.as_f64(q_r), kvb, bt.numpy(), sl.numpy(), SCALE, S)
+    assert_lse(lse_part.cpu().numpy(), rp_l, "ragged plan lse_part")
+    live = np.isfinite(rp_l)
+    used = live.reshape(B, 128, S)[:, 0, :].sum(1).tolist()
+    assert used == [len(p) for p in O.scan_plan([-(-L // 64) for L in lens], S)], used
+    assert min(used) < S
+    op = o_part.cpu().numpy()
+    assert_bar(op[live], rp_o[live], "ragged plan o_part")
+    assert np.isnan(op[~live]).all(), "an empty split's partial rows were written"
+
+
 def test_decode_nan_in_unused_tail_rows(M):
     q_abs, q_r, kv, bt, sl = _random_case([100, 33, 130], 1, seed=10, nan_tail=True)
     _decode_check(M, q_abs, q_r, kv, bt, sl, 2, "NaN past the end")
@@ -247,7 +278,7 @@ def test_decode_rising_scores_within_headroom(M):
 # bit-exact invariances
 # ---------------------------------------------------------------------------
 
-def test_page_placement_and_batch_independence_bit_exact(M):
+def test_page_placement_neighbour_values_and_rerun_bit_exact(M):
     q_abs, q_r, kv, bt, sl = _random_case([700, 64, 1500], 1, seed=13)
     S = 4
     o1, l1 = M.mla_decode_paged(q_abs.to(DEV), q_r.to(DEV), kv.to(DEV), bt.to(DEV), sl.to(DEV), S, SCALE)
@@ -257,15 +288,32 @@ def test_page_placement_and_batch_independence_bit_exact(M):
     kv2 = kv[perm]
     bt2 = torch.where(bt >= 0, inv[bt.clamp(min=0).long()].to(torch.int32), bt)
     o2, l2 = M.mla_decode_paged(q_abs.to(DEV), q_r.to(DEV), kv2.to(DEV), bt2.to(DEV), sl.to(DEV), S, SCALE)
-    # sequence 2 alone
-    o3, l3 = M.mla_decode_paged(q_abs[2:].contiguous().to(DEV), q_r[2:].contiguous().to(DEV), kv.to(DEV),
+    # other queries for the neighbours (same lengths, so the same split plan)
+    g = torch.Generator().manual_seed(2)
+    q_abs3, q_r3 = q_abs.clone(), q_r.clone()
+    q_abs3[:2] = (torch.randn(q_abs3[:2].shape, generator=g) * 0.05).to(torch.bfloat16)
+    q_r3[:2] = torch.randn(q_r3[:2].shape, generator=g).to(torch.bfloat16)
+    o3, l3 = M.mla_decode_paged(q_abs3.to(DEV), q_r3.to(DEV), kv.to(DEV), bt.to(DEV), sl.to(DEV), S, SCALE)
+    # sequence 2 alone: the plan depends on the batch's lengths, so only the
+    # combined result is compared, to the numerical bar
+    o5, l5 = M.mla_decode_paged(q_abs[2:].contiguous().to(DEV), q_r[2:].contiguous().to(DEV), kv.to(DEV),
                                 bt[2:].contiguous().to(DEV), sl[2:].contiguous().to(DEV), S, SCALE)
     # and a rerun: deterministic
     o4, l4 = M.mla_decode_paged(q_abs.to(DEV), q_r.to(DEV), kv.to(DEV), bt.to(DEV), sl.to(DEV), S, SCALE)
     torch.cuda.synchronize()
-    assert torch.equal(o1, o2) and torch.equal(l1, l2), "physical placement changed the result"
-    assert torch.equal(o1[2:], o3) and torch.equal(l1[2:], l3), "batch neighbours changed the result"
-    assert torch.equal(o1, o4) and torch.equal(l1, l4), "rerun is not bit-identical"
+
+    def same(oa, la, ob, lb):
+        # the partial rows of empty splits (lse = -inf) are not written
+        live = torch.isfinite(la)
+        return torch.equal(la, lb) and torch.equal(oa[live], ob[live])
+    assert same(o1, l1, o2, l2), "physical placement changed the result"
+    assert same(o1[2:], l1[2:], o3[2:], l3[2:]), "the neighbours' values changed the result"
+    assert same(o1, l1, o4, l4), "rerun is not bit-identical"
+    c1, cl1 = M.mla_combine_splits(o1, l1)
+    c5, cl5 = M.mla_combine_splits(o5, l5)
+    torch.cuda.synchronize()
+    assert_bar(c5.cpu().numpy(), c1[2:].cpu().numpy().astype(np.float64), "alone vs in batch")
+    assert_lse(cl5.cpu().numpy(), cl1[2:].cpu().numpy(), "alone vs in batch lse")
 
 
 # ---------------------------------------------------------------------------

@@ -302,13 +302,37 @@ def test_page_permutation_invariance():
 # split scan + combine
 # --------------------------------------------------------------------------
 
-def test_split_ranges_cover_pages():
-    for n in (0, 1, 5, 64, 1023):
-        for S in (1, 2, 7, 16, 64):
-            r = O.split_ranges(n, S)
-            assert len(r) == S
-            covered = [p for a, b in r for p in range(a, b)]
-            assert covered == list(range(n))
+def test_scan_plan_covers_rows_and_balances():
+    g = np.random.default_rng(5)
+    for rows in ([1024] * 16, [64] * 16, list(g.integers(0, 513, 64)), [0, 0, 3], [1], [260] * 1024,
+                 list(g.integers(0, 40, 300))):
+        p_tot, n_max = sum(rows), max(rows)
+        for S in (1, 2, 7, 16, 17, 64):
+            plan = O.scan_plan(rows, S)
+            W = -(-p_tot // O.SCAN_GROUPS) if p_tot else 1
+            if S > 1 and p_tot:
+                W = max(W, -(-(n_max - 1) // (S - 1)), 1)
+            load = {}
+            P = 0
+            for nr, pieces in zip(rows, plan):
+                # every page of the row exactly once, slots distinct and < S
+                covered = sorted(p for _, a, e in pieces for p in range(a, e))
+                assert covered == list(range(nr))
+                slots = [s_ for s_, _, _ in pieces]
+                assert len(set(slots)) == len(slots) and all(0 <= s_ < S for s_ in slots)
+                for s_, a, e in pieces:
+                    k = (P + a) // W if S > 1 else P // W
+                    assert k < O.SCAN_GROUPS
+                    if S > 1:
+                        assert (P + e - 1) // W == k  # a piece never crosses a range border
+                    load[k] = load.get(k, 0) + (e - a)
+                P += nr
+            if S > 1 and load:
+                assert max(load.values()) <= W
+    # equal rows that the ranges divide evenly: one piece per range
+    plan = O.scan_plan([1024] * 16, 17)
+    assert all(len(p) == 16 and [s for s, _, _ in p] == list(range(16)) for p in plan)
+    assert all(e - a == 64 for p in plan for _, a, e in p)
 
 
 @pytest.mark.parametrize("num_splits", [1, 2, 7, 20])

@@ -46,13 +46,13 @@ def test_causal_off_by_one_is_caught(monkeypatch):
 
 
 def test_split_plan_losing_last_page_is_caught(monkeypatch):
-    real = M.split_ranges
+    real = M.scan_plan
 
-    def lossy(n, S):
-        r = real(n, S)
-        return [(a, min(b, max(n - 1, 0))) for a, b in r]
-    _patch(monkeypatch, "split_ranges", lossy)
-    _expect_fail(lambda: pins.test_split_invariance(2), pins.test_split_ranges_cover_pages)
+    def lossy(rows, S, groups=M.SCAN_GROUPS):
+        return [[(s, a, e - 1 if e == nr and e - 1 > a else e) for s, a, e in pieces]
+                for nr, pieces in zip(rows, real(rows, S, groups))]
+    _patch(monkeypatch, "scan_plan", lossy)
+    _expect_fail(lambda: pins.test_split_invariance(2), pins.test_scan_plan_covers_rows_and_balances)
 
 
 def test_gather_ignoring_block_table_is_caught(monkeypatch):
