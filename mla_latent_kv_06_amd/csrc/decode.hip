@@ -60,6 +60,15 @@ static_assert(kLdsBytes <= 163840, "LDS budget");
 
 __device__ __forceinline__ int swz(int t) { return ((t & 3) << 1) ^ ((t >> 2) & 7); }
 
+// The lane id recomputed where it is used (two VALU ops). Written as
+// volatile asm so the compiler cannot hoist lane-dependent addresses out of
+// the piece loop, where they would be held, and spilled, across the tile loop.
+__device__ __forceinline__ int lane_here() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 __device__ __forceinline__ float shfl_xor32(float v) { return __shfl_xor(v, 32, 64); }
 
 // max(v[l], v[l ^ 32]) in every lane, on the VALU: v_permlane32_swap exchanges
@@ -528,12 +537,13 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
       if (n_tiles > 1) issue(tile0 + 1, 1);
       // queries: B operand of S^T = K . Q^T; lane (g, lo) holds dims 16kk+8g..+7 of head h_own
       if (n_tiles > 0) {
-        const bf16x8* qa = reinterpret_cast<const bf16x8*>(q_abs + (qbase + h_own) * kDc);
-        const bf16x8* qr = reinterpret_cast<const bf16x8*>(q_r + (qbase + h_own) * kDr);
-    #pragma unroll
-        for (int kk = 0; kk < 32; ++kk) qf[kk] = qa[2 * kk + g];
-    #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) qf[32 + kk] = qr[2 * kk + g];
+        const int ql = lane_here();
+        const bf16x8* qa = reinterpret_cast<const bf16x8*>(q_abs + (qbase + wave * 32 + (ql & 31)) * kDc);
+        const bf16x8* qr = reinterpret_cast<const bf16x8*>(q_r + (qbase + wave * 32 + (ql & 31)) * kDr);
+#pragma unroll
+        for (int kk = 0; kk < 32; ++kk) qf[kk] = qa[2 * kk + (ql >> 5)];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) qf[32 + kk] = qr[2 * kk + (ql >> 5)];
         wait_vmcnt<0>();
       }
 
@@ -541,16 +551,16 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
         // O^T = 0 through the matrix core, so O is only ever defined by MFMAs
         {
           const bf16x8 z = bf16x8{};
-    #pragma unroll
+#pragma unroll
           for (int cp = 0; cp < 4; ++cp)
-    #pragma unroll
+#pragma unroll
             for (int ht = 0; ht < 4; ++ht) O[cp][ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(z, z, f32x16{}, 0, 0, 0);
         }
         l_run = 0.f;
         bool over = false;
-    #pragma unroll
+#pragma unroll
         for (int k = 0; k < 4; ++k) pf[k] = bf16x8{};
-    #pragma unroll
+#pragma unroll
         for (int k = 0; k < 3; ++k) va[k] = bf16x8{};
 
         if (n_tiles > 0) {
@@ -613,38 +623,40 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
       // of one wave complete in order, so no barrier is needed between the two.
       constexpr int kEpiStride = 128 * 4 + 16;  // staged row: 512 bytes + 16 of padding against bank conflicts
       char* const ebuf = lds + wave * (32 * kEpiStride);
+      const int el = lane_here();
+      const int elo = el & 31, eg = el >> 5;
       float inv[4];
       bool empty[4];
-    #pragma unroll
+#pragma unroll
       for (int ht = 0; ht < 4; ++ht) {
-        const float l = lbuf[ht * 32 + lo];
+        const float l = lbuf[ht * 32 + elo];
         empty[ht] = !(l > 0.f);
         inv[ht] = empty[ht] ? 0.f : 1.0f / l;
       }
-    #pragma unroll
+#pragma unroll
       for (int ht = 0; ht < 4; ++ht) {
-    #pragma unroll
+#pragma unroll
         for (int cp = 0; cp < 4; ++cp)
-    #pragma unroll
+#pragma unroll
           for (int q = 0; q < 4; ++q) {
             f32x4 v;
-    #pragma unroll
+#pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = empty[ht] ? 0.f : O[cp][ht][4 * q + e] * inv[ht];
-            *reinterpret_cast<f32x4*>(ebuf + lo * kEpiStride + (32 * cp + 8 * q + 4 * g) * 4) = v;
+            *reinterpret_cast<f32x4*>(ebuf + elo * kEpiStride + (32 * cp + 8 * q + 4 * eg) * 4) = v;
           }
         asm volatile("" ::: "memory");
-    #pragma unroll
+#pragma unroll
         for (int j = 0; j < 16; ++j) {
-          const int r = 2 * j + g;
-          const f32x4 v = *reinterpret_cast<const f32x4*>(ebuf + r * kEpiStride + lo * 16);
-          float* orow = o_part + ((qbase + ht * 32 + r) * a.num_splits + split) * kDc + wave * 128 + lo * 4;
+          const int r = 2 * j + eg;
+          const f32x4 v = *reinterpret_cast<const f32x4*>(ebuf + r * kEpiStride + elo * 16);
+          float* orow = o_part + ((qbase + ht * 32 + r) * a.num_splits + split) * kDc + wave * 128 + elo * 4;
           *reinterpret_cast<f32x4*>(orow) = v;
         }
         asm volatile("" ::: "memory");
       }
-      if (g == 0) {
-        const float l = lbuf[h_own];
-        lse_part[(qbase + h_own) * a.num_splits + split] =
+      if (eg == 0) {
+        const float l = lbuf[wave * 32 + elo];
+        lse_part[(qbase + wave * 32 + elo) * a.num_splits + split] =
             l > 0.f ? (m_ref + __builtin_amdgcn_logf(l)) * 0.69314718055994530942f : -INFINITY;
       }
 
