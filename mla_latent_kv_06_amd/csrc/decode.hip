@@ -127,10 +127,21 @@ __device__ __forceinline__ void tile_barrier() {
 // (which would make it drain all outstanding loads); completion is tracked
 // with explicit vmcnt waits before the tile is read. An SALU write of M0
 // needs one wait state before an LDS-DMA instruction reads it.
+// kStream: each cache row is read once per launch (one query row per
+// sequence), so the loads are marked non-temporal (measured 2-4% faster:
+// less cache fill traffic and power under the streaming load). With several
+// query rows per sequence the same pages are read again by the other rows
+// and the default policy keeps them in L2 and the last-level cache.
+template <bool kStream>
 __device__ __forceinline__ void dma16(const char* sbase, unsigned voff, unsigned lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
-               "s"(lds_addr)
-               : "memory", "m0");
+  if constexpr (kStream)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(sbase),
+                 "s"(lds_addr)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+                 "s"(lds_addr)
+                 : "memory", "m0");
 }
 
 __device__ __forceinline__ bf16x8 cat8(const i16x4& v0, const i16x4& v1) {
@@ -173,6 +184,7 @@ __device__ __forceinline__ int wave_incl_scan32(int v, int lane) {
 
 }  // namespace
 
+template <bool kStream>
 __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
     const __bf16* __restrict__ q_abs, const __bf16* __restrict__ q_r, const char* __restrict__ kv,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seqlens,
@@ -318,7 +330,7 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
   auto issue = [&](int tile, int stage) {
     const DmaTarget t = dma_target(tile, stage);
 #pragma unroll
-    for (int k = 0; k < kDmaPerThread; ++k) dma16(t.src, dma_off[k], t.dst + k * (kThreads * 16));
+    for (int k = 0; k < kDmaPerThread; ++k) dma16<kStream>(t.src, dma_off[k], t.dst + k * (kThreads * 16));
   };
 
   bf16x8 qf[36];  // queries of the current piece
@@ -384,7 +396,7 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
         if (kk == 35) { va[0] = vfrag(it - 1, 0, 0); va[1] = vfrag(it - 1, 0, 1); }
       }
       if constexpr (dma) {
-        if ((kk & 3) == 1) dma16(t.src, dma_off[kk >> 2], t.dst + (kk >> 2) * (kThreads * 16));
+        if ((kk & 3) == 1) dma16<kStream>(t.src, dma_off[kk >> 2], t.dst + (kk >> 2) * (kThreads * 16));
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -677,8 +689,12 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
 }
 
 hipError_t launch_decode_paged(const DecodeParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(decode_paged_kernel, dim3(kScanGroups), dim3(kThreads), 0, stream, p.q_abs, p.q_r, p.kv,
-                     p.block_table, p.seqlens, p.o_part, p.lse_part, p);
+  if (p.s_q == 1)
+    hipLaunchKernelGGL(decode_paged_kernel<true>, dim3(kScanGroups), dim3(kThreads), 0, stream, p.q_abs, p.q_r,
+                       p.kv, p.block_table, p.seqlens, p.o_part, p.lse_part, p);
+  else
+    hipLaunchKernelGGL(decode_paged_kernel<false>, dim3(kScanGroups), dim3(kThreads), 0, stream, p.q_abs, p.q_r,
+                       p.kv, p.block_table, p.seqlens, p.o_part, p.lse_part, p);
   return hipGetLastError();
 }
 
