@@ -1,7 +1,8 @@
 """Benchmark: absorbed MLA decode over a paged latent cache on one MI355X.
 
 A step is one pass of the whole hot path for one layer: mla_absorb_q ->
-mla_decode_paged -> mla_combine_splits -> mla_up_proj. The default workload is
+mla_decode_paged -> stage 2 + up-projection (mla_combine_up_proj, one pass;
+--separate-stage2 runs mla_combine_splits and mla_up_proj instead). The default workload is
 B=16 sequences of 65536 cached tokens with 60 layers of latent cache resident
 (72.5 GB); step k uses layer k mod 60, so every step reads its 1.2 GB of cache
 from HBM (it cannot be served by the 256 MB last-level cache).
@@ -44,6 +45,8 @@ def parse():
     p.add_argument("--layers", type=int, default=0, help="resident cache layers (0: workload default)")
     p.add_argument("--splits", type=int, default=0, help="num_splits (0: library recommendation)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--separate-stage2", action="store_true",
+                   help="run mla_combine_splits and mla_up_proj as two kernels instead of mla_combine_up_proj")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle time for the baseline")
     return p.parse_args()
 
@@ -153,8 +156,10 @@ def main():
     out = torch.empty((B, s_q, 128, 128), dtype=torch.bfloat16, device=dev)
 
     stream = torch.cuda.current_stream()
-    nev = 5
+    sep = args.separate_stage2
+    nev = 5 if sep else 4
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    out_rows = out.view(T, 128, 128)
 
     def step(k, ev=None):
         layer = k % layers
@@ -163,10 +168,14 @@ def main():
         if ev: ev[1].record(stream)
         M.mla_decode_paged(q_abs, q_r, kv[layer], tables[layer], seqlens, S, o_part=o_part, lse_part=lse_part)
         if ev: ev[2].record(stream)
-        M.mla_combine_splits(o_part, lse_part, o_lat, lse)
-        if ev: ev[3].record(stream)
-        M.mla_up_proj(o_lat, w_uv, out)
-        if ev: ev[4].record(stream)
+        if sep:
+            M.mla_combine_splits(o_part, lse_part, o_lat, lse)
+            if ev: ev[3].record(stream)
+            M.mla_up_proj(o_lat, w_uv, out)
+        else:
+            # stage 2 and the up-projection in one pass (o_lat stays on chip)
+            M.mla_combine_up_proj(o_part, lse_part, w_uv, out_rows, lse)
+        if ev: ev[nev - 1].record(stream)
 
     for k in range(args.warmup):
         step(k)
@@ -187,7 +196,8 @@ def main():
     torch.cuda.synchronize()
     per = [[events[k][j].elapsed_time(events[k][j + 1]) for k in range(args.steps)] for j in range(nev - 1)]
     avg = [sum(x) / len(x) for x in per]
-    names = ["mla_absorb_q", "mla_decode_paged", "mla_combine_splits", "mla_up_proj"]
+    names = (["mla_absorb_q", "mla_decode_paged", "mla_combine_splits", "mla_up_proj"] if sep else
+             ["mla_absorb_q", "mla_decode_paged", "mla_combine_up_proj"])
 
     pairs = visible_pairs(lens, s_q)
     flop_attn = pairs * FLOP_PER_PAIR

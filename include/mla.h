@@ -159,6 +159,17 @@ mla_status mla_combine_splits(const float* o_part, const float* lse_part,
                               int B, int s_q, int H, int num_splits,
                               float* o_lat, float* lse, void* stream);
 
+/* Stage 2 fused with the up-projection: merges the split partials exactly as
+ * mla_combine_splits does and up-projects each merged row as mla_up_proj
+ * does, in one pass that never writes o_lat (one read of o_part and W_UV).
+ *   o_part, lse_part  as for mla_combine_splits (empty splits never read)
+ *   w_uv   bf16 [H, 128, 512]
+ *   out    bf16 [B * s_q, H, 128] output (rows in (b, i) order)
+ *   lse    fp32 [B, s_q, H] output, as mla_combine_splits
+ * B >= 1, s_q >= 1, H == MLA_HEADS, num_splits >= 1. */
+mla_status mla_combine_up_proj(const float* o_part, const float* lse_part, const void* w_uv, int B, int s_q,
+                               int H, int num_splits, void* out, float* lse, void* stream);
+
 /* Per-head up-projection of the latent output (W_UV has W_UK's layout):
  *     out[t, h, d] = sum_c o_lat[t, h, c] * W_UV[h, d, c]
  * o_lat is split into a bf16 high part and a bf16 remainder so the fp32

@@ -144,6 +144,23 @@ def mla_combine_splits(o_part, lse_part, o_lat=None, lse=None, stream=None):
     return o_lat, lse
 
 
+def mla_combine_up_proj(o_part, lse_part, w_uv, out=None, lse=None, stream=None):
+    """Merge + up-projection in one pass; returns (out [B*s_q, H, 128] bf16, lse [B, s_q, H] fp32)."""
+    B, s_q, _, S = lse_part.shape
+    _need(o_part, "o_part", torch.float32, (B, s_q, H, S, D_C))
+    _need(lse_part, "lse_part", torch.float32, (B, s_q, H, S))
+    _need(w_uv, "w_uv", torch.bfloat16, (H, D_HC, D_C))
+    if out is None:
+        out = torch.empty((B * s_q, H, D_HC), dtype=torch.bfloat16, device=o_part.device)
+    if lse is None:
+        lse = torch.empty((B, s_q, H), dtype=torch.float32, device=o_part.device)
+    _need(out, "out", torch.bfloat16, (B * s_q, H, D_HC))
+    _need(lse, "lse", torch.float32, (B, s_q, H))
+    _check(_lib.LIB.mla_combine_up_proj(_ptr(o_part), _ptr(lse_part), _ptr(w_uv), B, s_q, H, S, _ptr(out), _ptr(lse),
+                                        _stream(stream)), "mla_combine_up_proj")
+    return out, lse
+
+
 def mla_up_proj(o_lat, w_uv, out=None, stream=None):
     """out[..., h, :] = W_UV[h] @ o_lat[..., h, :]; o_lat [..., H, 512] fp32 -> out [..., H, 128] bf16."""
     lead = tuple(o_lat.shape[:-2])

@@ -30,6 +30,8 @@ SIGNATURES = {
                                  c_int, c_float, c_int, c_void_p, c_void_p, c_void_p]),
     "mla_combine_splits": (c_int, [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p]),
     "mla_up_proj": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_int, c_void_p]),
+    "mla_combine_up_proj": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_void_p,
+                                    c_void_p]),
     "mla_debug_gather": (c_int, [c_void_p, c_int64, c_void_p, c_int, c_void_p, c_int, c_int, c_void_p, c_void_p]),
 }
 

@@ -4,9 +4,9 @@
 //
 // One wave per row: lane k holds the LSE of split k (of each block of 64),
 // max and sum come from wave reductions, and each split's weight is
-// broadcast with readlane. Every lane owns 8 of the 512 latent columns and
-// streams the partial rows with 32-byte loads (2 KiB contiguous per split
-// across the wave), up to 16 splits' loads in flight. Splits with LSE = -inf
+// broadcast with readlane. Lane l owns latent columns 4l..4l+3 and
+// 256+4l..+3, so each load instruction covers 1 KiB of contiguous memory; up
+// to 16 splits' loads are in flight. Splits with LSE = -inf
 // are empty; their partial rows were never written and are not read.
 #include "mla_device.hpp"
 #include "decode.hpp"
@@ -38,15 +38,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int row = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
   if (row >= rows) return;
   const float* lp = lse_part + (int64_t)row * num_splits;
-  const float* op = o_part + (int64_t)row * num_splits * kDc + 8 * lane;
-  float* orow = o_lat + (int64_t)row * kDc + 8 * lane;
+  const float* op = o_part + (int64_t)row * num_splits * kDc + 4 * lane;
+  float* orow = o_lat + (int64_t)row * kDc + 4 * lane;
 
   float M = -INFINITY;
   for (int s = lane; s < num_splits; s += 64) M = fmaxf(M, lp[s]);
   M = wave_max(M);
   if (M == -INFINITY) {  // every split empty
     *reinterpret_cast<f32x4*>(orow) = f32x4{};
-    *reinterpret_cast<f32x4*>(orow + 4) = f32x4{};
+    *reinterpret_cast<f32x4*>(orow + kDc / 2) = f32x4{};
     if (lane == 0) lse[row] = -INFINITY;
     return;
   }
@@ -67,7 +67,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     for (int k = 0; k < kCombineChunk; ++k) {
       if (s0 + k < num_splits && weight(s0 + k) > 0.f) {
         v0[k] = *reinterpret_cast<const f32x4*>(op + (int64_t)(s0 + k) * kDc);
-        v1[k] = *reinterpret_cast<const f32x4*>(op + (int64_t)(s0 + k) * kDc + 4);
+        v1[k] = *reinterpret_cast<const f32x4*>(op + (int64_t)(s0 + k) * kDc + kDc / 2);
       }
     }
 #pragma unroll
@@ -82,7 +82,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     }
   }
   *reinterpret_cast<f32x4*>(orow) = a0;
-  *reinterpret_cast<f32x4*>(orow + 4) = a1;
+  *reinterpret_cast<f32x4*>(orow + kDc / 2) = a1;
   if (lane == 0) lse[row] = L;
 }
 

@@ -27,6 +27,9 @@ hipError_t launch_decode_paged(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_combine(const float* o_part, const float* lse_part, int rows, int num_splits,
                           float* o_lat, float* lse, hipStream_t stream);
 
+hipError_t launch_combine_up(const float* o_part, const float* lse_part, const __bf16* w_uv, int T, int num_splits,
+                             __bf16* out, float* lse, hipStream_t stream);
+
 hipError_t launch_absorb(const __bf16* q_c, const __bf16* w_uk, __bf16* q_abs, int T, hipStream_t stream);
 
 hipError_t launch_up_proj(const float* o_lat, const __bf16* w_uv, __bf16* out, int T, hipStream_t stream);

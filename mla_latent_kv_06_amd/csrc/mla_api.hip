@@ -98,6 +98,15 @@ mla_status mla_combine_splits(const float* o_part, const float* lse_part, int B,
                     "mla_combine_splits launch");
 }
 
+mla_status mla_combine_up_proj(const float* o_part, const float* lse_part, const void* w_uv, int B, int s_q, int H,
+                               int num_splits, void* out, float* lse, void* stream) {
+  const mla::Check c = mla::check_combine_up(o_part, lse_part, w_uv, B, s_q, H, num_splits, out, lse);
+  if (!c.ok()) return report(c);
+  return report_hip(mla::launch_combine_up(o_part, lse_part, static_cast<const __bf16*>(w_uv), B * s_q, num_splits,
+                                           static_cast<__bf16*>(out), lse, as_stream(stream)),
+                    "mla_combine_up_proj launch");
+}
+
 mla_status mla_up_proj(const float* o_lat, const void* w_uv, void* out, int64_t T, int H, void* stream) {
   const mla::Check c = mla::check_up_proj(o_lat, w_uv, out, T, H);
   if (!c.ok()) return report(c);

@@ -114,6 +114,13 @@ inline Check check_combine(const void* o_part, const void* lse_part, int B, int 
   return Check{};
 }
 
+inline Check check_combine_up(const void* o_part, const void* lse_part, const void* w_uv, int B, int s_q, int H,
+                              int num_splits, const void* out, const void* lse) {
+  MLA_TRY(check_combine(o_part, lse_part, B, s_q, H, num_splits, out, lse));
+  MLA_TRY(need_ptr(w_uv, "w_uv"));
+  return Check{};
+}
+
 inline Check check_gather(const void* kv, int64_t num_pages, const void* bt, int max_pages,
                           const void* seqlens, int B, int max_len, const void* out) {
   MLA_TRY(need_ptr(kv, "kv_cache"));

@@ -154,13 +154,38 @@ def test_combine_parity(M, S):
     if S > 1:
         lse_part[0, 0, :, -1] = float("-inf")   # an empty split
     lse_part[2, 1, 5, :] = float("-inf")        # a row with no keys at all
-    o_part[2, 1, 5] = 0
+    # the partial rows of empty splits are never written by the scan and must
+    # never be read: NaN there for the GPU, zeros for the oracle
+    ref_part = torch.where(torch.isneginf(lse_part)[..., None], torch.zeros(()), o_part)
+    o_part[torch.isneginf(lse_part)] = float("nan")
     _say(f"combine S={S}")
     o_lat, lse = M.mla_combine_splits(o_part.to(DEV), lse_part.to(DEV))
     torch.cuda.synchronize()
-    ref_o, ref_l = O.combine(o_part.double().numpy(), lse_part.double().numpy())
+    ref_o, ref_l = O.combine(ref_part.double().numpy(), lse_part.double().numpy())
     assert_bar(o_lat.cpu().numpy(), ref_o, f"combine S={S}")
     assert_lse(lse.cpu().numpy(), ref_l, f"combine S={S}")
+
+
+@pytest.mark.parametrize("B,s_q,S", [(1, 1, 1), (16, 1, 17), (3, 15, 3), (2, 512, 2), (2, 1, 70), (1, 1, 130), (3, 11, 5)])
+def test_combine_up_proj_parity(M, B, s_q, S):
+    """Merge + up-projection in one pass against the oracle's combine then up_proj."""
+    g = torch.Generator().manual_seed(400 + B + s_q + S)
+    o_part = torch.randn((B, s_q, 128, S, 512), generator=g)
+    lse_part = torch.randn((B, s_q, 128, S), generator=g) * 5
+    w_uv = (torch.randn((128, 128, 512), generator=g) / math.sqrt(512)).to(torch.bfloat16)
+    if S > 1:
+        lse_part[0, 0, :, -1] = float("-inf")
+    lse_part[-1, -1, 7, :] = float("-inf")
+    ref_part = torch.where(torch.isneginf(lse_part)[..., None], torch.zeros(()), o_part)
+    o_part[torch.isneginf(lse_part)] = float("nan")
+    _say(f"combine+up_proj B={B} s_q={s_q} S={S}")
+    out, lse = M.mla_combine_up_proj(o_part.to(DEV), lse_part.to(DEV), w_uv.to(DEV))
+    torch.cuda.synchronize()
+    ref_o, ref_l = O.combine(ref_part.double().numpy(), lse_part.double().numpy())
+    ref_out = O.up_proj(ref_o.reshape(B * s_q, 128, 512), O.as_f64(w_uv))
+    assert_bar(O.as_f64(out.cpu()), ref_out, f"combine+up_proj B={B} s_q={s_q} S={S}")
+    assert_lse(lse.cpu().numpy(), ref_l, f"combine+up_proj lse B={B} s_q={s_q} S={S}")
+    assert (O.as_f64(out.cpu())[-1, 7] == 0).all(), "a row with no keys must project to zero"
 
 
 # ---------------------------------------------------------------------------
