@@ -12,7 +12,10 @@ Everything is float64 numpy, written from the definitions on the pages:
     page of the same page, sections 1 and 3;
   * the split scan plus log-sum-exp reduction structure of the MI355X Kimi K3
     time-share study (jinnpan.com), "Inside the blocks" (stage 1 KV scan,
-    stage 2 KV-split reduction).
+    stage 2 KV-split reduction);
+  * the cache append with the decoupled RoPE key rotated in fp32 (teardown
+    page, sections 3 and 4), with the frequency and pair layout readings
+    stated beside the code.
 
 Each function is pinned by tests under ``tests/test_oracle*.py`` against
 closed forms, brute-force loops, the pages' storage arithmetic and the
@@ -24,4 +27,5 @@ from .mla_oracle import (  # noqa: F401
     scores_absorbed, softmax_rows, attend_absorbed, decode_absorbed,
     decode_naive, up_proj, SCAN_GROUPS, scan_plan, decode_split, combine, decode_rows,
     latent_row_elems, latent_row_bytes, mha_kv_bytes_per_token_layer,
+    ROPE_BASE, rope_angles, rope_rotate, chunk_positions, append_latent,
 )

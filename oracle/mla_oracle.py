@@ -332,3 +332,81 @@ def decode_rows(q_abs, q_r, kv_cache, block_table, seqlens, scale: float, picks)
             o, l = attend_absorbed(qa, qr, C[:n], R[:n], scale)
             out_o[k], out_l[k] = o[0], l[0]
     return out_o, out_l
+
+
+# --------------------------------------------------------------------------
+# cache append with the decoupled RoPE key (the step before the path)
+# --------------------------------------------------------------------------
+# The teardown page fixes the precision of the rotation (the plugin computes
+# RoPE in fp32, section 3; the cure for a phase error is a table generated in
+# fp32 and fp32 multiply-adds in the kernel, section 4) but not its
+# frequencies or pair layout. Readings taken here:
+#   * pair j of a d_R-vector is (x[2j], x[2j+1]), j = 0 .. d_R/2 - 1;
+#   * its frequency is theta_j = base^(-2j / d_R), base a parameter (10000);
+#   * at position p the pair turns by the angle p * theta_j, counter-clockwise
+#     in the (x[2j], x[2j+1]) plane;
+#   * token i of an s_q-token chunk of sequence b sits at position
+#     L_b - s_q + i (L_b counts the chunk), the position the causal reading
+#     above gives it; a chunk token with a negative position has no slot.
+
+ROPE_BASE = 10000.0
+
+
+def rope_angles(positions, d_r: int = 64, base: float = ROPE_BASE) -> np.ndarray:
+    """[..., d_r/2] angles p * theta_j for positions of any shape, float64."""
+    j = np.arange(d_r // 2, dtype=np.float64)
+    theta = np.power(float(base), -2.0 * j / d_r)
+    return np.asarray(positions, np.float64)[..., None] * theta
+
+
+def rope_rotate(x, positions, base: float = ROPE_BASE) -> np.ndarray:
+    """Rotate the last axis (d_R values) of x by RoPE at positions.
+
+    positions broadcasts against x.shape[:-1].
+    """
+    x = np.asarray(x, np.float64)
+    a = rope_angles(np.broadcast_to(np.asarray(positions), x.shape[:-1]), x.shape[-1], base)
+    c, s = np.cos(a), np.sin(a)
+    xe, xo = x[..., 0::2], x[..., 1::2]
+    y = np.empty_like(x)
+    y[..., 0::2] = xe * c - xo * s
+    y[..., 1::2] = xe * s + xo * c
+    return y
+
+
+def chunk_positions(seqlens, s_q: int) -> np.ndarray:
+    """[B, s_q] positions L_b - s_q + i of each sequence's new tokens."""
+    L = np.asarray(seqlens, np.int64)
+    return L[:, None] - int(s_q) + np.arange(int(s_q), dtype=np.int64)[None, :]
+
+
+def append_latent(kv_cache, block_table, seqlens, c_new, kr_new, base: float = ROPE_BASE):
+    """Cache after writing one chunk of new tokens.
+
+    kv_cache [P, page, d_c + d_R] (float64 values, copied, not modified);
+    c_new [B, s_q, d_c] and kr_new [B, s_q, d_R] (k_R before rotation).
+    Token (b, i) goes to logical row p = L_b - s_q + i of sequence b, i.e.
+    physical page block_table[b, p // page], row p % page: its c_KV unchanged,
+    its k_R rotated by position p. Tokens with p < 0 or past the block table
+    are not written. Returns (new cache, list of the (page, row) written).
+    """
+    cache = np.array(kv_cache, dtype=np.float64, copy=True)
+    bt = np.asarray(block_table, np.int64)
+    page = cache.shape[1]
+    c_new = np.asarray(c_new, np.float64)
+    kr_new = np.asarray(kr_new, np.float64)
+    d_c = c_new.shape[-1]
+    pos = chunk_positions(seqlens, c_new.shape[1])
+    written = []
+    for b in range(pos.shape[0]):
+        for i in range(pos.shape[1]):
+            p = int(pos[b, i])
+            if p < 0 or p // page >= bt.shape[1]:
+                continue
+            pg = int(bt[b, p // page])
+            if pg < 0 or pg >= cache.shape[0]:
+                raise ValueError("block table entry out of range")
+            cache[pg, p % page, :d_c] = c_new[b, i]
+            cache[pg, p % page, d_c:] = rope_rotate(kr_new[b, i], p, base)
+            written.append((pg, p % page))
+    return cache, written

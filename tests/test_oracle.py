@@ -4,6 +4,7 @@ None of these re-types an oracle formula: each check is a closed form, a
 brute-force loop in plain Python floats, a value printed on the pages, or an
 identity between two independently written paths (naive vs absorbed).
 """
+import cmath
 import json
 import math
 import os
@@ -401,3 +402,110 @@ def test_gather_of_bf16_bits_decodes_exactly():
     assert rows_bits.dtype == np.float64 and np.array_equal(rows_bits, rows_f64)
     ref = kv.to(torch.float64)[[3, 0, 4]].reshape(-1, 576)[:150].numpy()
     assert np.array_equal(rows_bits, ref)
+
+
+# --------------------------------------------------------------------------
+# RoPE and the cache append (teardown page, sections 3 and 4; the frequency,
+# pair-layout and position readings are stated in the oracle)
+# --------------------------------------------------------------------------
+
+def _rope_by_complex(x, p, base=10000.0):
+    """Textbook form of the rotation: each pair (x[2j], x[2j+1]) as a complex
+    number multiplied by e^(i p base^(-j/(d/2)))."""
+    d = len(x)
+    out = []
+    for j in range(d // 2):
+        z = complex(float(x[2 * j]), float(x[2 * j + 1])) * cmath.exp(1j * p * base ** (-j / (d // 2)))
+        out += [z.real, z.imag]
+    return np.array(out)
+
+
+def test_rope_position_zero_is_identity():
+    x = np.random.default_rng(1).normal(size=(5, 64))
+    assert np.array_equal(O.rope_rotate(x, 0), x)
+
+
+@pytest.mark.parametrize("p", [1, 7, 1000, 65535])
+def test_rope_is_complex_multiplication(p):
+    x = np.random.default_rng(p).normal(size=64)
+    # the angle p*theta carries an fp64 rounding of ~1e-16 * p radians
+    np.testing.assert_allclose(O.rope_rotate(x, p), _rope_by_complex(x, p), rtol=0, atol=1e-14 * max(p, 100))
+
+
+def test_rope_exact_one_radian_angles():
+    # pair 0 turns by p; pair 16 by p/100; pair 31 by p * 10000^(-31/32)
+    for j, p in [(0, 1), (16, 100), (31, 10000.0 ** (31 / 32))]:
+        e = np.zeros(64)
+        e[2 * j] = 1.0
+        y = O.rope_rotate(e, p)
+        assert y[2 * j] == pytest.approx(math.cos(1.0), abs=1e-12)
+        assert y[2 * j + 1] == pytest.approx(math.sin(1.0), abs=1e-12)
+        assert np.count_nonzero(np.abs(y) > 1e-15) == 2
+
+
+@pytest.mark.parametrize("p", [3, 4097, 65535])
+def test_rope_is_a_proper_rotation(p):
+    M = np.stack([O.rope_rotate(e, p) for e in np.eye(64)], axis=1)
+    np.testing.assert_allclose(M.T @ M, np.eye(64), atol=1e-12)
+    assert np.linalg.det(M) == pytest.approx(1.0, abs=1e-9)
+
+
+def test_rope_composes_and_scores_depend_on_offset_only():
+    rng = np.random.default_rng(5)
+    q, k = rng.normal(size=64), rng.normal(size=64)
+    for m, n in [(0, 0), (5, 3), (1000, 17), (40000, 39999), (12, 300)]:
+        np.testing.assert_allclose(O.rope_rotate(O.rope_rotate(q, n), m), O.rope_rotate(q, m + n), atol=1e-9)
+        lhs = O.rope_rotate(q, m) @ O.rope_rotate(k, n)
+        assert lhs == pytest.approx(O.rope_rotate(q, m - n) @ k, abs=1e-9)
+
+
+def test_chunk_positions_follow_causal_rule():
+    L, s_q = [5, 64, 300], 4
+    pos = O.chunk_positions(L, s_q)
+    for b, Lb in enumerate(L):
+        for i in range(s_q):
+            # a new token sees itself as its last key
+            assert pos[b, i] + 1 == O.visible_len(Lb, s_q, i)
+
+
+def _tiny_append_case(seed=3, page=4, P=9, B=3, s_q=3, d_c=5, d_r=4):
+    rng = np.random.default_rng(seed)
+    cache = rng.normal(size=(P, page, d_c + d_r))
+    seqlens = np.array([2, 7, 11])                    # sequence 0 is shorter than the chunk
+    perm = rng.permutation(P)
+    bt = np.full((B, 3), -1, np.int64)
+    bt[0, :1], bt[1, :2], bt[2, :3] = perm[:1], perm[1:3], perm[3:6]
+    c_new = rng.normal(size=(B, s_q, d_c))
+    kr_new = rng.normal(size=(B, s_q, d_r))
+    return cache, bt, seqlens, c_new, kr_new, page, d_c
+
+
+def test_append_matches_token_loop():
+    cache, bt, L, c_new, kr_new, page, d_c = _tiny_append_case()
+    out, written = O.append_latent(cache, bt, L, c_new, kr_new)
+    expect = cache.copy()
+    n_written = 0
+    for b in range(3):
+        for i in range(3):
+            p = int(L[b]) - 3 + i
+            if p < 0:
+                continue
+            row = expect[bt[b][p // page], p % page]
+            row[:d_c] = c_new[b, i]
+            row[d_c:] = _rope_by_complex(kr_new[b, i], p)
+            n_written += 1
+    np.testing.assert_allclose(out, expect, rtol=0, atol=1e-12)
+    assert len(written) == n_written == 8            # one token of sequence 0 has no slot
+
+
+def test_append_then_gather_returns_the_chunk():
+    cache, bt, L, c_new, kr_new, page, d_c = _tiny_append_case(seed=9)
+    out, _ = O.append_latent(cache, bt, L, c_new, kr_new)
+    for b in (1, 2):
+        before = O.gather_rows(cache, bt[b], int(L[b]))
+        after = O.gather_rows(out, bt[b], int(L[b]))
+        np.testing.assert_array_equal(after[:-3], before[:-3])
+        np.testing.assert_array_equal(after[-3:, :d_c], c_new[b])
+        for i in range(3):
+            np.testing.assert_allclose(after[-3 + i, d_c:], _rope_by_complex(kr_new[b, i], int(L[b]) - 3 + i),
+                                       atol=1e-12)

@@ -90,3 +90,49 @@ def test_softmax_without_max_subtraction_bias_is_caught(monkeypatch):
         return e / l, m[..., 0], l[..., 0]
     _patch(monkeypatch, "softmax_rows", biased)
     _expect_fail(pins.test_softmax_rows_sum_to_one, pins.test_closed_form_zero_query_is_mean)
+
+
+def test_rope_half_split_pairing_is_caught(monkeypatch):
+    def half_split(x, positions, base=M.ROPE_BASE):
+        x = np.asarray(x, np.float64)
+        d = x.shape[-1]
+        a = M.rope_angles(np.broadcast_to(np.asarray(positions), x.shape[:-1]), d, base)
+        c, s = np.cos(a), np.sin(a)
+        lo, hi = x[..., : d // 2], x[..., d // 2:]
+        return np.concatenate([lo * c - hi * s, lo * s + hi * c], axis=-1)
+    _patch(monkeypatch, "rope_rotate", half_split)
+    _expect_fail(lambda: pins.test_rope_is_complex_multiplication(7), pins.test_rope_exact_one_radian_angles)
+
+
+def test_rope_frequency_exponent_is_caught(monkeypatch):
+    real_angles = M.rope_angles
+
+    def wrong(positions, d_r=64, base=M.ROPE_BASE):   # base^(-j/d) instead of base^(-2j/d)
+        return real_angles(positions, 2 * d_r, base)[..., : d_r // 2]
+    _patch(monkeypatch, "rope_angles", wrong)
+    _expect_fail(pins.test_rope_exact_one_radian_angles, lambda: pins.test_rope_is_complex_multiplication(7))
+
+
+def test_rope_reflection_is_caught(monkeypatch):
+    def reflect(x, positions, base=M.ROPE_BASE):
+        x = np.asarray(x, np.float64)
+        a = M.rope_angles(np.broadcast_to(np.asarray(positions), x.shape[:-1]), x.shape[-1], base)
+        c, s = np.cos(a), np.sin(a)
+        y = np.empty_like(x)
+        y[..., 0::2] = x[..., 0::2] * c - x[..., 1::2] * s
+        y[..., 1::2] = -x[..., 0::2] * s + x[..., 1::2] * c      # wrong sign: not a rotation
+        return y
+    _patch(monkeypatch, "rope_rotate", reflect)
+    _expect_fail(lambda: pins.test_rope_is_a_proper_rotation(3),
+                 pins.test_rope_composes_and_scores_depend_on_offset_only)
+
+
+def test_append_off_by_one_position_is_caught(monkeypatch):
+    monkeypatch.setattr(M, "chunk_positions",
+                        lambda L, s_q: np.asarray(L, np.int64)[:, None] - s_q + 1 + np.arange(s_q)[None, :])
+    _expect_fail(pins.test_append_matches_token_loop, pins.test_append_then_gather_returns_the_chunk)
+
+
+def test_append_without_rotation_is_caught(monkeypatch):
+    monkeypatch.setattr(M, "rope_rotate", lambda x, positions, base=M.ROPE_BASE: np.asarray(x, np.float64))
+    _expect_fail(pins.test_append_matches_token_loop, pins.test_append_then_gather_returns_the_chunk)
