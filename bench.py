@@ -115,6 +115,50 @@ def cpu_baseline(inp_cpu, q_abs_cpu, target_s):
     }
 
 
+def time_next_rows(M, torch, kv, tables, seqlens, lens, B, s_q, layers, reps=200):
+    """The step before the path at this workload: writing the chunk's tokens
+    into the cache (c_KV copied, k_R rotated) and rotating the queries' RoPE
+    parts. Both are launch-bound at decode sizes, so `reps` launches are
+    captured in one HIP graph and the replay is timed with HIP events: the
+    per-launch time is the GPU's, without Python dispatch in between."""
+    dev = kv.device
+    T = B * s_q
+    g = torch.Generator(device=dev).manual_seed(77)
+    c_new = torch.randn((B, s_q, 512), device=dev, generator=g).to(torch.bfloat16)
+    kr_new = torch.randn((B, s_q, 64), device=dev, generator=g).to(torch.bfloat16)
+    q_rot = torch.randn((B, s_q, 128, 64), device=dev, generator=g).to(torch.bfloat16)
+    rope = M.mla_rope_table(max(lens) + 1, device=dev)
+    # per token: append reads 1024 + 128 input bytes and 32 (cos, sin) pairs,
+    # writes a 1152-byte row; the query rotation reads and writes 128 heads x
+    # 64 bf16 and reads the same 32 pairs
+    cases = [("mla_append_latent", lambda k: M.mla_append_latent(kv[k % layers], tables[k % layers], seqlens,
+                                                                 c_new, kr_new, rope), T * (1024 + 128 + 256 + 1152)),
+             ("mla_rope_q", lambda k: M.mla_rope_q(q_rot, seqlens, rope), T * (2 * 128 * 64 * 2 + 256))]
+    res = {}
+    for name, fn, nbytes in cases:
+        for k in range(10):
+            fn(k)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for k in range(reps):
+                fn(k)
+        graph.replay()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / reps * 1e3
+        gbs = nbytes / (us * 1e-6) / 1e9
+        res[name] = {"us_per_launch": round(us, 2), "bytes_per_launch": nbytes, "achieved_gbps": round(gbs, 1),
+                     "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "timing": f"HIP graph of {reps} launches"}
+        del graph
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -246,6 +290,9 @@ def main():
             "mfma_frac": round(flop_attn / (dec_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         },
     }
+    # cache append + query rotation, timed after the step (they write into the
+    # cache rows the step has already read)
+    result["next_rows"] = time_next_rows(M, torch, kv, tables, seqlens, lens, B, s_q, layers)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (fp64 oracle on host cores)", file=sys.stderr, flush=True)
         layer0 = {"kv_cache": kv[0].cpu(), "block_table": tables[0].cpu(), "seqlens": st0.seqlens,

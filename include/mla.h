@@ -180,6 +180,54 @@ mla_status mla_combine_up_proj(const float* o_part, const float* lse_part, const
 mla_status mla_up_proj(const float* o_lat, const void* w_uv, void* out,
                        int64_t T, int H, void* stream);
 
+/* ---- the step before the decode path: cache append and RoPE -------------
+ * The decoupled RoPE parts are rotated in fp32 from an fp32 table with fp32
+ * multiply-adds (teardown page: RoPE compute type fp32, section 3; an fp32
+ * table and fp32 multiply-adds against the phase error of fp16, section 4).
+ * Pair j of a 64-value vector x is (x[2j], x[2j+1]); at position p it turns
+ * counter-clockwise by p * theta_j, theta_j = base^(-2j/64):
+ *     y[2j]   = x[2j] cos - x[2j+1] sin,   y[2j+1] = x[2j] sin + x[2j+1] cos
+ * computed as fp32 fma and rounded once to bf16. Token i of an s_q-token
+ * chunk of sequence b has position L_b - s_q + i, where seqlens[b] = L_b
+ * already counts the chunk (the same rule as the causal limit of
+ * mla_decode_paged). */
+
+/* HOST function: fill the rotation table for positions 0 .. max_pos-1,
+ *     table[(p * 32 + j) * 2 + 0] = cos(p * theta_j),  [... + 1] = sin(...)
+ * computed in double and rounded to float. `table` is a HOST pointer to
+ * max_pos * 64 floats (no alignment rule); copy it to the device for the two
+ * functions below. base > 0 and finite; 1 <= max_pos <= 2^22.
+ * Returns MLA_ERR_NULL / MLA_ERR_SHAPE on bad arguments. */
+mla_status mla_rope_table(double base, int max_pos, float* table);
+
+/* Write a chunk of new tokens into the paged cache:
+ *     cache row L_b - s_q + i of sequence b  <-  c_new[b, i] ++ rope(kr_new[b, i])
+ * i.e. physical page block_table[b, p / 64], row p % 64 with p the token's
+ * position; the 512 c_KV values are copied bit for bit, the 64 k_R values
+ * rotated by p. Tokens with p < 0 or p >= min(max_pages * 64, max_pos) are
+ * not written. Other rows of the cache are not touched.
+ *   c_new    bf16 [B, s_q, 512]
+ *   kr_new   bf16 [B, s_q, 64]   (k_R before rotation)
+ *   rope     fp32 [max_pos, 32, 2] table from mla_rope_table (device copy)
+ *   kv_cache bf16 [num_pages, 64, 576], updated in place
+ *   block_table, seqlens: as mla_decode_paged (entries are clamped into
+ *   [0, num_pages), so a bad entry cannot write outside the cache)
+ * B >= 1, 1 <= s_q <= 4096, B * s_q <= 2^24, num_pages >= 1,
+ * max_pages >= 1, max_pos >= 1. Two tokens that map to the same cache row
+ * (a block table that shares pages between sequences) race. */
+mla_status mla_append_latent(const void* c_new, const void* kr_new, const float* rope, int max_pos,
+                             void* kv_cache, int64_t num_pages, const int32_t* block_table, int max_pages,
+                             const int32_t* seqlens, int B, int s_q, void* stream);
+
+/* Rotate the decoupled RoPE part of the chunk's queries in place:
+ *     q_r[b, i, h, :] <- rope(q_r[b, i, h, :]) at position L_b - s_q + i
+ * Rows whose position is negative or >= max_pos are left unchanged.
+ *   q_r  bf16 [B, s_q, H, 64], in place
+ *   rope fp32 [max_pos, 32, 2] (device copy of mla_rope_table's table)
+ * B >= 1, 1 <= s_q <= 4096, H == MLA_HEADS, B * s_q <= 2^21, max_pos >= 1. */
+mla_status mla_rope_q(void* q_r, const float* rope, int max_pos, const int32_t* seqlens, int B, int s_q, int H,
+                      void* stream);
+
 /* Test and debug aid: gather the logical cache rows of each sequence through
  * the block table with the same address arithmetic as mla_decode_paged.
  *   out bf16 [B, max_len, 576]: row t of sequence b is the cache row of token

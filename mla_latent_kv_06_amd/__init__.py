@@ -13,6 +13,8 @@ Shapes (H = 128 heads, content dim 128, latent 512, RoPE 64, page 64):
   o_part   fp32 [B, s_q, H, S, 512]       lse_part    fp32 [B, s_q, H, S]
   o_lat    fp32 [B, s_q, H, 512]          lse         fp32 [B, s_q, H]
   out      bf16 [B, s_q, H, 128]
+  c_new    bf16 [B, s_q, 512]             kr_new      bf16 [B, s_q, 64]
+  rope     fp32 [max_pos, 32, 2] (cos, sin of p * 10000^(-2j/64) by default)
 """
 from __future__ import annotations
 
@@ -187,6 +189,54 @@ def mla_debug_gather(kv_cache, block_table, seqlens, max_len: int, out=None, str
                                      _ptr(seqlens), B, int(max_len), _ptr(out), _stream(stream)),
            "mla_debug_gather")
     return out
+
+
+ROPE_BASE = 10000.0
+
+
+def mla_rope_table(max_pos: int, base: float = ROPE_BASE, device=None) -> torch.Tensor:
+    """RoPE cos/sin table [max_pos, 32, 2] fp32, built by the library on the host
+    (double, rounded to float) and copied to ``device`` (default: the current GPU)."""
+    table = torch.empty((int(max_pos), D_R // 2, 2), dtype=torch.float32)
+    _check(_lib.LIB.mla_rope_table(float(base), int(max_pos), table.data_ptr()), "mla_rope_table")
+    if device is None:
+        device = torch.device("cuda", torch.cuda.current_device())
+    return table.to(device)
+
+
+def mla_append_latent(kv_cache, block_table, seqlens, c_new, kr_new, rope, stream=None):
+    """Write the chunk's tokens into the cache in place (row L_b - s_q + i of
+    sequence b: c_new copied, kr_new rotated by that position); returns kv_cache."""
+    B, s_q = c_new.shape[0], c_new.shape[1]
+    _need(c_new, "c_new", torch.bfloat16, (B, s_q, D_C))
+    _need(kr_new, "kr_new", torch.bfloat16, (B, s_q, D_R))
+    if rope.dim() != 3 or rope.shape[1:] != (D_R // 2, 2):
+        raise ValueError(f"rope must be [max_pos, 32, 2], got {tuple(rope.shape)}")
+    _need(rope, "rope", torch.float32)
+    if kv_cache.dim() != 3 or kv_cache.shape[1:] != (PAGE, ROW):
+        raise ValueError(f"kv_cache must be [num_pages, 64, 576], got {tuple(kv_cache.shape)}")
+    _need(kv_cache, "kv_cache", torch.bfloat16)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError(f"block_table must be [B, max_pages], got {tuple(block_table.shape)}")
+    _need(block_table, "block_table", torch.int32)
+    _need(seqlens, "seqlens", torch.int32, (B,))
+    _check(_lib.LIB.mla_append_latent(_ptr(c_new), _ptr(kr_new), _ptr(rope), rope.shape[0], _ptr(kv_cache),
+                                      kv_cache.shape[0], _ptr(block_table), block_table.shape[1], _ptr(seqlens),
+                                      B, s_q, _stream(stream)), "mla_append_latent")
+    return kv_cache
+
+
+def mla_rope_q(q_r, seqlens, rope, stream=None):
+    """Rotate q_r [B, s_q, H, 64] in place by each chunk token's position; returns q_r."""
+    B, s_q = q_r.shape[0], q_r.shape[1]
+    _need(q_r, "q_r", torch.bfloat16, (B, s_q, H, D_R))
+    if rope.dim() != 3 or rope.shape[1:] != (D_R // 2, 2):
+        raise ValueError(f"rope must be [max_pos, 32, 2], got {tuple(rope.shape)}")
+    _need(rope, "rope", torch.float32)
+    _need(seqlens, "seqlens", torch.int32, (B,))
+    _check(_lib.LIB.mla_rope_q(_ptr(q_r), _ptr(rope), rope.shape[0], _ptr(seqlens), B, s_q, H, _stream(stream)),
+           "mla_rope_q")
+    return q_r
 
 
 def decode_layer(q_c, q_r, kv_cache, block_table, seqlens, w_uk, w_uv, num_splits: int | None = None,

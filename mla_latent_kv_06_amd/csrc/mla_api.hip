@@ -8,6 +8,7 @@
 #include <string>
 
 #include "../../include/mla.h"
+#include "append.hpp"
 #include "decode.hpp"
 #include "validate.hpp"
 
@@ -113,6 +114,33 @@ mla_status mla_up_proj(const float* o_lat, const void* w_uv, void* out, int64_t 
   return report_hip(mla::launch_up_proj(o_lat, static_cast<const __bf16*>(w_uv), static_cast<__bf16*>(out), (int)T,
                                         as_stream(stream)),
                     "mla_up_proj launch");
+}
+
+mla_status mla_rope_table(double base, int max_pos, float* table) {
+  const mla::Check c = mla::check_rope_table(base, max_pos, table, mla::kMaxRopePositions);
+  if (!c.ok()) return report(c);
+  mla::rope_table_host(base, max_pos, table);
+  return MLA_OK;
+}
+
+mla_status mla_append_latent(const void* c_new, const void* kr_new, const float* rope, int max_pos, void* kv_cache,
+                             int64_t num_pages, const int32_t* block_table, int max_pages, const int32_t* seqlens,
+                             int B, int s_q, void* stream) {
+  const mla::Check c = mla::check_append(c_new, kr_new, rope, max_pos, kv_cache, num_pages, block_table, max_pages,
+                                         seqlens, B, s_q);
+  if (!c.ok()) return report(c);
+  return report_hip(mla::launch_append_latent(static_cast<const __bf16*>(c_new), static_cast<const __bf16*>(kr_new),
+                                              rope, max_pos, static_cast<char*>(kv_cache), num_pages, block_table,
+                                              max_pages, seqlens, B, s_q, as_stream(stream)),
+                    "mla_append_latent launch");
+}
+
+mla_status mla_rope_q(void* q_r, const float* rope, int max_pos, const int32_t* seqlens, int B, int s_q, int H,
+                      void* stream) {
+  const mla::Check c = mla::check_rope_q(q_r, rope, max_pos, seqlens, B, s_q, H);
+  if (!c.ok()) return report(c);
+  return report_hip(mla::launch_rope_q(static_cast<__bf16*>(q_r), rope, max_pos, seqlens, B, s_q, as_stream(stream)),
+                    "mla_rope_q launch");
 }
 
 mla_status mla_debug_gather(const void* kv_cache, int64_t num_pages, const int32_t* block_table, int max_pages,

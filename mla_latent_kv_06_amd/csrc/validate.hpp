@@ -121,6 +121,43 @@ inline Check check_combine_up(const void* o_part, const void* lse_part, const vo
   return Check{};
 }
 
+inline Check check_rope_table(double base, int max_pos, const void* table, int max_positions) {
+  if (table == nullptr) return fail(MLA_ERR_NULL, "%s is NULL", "table");
+  if (!(base > 0.0) || base > 1e300) return fail(MLA_ERR_SHAPE, "%s must be positive and finite", "base");
+  MLA_TRY(need_range(max_pos, 1, max_positions, "max_pos"));
+  return Check{};
+}
+
+inline Check check_append(const void* c_new, const void* kr_new, const void* rope, int max_pos, const void* kv,
+                          int64_t num_pages, const void* bt, int max_pages, const void* seqlens, int B, int s_q) {
+  MLA_TRY(need_ptr(c_new, "c_new"));
+  MLA_TRY(need_ptr(kr_new, "kr_new"));
+  MLA_TRY(need_ptr(rope, "rope"));
+  MLA_TRY(need_ptr(kv, "kv_cache"));
+  MLA_TRY(need_ptr(bt, "block_table"));
+  MLA_TRY(need_ptr(seqlens, "seqlens"));
+  MLA_TRY(need_range(max_pos, 1, (1LL << 31) - 1, "max_pos"));
+  MLA_TRY(need_range(num_pages, 1, (1LL << 40), "num_pages"));
+  MLA_TRY(need_range(max_pages, 1, (1 << 24), "max_pages"));
+  MLA_TRY(need_range(B, 1, (1 << 20), "B"));
+  MLA_TRY(need_range(s_q, 1, kMaxSq, "s_q"));
+  MLA_TRY(need_range((long long)B * s_q, 1, (1LL << 24), "B * s_q"));
+  return Check{};
+}
+
+inline Check check_rope_q(const void* q_r, const void* rope, int max_pos, const void* seqlens, int B, int s_q,
+                          int H) {
+  MLA_TRY(need_ptr(q_r, "q_r"));
+  MLA_TRY(need_ptr(rope, "rope"));
+  MLA_TRY(need_ptr(seqlens, "seqlens"));
+  MLA_TRY(need_range(max_pos, 1, (1LL << 31) - 1, "max_pos"));
+  MLA_TRY(need_range(B, 1, (1 << 20), "B"));
+  MLA_TRY(need_range(s_q, 1, kMaxSq, "s_q"));
+  MLA_TRY(need_range(H, MLA_HEADS, MLA_HEADS, "H"));
+  MLA_TRY(need_range((long long)B * s_q, 1, (1LL << 21), "B * s_q"));
+  return Check{};
+}
+
 inline Check check_gather(const void* kv, int64_t num_pages, const void* bt, int max_pages,
                           const void* seqlens, int B, int max_len, const void* out) {
   MLA_TRY(need_ptr(kv, "kv_cache"));

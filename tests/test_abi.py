@@ -26,7 +26,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) == 11, names
+    assert len(names) == 14, names
     out = subprocess.run(["nm", "-D", "--defined-only", os.path.join(ROOT, "mla_latent_kv_06_amd", "libmla.so")],
                          capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\bT (mla_[a-z_]+)\b", out))
@@ -77,6 +77,20 @@ def test_other_entry_validation(lib):
     assert lib.mla_combine_splits(A, A, 1, 1, 128, 0, A, A, None) == 2
     assert lib.mla_combine_splits(A, A, 1, 1, 128, 2, MIS, A, None) == 3
     assert lib.mla_debug_gather(A, 3, A, 1, A, 1, 0, A, None) == 2
+    # cache append: c_new, kr_new, rope, max_pos, kv, num_pages, bt, max_pages, seqlens, B, s_q
+    assert lib.mla_append_latent(None, A, A, 64, A, 4, A, 2, A, 2, 1, None) == 1
+    assert lib.mla_append_latent(A, A, None, 64, A, 4, A, 2, A, 2, 1, None) == 1
+    assert lib.mla_append_latent(A, MIS, A, 64, A, 4, A, 2, A, 2, 1, None) == 3
+    assert lib.mla_append_latent(A, A, A, 0, A, 4, A, 2, A, 2, 1, None) == 2
+    assert lib.mla_append_latent(A, A, A, 64, A, 0, A, 2, A, 2, 1, None) == 2
+    assert lib.mla_append_latent(A, A, A, 64, A, 4, A, 2, A, 2, 0, None) == 2
+    assert lib.mla_append_latent(A, A, A, 64, A, 4, A, 2, A, 2, 5000, None) == 2
+    # query rotation: q_r, rope, max_pos, seqlens, B, s_q, H
+    assert lib.mla_rope_q(None, A, 64, A, 2, 1, 128, None) == 1
+    assert lib.mla_rope_q(A, A, 64, MIS, 2, 1, 128, None) == 3
+    assert lib.mla_rope_q(A, A, 64, A, 2, 1, 64, None) == 2
+    assert lib.mla_rope_q(A, A, 0, A, 2, 1, 128, None) == 2
+    assert lib.mla_rope_q(A, A, 64, A, 1 << 20, 4, 128, None) == 2   # B * s_q > 2^21
 
 
 def test_host_helpers(lib):
@@ -87,6 +101,27 @@ def test_host_helpers(lib):
     assert lib.mla_recommended_splits(1, 1, 2048, 256) == 32
     assert lib.mla_recommended_splits(4, 256, 16640, 256) in (1, 2)
     assert lib.mla_recommended_splits(16, 1, 4096, 256) in (8, 9, 11)
+
+
+def test_rope_table_host(lib):
+    """The library's host table against the oracle's fp64 angles rounded to fp32."""
+    import numpy as np
+    import oracle as O
+    n = 70000
+    tab = np.zeros((n, 32, 2), np.float32)
+    assert lib.mla_rope_table(10000.0, n, tab.ctypes.data) == 0
+    a = O.rope_angles(np.arange(n), 64)
+    ref = np.stack([np.cos(a), np.sin(a)], axis=-1)
+    # rounding to float costs at most 2^-25 for values of magnitude <= 1; the
+    # two sides form the angle with different pow routines (fp64 ulps of an
+    # angle up to 7e4 rad), far below that
+    assert np.abs(tab.astype(np.float64) - ref).max() <= 2.0 ** -24
+    assert (tab[0, :, 0] == 1).all() and (tab[0, :, 1] == 0).all()
+    assert lib.mla_rope_table(10000.0, 4, None) == 1
+    assert lib.mla_rope_table(0.0, 4, tab.ctypes.data) == 2
+    assert lib.mla_rope_table(float("inf"), 4, tab.ctypes.data) == 2
+    assert lib.mla_rope_table(10000.0, 0, tab.ctypes.data) == 2
+    assert lib.mla_rope_table(10000.0, (1 << 22) + 1, tab.ctypes.data) == 2
 
 
 def test_plan_splits(lib):
