@@ -15,7 +15,9 @@ Everything is float64 numpy, written from the definitions on the pages:
     stage 2 KV-split reduction);
   * the cache append with the decoupled RoPE key rotated in fp32 (teardown
     page, sections 3 and 4), with the frequency and pair layout readings
-    stated beside the code.
+    stated beside the code;
+  * the decompressed branch for chunks above the absorption threshold
+    (teardown page, section 3 threshold, section 4 path A in two stages).
 
 Each function is pinned by tests under ``tests/test_oracle*.py`` against
 closed forms, brute-force loops, the pages' storage arithmetic and the
@@ -28,4 +30,5 @@ from .mla_oracle import (  # noqa: F401
     decode_naive, up_proj, SCAN_GROUPS, scan_plan, decode_split, combine, decode_rows,
     latent_row_elems, latent_row_bytes, mha_kv_bytes_per_token_layer,
     ROPE_BASE, rope_angles, rope_rotate, chunk_positions, append_latent,
+    PREFILL_ABSORPTION_THRESHOLD, uses_absorption, decompress_kv, rope_keys, attend_mha,
 )

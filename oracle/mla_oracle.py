@@ -410,3 +410,80 @@ def append_latent(kv_cache, block_table, seqlens, c_new, kr_new, base: float = R
             cache[pg, p % page, d_c:] = rope_rotate(kr_new[b, i], p, base)
             written.append((pg, p % page))
     return cache, written
+
+
+# --------------------------------------------------------------------------
+# decompressed branch for long chunks, and the dispatch between the two
+# --------------------------------------------------------------------------
+# The teardown page keeps the absorbed form for chunks of up to
+# kPrefillThresh = 256 new tokens (section 3: the constant and the plugin's
+# prefill_absorption_threshold) and decompresses the latent cache per head
+# for longer chunks (path A of section 4, split into its two stages here:
+# per-head keys and values, then causal attention over them).
+
+PREFILL_ABSORPTION_THRESHOLD = 256
+
+
+def uses_absorption(s_q: int, threshold: int = PREFILL_ABSORPTION_THRESHOLD) -> bool:
+    """Whether an s_q-token chunk takes the absorbed path (s_q <= threshold)."""
+    return int(s_q) <= int(threshold)
+
+
+def decompress_kv(kv_cache, block_table, seqlens, w_uk, w_uv, max_len: int):
+    """Per-head keys and values of every cached token.
+
+    Returns K, V [B, H, max_len, d_hc]: K[b, h, t] = W_UK[h] . c_KV[t] and
+    V[b, h, t] = W_UV[h] . c_KV[t] for t < L_b, zero after.
+    """
+    w_uk = np.asarray(w_uk, np.float64)
+    w_uv = np.asarray(w_uv, np.float64)
+    Hn, d_hc, d_c = w_uk.shape
+    B = len(seqlens)
+    K = np.zeros((B, Hn, max_len, d_hc))
+    V = np.zeros((B, Hn, max_len, d_hc))
+    for b in range(B):
+        L = min(int(seqlens[b]), max_len)
+        C = np.asarray(gather_rows(kv_cache, block_table[b], max(L, 0)), np.float64)[:, :d_c]
+        K[b, :, :L] = np.einsum("tc,hdc->htd", C, w_uk)
+        V[b, :, :L] = np.einsum("tc,hdc->htd", C, w_uv)
+    return K, V
+
+
+def rope_keys(kv_cache, block_table, seqlens, max_len: int, d_c: int = 512):
+    """k_R of every cached token, [B, max_len, d_R] (zero past L_b)."""
+    kv = np.asarray(kv_cache)
+    d_r = kv.shape[2] - d_c
+    B = len(seqlens)
+    R = np.zeros((B, max_len, d_r))
+    for b in range(B):
+        L = min(int(seqlens[b]), max_len)
+        R[b, :L] = np.asarray(gather_rows(kv_cache, block_table[b], max(L, 0)), np.float64)[:, d_c:]
+    return R
+
+
+def attend_mha(q_c, q_r, K, V, R, seqlens, scale: float):
+    """Causal multi-head attention over decompressed keys and values.
+
+    q_c [B, s_q, H, d_hc], q_r [B, s_q, H, d_R]; K, V [B, H, max_len, d_hc];
+    R [B, max_len, d_R] (the shared RoPE keys). Query i of sequence b sees
+    keys t < visible_len(L_b, s_q, i) with score (q_c . K + q_r . k_R) * scale.
+    Returns out [B, s_q, H, d_hc] and lse [B, s_q, H] (0 and -inf for a
+    query with no visible key).
+    """
+    q_c = np.asarray(q_c, np.float64)
+    q_r = np.asarray(q_r, np.float64)
+    B, s_q, Hn, d_hc = q_c.shape
+    out = np.zeros((B, s_q, Hn, V.shape[-1]))
+    lse = np.full((B, s_q, Hn), -np.inf)
+    for b in range(B):
+        L = int(seqlens[b])
+        for i in range(s_q):
+            n = min(max(visible_len(L, s_q, i), 0), K.shape[2])
+            if n == 0:
+                continue
+            for h in range(Hn):
+                s = (K[b, h, :n] @ q_c[b, i, h] + R[b, :n] @ q_r[b, i, h]) * scale
+                p, m, l = softmax_rows(s[None])
+                out[b, i, h] = p[0] @ V[b, h, :n]
+                lse[b, i, h] = m[0] + np.log(l[0])
+    return out, lse

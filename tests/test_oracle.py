@@ -509,3 +509,82 @@ def test_append_then_gather_returns_the_chunk():
         for i in range(3):
             np.testing.assert_allclose(after[-3 + i, d_c:], _rope_by_complex(kr_new[b, i], int(L[b]) - 3 + i),
                                        atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# decompressed branch and the dispatch threshold (teardown page, sections 3-4)
+# --------------------------------------------------------------------------
+
+def test_dispatch_threshold_matches_teardown_page():
+    g = _golden("teardown_dispatch.json")
+    assert O.PREFILL_ABSORPTION_THRESHOLD == g["kPrefillThresh"] == g["prefill_absorption_threshold"]
+    assert O.uses_absorption(1) and O.uses_absorption(g["kPrefillThresh"])
+    assert not O.uses_absorption(g["kPrefillThresh"] + 1)
+    assert O.uses_absorption(512, threshold=512) and not O.uses_absorption(129, threshold=128)
+
+
+def test_decompress_kv_brute_force():
+    rng = np.random.default_rng(8)
+    Hn, d_hc, d_c, d_r, page = 2, 3, 5, 2, 4
+    kv = rng.normal(size=(6, page, d_c + d_r))
+    bt = np.array([[4, 1, 0], [2, 5, 3]])
+    L = [9, 5]
+    w_uk, w_uv = rng.normal(size=(Hn, d_hc, d_c)), rng.normal(size=(Hn, d_hc, d_c))
+    K, V = O.decompress_kv(kv, bt, L, w_uk, w_uv, max_len=10)
+    for b in range(2):
+        for t in range(10):
+            row = kv[bt[b][t // page], t % page] if t < L[b] else None
+            for h in range(Hn):
+                for d in range(d_hc):
+                    kk = sum(float(row[c]) * float(w_uk[h, d, c]) for c in range(d_c)) if row is not None else 0.0
+                    vv = sum(float(row[c]) * float(w_uv[h, d, c]) for c in range(d_c)) if row is not None else 0.0
+                    assert K[b, h, t, d] == pytest.approx(kk, abs=1e-12)
+                    assert V[b, h, t, d] == pytest.approx(vv, abs=1e-12)
+    R = O.rope_keys(kv, bt, L, 10, d_c=d_c)
+    assert np.array_equal(R[1, :5], np.stack([kv[bt[1][t // page], t % page, d_c:] for t in range(5)]))
+    assert (R[1, 5:] == 0).all()
+
+
+def test_attend_mha_brute_force():
+    rng = np.random.default_rng(9)
+    B, s_q, Hn, d, d_r, n_max = 2, 3, 2, 4, 2, 7
+    L = [7, 2]                                   # the second sequence is shorter than the chunk
+    q_c, q_r = rng.normal(size=(B, s_q, Hn, d)), rng.normal(size=(B, s_q, Hn, d_r))
+    K, V = rng.normal(size=(B, Hn, n_max, d)), rng.normal(size=(B, Hn, n_max, d))
+    R = rng.normal(size=(B, n_max, d_r))
+    out, lse = O.attend_mha(q_c, q_r, K, V, R, L, 0.3)
+    for b in range(B):
+        for i in range(s_q):
+            n = L[b] - s_q + i + 1
+            for h in range(Hn):
+                if n <= 0:
+                    assert lse[b, i, h] == -math.inf and (out[b, i, h] == 0).all()
+                    continue
+                s = [0.3 * (sum(q_c[b, i, h, k] * K[b, h, t, k] for k in range(d))
+                            + sum(q_r[b, i, h, k] * R[b, t, k] for k in range(d_r))) for t in range(n)]
+                m = max(s)
+                w = [math.exp(x - m) for x in s]
+                tot = sum(w)
+                for k in range(d):
+                    assert out[b, i, h, k] == pytest.approx(sum(w[t] * V[b, h, t, k] for t in range(n)) / tot,
+                                                            abs=1e-12)
+                assert lse[b, i, h] == pytest.approx(m + math.log(tot), abs=1e-12)
+
+
+def test_decompressed_branch_equals_naive_and_absorbed_paths():
+    """Both stages together reproduce path A (decode_naive), itself pinned to
+    the absorbed path, at real dimensions and a causal chunk."""
+    inp = tiny_inputs(B=2, s_q=4, seqlens=[70, 9], h=4, d_hc=128, d_c=512, d_r=64, page=64, seed=3)
+    f = {k: O.as_f64(inp[k]) for k in ("q_c", "q_r", "w_uk", "w_uv")}
+    kvb = O.as_f64(inp["kv_cache"])
+    bt, sl = inp["block_table"].numpy(), inp["seqlens"].numpy()
+    K, V = O.decompress_kv(kvb, bt, sl, f["w_uk"], f["w_uv"], max_len=70)
+    R = O.rope_keys(kvb, bt, sl, 70)
+    out, lse = O.attend_mha(f["q_c"], f["q_r"], K, V, R, sl, O.default_scale())
+    ref_out, ref_lse = O.decode_naive(f["q_c"], f["q_r"], kvb, bt, sl, f["w_uk"], f["w_uv"], O.default_scale())
+    np.testing.assert_allclose(out, ref_out, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, ref_lse, rtol=0, atol=1e-12)
+    qa = O.absorb(f["q_c"], f["w_uk"])
+    o_lat, lse_b = O.decode_absorbed(qa, f["q_r"], kvb, bt, sl, O.default_scale())
+    np.testing.assert_allclose(out, O.up_proj(o_lat, f["w_uv"]), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(lse, lse_b, rtol=0, atol=1e-11)

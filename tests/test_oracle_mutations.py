@@ -136,3 +136,22 @@ def test_append_off_by_one_position_is_caught(monkeypatch):
 def test_append_without_rotation_is_caught(monkeypatch):
     monkeypatch.setattr(M, "rope_rotate", lambda x, positions, base=M.ROPE_BASE: np.asarray(x, np.float64))
     _expect_fail(pins.test_append_matches_token_loop, pins.test_append_then_gather_returns_the_chunk)
+
+
+def test_decompress_swapping_weights_is_caught(monkeypatch):
+    real = M.decompress_kv
+    _patch(monkeypatch, "decompress_kv",
+           lambda kv, bt, L, w_uk, w_uv, max_len: real(kv, bt, L, w_uv, w_uk, max_len))
+    _expect_fail(pins.test_decompress_kv_brute_force, pins.test_decompressed_branch_equals_naive_and_absorbed_paths)
+
+
+def test_mha_without_rope_term_is_caught(monkeypatch):
+    real = M.attend_mha
+    _patch(monkeypatch, "attend_mha",
+           lambda q_c, q_r, K, V, R, L, scale: real(q_c, np.zeros_like(np.asarray(q_r, np.float64)), K, V, R, L, scale))
+    _expect_fail(pins.test_attend_mha_brute_force, pins.test_decompressed_branch_equals_naive_and_absorbed_paths)
+
+
+def test_dispatch_strict_threshold_is_caught(monkeypatch):
+    _patch(monkeypatch, "uses_absorption", lambda s_q, threshold=M.PREFILL_ABSORPTION_THRESHOLD: int(s_q) < threshold)
+    _expect_fail(pins.test_dispatch_threshold_matches_teardown_page)
