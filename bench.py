@@ -159,6 +159,47 @@ def time_next_rows(M, torch, kv, tables, seqlens, lens, B, s_q, layers, reps=200
     return res
 
 
+def time_decompressed_branch(M, torch, kv, tables, seqlens, lens, q_c, q_r, w_uk, w_uv, s_q, layers, reps=5):
+    """The decompressed branch (per-head K/V, then causal MHA) at this
+    workload, timed per kernel with HIP events, with its algorithmic FLOP
+    and bytes. The absorbed step above is the comparison the dispatch rule
+    makes."""
+    B = len(lens)
+    max_len = -(-max(lens) // 64) * 64
+    shape = (B, 128, max_len, 128)
+    k_nope = torch.empty(shape, dtype=torch.bfloat16, device=kv.device)
+    v = torch.empty(shape, dtype=torch.float16, device=kv.device)
+    out = torch.empty((B, s_q, 128, 128), dtype=torch.bfloat16, device=kv.device)
+    lse = torch.empty((B, s_q, 128), dtype=torch.float32, device=kv.device)
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    for k in range(2 + reps):
+        layer = k % layers
+        e = ev[k - 2] if k >= 2 else None
+        if e: e[0].record(stream)
+        M.mla_decompress_kv(kv[layer], tables[layer], seqlens, w_uk, w_uv, max_len, k_nope=k_nope, v=v)
+        if e: e[1].record(stream)
+        M.mla_prefill_mha(q_c, q_r, k_nope, v, kv[layer], tables[layer], seqlens, out=out, lse=lse)
+        if e: e[2].record(stream)
+    torch.cuda.synchronize()
+    t_dec = sum(e[0].elapsed_time(e[1]) for e in ev) / reps
+    t_mha = sum(e[1].elapsed_time(e[2]) for e in ev) / reps
+    tokens = sum(lens)
+    flop_dec = 2.0 * tokens * 512 * (2 * 128 * 128)
+    pairs = visible_pairs(lens, s_q)
+    flop_mha = 2.0 * pairs * 128 * (192 + 128)
+    bytes_dec = tokens * (1024 + 2 * 128 * 128 * 2) + 2 * 128 * 128 * 512 * 2
+    del k_nope, v
+    return {
+        "mla_decompress_kv": {"ms": round(t_dec, 4), "flop": flop_dec, "tflops": round(flop_dec / (t_dec * 1e-3) / 1e12, 1),
+                              "mfma_frac": round(flop_dec / (t_dec * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                              "bytes": bytes_dec, "gbps": round(bytes_dec / (t_dec * 1e-3) / 1e9, 1)},
+        "mla_prefill_mha": {"ms": round(t_mha, 4), "flop": flop_mha, "tflops": round(flop_mha / (t_mha * 1e-3) / 1e12, 1),
+                            "mfma_frac": round(flop_mha / (t_mha * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "branch_ms": round(t_dec + t_mha, 4),
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -293,6 +334,12 @@ def main():
     # cache append + query rotation, timed after the step (they write into the
     # cache rows the step has already read)
     result["next_rows"] = time_next_rows(M, torch, kv, tables, seqlens, lens, B, s_q, layers)
+    if s_q > 1:
+        # the decompressed branch the dispatch rule would take above 256 new
+        # tokens, timed at this chunk length for comparison with the step
+        result["next_rows"]["decompressed_branch"] = time_decompressed_branch(
+            M, torch, kv, tables, seqlens, lens, q_c, q_r, w_uk, w_uv, s_q, layers)
+        result["next_rows"]["decompressed_branch"]["absorbed_step_ms"] = round(ms_step, 4)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (fp64 oracle on host cores)", file=sys.stderr, flush=True)
         layer0 = {"kv_cache": kv[0].cpu(), "block_table": tables[0].cpu(), "seqlens": st0.seqlens,

@@ -228,6 +228,51 @@ mla_status mla_append_latent(const void* c_new, const void* kr_new, const float*
 mla_status mla_rope_q(void* q_r, const float* rope, int max_pos, const int32_t* seqlens, int B, int s_q, int H,
                       void* stream);
 
+/* ---- decompressed branch for long chunks ---------------------------------
+ * The teardown page keeps the absorbed form for chunks of up to 256 new
+ * tokens (section 3: kPrefillThresh and the plugin's
+ * prefill_absorption_threshold) and decompresses the latent cache per head
+ * above that (path A of section 4), in two stages:
+ *   K[b, h, t, :] = W_UK[h] . c_KV[t],  V[b, h, t, :] = W_UV[h] . c_KV[t]
+ *   out[b, i, h] = softmax_t((q_c[b,i,h] . K[b,h,t] + q_R[b,i,h] . k_R[t]) * scale) . V[b,h,t]
+ * over t <= L_b - s_q + i (the causal rule of mla_decode_paged); out is the
+ * final per-head output (no up-projection). */
+
+/* 1 if an s_q-token chunk takes the absorbed path (s_q <= 256), else 0. */
+int mla_prefill_uses_absorption(int s_q);
+
+/* Bytes of one of the K and V buffers: B * 128 * max_len * 128 16-bit values
+ * (0 for non-positive sizes). */
+size_t mla_decompressed_kv_bytes(int B, int max_len);
+
+/* Stage 1: per-head keys and values of every cached token, bf16 MFMA with
+ * fp32 accumulation, rounded once: keys to bf16, values to fp16 (the
+ * attention's P.V product runs in fp16, three more significant bits than
+ * bf16; values must stay below 65504 in magnitude, which the method's
+ * weight scale keeps them far from).
+ *   kv_cache, block_table, seqlens, num_pages, max_pages: as mla_decode_paged
+ *   w_uk, w_uv  bf16 [H, 128, 512]
+ *   k_nope      bf16 [B, H, max_len, 128] output (head-major)
+ *   v           fp16 [B, H, max_len, 128] output (head-major)
+ *   rows t < min(L_b, max_len) are written, the rest are not touched
+ * B >= 1, max_len >= 1 and a multiple of 64 (MLA_PAGE), B * max_len <= 2^31. */
+mla_status mla_decompress_kv(const void* kv_cache, int64_t num_pages, const int32_t* block_table, int max_pages,
+                             const int32_t* seqlens, int B, int max_len, const void* w_uk, const void* w_uv,
+                             void* k_nope, void* v, void* stream);
+
+/* Stage 2: causal attention over stage 1's K and V and the cache's k_R.
+ *   q_c bf16 [B, s_q, H, 128], q_r bf16 [B, s_q, H, 64] (rotated)
+ *   k_nope, v  from mla_decompress_kv with the same max_len and inputs
+ *   out bf16 [B, s_q, H, 128], lse fp32 [B, s_q, H] (natural log of the
+ *   sum of exp(scaled score)); a query with no visible key gets out = 0 and
+ *   lse = -inf. Queries see at most min(L_b, max_len) keys.
+ * B >= 1, s_q >= 1, B * s_q <= 2^24, H == MLA_HEADS, max_len as above,
+ * softmax_scale positive and finite. */
+mla_status mla_prefill_mha(const void* q_c, const void* q_r, const void* k_nope, const void* v, int max_len,
+                           const void* kv_cache, int64_t num_pages, const int32_t* block_table, int max_pages,
+                           const int32_t* seqlens, int B, int s_q, int H, float softmax_scale, void* out, float* lse,
+                           void* stream);
+
 /* Test and debug aid: gather the logical cache rows of each sequence through
  * the block table with the same address arithmetic as mla_decode_paged.
  *   out bf16 [B, max_len, 576]: row t of sequence b is the cache row of token

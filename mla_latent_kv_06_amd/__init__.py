@@ -239,6 +239,63 @@ def mla_rope_q(q_r, seqlens, rope, stream=None):
     return q_r
 
 
+def mla_prefill_uses_absorption(s_q: int) -> bool:
+    """Whether an s_q-token chunk takes the absorbed path (s_q <= 256)."""
+    return bool(_lib.LIB.mla_prefill_uses_absorption(int(s_q)))
+
+
+def _cache_args(kv_cache, block_table, seqlens, B):
+    if kv_cache.dim() != 3 or kv_cache.shape[1:] != (PAGE, ROW):
+        raise ValueError(f"kv_cache must be [num_pages, 64, 576], got {tuple(kv_cache.shape)}")
+    _need(kv_cache, "kv_cache", torch.bfloat16)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError(f"block_table must be [B, max_pages], got {tuple(block_table.shape)}")
+    _need(block_table, "block_table", torch.int32)
+    _need(seqlens, "seqlens", torch.int32, (B,))
+
+
+def mla_decompress_kv(kv_cache, block_table, seqlens, w_uk, w_uv, max_len: int, k_nope=None, v=None, stream=None):
+    """Per-head keys (bf16) and values (fp16) [B, H, max_len, 128] of every
+    cached token (rows past a sequence's length are left as they were)."""
+    B = block_table.shape[0]
+    _cache_args(kv_cache, block_table, seqlens, B)
+    _need(w_uk, "w_uk", torch.bfloat16, (H, D_HC, D_C))
+    _need(w_uv, "w_uv", torch.bfloat16, (H, D_HC, D_C))
+    shape = (B, H, int(max_len), D_HC)
+    if k_nope is None:
+        k_nope = torch.empty(shape, dtype=torch.bfloat16, device=kv_cache.device)
+    if v is None:
+        v = torch.empty(shape, dtype=torch.float16, device=kv_cache.device)
+    _need(k_nope, "k_nope", torch.bfloat16, shape)
+    _need(v, "v", torch.float16, shape)
+    _check(_lib.LIB.mla_decompress_kv(_ptr(kv_cache), kv_cache.shape[0], _ptr(block_table), block_table.shape[1],
+                                      _ptr(seqlens), B, int(max_len), _ptr(w_uk), _ptr(w_uv), _ptr(k_nope), _ptr(v),
+                                      _stream(stream)), "mla_decompress_kv")
+    return k_nope, v
+
+
+def mla_prefill_mha(q_c, q_r, k_nope, v, kv_cache, block_table, seqlens, softmax_scale: float = DEFAULT_SCALE,
+                    out=None, lse=None, stream=None):
+    """Causal attention over decompressed K/V; returns (out [B,s_q,H,128] bf16, lse [B,s_q,H] fp32)."""
+    B, s_q = q_c.shape[0], q_c.shape[1]
+    _need(q_c, "q_c", torch.bfloat16, (B, s_q, H, D_HC))
+    _need(q_r, "q_r", torch.bfloat16, (B, s_q, H, D_R))
+    max_len = k_nope.shape[2]
+    _need(k_nope, "k_nope", torch.bfloat16, (B, H, max_len, D_HC))
+    _need(v, "v", torch.float16, (B, H, max_len, D_HC))
+    _cache_args(kv_cache, block_table, seqlens, B)
+    if out is None:
+        out = torch.empty((B, s_q, H, D_HC), dtype=torch.bfloat16, device=q_c.device)
+    if lse is None:
+        lse = torch.empty((B, s_q, H), dtype=torch.float32, device=q_c.device)
+    _need(out, "out", torch.bfloat16, (B, s_q, H, D_HC))
+    _need(lse, "lse", torch.float32, (B, s_q, H))
+    _check(_lib.LIB.mla_prefill_mha(_ptr(q_c), _ptr(q_r), _ptr(k_nope), _ptr(v), max_len, _ptr(kv_cache),
+                                    kv_cache.shape[0], _ptr(block_table), block_table.shape[1], _ptr(seqlens), B, s_q,
+                                    H, float(softmax_scale), _ptr(out), _ptr(lse), _stream(stream)), "mla_prefill_mha")
+    return out, lse
+
+
 def decode_layer(q_c, q_r, kv_cache, block_table, seqlens, w_uk, w_uv, num_splits: int | None = None,
                  softmax_scale: float = DEFAULT_SCALE, max_len: int | None = None, stream=None):
     """The whole hot path for one layer: absorb -> split scan -> combine -> up-projection.
@@ -256,3 +313,25 @@ def decode_layer(q_c, q_r, kv_cache, block_table, seqlens, w_uk, w_uv, num_split
     o_lat, lse = mla_combine_splits(o_part, lse_part, stream=stream)
     out = mla_up_proj(o_lat, w_uv, stream=stream)
     return dict(q_abs=q_abs, o_part=o_part, lse_part=lse_part, o_lat=o_lat, lse=lse, out=out)
+
+
+def attention_layer(q_c, q_r, kv_cache, block_table, seqlens, w_uk, w_uv, max_len: int,
+                    softmax_scale: float = DEFAULT_SCALE, num_splits: int | None = None, absorbed: bool | None = None,
+                    stream=None):
+    """One MLA attention layer for a chunk of s_q new tokens per sequence,
+    dispatched as the teardown page does (section 3): the absorbed path
+    (decode_layer) for s_q <= 256, the decompressed branch (mla_decompress_kv,
+    then mla_prefill_mha) above. ``absorbed`` forces a path; ``max_len`` is the
+    longest sequence (host int). Returns a dict with ``path``, ``out``
+    [B, s_q, H, 128] bf16 and ``lse`` [B, s_q, H] fp32 plus the intermediates."""
+    B, s_q = q_c.shape[0], q_c.shape[1]
+    use_absorbed = mla_prefill_uses_absorption(s_q) if absorbed is None else bool(absorbed)
+    if use_absorbed:
+        r = decode_layer(q_c, q_r, kv_cache, block_table, seqlens, w_uk, w_uv, num_splits, softmax_scale,
+                         max_len, stream)
+        r["path"] = "absorbed"
+        return r
+    ml = -(-int(max_len) // PAGE) * PAGE
+    k_nope, v = mla_decompress_kv(kv_cache, block_table, seqlens, w_uk, w_uv, ml, stream=stream)
+    out, lse = mla_prefill_mha(q_c, q_r, k_nope, v, kv_cache, block_table, seqlens, softmax_scale, stream=stream)
+    return dict(path="decompressed", k_nope=k_nope, v=v, out=out, lse=lse)

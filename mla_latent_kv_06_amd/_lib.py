@@ -37,6 +37,12 @@ SIGNATURES = {
     "mla_append_latent": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_int64, c_void_p, c_int, c_void_p,
                                   c_int, c_int, c_void_p]),
     "mla_rope_q": (c_int, [c_void_p, c_void_p, c_int, c_void_p, c_int, c_int, c_int, c_void_p]),
+    "mla_prefill_uses_absorption": (c_int, [c_int]),
+    "mla_decompressed_kv_bytes": (c_size_t, [c_int, c_int]),
+    "mla_decompress_kv": (c_int, [c_void_p, c_int64, c_void_p, c_int, c_void_p, c_int, c_int, c_void_p, c_void_p,
+                                  c_void_p, c_void_p, c_void_p]),
+    "mla_prefill_mha": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_int64, c_void_p, c_int,
+                                c_void_p, c_int, c_int, c_int, c_float, c_void_p, c_void_p, c_void_p]),
 }
 
 

@@ -10,6 +10,7 @@
 #include "../../include/mla.h"
 #include "append.hpp"
 #include "decode.hpp"
+#include "prefill.hpp"
 #include "validate.hpp"
 
 namespace {
@@ -141,6 +142,41 @@ mla_status mla_rope_q(void* q_r, const float* rope, int max_pos, const int32_t* 
   if (!c.ok()) return report(c);
   return report_hip(mla::launch_rope_q(static_cast<__bf16*>(q_r), rope, max_pos, seqlens, B, s_q, as_stream(stream)),
                     "mla_rope_q launch");
+}
+
+int mla_prefill_uses_absorption(int s_q) { return s_q <= mla::kPrefillAbsorptionThreshold ? 1 : 0; }
+
+size_t mla_decompressed_kv_bytes(int B, int max_len) {
+  if (B <= 0 || max_len <= 0) return 0;
+  return (size_t)B * MLA_HEADS * (size_t)max_len * MLA_D_HC * 2;
+}
+
+mla_status mla_decompress_kv(const void* kv_cache, int64_t num_pages, const int32_t* block_table, int max_pages,
+                             const int32_t* seqlens, int B, int max_len, const void* w_uk, const void* w_uv,
+                             void* k_nope, void* v, void* stream) {
+  const mla::Check c = mla::check_decompress(kv_cache, num_pages, block_table, max_pages, seqlens, B, max_len, w_uk,
+                                             w_uv, k_nope, v);
+  if (!c.ok()) return report(c);
+  return report_hip(mla::launch_decompress_kv(static_cast<const char*>(kv_cache), num_pages, block_table, max_pages,
+                                              seqlens, B, max_len, static_cast<const __bf16*>(w_uk),
+                                              static_cast<const __bf16*>(w_uv), static_cast<__bf16*>(k_nope),
+                                              static_cast<_Float16*>(v), as_stream(stream)),
+                    "mla_decompress_kv launch");
+}
+
+mla_status mla_prefill_mha(const void* q_c, const void* q_r, const void* k_nope, const void* v, int max_len,
+                           const void* kv_cache, int64_t num_pages, const int32_t* block_table, int max_pages,
+                           const int32_t* seqlens, int B, int s_q, int H, float softmax_scale, void* out, float* lse,
+                           void* stream) {
+  const mla::Check c = mla::check_prefill_mha(q_c, q_r, k_nope, v, max_len, kv_cache, num_pages, block_table,
+                                              max_pages, seqlens, B, s_q, H, softmax_scale, out, lse);
+  if (!c.ok()) return report(c);
+  return report_hip(mla::launch_prefill_mha(static_cast<const __bf16*>(q_c), static_cast<const __bf16*>(q_r),
+                                            static_cast<const __bf16*>(k_nope), static_cast<const _Float16*>(v), max_len,
+                                            static_cast<const char*>(kv_cache), num_pages, block_table, max_pages,
+                                            seqlens, B, s_q, softmax_scale * 1.44269504088896340736f,
+                                            static_cast<__bf16*>(out), lse, as_stream(stream)),
+                    "mla_prefill_mha launch");
 }
 
 mla_status mla_debug_gather(const void* kv_cache, int64_t num_pages, const int32_t* block_table, int max_pages,

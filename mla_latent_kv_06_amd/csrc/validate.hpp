@@ -158,6 +158,48 @@ inline Check check_rope_q(const void* q_r, const void* rope, int max_pos, const 
   return Check{};
 }
 
+inline Check check_decompress(const void* kv, int64_t num_pages, const void* bt, int max_pages, const void* seqlens,
+                              int B, int max_len, const void* w_uk, const void* w_uv, const void* k, const void* v) {
+  MLA_TRY(need_ptr(kv, "kv_cache"));
+  MLA_TRY(need_ptr(bt, "block_table"));
+  MLA_TRY(need_ptr(seqlens, "seqlens"));
+  MLA_TRY(need_ptr(w_uk, "w_uk"));
+  MLA_TRY(need_ptr(w_uv, "w_uv"));
+  MLA_TRY(need_ptr(k, "k_nope"));
+  MLA_TRY(need_ptr(v, "v"));
+  MLA_TRY(need_range(num_pages, 1, (1LL << 40), "num_pages"));
+  MLA_TRY(need_range(max_pages, 1, (1 << 24), "max_pages"));
+  MLA_TRY(need_range(B, 1, (1 << 20), "B"));
+  MLA_TRY(need_range(max_len, 1, (1 << 30), "max_len"));
+  if (max_len % MLA_PAGE != 0) return fail(MLA_ERR_SHAPE, "%s must be a multiple of 64 (got %lld)", "max_len", max_len);
+  MLA_TRY(need_range((long long)B * max_len, 1, (1LL << 31), "B * max_len"));
+  return Check{};
+}
+
+inline Check check_prefill_mha(const void* q_c, const void* q_r, const void* k, const void* v, int max_len,
+                               const void* kv, int64_t num_pages, const void* bt, int max_pages, const void* seqlens,
+                               int B, int s_q, int H, float scale, const void* out, const void* lse) {
+  MLA_TRY(need_ptr(q_c, "q_c"));
+  MLA_TRY(need_ptr(q_r, "q_r"));
+  MLA_TRY(need_ptr(out, "out"));
+  MLA_TRY(need_ptr(lse, "lse"));
+  MLA_TRY(need_ptr(k, "k_nope"));
+  MLA_TRY(need_ptr(v, "v"));
+  MLA_TRY(need_ptr(kv, "kv_cache"));
+  MLA_TRY(need_ptr(bt, "block_table"));
+  MLA_TRY(need_ptr(seqlens, "seqlens"));
+  MLA_TRY(need_range(num_pages, 1, (1LL << 40), "num_pages"));
+  MLA_TRY(need_range(max_pages, 1, (1 << 24), "max_pages"));
+  MLA_TRY(need_range(B, 1, (1 << 20), "B"));
+  MLA_TRY(need_range(max_len, 1, (1 << 30), "max_len"));
+  if (max_len % MLA_PAGE != 0) return fail(MLA_ERR_SHAPE, "%s must be a multiple of 64 (got %lld)", "max_len", max_len);
+  MLA_TRY(need_range(s_q, 1, (1 << 20), "s_q"));
+  MLA_TRY(need_range(H, MLA_HEADS, MLA_HEADS, "H"));
+  MLA_TRY(need_range((long long)B * s_q, 1, (1LL << 24), "B * s_q"));
+  if (!(scale > 0.f) || scale > 3.0e38f) return fail(MLA_ERR_SHAPE, "%s must be positive and finite", "softmax_scale");
+  return Check{};
+}
+
 inline Check check_gather(const void* kv, int64_t num_pages, const void* bt, int max_pages,
                           const void* seqlens, int B, int max_len, const void* out) {
   MLA_TRY(need_ptr(kv, "kv_cache"));

@@ -26,7 +26,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) == 14, names
+    assert len(names) == 18, names
     out = subprocess.run(["nm", "-D", "--defined-only", os.path.join(ROOT, "mla_latent_kv_06_amd", "libmla.so")],
                          capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\bT (mla_[a-z_]+)\b", out))
@@ -91,6 +91,17 @@ def test_other_entry_validation(lib):
     assert lib.mla_rope_q(A, A, 64, A, 2, 1, 64, None) == 2
     assert lib.mla_rope_q(A, A, 0, A, 2, 1, 128, None) == 2
     assert lib.mla_rope_q(A, A, 64, A, 1 << 20, 4, 128, None) == 2   # B * s_q > 2^21
+    # decompressed branch: kv, num_pages, bt, max_pages, seqlens, B, max_len, w_uk, w_uv, k, v
+    assert lib.mla_decompress_kv(A, 4, A, 2, A, 2, 128, None, A, A, A, None) == 1
+    assert lib.mla_decompress_kv(A, 4, A, 2, A, 2, 100, A, A, A, A, None) == 2     # not a multiple of 64
+    assert lib.mla_decompress_kv(A, 4, A, 2, A, 0, 128, A, A, A, A, None) == 2
+    assert lib.mla_decompress_kv(A, 4, A, 2, A, 2, 128, A, A, MIS, A, None) == 3
+    # q_c, q_r, k, v, max_len, kv, num_pages, bt, max_pages, seqlens, B, s_q, H, scale, out, lse
+    assert lib.mla_prefill_mha(A, A, None, A, 128, A, 4, A, 2, A, 2, 300, 128, 0.07, A, A, None) == 1
+    assert lib.mla_prefill_mha(A, A, A, A, 96, A, 4, A, 2, A, 2, 300, 128, 0.07, A, A, None) == 2
+    assert lib.mla_prefill_mha(A, A, A, A, 128, A, 4, A, 2, A, 2, 300, 64, 0.07, A, A, None) == 2
+    assert lib.mla_prefill_mha(A, A, A, A, 128, A, 4, A, 2, A, 2, 300, 128, 0.0, A, A, None) == 2
+    assert lib.mla_prefill_mha(A, A, A, A, 128, A, 4, A, 2, A, 2, 0, 128, 0.07, A, A, None) == 2
 
 
 def test_host_helpers(lib):
@@ -101,6 +112,17 @@ def test_host_helpers(lib):
     assert lib.mla_recommended_splits(1, 1, 2048, 256) == 32
     assert lib.mla_recommended_splits(4, 256, 16640, 256) in (1, 2)
     assert lib.mla_recommended_splits(16, 1, 4096, 256) in (8, 9, 11)
+
+
+def test_prefill_dispatch_and_sizes(lib):
+    import json
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "teardown_dispatch.json")))
+    thr = g["kPrefillThresh"]
+    assert lib.mla_prefill_uses_absorption(1) == 1
+    assert lib.mla_prefill_uses_absorption(thr) == 1
+    assert lib.mla_prefill_uses_absorption(thr + 1) == 0
+    assert lib.mla_decompressed_kv_bytes(4, 16640) == 4 * 128 * 16640 * 128 * 2
+    assert lib.mla_decompressed_kv_bytes(0, 64) == 0
 
 
 def test_rope_table_host(lib):
