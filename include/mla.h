@@ -254,7 +254,8 @@ size_t mla_decompressed_kv_bytes(int B, int max_len);
  *   w_uk, w_uv  bf16 [H, 128, 512]
  *   k_nope      bf16 [B, H, max_len, 128] output (head-major)
  *   v           fp16 [B, H, max_len, 128] output (head-major)
- *   rows t < min(L_b, max_len) are written, the rest are not touched
+ *   rows t < min(L_b, max_len) are written, rows from there to the end of
+ *   that 64-token page are zero-filled, later rows are not touched
  * B >= 1, max_len >= 1 and a multiple of 64 (MLA_PAGE), B * max_len <= 2^31. */
 mla_status mla_decompress_kv(const void* kv_cache, int64_t num_pages, const int32_t* block_table, int max_pages,
                              const int32_t* seqlens, int B, int max_len, const void* w_uk, const void* w_uv,
@@ -263,6 +264,8 @@ mla_status mla_decompress_kv(const void* kv_cache, int64_t num_pages, const int3
 /* Stage 2: causal attention over stage 1's K and V and the cache's k_R.
  *   q_c bf16 [B, s_q, H, 128], q_r bf16 [B, s_q, H, 64] (rotated)
  *   k_nope, v  from mla_decompress_kv with the same max_len and inputs
+ *              (the attention reads whole pages of K and V; the zero-filled
+ *              page tails keep garbage out of P . V)
  *   out bf16 [B, s_q, H, 128], lse fp32 [B, s_q, H] (natural log of the
  *   sum of exp(scaled score)); a query with no visible key gets out = 0 and
  *   lse = -inf. Queries see at most min(L_b, max_len) keys.

@@ -7,6 +7,9 @@
 // (V feeds the attention's P.V product, which runs in fp16 for three more
 // significant bits at the same matrix-core rate).
 //
+// Rows t < L_b are written and rows L_b .. the end of that page are
+// zero-filled, so the attention stage can read K and V in whole pages.
+//
 // Workgroup = (head h, sequence b, 256-token tile): the 256 x 256 output tile
 // D^T[n, t] with n = the 128 K rows then the 128 V rows of head h. The
 // latent columns are streamed through LDS in chunks of 64 (double-buffered:
@@ -125,26 +128,48 @@ __global__ __launch_bounds__(256) void decompress_kv_kernel(const char* __restri
     __syncthreads();
   }
 
-  // ---- epilogue: lane owns token 128tb + 32ti + lo and output rows
-  // 32mi + 8q + 4g + 0..3 (4 consecutive d): one 8-byte store each
+  // ---- epilogue: the tile goes through LDS so that global writes cover
+  // whole 256-byte rows (a (b, h, tile) block of K, and of V, is one
+  // contiguous 64 KiB range). Lane owns token 128tb + 32ti + lo and output
+  // rows 32mi + 8q + 4g + 0..3; LDS row = 128 values, 16-byte chunk c of
+  // token row r stored at chunk c ^ (r & 15).
+  {
+    char* region = lds + nb * (kDecTok * 256);
 #pragma unroll
-  for (int ti = 0; ti < 4; ++ti) {
-    const int t = t0 + 128 * tb + 32 * ti + lo;
-    if (t >= L) continue;
-    const int64_t row = (((int64_t)b * kH + h) * max_len + t) * kDhc;
+    for (int ti = 0; ti < 4; ++ti) {
+      const int r = 128 * tb + 32 * ti + lo;
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+      for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4 a = {acc[mi][ti][4 * q], acc[mi][ti][4 * q + 1], acc[mi][ti][4 * q + 2], acc[mi][ti][4 * q + 3]};
-        const int d = 32 * mi + 8 * q + 4 * g;
-        if (nb == 0) {
-          *reinterpret_cast<bf16x4*>(k_out + row + d) = bf16x4{(__bf16)a[0], (__bf16)a[1], (__bf16)a[2], (__bf16)a[3]};
-        } else {
-          *reinterpret_cast<f16x4*>(v_out + row + d) =
-              f16x4{(_Float16)a[0], (_Float16)a[1], (_Float16)a[2], (_Float16)a[3]};
+        for (int q = 0; q < 4; ++q) {
+          const f32x16& a = acc[mi][ti];
+          const int d = 32 * mi + 8 * q + 4 * g;
+          char* dst = region + r * 256 + (((d >> 3) ^ (r & 15)) << 4) + (d & 4) * 2;
+          if (nb == 0)
+            *reinterpret_cast<bf16x4*>(dst) = bf16x4{(__bf16)a[4 * q], (__bf16)a[4 * q + 1], (__bf16)a[4 * q + 2],
+                                                     (__bf16)a[4 * q + 3]};
+          else
+            *reinterpret_cast<f16x4*>(dst) = f16x4{(_Float16)a[4 * q], (_Float16)a[4 * q + 1],
+                                                   (_Float16)a[4 * q + 2], (_Float16)a[4 * q + 3]};
         }
-      }
+    }
+  }
+  __syncthreads();
+  // rows t < L are written, rows L .. (end of L's page) are zero-filled (the
+  // attention stage reads whole pages of K and V), later rows are not touched
+  const int L_pad = (L + kPage - 1) / kPage * kPage;
+  char* kdst = reinterpret_cast<char*>(k_out + (((int64_t)b * kH + h) * max_len + t0) * kDhc);
+  char* vdst = reinterpret_cast<char*>(v_out + (((int64_t)b * kH + h) * max_len + t0) * kDhc);
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int q = 256 * k + tid, r = q >> 4, c = q & 15;
+    const int t = t0 + r;
+    if (t >= L_pad) continue;
+    const int src = r * 256 + ((c ^ (r & 15)) << 4);
+    const bool live = t < L;
+    *reinterpret_cast<f32x4*>(kdst + r * 256 + c * 16) = live ? *reinterpret_cast<const f32x4*>(lds + src) : f32x4{};
+    *reinterpret_cast<f32x4*>(vdst + r * 256 + c * 16) =
+        live ? *reinterpret_cast<const f32x4*>(lds + kDecTok * 256 + src) : f32x4{};
   }
 }
 

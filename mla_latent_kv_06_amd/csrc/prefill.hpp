@@ -12,7 +12,7 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 constexpr int kPrefillAbsorptionThreshold = 256;  // chunks up to this many new tokens stay absorbed
 
 // K [B, 128, max_len, 128] bf16 and V (same shape) fp16: rows t < L_b of
-// each (b, h); others untouched.
+// each (b, h), zeros up to the end of L_b's page; later rows untouched.
 hipError_t launch_decompress_kv(const char* kv, int64_t num_pages, const int32_t* block_table, int max_pages,
                                 const int32_t* seqlens, int B, int max_len, const __bf16* w_uk, const __bf16* w_uv,
                                 __bf16* k_out, _Float16* v_out, hipStream_t stream);

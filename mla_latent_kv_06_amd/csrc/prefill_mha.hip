@@ -7,14 +7,18 @@
 // heads, read from the paged cache) and 128-dim values.
 //
 // Workgroup = (sequence b, head h, block of 128 queries), 4 waves of 32
-// queries. The keys stream in tiles of 64 (one page) through two LDS stages
-// (the next tile's global loads are in flight during this tile's MFMAs):
+// queries. The keys stream in tiles of 64 (one page) through a ring of three
+// LDS stages filled with 16-byte direct-to-LDS loads, two tiles ahead of the
+// one being computed (the per-tile compute is shorter than a memory round
+// trip, so one tile of lookahead would leave each tile waiting on memory):
 //   * QK: S^T[32 tokens, 32 queries] per token half on v_mfma_f32_32x32x16_bf16,
 //     A = key rows from LDS, B = the wave's queries held in 48 VGPRs; a lane
 //     owns one query and 16 of each 32 tokens;
-//   * softmax in the exp2 domain with a per-query reference max that is only
-//     raised (rescaling the accumulator) when a tile's max exceeds it by more
-//     than 8, so P <= 2^8;
+//   * softmax in the exp2 domain against a per-query reference max taken from
+//     the query's first tile; P = 2^(x - ref) may grow to 2^14 above it, which
+//     fp16 P and the fp32 sums hold, so the accumulator is never rescaled (and
+//     never touched by VALU). If a score exceeds its reference by more than
+//     that, the workgroup rescans the block once with the exact maximum;
 //   * PV: O^T[128 dims, 32 queries] += V^T . P^T on v_mfma_f32_32x32x16_f16
 //     (fp16 V from stage 1 and fp16 P <= 2^8: three more significant bits
 //     than bf16 at the same rate), P^T taken straight from the lane's own
@@ -32,13 +36,44 @@ constexpr int kMhaTok = 64;      // keys per tile (one page)
 constexpr int kKRow = 256;       // bytes of a content-key or value row
 constexpr int kRRow = 128;       // bytes of a RoPE-key row
 constexpr int kMhaStage = kMhaTok * (2 * kKRow + kRRow);  // 40 KiB: K, V, k_R
-constexpr float kRescaleSlack = 8.f;                      // log2 units
+constexpr int kMhaStages = 3;
+constexpr int kMhaDmaPerWave = 10;                        // 1 KiB loads per wave per tile: 4 K, 4 V, 2 k_R
+constexpr float kRefSlack = 14.f;                         // log2 units: P <= 2^14 < 65504 (fp16)
 
 // 16-byte chunk positions: key rows (QK reads 16 consecutive rows at one
 // chunk), value rows (transposed reads of 4 rows x 4 chunks), RoPE rows
 __device__ __forceinline__ int swz_k(int row, int chunk) { return (chunk ^ (row & 15)) << 4; }
 __device__ __forceinline__ int swz_v(int row, int chunk) { return (chunk ^ ((row & 3) << 2)) << 4; }
 __device__ __forceinline__ int swz_r(int row, int chunk) { return (chunk ^ ((row >> 1) & 7)) << 4; }
+
+// One 16-byte-per-lane direct-to-LDS load: lane l's 16 bytes from
+// sbase + voff land at LDS byte address lds_addr + 16 l (lds_addr and sbase
+// uniform). Written as asm so that later LDS reads are not treated as
+// overlapping it; completion is tracked with explicit vmcnt waits. An SALU
+// write of M0 needs one wait state before the LDS-DMA instruction reads it.
+__device__ __forceinline__ void dma16(const char* sbase, unsigned voff, unsigned lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_addr)
+               : "memory", "m0");
+}
+
+// Workgroup barrier after this wave's own loads of the tile have been waited
+// for with vmcnt; unlike __syncthreads() it does not drain the loads of the
+// tiles still in flight.
+__device__ __forceinline__ void tile_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Score accumulation kept in VGPRs (the softmax reads it with VALU) while
+// the accumulator registers hold O^T. Written as asm: the first MFMA of a
+// chain takes the literal 0 as its accumulator input (no zeroing moves), and
+// a chain whose srcC is exactly the previous destination needs no wait
+// states. VALU may read an asm MFMA's result only after it has drained (at
+// most 16 passes + 2; 24 wait states here), hence the fence tied to the value.
+__device__ __forceinline__ void mfma_s_first(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_s(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_result_fence(f32x16& d) { asm("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(d)); }
 
 __device__ __forceinline__ f16x8 cat8(i16x4 a, i16x4 b) {
   const f16x4 x = __builtin_bit_cast(f16x4, a), y = __builtin_bit_cast(f16x4, b);
@@ -55,7 +90,7 @@ __global__ __launch_bounds__(256) void prefill_mha_kernel(const __bf16* __restri
                                                           const int32_t* __restrict__ seqlens, int s_q, float scale_log2,
                                                           __bf16* __restrict__ out, float* __restrict__ lse,
                                                           int n_qb, int B, int total, int per_xcd) {
-  __shared__ __attribute__((aligned(16))) char lds[2 * kMhaStage];
+  __shared__ __attribute__((aligned(1024))) char lds[kMhaStages * kMhaStage];
   const int x = blockIdx.x;
   const int id = (x & 7) * per_xcd + (x >> 3);
   if (id >= total) return;
@@ -94,146 +129,176 @@ __global__ __launch_bounds__(256) void prefill_mha_kernel(const __bf16* __restri
     for (int ks = 0; ks < 4; ++ks) qf[8 + ks] = q_live ? qr[2 * ks + g] : bf16x8{};
   }
 
-  // ---- loader: per tile 64 rows of K and V (1024 pieces each, 4 per thread)
-  // and of k_R (512 pieces, 2 per thread)
+  // ---- loader: wave w fills 1 KiB blocks 4w..4w+3 of the K and V regions
+  // (rows 16w..16w+15) and blocks 2w, 2w+1 of the k_R region (rows
+  // 16w..16w+15); lane l's slot in a block holds the logical chunk that the
+  // swizzle puts there. Rows past L_b come from the zero-filled tail of the
+  // last page of K and V (stage 1 writes it) and from the cache for k_R
+  // (masked out of the scores).
   const char* kbase = reinterpret_cast<const char*>(k_nope + ((int64_t)b * kH + h) * max_len * kDhc);
   const char* vbase = reinterpret_cast<const char*>(v_in + ((int64_t)b * kH + h) * max_len * kDhc);
-  f32x4 kvv[4], vvv[4], rvv[2];
-  auto load = [&](int it) {
-    const int t0 = it * kMhaTok;
+  unsigned koff[4], voff[4], roff[2];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int q = 256 * k + tid, row = q >> 4, ch = q & 15;
-      kvv[k] = *reinterpret_cast<const f32x4*>(kbase + (int64_t)(t0 + row) * kKRow + ch * 16);
-      vvv[k] = *reinterpret_cast<const f32x4*>(vbase + (int64_t)(t0 + row) * kKRow + ch * 16);
-    }
-    const int64_t page = physical_page(block_table, max_pages, b, it, num_pages);
+  for (int j = 0; j < 4; ++j) {
+    const int row = 16 * wave + 4 * j + (lane >> 4), ph = lane & 15;
+    koff[j] = row * kKRow + ((ph ^ (row & 15)) << 4);
+    voff[j] = row * kKRow + ((ph ^ ((row & 3) << 2)) << 4);
+  }
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int q = 256 * k + tid, row = q >> 3, ch = q & 7;
-      rvv[k] = *reinterpret_cast<const f32x4*>(kv + page * kPageBytes + (int64_t)row * kRowBytes + kDc * 2 + ch * 16);
-    }
-  };
-  auto store = [&](int it) {
-    char* st = lds + (it & 1) * kMhaStage;
-    const int valid = L - it * kMhaTok;  // value rows past the sequence become zeros
+  for (int j = 0; j < 2; ++j) {
+    const int row = 16 * wave + 8 * j + (lane >> 3), ph = lane & 7;
+    roff[j] = row * kRowBytes + kDc * 2 + ((ph ^ ((row >> 1) & 7)) << 4);
+  }
+  const unsigned lds0 = (unsigned)(uintptr_t)(lds_void_t*)lds;
+  auto issue = [&](int it) {
+    const unsigned st = lds0 + ((unsigned)it % (unsigned)kMhaStages) * kMhaStage;
+    const char* ks = kbase + (int64_t)it * kMhaTok * kKRow;
+    const char* vs = vbase + (int64_t)it * kMhaTok * kKRow;
+    const char* rs = kv + physical_page(block_table, max_pages, b, it, num_pages) * kPageBytes;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int q = 256 * k + tid, row = q >> 4, ch = q & 15;
-      *reinterpret_cast<f32x4*>(st + row * kKRow + swz_k(row, ch)) = kvv[k];
-      *reinterpret_cast<f32x4*>(st + kMhaTok * kKRow + row * kKRow + swz_v(row, ch)) =
-          row < valid ? vvv[k] : f32x4{};
+    for (int j = 0; j < 4; ++j) {
+      dma16(ks, koff[j], st + (4 * wave + j) * 1024);
+      dma16(vs, voff[j], st + kMhaTok * kKRow + (4 * wave + j) * 1024);
     }
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int q = 256 * k + tid, row = q >> 3, ch = q & 7;
-      *reinterpret_cast<f32x4*>(st + 2 * kMhaTok * kKRow + row * kRRow + swz_r(row, ch)) = rvv[k];
-    }
+    for (int j = 0; j < 2; ++j) dma16(rs, roff[j], st + 2 * kMhaTok * kKRow + (2 * wave + j) * 1024);
   };
 
-  // ---- V^T operand offsets: group G = lane >> 4, ii = lane & 15 reads token
-  // row 4(G >> 1) + (ii >> 2) (+8 for the second half, +16 per k-step, +32 per
-  // token half) and 4 columns 16(G & 1) + 4(ii & 3) of a 32-column tile
+  // ---- LDS read offsets, all lane constants plus compile-time immediates:
+  // QK A operand: key row 32sh + lo, chunk 2ks + g (K: 8 k-steps, k_R: 4);
+  // the row's swizzle depends only on lo. V^T operand: group G = lane >> 4,
+  // ii = lane & 15 reads token row 4(G >> 1) + (ii >> 2) (+8 for the second
+  // half, +16 per k-step, +32 per token half) and 4 columns 16(G & 1) +
+  // 4(ii & 3) of a 32-column tile cp.
+  int qk_k[8], qk_r[4], pv_v[4];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) qk_k[ks] = lo * kKRow + swz_k(lo, 2 * ks + g);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) qk_r[ks] = 2 * kMhaTok * kKRow + lo * kRRow + swz_r(lo, 2 * ks + g);
   const int Gq = lane >> 4, ii = lane & 15;
   const int t_lane = 4 * (Gq >> 1) + (ii >> 2);
   const int jl = 2 * (Gq & 1) + ((ii & 3) >> 1);
-  auto vfrag = [&](const char* vt, int kk, int cp) -> f16x8 {
-    const int t = 16 * kk + t_lane;  // kk = 2 * token half + k-step
-    const int j = 4 * cp + jl;
-    const char* a0 = vt + t * kKRow + swz_v(t, j) + (ii & 1) * 8;
-    const char* a1 = vt + (t + 8) * kKRow + swz_v(t + 8, j) + (ii & 1) * 8;
-    return cat8(__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)a0),
-                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)a1));
-  };
+#pragma unroll
+  for (int cp = 0; cp < 4; ++cp)
+    pv_v[cp] = kMhaTok * kKRow + t_lane * kKRow + swz_v(t_lane, 4 * cp + jl) + (ii & 1) * 8;
 
   f32x16 O[4];
-#pragma unroll
-  for (int cp = 0; cp < 4; ++cp) O[cp] = f32x16{};
-  float m_ref = -INFINITY;  // reference max of this lane's query (log2 units)
-  float l_run = 0.f;        // this lane's share of sum 2^(x - m_ref)
+  float m_ref = -INFINITY;   // reference max of this lane's query (log2 units)
+  float m_seen = -INFINITY;  // true running max of this lane's query
+  float l_run = 0.f;         // this lane's share of sum 2^(x - m_ref)
 
-  if (n_tiles > 0) {
-    load(0);
-    store(0);
-  }
-  __syncthreads();
-  for (int it = 0; it < n_tiles; ++it) {
-    if (it + 1 < n_tiles) load(it + 1);
-    const char* st = lds + (it & 1) * kMhaStage;
-    const char* kt = st;
-    const char* vt = st + kMhaTok * kKRow;
-    const char* rt = st + 2 * kMhaTok * kKRow;
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int cp = 0; cp < 4; ++cp) O[cp] = f32x16{};
+    l_run = 0.f;
+    bool over = false;
+    if (n_tiles > 0) issue(0);
+    if (n_tiles > 1) issue(1);
+    for (int it = 0; it < n_tiles; ++it) {
+      // tile it has landed (only tile it+1's loads may still be in flight);
+      // after the barrier every wave is done with tile it-1, whose stage
+      // (it+2) % 3 is refilled now
+      if (it + 1 < n_tiles) wait_vmcnt<kMhaDmaPerWave>(); else wait_vmcnt<0>();
+      tile_barrier();
+      if (it + 2 < n_tiles) issue(it + 2);
+      const char* st = lds + ((unsigned)it % (unsigned)kMhaStages) * kMhaStage;  // unsigned: lets the reads fold immediates
 
-    // QK for both token halves
-    f32x16 S[2];
+      // QK for both token halves (raw scores; the scale is applied in the exp),
+      // in program order: the key fragment of MFMA k+3 is read right after
+      // MFMA k, so three LDS reads are in flight and no more registers are held
+      f32x16 S[2];
+      {
+        auto kfrag = [&](int k) -> bf16x8 {  // k = 12 sh + ks
+          const int sh = k / 12, ks = k % 12;
+          const int off = ks < 8 ? qk_k[ks] + sh * 32 * kKRow : qk_r[ks - 8] + sh * 32 * kRRow;
+          return *reinterpret_cast<const bf16x8*>(st + off);
+        };
+        bf16x8 kf[4];
 #pragma unroll
-    for (int sh = 0; sh < 2; ++sh) {
-      const int row = 32 * sh + lo;
-      S[sh] = f32x16{};
+        for (int k = 0; k < 3; ++k) kf[k] = kfrag(k);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + row * kKRow + swz_k(row, 2 * ks + g));
-        S[sh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], S[sh], 0, 0, 0);
+        for (int k = 0; k < 24; ++k) {
+          const int sh = k / 12, ks = k % 12;
+          if (ks == 0)
+            mfma_s_first(S[sh], kf[k & 3], qf[ks]);
+          else
+            mfma_s(S[sh], kf[k & 3], qf[ks]);
+          if (k + 3 < 24) kf[(k + 3) & 3] = kfrag(k + 3);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        mfma_result_fence(S[0]);
+        mfma_result_fence(S[1]);
+        __builtin_amdgcn_sched_barrier(0);
       }
+
+      // the causal limit (and the sequence end) only cut tiles past the
+      // block's first query's limit: one uniform branch, taken rarely
+      const int t0 = it * kMhaTok;
+      if (t0 + kMhaTok > n_first) {
+        const int lim = n_vis - t0 - 4 * g;  // token t0 + 32sh + 8(r>>2) + 4g + (r&3) is visible iff below n_vis
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(rt + row * kRRow + swz_r(row, 2 * ks + g));
-        S[sh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[8 + ks], S[sh], 0, 0, 0);
+        for (int sh = 0; sh < 2; ++sh)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            S[sh][r] = (32 * sh + 8 * (r >> 2) + (r & 3)) < lim ? S[sh][r] : -INFINITY;
+      }
+      // softmax_scale > 0, so the max of the raw scores gives the max of the
+      // scaled ones
+      float mt = fmaxf(S[0][0], S[0][1]);
+#pragma unroll
+      for (int r = 2; r < 16; ++r) mt = fmaxf(mt, S[0][r]);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, S[1][r]);
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * scale_log2;
+      // the first tile with a visible key sets the reference (nothing has been
+      // accumulated yet); later tiles only record whether they outgrew it
+      m_seen = fmaxf(m_seen, mt);
+      if (m_ref == -INFINITY) m_ref = mt;
+      over |= mt > m_ref + kRefSlack;
+      // P = 2^(s * scale_log2 - m_ref) in one fma; masked scores give 0, and
+      // while this lane's query has seen no key all its scores are masked (an
+      // offset of 0 keeps -inf - (-inf) out)
+      const float off = m_ref == -INFINITY ? 0.f : -m_ref;
+      f16x8 pb[4];
+#pragma unroll
+      for (int sh = 0; sh < 2; ++sh)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[sh][r], scale_log2, off));
+          l_run += p;
+          pb[2 * sh + (r >> 3)][r & 7] = (_Float16)p;
+        }
+
+      // PV over the tile's 4 k-steps of 16 tokens (P^T from this lane's
+      // scores); V^T fragments through four per-tile bases plus immediates,
+      // read two MFMAs ahead
+      {
+        const char* vb[4];
+#pragma unroll
+        for (int cp = 0; cp < 4; ++cp) vb[cp] = st + pv_v[cp];
+        auto vfrag = [&](int k) -> f16x8 {  // k = 4 kk + cp
+          const char* a = vb[k & 3] + (k >> 2) * 16 * kKRow;
+          return cat8(__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)a),
+                      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(a + 8 * kKRow)));
+        };
+        f16x8 vf[3];
+        vf[0] = vfrag(0);
+        vf[1] = vfrag(1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          O[k & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[k % 3], pb[k >> 2], O[k & 3], 0, 0, 0);
+          if (k + 2 < 16) vf[(k + 2) % 3] = vfrag(k + 2);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
 
-    // scores in log2 units; the causal limit (and the sequence end) only
-    // cut tiles past the block's first query's limit
-    const int t0 = it * kMhaTok;
-    float xs[2][16];
-    const bool cut = t0 + kMhaTok > n_first;
-#pragma unroll
-    for (int sh = 0; sh < 2; ++sh)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float v = S[sh][r] * scale_log2;
-        const int t = t0 + 32 * sh + 8 * (r >> 2) + 4 * g + (r & 3);
-        xs[sh][r] = (!cut || t < n_vis) ? v : -INFINITY;
-      }
-    float mt = -INFINITY;
-#pragma unroll
-    for (int sh = 0; sh < 2; ++sh)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, xs[sh][r]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    // raise the reference (and rescale what has been accumulated) only when
-    // this tile's max exceeds it by more than the slack
-    const bool raise = mt > m_ref + kRescaleSlack;
-    if (__any(raise)) {
-      const float nr = raise ? mt : m_ref;
-      const float alpha = (raise && m_ref != -INFINITY) ? __builtin_amdgcn_exp2f(m_ref - nr) : (raise ? 0.f : 1.f);
-#pragma unroll
-      for (int cp = 0; cp < 4; ++cp)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) O[cp][r] *= alpha;
-      l_run *= alpha;
-      m_ref = nr;
-    }
-    f16x8 pb[4];
-    const bool any_key = m_ref != -INFINITY;
-#pragma unroll
-    for (int sh = 0; sh < 2; ++sh)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = any_key ? __builtin_amdgcn_exp2f(xs[sh][r] - m_ref) : 0.f;
-        l_run += p;
-        pb[2 * sh + (r >> 3)][r & 7] = (_Float16)p;
-      }
-
-    // PV over the tile's 4 k-steps of 16 tokens (P^T from this lane's scores)
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-      for (int cp = 0; cp < 4; ++cp)
-        O[cp] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vfrag(vt, kk, cp), pb[kk], O[cp], 0, 0, 0);
-
-    if (it + 1 < n_tiles) store(it + 1);
-    __syncthreads();
+    // every score within the slack of its reference: done; otherwise rescan
+    // the block once with the exact maxima (which cannot be exceeded)
+    if (!__syncthreads_or(over) || pass == 1) break;
+    m_ref = m_seen;
   }
 
   // ---- epilogue: lane owns query iq, dims 32cp + 8q + 4g + 0..3

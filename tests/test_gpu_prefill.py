@@ -74,7 +74,9 @@ def test_decompress_kv_parity(M, lens):
     for b, L in enumerate(lens):
         assert_bar(gk[b, :, :L], refK[b, :, :L], f"K b={b}")
         assert_bar(gv[b, :, :L], refV[b, :, :L], f"V b={b}")
-        assert np.isnan(gk[b, :, L:]).all() and np.isnan(gv[b, :, L:]).all(), "rows past L_b were written"
+        pad = -(-L // 64) * 64
+        assert (gk[b, :, L:pad] == 0).all() and (gv[b, :, L:pad] == 0).all(), "the rest of L_b's page is not zero"
+        assert np.isnan(gk[b, :, pad:]).all() and np.isnan(gv[b, :, pad:]).all(), "rows past L_b's page were written"
 
 
 @pytest.mark.parametrize("lens,s_q", [([300, 77], 3), ([1000], 300), ([5, 130], 9)])
@@ -134,3 +136,28 @@ def test_decompressed_branch_prefill_config_sampled(M):
     got_l = np.array([float(r["lse"][b, i, h]) for b, i, h in picks])
     assert_bar(got_o, ref_o, "decompressed prefill sampled", l1_rel=5e-3)
     assert_lse(got_l, ref_l, "decompressed prefill sampled lse")
+
+
+def test_prefill_mha_score_jump_triggers_exact_rescan(M):
+    """A key far above every score of a query's first tile (more than 2^14 in
+    weight) makes the workgroup rescan with the exact maxima; the result must
+    still match the oracle."""
+    lens, s_q = [700], 5
+    c = _case(lens, s_q, seed=99)
+    max_len = 704
+    g = torch.Generator().manual_seed(100)
+    k = (torch.randn((1, 128, max_len, 128), generator=g) * 0.1).to(torch.bfloat16)
+    v = torch.randn((1, 128, max_len, 128), generator=g).to(torch.float16)
+    k[:, :, 700:] = 0
+    v[:, :, 700:] = 0
+    k[0, :, 650, 0] = 400.0                          # score 400 * q_c[..., 0] / sqrt(192)
+    q_c = c["q_c"].clone()
+    q_c[..., 0] = 1.0
+    _say("prefill_mha rescan")
+    kvd, btd, sld = c["kv"].to(DEV), c["bt"].to(DEV), c["sl"].to(DEV)
+    out, lse = M.mla_prefill_mha(q_c.to(DEV), c["q_r"].to(DEV), k.to(DEV), v.to(DEV), kvd, btd, sld, SCALE)
+    torch.cuda.synchronize()
+    R = O.rope_keys(O.bf16_bits(c["kv"]), c["bt"].numpy(), c["sl"].numpy(), max_len)
+    ref_o, ref_l = O.attend_mha(O.as_f64(q_c), O.as_f64(c["q_r"]), O.as_f64(k), O.as_f64(v), R, c["sl"].numpy(), SCALE)
+    assert_bar(O.as_f64(out.cpu()), ref_o, "prefill_mha rescan out")
+    assert_lse(lse.cpu().numpy(), ref_l, "prefill_mha rescan lse")
