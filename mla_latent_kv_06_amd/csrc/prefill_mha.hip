@@ -36,7 +36,7 @@ constexpr int kMhaTok = 64;      // keys per tile (one page)
 constexpr int kKRow = 256;       // bytes of a content-key or value row
 constexpr int kRRow = 128;       // bytes of a RoPE-key row
 constexpr int kMhaStage = kMhaTok * (2 * kKRow + kRRow);  // 40 KiB: K, V, k_R
-constexpr int kMhaStages = 3;
+constexpr int kMhaStages = 2;
 constexpr int kMhaDmaPerWave = 10;                        // 1 KiB loads per wave per tile: 4 K, 4 V, 2 k_R
 constexpr float kRefSlack = 14.f;                         // log2 units: P <= 2^14 < 65504 (fp16)
 
@@ -82,7 +82,7 @@ __device__ __forceinline__ f16x8 cat8(i16x4 a, i16x4 b) {
 
 }  // namespace
 
-__global__ __launch_bounds__(256) void prefill_mha_kernel(const __bf16* __restrict__ q_c, const __bf16* __restrict__ q_r,
+__global__ __launch_bounds__(256, 2) void prefill_mha_kernel(const __bf16* __restrict__ q_c, const __bf16* __restrict__ q_r,
                                                           const __bf16* __restrict__ k_nope,
                                                           const _Float16* __restrict__ v_in, int max_len,
                                                           const char* __restrict__ kv, int64_t num_pages,
@@ -193,14 +193,12 @@ __global__ __launch_bounds__(256) void prefill_mha_kernel(const __bf16* __restri
     l_run = 0.f;
     bool over = false;
     if (n_tiles > 0) issue(0);
-    if (n_tiles > 1) issue(1);
     for (int it = 0; it < n_tiles; ++it) {
-      // tile it has landed (only tile it+1's loads may still be in flight);
-      // after the barrier every wave is done with tile it-1, whose stage
-      // (it+2) % 3 is refilled now
-      if (it + 1 < n_tiles) wait_vmcnt<kMhaDmaPerWave>(); else wait_vmcnt<0>();
+      // tile it has landed; after the barrier every wave is done with tile
+      // it-1, whose stage is refilled with tile it+1 now
+      wait_vmcnt<0>();
       tile_barrier();
-      if (it + 2 < n_tiles) issue(it + 2);
+      if (it + 1 < n_tiles) issue(it + 1);
       const char* st = lds + ((unsigned)it % (unsigned)kMhaStages) * kMhaStage;  // unsigned: lets the reads fold immediates
 
       // QK for both token halves (raw scores; the scale is applied in the exp),
@@ -296,8 +294,16 @@ __global__ __launch_bounds__(256) void prefill_mha_kernel(const __bf16* __restri
     }
 
     // every score within the slack of its reference: done; otherwise rescan
-    // the block once with the exact maxima (which cannot be exceeded)
-    if (!__syncthreads_or(over) || pass == 1) break;
+    // the block once with the exact maxima (which cannot be exceeded). The
+    // per-wave flags go through the (now idle) start of the LDS ring.
+    __syncthreads();
+    int* flags = reinterpret_cast<int*>(lds);
+    const bool wave_over = __any(over);
+    if (lane == 0) flags[wave] = wave_over ? 1 : 0;
+    __syncthreads();
+    const bool again = (flags[0] | flags[1] | flags[2] | flags[3]) != 0;
+    if (!again || pass == 1) break;
+    __syncthreads();  // every wave has read the flags before the rescan's loads land
     m_ref = m_seen;
   }
 
