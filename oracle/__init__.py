@@ -17,7 +17,10 @@ Everything is float64 numpy, written from the definitions on the pages:
     page, sections 3 and 4), with the frequency and pair layout readings
     stated beside the code;
   * the decompressed branch for chunks above the absorption threshold
-    (teardown page, section 3 threshold, section 4 path A in two stages).
+    (teardown page, section 3 threshold, section 4 path A in two stages);
+  * an 8-bit latent cache (FP8 E4M3 codes with one power-of-two scale per
+    token, k_R kept in bf16), the analog of the teardown page's quantized
+    latent gather (section 5), with the format readings stated beside it.
 
 Each function is pinned by tests under ``tests/test_oracle*.py`` against
 closed forms, brute-force loops, the pages' storage arithmetic and the
@@ -31,4 +34,6 @@ from .mla_oracle import (  # noqa: F401
     latent_row_elems, latent_row_bytes, mha_kv_bytes_per_token_layer,
     ROPE_BASE, rope_angles, rope_rotate, chunk_positions, append_latent,
     PREFILL_ABSORPTION_THRESHOLD, uses_absorption, decompress_kv, rope_keys, attend_mha,
+    FP8_MAX, e4m3_value, e4m3_encode, fp8_scale_exponent, quantize_latent_fp8, dequantize_latent_fp8,
+    fp8_page_bytes, pack_fp8_cache, unpack_fp8_pages, dequantize_fp8_pages, PagedFp8Cache,
 )

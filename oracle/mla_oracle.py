@@ -35,6 +35,8 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
 
 def bf16_bits(x) -> np.ndarray:
     """Zero-copy uint16 view of a CPU torch bf16 tensor (its bit patterns)."""
+    if str(getattr(x, "dtype", "")) != "torch.bfloat16":
+        raise TypeError(f"bf16_bits takes a bfloat16 tensor, got {getattr(x, 'dtype', type(x))}")
     return x.detach().cpu().contiguous().view(__import__("torch").int16).numpy().view(np.uint16)
 
 
@@ -82,14 +84,18 @@ def gather_rows(kv_cache: np.ndarray, block_table_row: np.ndarray, n_tokens: int
     Token t lives in physical page block_table_row[t // page] at row t % page.
     Only the entries the sequence needs are read; they must be valid page ids.
     A uint16 cache is taken as bf16 bit patterns and decoded exactly after the
-    gather (so a large cache never has to exist in float64).
+    gather (so a large cache never has to exist in float64); a PagedFp8Cache
+    is dequantized after the gather in the same way.
     """
-    kv = np.asarray(kv_cache)
+    fp8 = isinstance(kv_cache, PagedFp8Cache)
+    kv = kv_cache if fp8 else np.asarray(kv_cache)
     page = kv.shape[1]
     n_pages = -(-int(n_tokens) // page)
     ids = np.asarray(block_table_row[:n_pages], dtype=np.int64)
     if n_pages and (ids.min() < 0 or ids.max() >= kv.shape[0]):
         raise ValueError("block table entry out of range")
+    if fp8:   # an 8-bit cache is dequantized after the gather
+        return kv.rows_of_pages(ids).reshape(n_pages * page, kv.shape[2])[:n_tokens]
     rows = kv[ids].reshape(n_pages * page, kv.shape[2])[:n_tokens]
     if rows.dtype == np.uint16:
         return bf16_bits_to_f64(rows)
@@ -264,7 +270,7 @@ def decode_split(q_abs, q_r, kv_cache, block_table, seqlens, scale: float, num_s
     q_abs = np.asarray(q_abs, np.float64)
     q_r = np.asarray(q_r, np.float64)
     B, s_q, Hn, d_c = q_abs.shape
-    page = np.asarray(kv_cache).shape[1]
+    page = (kv_cache.shape if isinstance(kv_cache, PagedFp8Cache) else np.asarray(kv_cache).shape)[1]
     o = np.zeros((B, s_q, Hn, num_splits, d_c))
     lse = np.full((B, s_q, Hn, num_splits), -np.inf)
     vis = [[max(visible_len(int(seqlens[b]), s_q, i), 0) for i in range(s_q)] for b in range(B)]
@@ -451,8 +457,7 @@ def decompress_kv(kv_cache, block_table, seqlens, w_uk, w_uv, max_len: int):
 
 def rope_keys(kv_cache, block_table, seqlens, max_len: int, d_c: int = 512):
     """k_R of every cached token, [B, max_len, d_R] (zero past L_b)."""
-    kv = np.asarray(kv_cache)
-    d_r = kv.shape[2] - d_c
+    d_r = (kv_cache.shape if isinstance(kv_cache, PagedFp8Cache) else np.asarray(kv_cache).shape)[2] - d_c
     B = len(seqlens)
     R = np.zeros((B, max_len, d_r))
     for b in range(B):
@@ -487,3 +492,144 @@ def attend_mha(q_c, q_r, K, V, R, seqlens, scale: float):
                 out[b, i, h] = p[0] @ V[b, h, :n]
                 lse[b, i, h] = m[0] + np.log(l[0])
     return out, lse
+
+
+# --------------------------------------------------------------------------
+# 8-bit latent cache: c_KV in FP8 E4M3 with one power-of-two scale per token
+# --------------------------------------------------------------------------
+# The teardown page reads a 4-bit (NVFP4) latent cache with 16-byte vector
+# loads whose page base and dimension offset must be 16-byte aligned
+# (section 5, the misaligned-address failure), and gives neither the element
+# format nor the scaling. Readings taken here, for an 8-bit cache:
+#   * c_KV is stored in OCP FP8 E4M3: sign, 4 exponent bits with bias 7 and
+#     3 mantissa bits; exponent 0 holds the subnormals m/8 * 2^-6; there are
+#     no infinities, S.1111.111 is NaN and the largest finite value is 448;
+#   * k_R keeps its bf16 bits (the rotated key is stored exactly);
+#   * each token's c_KV shares one scale 2^k: the smallest power of two with
+#     max|c_KV| <= 448 * 2^k, k clamped to [-126, 127] (-126 for a zero row),
+#     so no element ever saturates;
+#   * an element's code is c / 2^k rounded to the nearest E4M3 value, ties to
+#     the even mantissa, with the sign bit of c (a negative value that rounds
+#     to zero is stored as -0);
+#   * the stored value of a code is its E4M3 value times 2^k;
+#   * a page of 64 tokens is three arrays, each starting on a 16-byte
+#     boundary: 64 x 512 codes, then 64 x 64 bf16 k_R, then 64 float32
+#     scales (41216 bytes).
+
+FP8_MAX = 448.0
+FP8_SCALE_EXP_MIN = -126
+FP8_SCALE_EXP_MAX = 127
+
+
+def e4m3_value(codes) -> np.ndarray:
+    """Exact float64 value of E4M3 codes (NaN for S.1111.111)."""
+    c = np.asarray(codes).astype(np.int64)
+    e = (c >> 3) & 15
+    m = c & 7
+    mag = np.where(e == 0, m * 2.0 ** -9, (8 + m) * np.ldexp(1.0, e - 10))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return np.where(c & 0x80, -mag, mag)
+
+
+def e4m3_encode(v) -> np.ndarray:
+    """Nearest E4M3 code of exact values with |v| <= 448, ties to even, sign kept."""
+    v = np.asarray(v, np.float64)
+    a = np.abs(v)
+    if not np.all(a <= FP8_MAX):
+        raise ValueError("E4M3 encode: value outside [-448, 448] or NaN")
+    _, x = np.frexp(a)                      # a = f * 2^x, f in [0.5, 1); x = 0 for a = 0
+    E = np.maximum(x - 1, -6)               # binade of a; below 2^-6 the subnormal spacing
+    q = np.round(np.ldexp(a, 3 - E))        # a in units of the binade's spacing 2^(E-3); ties to even
+    up = q >= 16                            # rounded up into the next binade
+    E = np.where(up, E + 1, E)
+    q = np.where(up, 8, q).astype(np.int64)
+    normal = q >= 8
+    e_field = np.where(normal, E + 7, 0)
+    m_field = np.where(normal, q - 8, q)
+    return ((np.signbit(v).astype(np.int64) << 7) | (e_field << 3) | m_field).astype(np.uint8)
+
+
+def fp8_scale_exponent(amax) -> np.ndarray:
+    """k of a token's scale: the smallest integer with amax <= 448 * 2^k, clamped."""
+    a = np.asarray(amax, np.float64)
+    f, x = np.frexp(a)                      # 448 * 2^k = 0.875 * 2^(k + 9)
+    k = x - 9 + (f > 0.875)
+    k = np.clip(k, FP8_SCALE_EXP_MIN, FP8_SCALE_EXP_MAX)
+    return np.where(a == 0, FP8_SCALE_EXP_MIN, k).astype(np.int64)
+
+
+def quantize_latent_fp8(c):
+    """(codes uint8 [..., d_c], k int64 [...]) of latent rows c [..., d_c]."""
+    c = np.asarray(c, np.float64)
+    k = fp8_scale_exponent(np.abs(c).max(axis=-1))
+    return e4m3_encode(np.ldexp(c, -k[..., None])), k
+
+
+def dequantize_latent_fp8(codes, k) -> np.ndarray:
+    """Stored values: E4M3 value of each code times 2^k of its token."""
+    return np.ldexp(e4m3_value(codes), np.asarray(k, np.int64)[..., None])
+
+
+def fp8_page_bytes(page: int = 64, d_c: int = 512, d_r: int = 64) -> int:
+    """Bytes of one page of the 8-bit cache: codes, bf16 k_R and float32 scales."""
+    return page * d_c + page * d_r * 2 + page * 4
+
+
+def pack_fp8_cache(kv_bits, d_c: int = 512, chunk_pages: int = 256) -> np.ndarray:
+    """8-bit pages [P, fp8_page_bytes] of a bf16 cache given as bit patterns [P, page, d_c + d_R]."""
+    kv_bits = np.asarray(kv_bits)
+    if kv_bits.dtype != np.uint16:
+        raise ValueError("pack_fp8_cache takes the bf16 bit patterns (uint16)")
+    P, page, row = kv_bits.shape
+    d_r = row - d_c
+    out = np.zeros((P, fp8_page_bytes(page, d_c, d_r)), np.uint8)
+    o_rope, o_scale = page * d_c, page * d_c + page * d_r * 2
+    for p0 in range(0, P, chunk_pages):
+        blk = kv_bits[p0:p0 + chunk_pages]
+        n = blk.shape[0]
+        codes, k = quantize_latent_fp8(bf16_bits_to_f64(blk[..., :d_c]))
+        out[p0:p0 + n, :o_rope] = codes.reshape(n, page * d_c)
+        out[p0:p0 + n, o_rope:o_scale] = np.ascontiguousarray(blk[..., d_c:]).view(np.uint8).reshape(n, -1)
+        scale = np.ldexp(1.0, k).astype("<f4")
+        out[p0:p0 + n, o_scale:] = scale.view(np.uint8).reshape(n, -1)
+    return out
+
+
+def unpack_fp8_pages(pages, page: int = 64, d_c: int = 512, d_r: int = 64):
+    """(codes [n, page, d_c] uint8, k_R bits [n, page, d_R] uint16, scales [n, page] float32)."""
+    pages = np.ascontiguousarray(pages, np.uint8)
+    n = pages.shape[0]
+    if pages.shape[1] != fp8_page_bytes(page, d_c, d_r):
+        raise ValueError("page size does not match the 8-bit layout")
+    o_rope, o_scale = page * d_c, page * d_c + page * d_r * 2
+    codes = pages[:, :o_rope].reshape(n, page, d_c)
+    rope = pages[:, o_rope:o_scale].copy().view("<u2").reshape(n, page, d_r)
+    scale = pages[:, o_scale:].copy().view("<f4").reshape(n, page)
+    return codes, rope, scale
+
+
+def dequantize_fp8_pages(pages, page: int = 64, d_c: int = 512, d_r: int = 64) -> np.ndarray:
+    """float64 rows [n, page, d_c + d_R] stored by 8-bit pages."""
+    codes, rope, scale = unpack_fp8_pages(pages, page, d_c, d_r)
+    c = e4m3_value(codes) * scale.astype(np.float64)[..., None]
+    return np.concatenate([c, bf16_bits_to_f64(rope)], axis=-1)
+
+
+class PagedFp8Cache:
+    """An 8-bit paged cache (uint8 pages [P, fp8_page_bytes]) as the decode
+    oracles read it: gather_rows dequantizes only the pages a sequence uses,
+    and np.asarray gives the whole cache in float64 (small caches only)."""
+
+    def __init__(self, pages, page: int = 64, d_c: int = 512, d_r: int = 64):
+        self.pages = np.asarray(pages, np.uint8)
+        self.page, self.d_c, self.d_r = page, d_c, d_r
+        if self.pages.ndim != 2 or self.pages.shape[1] != fp8_page_bytes(page, d_c, d_r):
+            raise ValueError("expected uint8 pages [P, fp8_page_bytes]")
+        self.shape = (self.pages.shape[0], page, d_c + d_r)
+
+    def rows_of_pages(self, ids) -> np.ndarray:
+        return dequantize_fp8_pages(self.pages[np.asarray(ids, np.int64)], self.page, self.d_c, self.d_r)
+
+    def __array__(self, dtype=None, copy=None):
+        out = dequantize_fp8_pages(self.pages, self.page, self.d_c, self.d_r)
+        return out if dtype is None else out.astype(dtype)

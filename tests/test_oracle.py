@@ -588,3 +588,131 @@ def test_decompressed_branch_equals_naive_and_absorbed_paths():
     o_lat, lse_b = O.decode_absorbed(qa, f["q_r"], kvb, bt, sl, O.default_scale())
     np.testing.assert_allclose(out, O.up_proj(o_lat, f["w_uv"]), rtol=0, atol=1e-11)
     np.testing.assert_allclose(lse, lse_b, rtol=0, atol=1e-11)
+
+
+# --------------------------------------------------------------------------
+# 8-bit latent cache (FP8 E4M3 codes, one power-of-two scale per token)
+# --------------------------------------------------------------------------
+# The E4M3 value table and round-to-nearest-even are pinned to torch's own
+# float8_e4m3fn type (an independent implementation of the OCP format), the
+# scale rule to a brute-force search, the page layout to byte offsets worked
+# out by hand, and the 8-bit decode to the definition "attention over the
+# stored values".
+
+def _torch_e4m3_table():
+    return torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+
+
+def test_e4m3_values_match_torch_float8_and_format_landmarks():
+    got = O.e4m3_value(np.arange(256))
+    ref = _torch_e4m3_table()
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(got[fin], ref[fin])
+    assert np.array_equal(np.signbit(got[fin]), np.signbit(ref[fin]))
+    # landmarks of the format: largest finite, smallest normal and subnormal, one
+    assert got[0x7E] == 448.0 and got[0x08] == 2.0 ** -6 and got[0x01] == 2.0 ** -9 and got[0x38] == 1.0
+    assert np.isnan(got[0x7F]) and np.isnan(got[0xFF])
+    assert np.all(np.diff(got[:0x7F]) > 0)          # codes 0x00..0x7E increase strictly
+
+
+def _all_bf16_within(limit):
+    bits = np.arange(65536, dtype=np.uint32)
+    with np.errstate(invalid="ignore"):
+        v = (bits << 16).view(np.float32).astype(np.float64)
+    return v[np.isfinite(v) & (np.abs(v) <= limit)]
+
+
+def test_e4m3_encode_matches_torch_cast_on_every_bf16_value_and_midpoint():
+    """Every value the quantizer can meet (a bf16 value times a power of two,
+    at most 448 in magnitude) has at most 8 significant bits; all of them, and
+    the exact midpoints between neighbouring E4M3 values (the ties), round as
+    torch's cast to float8_e4m3fn does, sign of zero included."""
+    table = _torch_e4m3_table()
+    pos = np.unique(table[(~np.isnan(table)) & (table >= 0)])
+    mids = (pos[:-1] + pos[1:]) / 2
+    v = np.concatenate([_all_bf16_within(448.0), mids, -mids, [0.0, -0.0]])
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.e4m3_encode(v), ref)
+
+
+def test_e4m3_encode_is_nearest_with_ties_to_even_by_brute_force():
+    table = _torch_e4m3_table()
+    codes = [c for c in range(256) if not math.isnan(table[c])]
+    rng = np.random.default_rng(8)
+    vals = list(rng.uniform(-448, 448, 300)) + list(rng.uniform(-2 ** -5, 2 ** -5, 300)) + [2.5 * 2 ** -9, 9.5 * 2 ** -9]
+    enc = O.e4m3_encode(np.array(vals))
+    for v, c in zip(vals, enc):
+        best = min(abs(v - table[k]) for k in codes)
+        assert abs(v - table[c]) == best
+        ties = [k for k in codes if abs(v - table[k]) == best and (k & 0x80) == (0x80 if v < 0 else 0)]
+        if len(ties) > 1:
+            assert c % 2 == 0, f"tie at {v} not rounded to the even mantissa"
+    with pytest.raises(ValueError):
+        O.e4m3_encode(np.array([448.5]))
+
+
+def test_fp8_scale_exponent_is_the_smallest_that_fits_by_search():
+    rng = np.random.default_rng(9)
+    amax = np.concatenate([np.exp(rng.uniform(-80, 80, 200)), [448.0, 449.0, 448.0 * 2 ** -20, 224.0, 1.0,
+                                                               np.nextafter(448.0, 0), 2.0 ** -140, 3e38]])
+    got = O.fp8_scale_exponent(amax)
+    for a, k in zip(amax, got):
+        want = next(j for j in range(-300, 300) if a <= 448.0 * 2.0 ** j)
+        assert k == min(max(want, -126), 127), (a, k, want)
+    assert O.fp8_scale_exponent(np.array([0.0]))[0] == -126
+
+
+def test_quantize_latent_fp8_error_bound_and_no_saturation():
+    rng = np.random.default_rng(10)
+    c = torch.from_numpy(rng.standard_normal((64, 512)) * np.exp(rng.uniform(-20, 20, (64, 1)))).to(torch.bfloat16)
+    x = O.as_f64(c)
+    codes, k = O.quantize_latent_fp8(x)
+    back = O.dequantize_latent_fp8(codes, k)
+    s = np.ldexp(1.0, k)[:, None]
+    normal = np.abs(x) >= 2.0 ** -6 * s
+    # half a spacing of E4M3: 2^-4 relative in the normal range, 2^-10 * s below it
+    assert np.all(np.abs(back - x)[normal] <= 2.0 ** -4 * np.abs(x)[normal])
+    assert np.all(np.abs(back - x)[~normal] <= (2.0 ** -10 * s + 0 * x)[~normal])
+    amax_codes = np.abs(O.e4m3_value(codes)).max(axis=1)
+    assert np.all(amax_codes <= 448.0)
+    assert np.all(np.abs(x).max(axis=1) / s[:, 0] > 224.0)   # a smaller scale would overflow
+    assert np.array_equal(np.signbit(O.e4m3_value(codes)), np.signbit(x))
+
+
+def test_fp8_page_layout_by_hand():
+    P, page, d_c, d_r = 2, 64, 512, 64
+    kv = torch.zeros((P, page, d_c + d_r), dtype=torch.bfloat16)
+    kv[1, 5, 7] = 3.0
+    kv[1, 5, 100] = -0.5
+    kv[1, 5, d_c + 3] = 1.25
+    pages = O.pack_fp8_cache(O.bf16_bits(kv))
+    assert pages.shape == (P, 64 * 512 + 64 * 128 + 64 * 4) == (P, 41216)
+    # token (page 1, row 5): max |c| = 3 -> smallest 2^k with 3 <= 448 * 2^k is 2^-7
+    assert pages[1, 5 * 512 + 7] == 0x7C                  # 3 / 2^-7 = 384 = 1.5 * 2^8: 0.1111.100
+    assert pages[1, 5 * 512 + 100] == 0xE8               # -0.5 / 2^-7 = -64 = -2^6: 1.1101.000
+    assert pages[1, 32768 + 5 * 128 + 6] == 0xA0 and pages[1, 32768 + 5 * 128 + 7] == 0x3F   # bf16 1.25, LE
+    assert pages[1, 40960 + 5 * 4: 40960 + 5 * 4 + 4].view("<f4")[0] == 2.0 ** -7
+    assert pages[0, 40960: 40960 + 4].view("<f4")[0] == 2.0 ** -126   # zero row
+    assert not pages[0, :32768].any()
+
+
+def test_fp8_cache_decode_is_attention_over_stored_values():
+    inp = tiny_inputs(B=3, s_q=2, seqlens=[70, 9, 130], h=4, d_hc=128, d_c=512, d_r=64, page=64, seed=21)
+    kv16 = inp["kv_cache"].to(torch.bfloat16)
+    pages = O.pack_fp8_cache(O.bf16_bits(kv16))
+    cache8 = O.PagedFp8Cache(pages)
+    stored = O.dequantize_fp8_pages(pages)
+    bt, sl = inp["block_table"].numpy(), inp["seqlens"].numpy()
+    qa = O.absorb(O.as_f64(inp["q_c"]), O.as_f64(inp["w_uk"]))
+    qr = O.as_f64(inp["q_r"])
+    o8, l8 = O.decode_absorbed(qa, qr, cache8, bt, sl, O.default_scale())
+    o_ref, l_ref = O.decode_absorbed(qa, qr, stored, bt, sl, O.default_scale())
+    assert np.array_equal(o8, o_ref) and np.array_equal(l8, l_ref)
+    # k_R is stored exactly; c_KV within half an E4M3 spacing of the bf16 cache
+    kvb = O.as_f64(kv16)
+    assert np.array_equal(stored[..., 512:], kvb[..., 512:])
+    assert np.all(np.abs(stored[..., :512] - kvb[..., :512]) <= 2.0 ** -4 * np.abs(kvb[..., :512]) + 2.0 ** -12)
+    # and the attention result stays close to the bf16 cache's
+    o16, l16 = O.decode_absorbed(qa, qr, kvb, bt, sl, O.default_scale())
+    assert np.abs(o8 - o16).max() < 0.05 * np.abs(o16).max()

@@ -155,3 +155,72 @@ def test_mha_without_rope_term_is_caught(monkeypatch):
 def test_dispatch_strict_threshold_is_caught(monkeypatch):
     _patch(monkeypatch, "uses_absorption", lambda s_q, threshold=M.PREFILL_ABSORPTION_THRESHOLD: int(s_q) < threshold)
     _expect_fail(pins.test_dispatch_threshold_matches_teardown_page)
+
+
+def test_e4m3_round_half_away_from_zero_is_caught(monkeypatch):
+    real = M.e4m3_encode
+
+    def half_up(v):
+        v = np.asarray(v, np.float64)
+        a = np.abs(v)
+        _, x = np.frexp(a)
+        E = np.maximum(x - 1, -6)
+        ulp = np.ldexp(1.0, E - 3)
+        return real(np.copysign(np.floor(a / ulp + 0.5) * ulp, v))   # ties away from zero
+    _patch(monkeypatch, "e4m3_encode", half_up)
+    _expect_fail(pins.test_e4m3_encode_matches_torch_cast_on_every_bf16_value_and_midpoint,
+                 pins.test_e4m3_encode_is_nearest_with_ties_to_even_by_brute_force)
+
+
+def test_e4m3_unsigned_zero_is_caught(monkeypatch):
+    real = M.e4m3_encode
+
+    def no_neg_zero(v):
+        c = real(v)
+        return np.where(c == 0x80, 0, c).astype(np.uint8)
+    _patch(monkeypatch, "e4m3_encode", no_neg_zero)
+    _expect_fail(pins.test_e4m3_encode_matches_torch_cast_on_every_bf16_value_and_midpoint,
+                 pins.test_quantize_latent_fp8_error_bound_and_no_saturation)
+
+
+def test_e4m3_subnormal_scale_is_caught(monkeypatch):
+    real = M.e4m3_value
+
+    def wrong(codes):
+        c = np.asarray(codes).astype(np.int64)
+        v = real(c)
+        return np.where(((c >> 3) & 15) == 0, v / 2, v)   # subnormals m/8 * 2^-7
+    _patch(monkeypatch, "e4m3_value", wrong)
+    _expect_fail(pins.test_e4m3_values_match_torch_float8_and_format_landmarks)
+
+
+def test_fp8_scale_off_by_one_is_caught(monkeypatch):
+    real = M.fp8_scale_exponent
+    _patch(monkeypatch, "fp8_scale_exponent", lambda a: real(a) + 1)
+    _expect_fail(pins.test_fp8_scale_exponent_is_the_smallest_that_fits_by_search,
+                 pins.test_quantize_latent_fp8_error_bound_and_no_saturation)
+
+
+def test_fp8_scale_saturating_rule_is_caught(monkeypatch):
+    # the MX rule 2^(floor(log2 amax) - 8), which clips amax in (448, 512) * 2^k
+    def mx_rule(a):
+        a = np.asarray(a, np.float64)
+        _, x = np.frexp(a)
+        return np.where(a == 0, -126, np.clip(x - 9, -126, 127)).astype(np.int64)
+    _patch(monkeypatch, "fp8_scale_exponent", mx_rule)
+    _expect_fail(pins.test_fp8_scale_exponent_is_the_smallest_that_fits_by_search)
+
+
+def test_fp8_page_with_swapped_rope_and_scale_is_caught(monkeypatch):
+    real = M.pack_fp8_cache
+
+    def swapped(kv_bits, d_c=512, chunk_pages=256):
+        out = real(kv_bits, d_c, chunk_pages)
+        page = np.asarray(kv_bits).shape[1]
+        o_rope, o_scale = page * d_c, page * d_c + page * 128
+        fixed = out.copy()
+        fixed[:, o_rope:o_rope + page * 4] = out[:, o_scale:]
+        fixed[:, o_rope + page * 4:] = out[:, o_rope:o_scale]
+        return fixed
+    _patch(monkeypatch, "pack_fp8_cache", swapped)
+    _expect_fail(pins.test_fp8_page_layout_by_hand)
