@@ -11,7 +11,9 @@ Prints one JSON line (rank 0):
   value            whole-step throughput, algorithmic TFLOP/s
   roofline         the dominant kernel (mla_decode_paged) against HBM
   cpu_baseline     the fp64 CPU oracle on a bounded sample of the workload
-plus effective KV GB/s and per-kernel times.
+plus effective KV GB/s, per-kernel times and, under next_rows, the cache
+append and query rotation, the same step over the 8-bit cache
+(mla_decode_paged_fp8), and for chunks of s_q > 1 the decompressed branch.
 """
 from __future__ import annotations
 
@@ -48,6 +50,7 @@ def parse():
     p.add_argument("--separate-stage2", action="store_true",
                    help="run mla_combine_splits and mla_up_proj as two kernels instead of mla_combine_up_proj")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle time for the baseline")
+    p.add_argument("--no-fp8", action="store_true", help="skip the 8-bit cache leg")
     return p.parse_args()
 
 
@@ -200,6 +203,72 @@ def time_decompressed_branch(M, torch, kv, tables, seqlens, lens, q_c, q_r, w_uk
     }
 
 
+FP8_BYTES_PER_TOKEN = 512 + 64 * 2 + 4   # E4M3 codes, bf16 k_R, fp32 scale
+
+
+def time_fp8_cache(M, torch, kv, tables, seqlens, lens, q_c, q_r, w_uk, w_uv, S, layers, steps, warmup,
+                   flop_step, flop_attn, q_bytes, olat_bytes):
+    """The same step over the 8-bit cache: every resident layer converted once
+    (mla_quantize_cache_fp8), then absorb -> mla_decode_paged_fp8 ->
+    mla_combine_up_proj, rotating through the layers as the main loop does."""
+    B, s_q = q_c.shape[0], q_c.shape[1]
+    T = B * s_q
+    dev = q_c.device
+    kv8 = torch.empty((layers, kv.shape[1], 41216), dtype=torch.uint8, device=dev)
+    for l in range(layers):
+        M.mla_quantize_cache_fp8(kv[l], kv8[l])
+    torch.cuda.synchronize()
+    q_abs = torch.empty((B, s_q, 128, 512), dtype=torch.bfloat16, device=dev)
+    o_part = torch.empty((B, s_q, 128, S, 512), dtype=torch.float32, device=dev)
+    lse_part = torch.empty((B, s_q, 128, S), dtype=torch.float32, device=dev)
+    out = torch.empty((T, 128, 128), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, s_q, 128), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+
+    def step(k, e=None):
+        layer = k % layers
+        if e: e[0].record(stream)
+        M.mla_absorb_q(q_c, w_uk, q_abs)
+        if e: e[1].record(stream)
+        M.mla_decode_paged_fp8(q_abs, q_r, kv8[layer], tables[layer], seqlens, S, o_part=o_part, lse_part=lse_part)
+        if e: e[2].record(stream)
+        M.mla_combine_up_proj(o_part, lse_part, w_uv, out, lse)
+        if e: e[3].record(stream)
+
+    for k in range(warmup):
+        step(k)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        step(warmup + k)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for k in range(steps):
+        step(warmup + k, ev[k])
+    torch.cuda.synchronize()
+    per = [sum(ev[k][j].elapsed_time(ev[k][j + 1]) for k in range(steps)) / steps for j in range(3)]
+    ms_step = wall / steps * 1e3
+    kv_bytes = sum(lens) * FP8_BYTES_PER_TOKEN
+    dec_bytes = kv_bytes + q_bytes + olat_bytes
+    dec_ms = per[1]
+    del kv8
+    return {
+        "cache": "c_KV in E4M3 with a power-of-two scale per token, k_R in bf16: "
+                 f"{FP8_BYTES_PER_TOKEN} bytes per token instead of {KV_BYTES_PER_TOKEN}",
+        "ms_per_step": round(ms_step, 4),
+        "value_tflops": round(flop_step / (ms_step * 1e-3) / 1e12, 2),
+        "kernels_ms": {"mla_absorb_q": round(per[0], 4), "mla_decode_paged_fp8": round(dec_ms, 4),
+                       "mla_combine_up_proj": round(per[2], 4)},
+        "decode_roofline": {"bound": "hbm", "achieved": round(dec_bytes / (dec_ms * 1e-3) / 1e9, 1),
+                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": round(dec_bytes / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                            "algorithmic_bytes_per_launch": dec_bytes,
+                            "decode_tflops": round(flop_attn / (dec_ms * 1e-3) / 1e12, 1),
+                            "mfma_frac": round(flop_attn / (dec_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -334,6 +403,11 @@ def main():
     # cache append + query rotation, timed after the step (they write into the
     # cache rows the step has already read)
     result["next_rows"] = time_next_rows(M, torch, kv, tables, seqlens, lens, B, s_q, layers)
+    if not args.no_fp8:
+        print("[bench] 8-bit cache: convert the resident layers, time the same steps", file=sys.stderr, flush=True)
+        result["next_rows"]["fp8_cache"] = time_fp8_cache(
+            M, torch, kv, tables, seqlens, lens, q_c, q_r, w_uk, w_uv, S, layers, args.steps, args.warmup,
+            flop_step, flop_attn, q_bytes, olat_bytes)
     if s_q > 1:
         # the decompressed branch the dispatch rule would take above 256 new
         # tokens, timed at this chunk length for comparison with the step

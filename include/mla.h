@@ -276,6 +276,51 @@ mla_status mla_prefill_mha(const void* q_c, const void* q_r, const void* k_nope,
                            const int32_t* seqlens, int B, int s_q, int H, float softmax_scale, void* out, float* lse,
                            void* stream);
 
+/* ---- 8-bit latent cache ---------------------------------------------------
+ * The teardown page reads a quantized latent cache with 16-byte vector loads
+ * that need 16-byte aligned page bases and dimension offsets (section 5). This
+ * library's 8-bit cache stores c_KV in OCP FP8 E4M3 (1 sign, 4 exponent bits
+ * with bias 7, 3 mantissa bits; largest finite value 448; no infinities) with
+ * one power-of-two scale per token, and keeps k_R in bf16:
+ *   scale 2^k, k the smallest integer with max_c |c_KV[c]| <= 448 * 2^k,
+ *     clamped to [-126, 127] (an all-zero row gets 2^-126), so nothing saturates;
+ *   code[c] = c_KV[c] / 2^k rounded to the nearest E4M3 value, ties to even,
+ *     with the sign of c_KV[c] (a negative value that rounds to 0 becomes -0);
+ *   stored value = E4M3(code[c]) * 2^k.
+ * A page of 64 tokens is MLA_FP8_PAGE_BYTES = 41216 bytes, three arrays:
+ *   bytes [0, 32768)      uint8 codes [64][512]
+ *   bytes [32768, 40960)  bf16 k_R [64][64]
+ *   bytes [40960, 41216)  fp32 scales [64] (each exactly 2^k)
+ * The cache holds 644 bytes per token instead of 1152. Decoding over it gives
+ * the attention of mla_decode_paged over the stored values (the scan converts
+ * codes to bf16 exactly and computes as the bf16 scan does). c_KV inputs must
+ * be finite. */
+enum { MLA_FP8_PAGE_BYTES = 41216 };
+
+/* Convert a bf16 cache to the 8-bit layout page for page (page p of kv_fp8
+ * holds the 64 rows of page p of kv_cache).
+ *   kv_cache bf16 [num_pages, 64, 576];  kv_fp8 uint8 [num_pages, 41216] output
+ * 1 <= num_pages <= 2^26. */
+mla_status mla_quantize_cache_fp8(const void* kv_cache, int64_t num_pages, void* kv_fp8, void* stream);
+
+/* mla_append_latent into the 8-bit cache: c_new[b, i] quantized as above
+ * (one scale per token), kr_new[b, i] rotated in fp32 and rounded to bf16.
+ * kv_fp8 uint8 [num_pages, 41216], updated in place; all other arguments and
+ * rules as mla_append_latent. */
+mla_status mla_append_latent_fp8(const void* c_new, const void* kr_new, const float* rope, int max_pos,
+                                 void* kv_fp8, int64_t num_pages, const int32_t* block_table, int max_pages,
+                                 const int32_t* seqlens, int B, int s_q, void* stream);
+
+/* mla_decode_paged over the 8-bit cache: kv_fp8 uint8 [num_pages, 41216];
+ * every other argument, rule and output as mla_decode_paged (feed o_part and
+ * lse_part to mla_combine_splits or mla_combine_up_proj). */
+mla_status mla_decode_paged_fp8(const void* q_abs, const void* q_r,
+                                const void* kv_fp8, int64_t num_pages,
+                                const int32_t* block_table, int max_pages,
+                                const int32_t* seqlens, int B, int s_q, int H,
+                                float softmax_scale, int num_splits,
+                                float* o_part, float* lse_part, void* stream);
+
 /* Test and debug aid: gather the logical cache rows of each sequence through
  * the block table with the same address arithmetic as mla_decode_paged.
  *   out bf16 [B, max_len, 576]: row t of sequence b is the cache row of token

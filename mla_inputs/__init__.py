@@ -172,6 +172,27 @@ def make_cache_on_device(num_pages: int, layers: int, seed: int, device) -> torc
     return out
 
 
+FP8_PAGE_BYTES = PAGE * D_C + PAGE * D_R * 2 + PAGE * 4   # 41216: codes, bf16 k_R, float32 scales
+
+
+def random_fp8_pages(num_pages: int, seed: int, k_lo: int = -10, k_hi: int = -6) -> torch.Tensor:
+    """uint8 [num_pages, 41216] in the 8-bit cache layout, filled with seeded
+    data (no quantization happens here): E4M3 codes uniform over all bytes
+    with the two NaN codes 0x7F / 0xFF replaced by 0x7E / 0xFE, k_R ~ N(0, 1)
+    rounded to bf16, and per-token scales 2^k, k uniform in [k_lo, k_hi],
+    stored as float32 bit patterns (k + 127) << 23."""
+    g = torch.Generator().manual_seed(seed)
+    out = torch.empty((num_pages, FP8_PAGE_BYTES), dtype=torch.uint8)
+    codes = out[:, :PAGE * D_C]
+    codes.copy_(torch.randint(0, 256, (num_pages, PAGE * D_C), generator=g, dtype=torch.uint8))
+    codes[(codes & 0x7F) == 0x7F] -= 1
+    rope = _randn_bf16((num_pages, PAGE * D_R), g)
+    out[:, PAGE * D_C:PAGE * D_C + PAGE * D_R * 2] = rope.view(torch.uint8).view(num_pages, -1)
+    k = torch.randint(k_lo, k_hi + 1, (num_pages, PAGE), generator=g, dtype=torch.int32)
+    out[:, PAGE * D_C + PAGE * D_R * 2:] = ((k + 127) << 23).view(torch.uint8).view(num_pages, -1)
+    return out
+
+
 def tiny_inputs(B: int, s_q: int, seqlens, h: int, d_hc: int, d_c: int, d_r: int,
                 page: int, seed: int = 7, pool_extra: int = 3):
     """Small float64 inputs of arbitrary dims for brute-force oracle checks.

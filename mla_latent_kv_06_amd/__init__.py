@@ -130,6 +130,58 @@ def mla_decode_paged(q_abs, q_r, kv_cache, block_table, seqlens, num_splits: int
     return o_part, lse_part
 
 
+FP8_PAGE_BYTES = 41216  # MLA_FP8_PAGE_BYTES: 64 x 512 E4M3 codes, 64 x 64 bf16 k_R, 64 fp32 scales
+
+
+def is_fp8_cache(kv_cache) -> bool:
+    """Whether kv_cache is the 8-bit layout (uint8 [num_pages, 41216])."""
+    return kv_cache.dtype == torch.uint8
+
+
+def _need_fp8_cache(kv_fp8, name="kv_fp8"):
+    if kv_fp8.dim() != 2 or kv_fp8.shape[1] != FP8_PAGE_BYTES:
+        raise ValueError(f"{name} must be [num_pages, {FP8_PAGE_BYTES}] uint8, got {tuple(kv_fp8.shape)}")
+    _need(kv_fp8, name, torch.uint8)
+
+
+def mla_decode_paged_fp8(q_abs, q_r, kv_fp8, block_table, seqlens, num_splits: int,
+                         softmax_scale: float = DEFAULT_SCALE, o_part=None, lse_part=None, stream=None):
+    """mla_decode_paged over the 8-bit cache (uint8 [num_pages, 41216]); same outputs."""
+    B, s_q = q_abs.shape[0], q_abs.shape[1]
+    _need(q_abs, "q_abs", torch.bfloat16, (B, s_q, H, D_C))
+    _need(q_r, "q_r", torch.bfloat16, (B, s_q, H, D_R))
+    _need_fp8_cache(kv_fp8)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError(f"block_table must be [B, max_pages], got {tuple(block_table.shape)}")
+    _need(block_table, "block_table", torch.int32)
+    _need(seqlens, "seqlens", torch.int32, (B,))
+    S = int(num_splits)
+    if o_part is None:
+        o_part = torch.empty((B, s_q, H, S, D_C), dtype=torch.float32, device=q_abs.device)
+    if lse_part is None:
+        lse_part = torch.empty((B, s_q, H, S), dtype=torch.float32, device=q_abs.device)
+    _need(o_part, "o_part", torch.float32, (B, s_q, H, S, D_C))
+    _need(lse_part, "lse_part", torch.float32, (B, s_q, H, S))
+    _check(_lib.LIB.mla_decode_paged_fp8(
+        _ptr(q_abs), _ptr(q_r), _ptr(kv_fp8), kv_fp8.shape[0], _ptr(block_table), block_table.shape[1],
+        _ptr(seqlens), B, s_q, H, float(softmax_scale), S, _ptr(o_part), _ptr(lse_part), _stream(stream)),
+        "mla_decode_paged_fp8")
+    return o_part, lse_part
+
+
+def mla_quantize_cache_fp8(kv_cache, out=None, stream=None):
+    """bf16 cache [P, 64, 576] -> 8-bit cache uint8 [P, 41216], page for page."""
+    if kv_cache.dim() != 3 or kv_cache.shape[1:] != (PAGE, ROW):
+        raise ValueError(f"kv_cache must be [num_pages, 64, 576], got {tuple(kv_cache.shape)}")
+    _need(kv_cache, "kv_cache", torch.bfloat16)
+    P = kv_cache.shape[0]
+    if out is None:
+        out = torch.empty((P, FP8_PAGE_BYTES), dtype=torch.uint8, device=kv_cache.device)
+    _need(out, "out", torch.uint8, (P, FP8_PAGE_BYTES))
+    _check(_lib.LIB.mla_quantize_cache_fp8(_ptr(kv_cache), P, _ptr(out), _stream(stream)), "mla_quantize_cache_fp8")
+    return out
+
+
 def mla_combine_splits(o_part, lse_part, o_lat=None, lse=None, stream=None):
     """LSE-weighted merge; returns (o_lat [B,s_q,H,512] fp32, lse [B,s_q,H] fp32)."""
     B, s_q, _, S = lse_part.shape
@@ -226,6 +278,26 @@ def mla_append_latent(kv_cache, block_table, seqlens, c_new, kr_new, rope, strea
     return kv_cache
 
 
+def mla_append_latent_fp8(kv_fp8, block_table, seqlens, c_new, kr_new, rope, stream=None):
+    """mla_append_latent into the 8-bit cache (c_new quantized per token, kr_new
+    rotated); returns kv_fp8."""
+    B, s_q = c_new.shape[0], c_new.shape[1]
+    _need(c_new, "c_new", torch.bfloat16, (B, s_q, D_C))
+    _need(kr_new, "kr_new", torch.bfloat16, (B, s_q, D_R))
+    if rope.dim() != 3 or rope.shape[1:] != (D_R // 2, 2):
+        raise ValueError(f"rope must be [max_pos, 32, 2], got {tuple(rope.shape)}")
+    _need(rope, "rope", torch.float32)
+    _need_fp8_cache(kv_fp8)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError(f"block_table must be [B, max_pages], got {tuple(block_table.shape)}")
+    _need(block_table, "block_table", torch.int32)
+    _need(seqlens, "seqlens", torch.int32, (B,))
+    _check(_lib.LIB.mla_append_latent_fp8(_ptr(c_new), _ptr(kr_new), _ptr(rope), rope.shape[0], _ptr(kv_fp8),
+                                          kv_fp8.shape[0], _ptr(block_table), block_table.shape[1], _ptr(seqlens),
+                                          B, s_q, _stream(stream)), "mla_append_latent_fp8")
+    return kv_fp8
+
+
 def mla_rope_q(q_r, seqlens, rope, stream=None):
     """Rotate q_r [B, s_q, H, 64] in place by each chunk token's position; returns q_r."""
     B, s_q = q_r.shape[0], q_r.shape[1]
@@ -302,14 +374,15 @@ def decode_layer(q_c, q_r, kv_cache, block_table, seqlens, w_uk, w_uv, num_split
 
     Returns a dict with every intermediate (q_abs, o_part, lse_part, o_lat, lse, out).
     ``max_len`` (longest sequence, host int) only feeds the split heuristic.
+    ``kv_cache`` is the bf16 cache [P, 64, 576] or the 8-bit one (uint8 [P, 41216]).
     """
     B, s_q = q_c.shape[0], q_c.shape[1]
     if num_splits is None:
         ml = int(max_len) if max_len is not None else block_table.shape[1] * PAGE
         num_splits = mla_recommended_splits(B, s_q, ml)
     q_abs = mla_absorb_q(q_c, w_uk, stream=stream)
-    o_part, lse_part = mla_decode_paged(q_abs, q_r, kv_cache, block_table, seqlens, num_splits,
-                                        softmax_scale, stream=stream)
+    scan = mla_decode_paged_fp8 if is_fp8_cache(kv_cache) else mla_decode_paged
+    o_part, lse_part = scan(q_abs, q_r, kv_cache, block_table, seqlens, num_splits, softmax_scale, stream=stream)
     o_lat, lse = mla_combine_splits(o_part, lse_part, stream=stream)
     out = mla_up_proj(o_lat, w_uv, stream=stream)
     return dict(q_abs=q_abs, o_part=o_part, lse_part=lse_part, o_lat=o_lat, lse=lse, out=out)
@@ -331,6 +404,8 @@ def attention_layer(q_c, q_r, kv_cache, block_table, seqlens, w_uk, w_uv, max_le
                          max_len, stream)
         r["path"] = "absorbed"
         return r
+    if is_fp8_cache(kv_cache):
+        raise ValueError("the decompressed branch reads the bf16 cache; the 8-bit cache serves the absorbed path")
     ml = -(-int(max_len) // PAGE) * PAGE
     k_nope, v = mla_decompress_kv(kv_cache, block_table, seqlens, w_uk, w_uv, ml, stream=stream)
     out, lse = mla_prefill_mha(q_c, q_r, k_nope, v, kv_cache, block_table, seqlens, softmax_scale, stream=stream)

@@ -41,6 +41,11 @@ SIGNATURES = {
     "mla_decompressed_kv_bytes": (c_size_t, [c_int, c_int]),
     "mla_decompress_kv": (c_int, [c_void_p, c_int64, c_void_p, c_int, c_void_p, c_int, c_int, c_void_p, c_void_p,
                                   c_void_p, c_void_p, c_void_p]),
+    "mla_quantize_cache_fp8": (c_int, [c_void_p, c_int64, c_void_p, c_void_p]),
+    "mla_append_latent_fp8": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_int64, c_void_p, c_int,
+                                      c_void_p, c_int, c_int, c_void_p]),
+    "mla_decode_paged_fp8": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_int, c_void_p, c_int, c_int,
+                                     c_int, c_float, c_int, c_void_p, c_void_p, c_void_p]),
     "mla_prefill_mha": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_int64, c_void_p, c_int,
                                 c_void_p, c_int, c_int, c_int, c_float, c_void_p, c_void_p, c_void_p]),
 }

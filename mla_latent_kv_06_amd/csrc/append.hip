@@ -13,6 +13,7 @@
 
 #include "mla_device.hpp"
 #include "append.hpp"
+#include "fp8_cache.hpp"
 
 namespace mla {
 
@@ -64,6 +65,57 @@ __global__ __launch_bounds__(256) void append_latent_kernel(const __bf16* __rest
   }
 }
 
+// The same append into the 8-bit cache: one wave per chunk token quantizes
+// its c_KV row (8 values per lane, 8 code bytes stored per lane), lanes
+// 0..31 rotate one k_R pair each, lane 0 stores the token's scale.
+__global__ __launch_bounds__(256) void append_latent_fp8_kernel(const __bf16* __restrict__ c_new,
+                                                                const __bf16* __restrict__ kr_new,
+                                                                const float2* __restrict__ rope, int max_pos,
+                                                                char* __restrict__ kv, int64_t num_pages,
+                                                                const int32_t* __restrict__ block_table,
+                                                                int max_pages, const int32_t* __restrict__ seqlens,
+                                                                int T, int s_q) {
+  const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
+  if (t >= T) return;
+  const int b = t / s_q, i = t - b * s_q;
+  const int64_t cap = (int64_t)max_pages * kPage < max_pos ? (int64_t)max_pages * kPage : max_pos;
+  const int p = chunk_position(seqlens, b, i, s_q, cap);
+  if (p < 0) return;
+  const int64_t page = physical_page(block_table, max_pages, b, p >> 6, num_pages);
+  char* base = kv + page * kFp8PageBytes;
+  const int r = p & (kPage - 1);
+  int k;
+  const uint2 codes = quantize_row_fp8(reinterpret_cast<const bf16x8*>(c_new + (int64_t)t * kDc)[lane], k);
+  reinterpret_cast<uint2*>(base + r * kDc)[lane] = codes;
+  if (lane < kDr / 2) {
+    const bf16x2 x = reinterpret_cast<const bf16x2*>(kr_new + (int64_t)t * kDr)[lane];
+    const float2 cs = rope[(int64_t)p * (kDr / 2) + lane];
+    reinterpret_cast<bf16x2*>(base + kFp8RopeOffset + r * kDr * 2)[lane] = rotate_pair(x, cs);
+  }
+  if (lane == 0) reinterpret_cast<float*>(base + kFp8ScaleOffset)[r] = fp8_scale_value(k);
+}
+
+// bf16 pages [num_pages, 64, 576] -> 8-bit pages [num_pages, 41216 bytes],
+// page for page: one wave per token row.
+__global__ __launch_bounds__(256) void quantize_cache_fp8_kernel(const char* __restrict__ kv, int64_t num_pages,
+                                                                 char* __restrict__ out) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= num_pages * kPage) return;
+  const int64_t page = row >> 6;
+  const int r = (int)(row & (kPage - 1));
+  const char* src = kv + page * kPageBytes + (int64_t)r * kRowBytes;
+  char* base = out + page * kFp8PageBytes;
+  int k;
+  const uint2 codes = quantize_row_fp8(reinterpret_cast<const bf16x8*>(src)[lane], k);
+  reinterpret_cast<uint2*>(base + r * kDc)[lane] = codes;
+  if (lane < kDr * 2 / 16)
+    reinterpret_cast<f32x4*>(base + kFp8RopeOffset + r * kDr * 2)[lane] =
+        reinterpret_cast<const f32x4*>(src + kDc * 2)[lane];
+  if (lane == 0) reinterpret_cast<float*>(base + kFp8ScaleOffset)[r] = fp8_scale_value(k);
+}
+
 // q_R [T, H, 64] rotated in place: one thread per 4 pairs (16 bytes). Rows of
 // tokens without a position below max_pos are left as they are.
 __global__ __launch_bounds__(256) void rope_q_kernel(__bf16* __restrict__ q_r, const float2* __restrict__ rope,
@@ -97,6 +149,22 @@ hipError_t launch_append_latent(const __bf16* c_new, const __bf16* kr_new, const
   hipLaunchKernelGGL(append_latent_kernel, dim3((T + 3) / 4), dim3(256), 0, stream, c_new, kr_new,
                      reinterpret_cast<const float2*>(rope), max_pos, kv, num_pages, block_table, max_pages, seqlens,
                      T, s_q);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_latent_fp8(const __bf16* c_new, const __bf16* kr_new, const float* rope, int max_pos,
+                                    char* kv, int64_t num_pages, const int32_t* block_table, int max_pages,
+                                    const int32_t* seqlens, int B, int s_q, hipStream_t stream) {
+  const int T = B * s_q;
+  hipLaunchKernelGGL(append_latent_fp8_kernel, dim3((T + 3) / 4), dim3(256), 0, stream, c_new, kr_new,
+                     reinterpret_cast<const float2*>(rope), max_pos, kv, num_pages, block_table, max_pages, seqlens,
+                     T, s_q);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_cache_fp8(const char* kv, int64_t num_pages, char* out, hipStream_t stream) {
+  const int64_t blocks = num_pages * (kPage / 4);
+  hipLaunchKernelGGL(quantize_cache_fp8_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, kv, num_pages, out);
   return hipGetLastError();
 }
 

@@ -41,6 +41,7 @@
 
 #include "mla_device.hpp"
 #include "decode.hpp"
+#include "fp8_cache.hpp"
 
 namespace mla {
 
@@ -58,7 +59,42 @@ constexpr int kScanGroups = 256;                  // workgroups of a scan (one p
 static_assert(kDmaPerThread * kThreads * 16 == kStageBytes, "stage must split into 16-byte loads");
 static_assert(kLdsBytes <= 163840, "LDS budget");
 
+// 8-bit cache: a stage holds the tile's 32 rows of 512 codes, then its 32 k_R
+// rows of 128 bytes, then its 32 scales; a thread issues 6 loads per tile
+// (4 code chunks, 1 k_R chunk, and in lanes 0-1 of every wave 1 scale chunk).
+constexpr int kStage8Rope = kTok * kDc;                      // 16384
+constexpr int kStage8Scale = kStage8Rope + kTok * kDr * 2;   // 20480
+constexpr int kStage8Bytes = kStage8Scale + kTok * 4;        // 20608
+constexpr int kDma8PerThread = 6;
+static_assert(4 * kThreads * 16 == kStage8Rope && kThreads * 16 == kTok * kDr * 2 && 8 * 16 == kTok * 4,
+              "8-bit stage must split into 16-byte loads");
+static_assert(kStage8Bytes % 16 == 0, "8-bit stages start on 16-byte boundaries");
+
+template <bool kFp8>
+struct StageFmt {
+  static constexpr int bytes = kFp8 ? kStage8Bytes : kStageBytes;
+  static constexpr int dma = kFp8 ? kDma8PerThread : kDmaPerThread;
+  static constexpr int lds = kStages * bytes + kPBytes;
+};
+static_assert(StageFmt<true>::lds <= 163840, "LDS budget");
+
 __device__ __forceinline__ int swz(int t) { return ((t & 3) << 1) ^ ((t >> 2) & 7); }
+// 8-bit stage: chunk c of code row t sits at c ^ swz8(t) (low 3 bits). Rows
+// 0..7 of a run of eight differ in the low 3 bits and rows t, t+8 in bit 2, so
+// both the 16-byte QK reads (eight consecutive rows) and the transposed
+// 8-byte PV reads (rows 16ks + 8a + 4g + b, a < 2, b < 4) hit eight distinct
+// 16-byte slots of a 128-byte line. k_R rows (128 bytes) use c ^ (t & 7).
+__device__ __forceinline__ int swz8(int t) { return (t & 7) ^ ((t >> 1) & 4); }
+
+// 8 E4M3 codes (byte j of d0:d1 = element j) -> 8 bf16 values times scale; the
+// scale is a power of two, so every product is exact
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(unsigned d0, unsigned d1, float scale) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, scale, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, scale, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, scale, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, scale, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
 
 // The lane id recomputed where it is used (two VALU ops). Written as
 // volatile asm so the compiler cannot hoist lane-dependent addresses out of
@@ -93,6 +129,16 @@ __device__ __forceinline__ void mfma_qk_first(f32x16& d, const bf16x8& a, const 
 }
 __device__ __forceinline__ void mfma_qk(f32x16& d, const bf16x8& a, const bf16x8& b) {
   asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+// The same chain when the A operand was just written by VALU (the 8-bit
+// path converts it in registers): an MFMA may read a VGPR that a VALU
+// instruction wrote only after 2 wait states, which the compiler does not
+// insert in front of inline asm; 3 are given.
+__device__ __forceinline__ void mfma_qk8_first(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_qk8(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
 }
 // VALU may read an MFMA result only after the MFMA has drained (at most
 // 16 passes + 2 on CDNA; 24 wait states here). Tied to the value so no read
@@ -144,6 +190,10 @@ __device__ __forceinline__ void dma16(const char* sbase, unsigned voff, unsigned
                  : "memory", "m0");
 }
 
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2_t;
+
 __device__ __forceinline__ bf16x8 cat8(const i16x4& v0, const i16x4& v1) {
   const bf16x4 b0 = __builtin_bit_cast(bf16x4, v0);
   const bf16x4 b1 = __builtin_bit_cast(bf16x4, v1);
@@ -184,13 +234,19 @@ __device__ __forceinline__ int wave_incl_scan32(int v, int lane) {
 
 }  // namespace
 
-template <bool kStream>
+// kFp8: the cache is the 8-bit layout of fp8_cache.hpp instead of bf16 rows.
+// Its codes are turned into bf16 operands in registers: a K fragment with the
+// lane's token scale in the same conversion, a V^T fragment (8 tokens of one
+// column, read transposed) at scale 1 with the tokens' scales folded into P
+// (P' = P * 2^k_t is exact), so the matrix work is the bf16 kernel's.
+template <bool kStream, bool kFp8>
 __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
     const __bf16* __restrict__ q_abs, const __bf16* __restrict__ q_r, const char* __restrict__ kv,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seqlens,
     float* __restrict__ o_part, float* __restrict__ lse_part, DecodeParams a) {
-  __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
-  char* const pbuf = lds + kStages * kStageBytes;
+  using F = StageFmt<kFp8>;
+  __shared__ __attribute__((aligned(1024))) char lds[F::lds];
+  char* const pbuf = lds + kStages * F::bytes;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -286,6 +342,13 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
   int qk_off[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) qk_off[r] = lo * kRowBytes + (((2 * r + g) ^ swz(lo)) << 4);
+  // 8-bit: code chunk m = 4a + r (dims 32m + 16g .. +15, two MFMAs) of row lo
+  // at qk8_off[r] + 128a; k_R chunk 2r' + g at rope8_off + ((32 r') ^ rope8_x)
+  int qk8_off[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) qk8_off[r] = lo * kDc + (((2 * r + g) ^ swz8(lo)) << 4);
+  const int rope8_off = kStage8Rope + lo * (kDr * 2);
+  const int rope8_x = (g ^ (lo & 7)) << 4;
   // PV A operand (V^T) for this wave's columns 128w + 32c' through transposed
   // reads; group G = lane>>4, ii = lane&15 fetches row 4(G>>1) + (ii>>2)
   // (+8 half, +16 k-step), columns 16(G&1) + 4(ii&3)..+3 of the 32-column tile.
@@ -305,15 +368,43 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
           pv_off[cp][hf][ks] = t * kRowBytes + ((j ^ swz(t)) << 4) + (ii & 1) * 8 + wave * 256;
         }
   }
+  // 8-bit PV A operand through ds_read_b64_tr_b8: in each 16-lane group G,
+  // lane 8h + j receives byte j of the 8 bytes that lanes 2k + h of the group
+  // address, as its element k. Lane (G, k, h) therefore addresses row
+  // 4(G>>1) + 8(k>>2) + (k&3) (+16 per k-step), columns 16(G&1) + 8h .. +7 of
+  // the 32-column tile: lane l then holds column l&31 for the tokens of
+  // k-slot j = 8(l>>5)... order that P^T uses (16ks + 8(j>>2) + 4(l>>5) + (j&3)).
+  int pv8_off[4];  // [c']; add 8192 (16 rows) for k-step 1
+  {
+    const int G = lane >> 4, kq = (lane & 15) >> 1, h = lane & 1;
+    const int t = 8 * (kq >> 2) + 4 * (G >> 1) + (kq & 3);
+#pragma unroll
+    for (int cp = 0; cp < 4; ++cp)
+      pv8_off[cp] = t * kDc + wave * 128 + (((2 * cp + (G & 1)) ^ swz8(t)) << 4) + 8 * h;
+  }
   // DMA: thread tid fills chunk slot q = k*256 + tid of a stage; the matching
   // source chunk of the 32-row half page is (row q/72, chunk (q%72) ^ swz(row))
-  unsigned dma_off[kDmaPerThread];
+  unsigned dma_off[F::dma];
+  if constexpr (kFp8) {
+    // code slot q = k*256 + tid (k < 4): row q/32, source chunk (q%32) ^ swz8(row);
+    // k_R slot tid: row tid/8, source chunk (tid%8) ^ (row&7); scale slot
+    // 2*wave + lane (lanes 0-1)
 #pragma unroll
-  for (int k = 0; k < kDmaPerThread; ++k) {
-    const unsigned q = k * kThreads + tid;
-    const unsigned t = q / 72u;
-    const unsigned p = q - t * 72u;
-    dma_off[k] = t * kRowBytes + ((p ^ swz(t)) << 4);
+    for (int k = 0; k < 4; ++k) {
+      const unsigned q = k * kThreads + tid;
+      const unsigned t = q >> 5;
+      dma_off[k] = t * kDc + (((q & 31) ^ swz8(t)) << 4);
+    }
+    dma_off[4] = (tid >> 3) * (kDr * 2) + (((tid & 7) ^ ((tid >> 3) & 7)) << 4);
+    dma_off[5] = (2 * wave + (tid & 1)) * 16;
+  } else {
+#pragma unroll
+    for (int k = 0; k < kDmaPerThread; ++k) {
+      const unsigned q = k * kThreads + tid;
+      const unsigned t = q / 72u;
+      const unsigned p = q - t * 72u;
+      dma_off[k] = t * kRowBytes + ((p ^ swz(t)) << 4);
+    }
   }
   // DMA of one 32-token tile (half a page) into an LDS stage, 9 loads per
   // thread; issue_part(k) issues load k so the loads can be spread between
@@ -322,15 +413,37 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
     const char* src;
     unsigned dst;
   };
+  // 8-bit: src is the page's first byte, dst the stage's wave slice
   auto dma_target = [&](int tile, int stage) -> DmaTarget {
     const int64_t page = physical_page(block_table, a.max_pages, b, tile >> 1, a.num_pages);
-    return DmaTarget{kv + page * kPageBytes + (tile & 1) * kStageBytes,
-                     (unsigned)(uintptr_t)(lds_void_t*)(lds + stage * kStageBytes + wave * 1024)};
+    if constexpr (kFp8)
+      return DmaTarget{kv + page * kFp8PageBytes,
+                       (unsigned)(uintptr_t)(lds_void_t*)(lds + stage * F::bytes + wave * 1024)};
+    else
+      return DmaTarget{kv + page * kPageBytes + (tile & 1) * kStageBytes,
+                       (unsigned)(uintptr_t)(lds_void_t*)(lds + stage * kStageBytes + wave * 1024)};
+  };
+  // load k of a tile (k is a compile-time constant at every call); the 8-bit
+  // tile is half `tile & 1` of its page in each of the page's three arrays
+  auto dma_piece = [&](const DmaTarget& t, int k, int tile) {
+    if constexpr (kFp8) {
+      const int half = tile & 1;
+      if (k < 4) {
+        dma16<kStream>(t.src + half * (kTok * kDc), dma_off[k], t.dst + k * (kThreads * 16));
+      } else if (k == 4) {
+        dma16<kStream>(t.src + kFp8RopeOffset + half * (kTok * kDr * 2), dma_off[4], t.dst + kStage8Rope);
+      } else if ((tid & 63) < 2) {
+        dma16<kStream>(t.src + kFp8ScaleOffset + half * (kTok * 4), dma_off[5],
+                       t.dst - wave * 1024 + kStage8Scale + wave * 32);
+      }
+    } else {
+      dma16<kStream>(t.src, dma_off[k], t.dst + k * (kThreads * 16));
+    }
   };
   auto issue = [&](int tile, int stage) {
     const DmaTarget t = dma_target(tile, stage);
 #pragma unroll
-    for (int k = 0; k < kDmaPerThread; ++k) dma16<kStream>(t.src, dma_off[k], t.dst + k * (kThreads * 16));
+    for (int k = 0; k < F::dma; ++k) dma_piece(t, k, tile);
   };
 
   bf16x8 qf[36];  // queries of the current piece
@@ -343,15 +456,30 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
 
   // ---- PV pieces: V^T fragment (k-step ks, column tile c') and P^T fragment
   // (k-step ks, head tile ht) of tile ip, and the 4 MFMAs of one (ks, c')
-  auto vfrag = [&](int ip, int ks, int cp) -> bf16x8 {
-    const char* tv = lds + (ip & (kStages - 1)) * kStageBytes + (cp >> 1) * 128;
-    return cat8(__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(tv + pv_off[cp & 1][0][ks])),
-                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(tv + pv_off[cp & 1][1][ks])));
+  // a V^T fragment as read from LDS: bf16 values, or for the 8-bit cache the
+  // 8 codes of one transposed read, converted (scale 1) right before its MFMAs
+  using VFrag = std::conditional_t<kFp8, i32x2, bf16x8>;
+  auto vop = [&](const VFrag& v) -> bf16x8 {
+    if constexpr (kFp8)
+      return fp8x8_to_bf16((unsigned)v[0], (unsigned)v[1], 1.0f);
+    else
+      return v;
+  };
+  auto vfrag = [&](int ip, int ks, int cp) -> VFrag {
+    if constexpr (kFp8) {
+      const char* tv = lds + (ip & (kStages - 1)) * F::bytes + pv8_off[cp] + ks * (16 * kDc);
+      return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)tv);
+    } else {
+      const char* tv = lds + (ip & (kStages - 1)) * kStageBytes + (cp >> 1) * 128;
+      return cat8(__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(tv + pv_off[cp & 1][0][ks])),
+                  __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(tv + pv_off[cp & 1][1][ks])));
+    }
   };
   auto pfrag = [&](int ip, int ks, int ht) -> bf16x8 {
     return *reinterpret_cast<const bf16x8*>(pbuf + (ip & 1) * 8 * 1024 + (ht * 2 + ks) * 1024 + lane * 16);
   };
-  auto mm4 = [&](int cp, const bf16x8& va, const bf16x8* pf) {
+  auto mm4 = [&](int cp, const VFrag& vf, const bf16x8* pf) {
+    const bf16x8 va = vop(vf);
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht)
       O[cp][ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[ht], O[cp][ht], 0, 0, 0);
@@ -360,7 +488,8 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
   // MFMAs (k-step 1, column tile 3) to run right after the next tile
   // barrier, where they cover the latency of the first K reads of QK(i+2);
   // zero operands (a no-op MFMA) when there is no earlier tile
-  bf16x8 pf[4], va[3];
+  bf16x8 pf[4];
+  VFrag va[3];
 
   // ---- phase A: S^T[token, head] = K(it) . Q^T over 576 dims, pinned in
   // program order: the K fragment for MFMA kk+3 is read right after MFMA kk,
@@ -371,6 +500,60 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
   auto qk = [&](int it, auto dma_tag, auto pv_tag) -> f32x16 {
     constexpr bool dma = decltype(dma_tag)::value;
     constexpr bool pv = decltype(pv_tag)::value;  // prefetch PV(it-1) operands
+    if constexpr (kFp8) {
+      // 8-bit: MFMA kk < 32 takes half kk&1 of code chunk kk>>1, converted with
+      // the lane's token scale; MFMAs 32..35 take the bf16 k_R fragments.
+      // Chunk m >= 3 is read after MFMA 2m - 5 into slot m & 3 (free since its
+      // chunk m - 4 was converted), four MFMAs before its first conversion;
+      // k_R fragment r goes to slot r after MFMA 27 + r (r < 3) or 31 (r = 3).
+      const char* tb = lds + (it & (kStages - 1)) * F::bytes;
+      DmaTarget t{nullptr, 0u};
+      if constexpr (dma) t = dma_target(tile0 + it + 2, (it + 2) & (kStages - 1));
+      const float ksc = *reinterpret_cast<const float*>(tb + kStage8Scale + lo * 4);
+      u32x4 raw[4];
+#pragma unroll
+      for (int m = 0; m < 3; ++m) raw[m] = *reinterpret_cast<const u32x4*>(tb + qk8_off[m]);
+      __builtin_amdgcn_sched_barrier(0);
+      mm4(3, va[1], pf);  // deferred tail of the previous PV
+      __builtin_amdgcn_sched_barrier(0);
+      f32x16 S;
+      bf16x8 af = fp8x8_to_bf16(raw[0][0], raw[0][1], ksc);
+#pragma unroll
+      for (int kk = 0; kk < 36; ++kk) {
+        if (kk == 0)
+          mfma_qk8_first(S, af, qf[0]);
+        else
+          mfma_qk8(S, af, qf[kk]);
+        if ((kk & 1) && kk <= 25) {
+          const int m = (kk + 5) >> 1;
+          raw[m & 3] = *reinterpret_cast<const u32x4*>(tb + qk8_off[m & 3] + 128 * (m >> 2));
+        }
+        if (kk >= 27 && kk <= 29) {
+          const int r = kk - 27;
+          raw[r] = *reinterpret_cast<const u32x4*>(tb + rope8_off + ((32 * r) ^ rope8_x));
+        }
+        if (kk == 31) raw[3] = *reinterpret_cast<const u32x4*>(tb + rope8_off + (96 ^ rope8_x));
+        if constexpr (pv) {
+          if (kk == 33) { pf[0] = pfrag(it - 1, 0, 0); pf[1] = pfrag(it - 1, 0, 1); }
+          if (kk == 34) { pf[2] = pfrag(it - 1, 0, 2); pf[3] = pfrag(it - 1, 0, 3); }
+          if (kk == 35) { va[0] = vfrag(it - 1, 0, 0); va[1] = vfrag(it - 1, 0, 1); }
+        }
+        if constexpr (dma) {
+          if ((kk & 3) == 1 && (kk >> 2) < F::dma) dma_piece(t, kk >> 2, tile0 + it + 2);
+        }
+        const int n = kk + 1;  // operand of the next MFMA
+        if (n < 32) {
+          const u32x4& c = raw[(n >> 1) & 3];
+          af = (n & 1) ? fp8x8_to_bf16(c[2], c[3], ksc) : fp8x8_to_bf16(c[0], c[1], ksc);
+        } else if (n < 36) {
+          af = __builtin_bit_cast(bf16x8, raw[n - 32]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      mfma_result_fence(S);
+      __builtin_amdgcn_sched_barrier(0);
+      return S;
+    }
     const char* tb = lds + (it & (kStages - 1)) * kStageBytes;
     DmaTarget t{nullptr, 0u};
     if constexpr (dma) t = dma_target(tile0 + it + 2, (it + 2) & (kStages - 1));
@@ -396,7 +579,7 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
         if (kk == 35) { va[0] = vfrag(it - 1, 0, 0); va[1] = vfrag(it - 1, 0, 1); }
       }
       if constexpr (dma) {
-        if ((kk & 3) == 1) dma16<kStream>(t.src, dma_off[kk >> 2], t.dst + (kk >> 2) * (kThreads * 16));
+        if ((kk & 3) == 1) dma_piece(t, kk >> 2, tile0 + it + 2);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -452,9 +635,27 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
       l_run += xs[r + e];
     }
   };
-  auto sm_pack = [&]() {
+  // 8-bit: P' = P * (scale of the token), exact since the scale is a power of
+  // two; the lane's tokens 8q + 4g + e (q, e < 4) have their scales in four
+  // 16-byte runs. Scales of rows past the visible length are not data.
+  auto sm_pack = [&](int it) {
+    if constexpr (kFp8) {
+      const char* sb = lds + (it & (kStages - 1)) * F::bytes + kStage8Scale + 16 * g;
+      const int vlim = t_end - (tile0 + it) * kTok - 4 * g;   // >= 32 except in the tail tile
 #pragma unroll
-    for (int r = 0; r < 16; ++r) pb[r >> 3][r & 7] = (__bf16)xs[r];
+      for (int q = 0; q < 4; ++q) {
+        f32x4 sc = *reinterpret_cast<const f32x4*>(sb + 32 * q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * q + e;
+          pb[r >> 3][r & 7] = (__bf16)(xs[r] * ((8 * q + e) < vlim ? sc[e] : 0.f));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pb[r >> 3][r & 7] = (__bf16)xs[r];
+    }
   };
   auto sm_publish = [&](int it) {
     char* ps = pbuf + ((it & 1) * 8 + wave * 2) * 1024 + lane * 16;
@@ -472,7 +673,7 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
     sm_ref(over);
     sm_exp(0);
     sm_exp(8);
-    sm_pack();
+    sm_pack(it);
     sm_publish(it);
     MLA_FENCE();
   };
@@ -491,7 +692,7 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
     va[2] = vfrag(ip, 1, 1);
     MLA_FENCE();
     sm_exp(8);             mm4(0, va[1], pf); va[0] = vfrag(ip, 1, 2); interleave<4>(); MLA_FENCE();
-    sm_pack();             mm4(1, va[2], pf); va[1] = vfrag(ip, 1, 3); interleave<2>(); MLA_FENCE();
+    sm_pack(it);           mm4(1, va[2], pf); va[1] = vfrag(ip, 1, 3); interleave<2>(); MLA_FENCE();
     sm_publish(it);        mm4(2, va[0], pf); MLA_FENCE();
     // mm4(3, va[1], pf) of PV(ip) runs at the start of the next QK
   };
@@ -513,9 +714,16 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
   auto zero_tail = [&](int it) {
     const int valid = t_end - (tile0 + it) * kTok;
     if (valid < kTok) {
-      char* tb = lds + (it & (kStages - 1)) * kStageBytes;
-      for (int q = tid; q < (kTok - valid) * (kRowBytes / 16); q += kThreads)
-        *reinterpret_cast<f32x4*>(tb + valid * kRowBytes + q * 16) = f32x4{};
+      char* tb = lds + (it & (kStages - 1)) * F::bytes;
+      if constexpr (kFp8) {
+        // code rows only: k_R rows feed scores that are masked, and scales are
+        // masked where P is formed
+        for (int q = tid; q < (kTok - valid) * (kDc / 16); q += kThreads)
+          *reinterpret_cast<f32x4*>(tb + valid * kDc + q * 16) = f32x4{};
+      } else {
+        for (int q = tid; q < (kTok - valid) * (kRowBytes / 16); q += kThreads)
+          *reinterpret_cast<f32x4*>(tb + valid * kRowBytes + q * 16) = f32x4{};
+      }
     }
   };
 
@@ -553,7 +761,8 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
         const bf16x8* qa = reinterpret_cast<const bf16x8*>(q_abs + (qbase + wave * 32 + (ql & 31)) * kDc);
         const bf16x8* qr = reinterpret_cast<const bf16x8*>(q_r + (qbase + wave * 32 + (ql & 31)) * kDr);
 #pragma unroll
-        for (int kk = 0; kk < 32; ++kk) qf[kk] = qa[2 * kk + (ql >> 5)];
+        for (int kk = 0; kk < 32; ++kk)  // 8-bit: dims 32(kk>>1) + 16g + 8(kk&1) .. +7, as the code reads
+          qf[kk] = kFp8 ? qa[4 * (kk >> 1) + 2 * (ql >> 5) + (kk & 1)] : qa[2 * kk + (ql >> 5)];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) qf[32 + kk] = qr[2 * kk + (ql >> 5)];
         wait_vmcnt<0>();
@@ -573,7 +782,7 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
 #pragma unroll
         for (int k = 0; k < 4; ++k) pf[k] = bf16x8{};
 #pragma unroll
-        for (int k = 0; k < 3; ++k) va[k] = bf16x8{};
+        for (int k = 0; k < 3; ++k) va[k] = VFrag{};
 
         if (n_tiles > 0) {
           // Iteration j issues DMA(j+2) inside its QK phase (only for tiles that
@@ -585,7 +794,7 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
             if (n_tiles > 1) issue(tile0 + 1, 1);
           }
           // tile 0: QK + softmax only
-          if (n_tiles > 1) wait_vmcnt<kDmaPerThread>(); else wait_vmcnt<0>();
+          if (n_tiles > 1) wait_vmcnt<F::dma>(); else wait_vmcnt<0>();
           tile_barrier();
           zero_tail(0);
           if (n_tiles > 2)
@@ -596,13 +805,13 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
           // last two tiles issue no further DMA
           int it = 1;
           for (; it + 2 < n_tiles; ++it) {
-            wait_vmcnt<kDmaPerThread>();
+            wait_vmcnt<F::dma>();
             tile_barrier();
             zero_tail(it);
             softmax_pv(it, over, std::true_type{});
           }
           for (; it < n_tiles; ++it) {
-            if (it + 1 < n_tiles) wait_vmcnt<kDmaPerThread>(); else wait_vmcnt<0>();
+            if (it + 1 < n_tiles) wait_vmcnt<F::dma>(); else wait_vmcnt<0>();
             tile_barrier();
             zero_tail(it);
             softmax_pv(it, over, std::false_type{});
@@ -690,11 +899,21 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(
 
 hipError_t launch_decode_paged(const DecodeParams& p, hipStream_t stream) {
   if (p.s_q == 1)
-    hipLaunchKernelGGL(decode_paged_kernel<true>, dim3(kScanGroups), dim3(kThreads), 0, stream, p.q_abs, p.q_r,
-                       p.kv, p.block_table, p.seqlens, p.o_part, p.lse_part, p);
+    hipLaunchKernelGGL((decode_paged_kernel<true, false>), dim3(kScanGroups), dim3(kThreads), 0, stream, p.q_abs,
+                       p.q_r, p.kv, p.block_table, p.seqlens, p.o_part, p.lse_part, p);
   else
-    hipLaunchKernelGGL(decode_paged_kernel<false>, dim3(kScanGroups), dim3(kThreads), 0, stream, p.q_abs, p.q_r,
-                       p.kv, p.block_table, p.seqlens, p.o_part, p.lse_part, p);
+    hipLaunchKernelGGL((decode_paged_kernel<false, false>), dim3(kScanGroups), dim3(kThreads), 0, stream, p.q_abs,
+                       p.q_r, p.kv, p.block_table, p.seqlens, p.o_part, p.lse_part, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_paged_fp8(const DecodeParams& p, hipStream_t stream) {
+  if (p.s_q == 1)
+    hipLaunchKernelGGL((decode_paged_kernel<true, true>), dim3(kScanGroups), dim3(kThreads), 0, stream, p.q_abs,
+                       p.q_r, p.kv, p.block_table, p.seqlens, p.o_part, p.lse_part, p);
+  else
+    hipLaunchKernelGGL((decode_paged_kernel<false, true>), dim3(kScanGroups), dim3(kThreads), 0, stream, p.q_abs,
+                       p.q_r, p.kv, p.block_table, p.seqlens, p.o_part, p.lse_part, p);
   return hipGetLastError();
 }
 

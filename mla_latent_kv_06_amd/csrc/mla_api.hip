@@ -10,6 +10,7 @@
 #include "../../include/mla.h"
 #include "append.hpp"
 #include "decode.hpp"
+#include "fp8_cache.hpp"
 #include "prefill.hpp"
 #include "validate.hpp"
 
@@ -29,6 +30,31 @@ mla_status report_hip(hipError_t e, const char* what) {
 }
 
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+mla_status decode_paged_any(const void* q_abs, const void* q_r, const void* kv_cache, int64_t num_pages,
+                            const int32_t* block_table, int max_pages, const int32_t* seqlens, int B, int s_q, int H,
+                            float softmax_scale, int num_splits, float* o_part, float* lse_part, void* stream,
+                            bool fp8) {
+  const mla::Check c = mla::check_decode(q_abs, q_r, kv_cache, num_pages, block_table, max_pages, seqlens, B, s_q, H,
+                                         softmax_scale, num_splits, o_part, lse_part);
+  if (!c.ok()) return report(c);
+  mla::DecodeParams p{};
+  p.q_abs = static_cast<const __bf16*>(q_abs);
+  p.q_r = static_cast<const __bf16*>(q_r);
+  p.kv = static_cast<const char*>(kv_cache);
+  p.num_pages = num_pages;
+  p.block_table = block_table;
+  p.max_pages = max_pages;
+  p.seqlens = seqlens;
+  p.B = B;
+  p.s_q = s_q;
+  p.num_splits = num_splits;
+  p.scale_log2 = softmax_scale * 1.44269504088896340736f;
+  p.o_part = o_part;
+  p.lse_part = lse_part;
+  if (fp8) return report_hip(mla::launch_decode_paged_fp8(p, as_stream(stream)), "mla_decode_paged_fp8 launch");
+  return report_hip(mla::launch_decode_paged(p, as_stream(stream)), "mla_decode_paged launch");
+}
 
 }  // namespace
 
@@ -72,24 +98,38 @@ mla_status mla_decode_paged(const void* q_abs, const void* q_r, const void* kv_c
                             const int32_t* block_table, int max_pages, const int32_t* seqlens, int B, int s_q,
                             int H, float softmax_scale, int num_splits, float* o_part, float* lse_part,
                             void* stream) {
-  const mla::Check c = mla::check_decode(q_abs, q_r, kv_cache, num_pages, block_table, max_pages, seqlens, B, s_q, H,
-                                         softmax_scale, num_splits, o_part, lse_part);
+  return decode_paged_any(q_abs, q_r, kv_cache, num_pages, block_table, max_pages, seqlens, B, s_q, H, softmax_scale,
+                          num_splits, o_part, lse_part, stream, false);
+}
+
+
+mla_status mla_decode_paged_fp8(const void* q_abs, const void* q_r, const void* kv_fp8, int64_t num_pages,
+                                const int32_t* block_table, int max_pages, const int32_t* seqlens, int B, int s_q,
+                                int H, float softmax_scale, int num_splits, float* o_part, float* lse_part,
+                                void* stream) {
+  return decode_paged_any(q_abs, q_r, kv_fp8, num_pages, block_table, max_pages, seqlens, B, s_q, H, softmax_scale,
+                          num_splits, o_part, lse_part, stream, true);
+}
+
+mla_status mla_quantize_cache_fp8(const void* kv_cache, int64_t num_pages, void* kv_fp8, void* stream) {
+  const mla::Check c = mla::check_quantize_cache(kv_cache, num_pages, kv_fp8);
   if (!c.ok()) return report(c);
-  mla::DecodeParams p{};
-  p.q_abs = static_cast<const __bf16*>(q_abs);
-  p.q_r = static_cast<const __bf16*>(q_r);
-  p.kv = static_cast<const char*>(kv_cache);
-  p.num_pages = num_pages;
-  p.block_table = block_table;
-  p.max_pages = max_pages;
-  p.seqlens = seqlens;
-  p.B = B;
-  p.s_q = s_q;
-  p.num_splits = num_splits;
-  p.scale_log2 = softmax_scale * 1.44269504088896340736f;
-  p.o_part = o_part;
-  p.lse_part = lse_part;
-  return report_hip(mla::launch_decode_paged(p, as_stream(stream)), "mla_decode_paged launch");
+  return report_hip(mla::launch_quantize_cache_fp8(static_cast<const char*>(kv_cache), num_pages,
+                                                   static_cast<char*>(kv_fp8), as_stream(stream)),
+                    "mla_quantize_cache_fp8 launch");
+}
+
+mla_status mla_append_latent_fp8(const void* c_new, const void* kr_new, const float* rope, int max_pos, void* kv_fp8,
+                                 int64_t num_pages, const int32_t* block_table, int max_pages, const int32_t* seqlens,
+                                 int B, int s_q, void* stream) {
+  const mla::Check c = mla::check_append(c_new, kr_new, rope, max_pos, kv_fp8, num_pages, block_table, max_pages,
+                                         seqlens, B, s_q);
+  if (!c.ok()) return report(c);
+  return report_hip(mla::launch_append_latent_fp8(static_cast<const __bf16*>(c_new),
+                                                  static_cast<const __bf16*>(kr_new), rope, max_pos,
+                                                  static_cast<char*>(kv_fp8), num_pages, block_table, max_pages,
+                                                  seqlens, B, s_q, as_stream(stream)),
+                    "mla_append_latent_fp8 launch");
 }
 
 mla_status mla_combine_splits(const float* o_part, const float* lse_part, int B, int s_q, int H, int num_splits,

@@ -145,6 +145,13 @@ inline Check check_append(const void* c_new, const void* kr_new, const void* rop
   return Check{};
 }
 
+inline Check check_quantize_cache(const void* kv, int64_t num_pages, const void* out) {
+  MLA_TRY(need_ptr(kv, "kv_cache"));
+  MLA_TRY(need_ptr(out, "kv_fp8"));
+  MLA_TRY(need_range(num_pages, 1, (1LL << 26), "num_pages"));
+  return Check{};
+}
+
 inline Check check_rope_q(const void* q_r, const void* rope, int max_pos, const void* seqlens, int B, int s_q,
                           int H) {
   MLA_TRY(need_ptr(q_r, "q_r"));
