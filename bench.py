@@ -33,6 +33,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 FLOP_PER_PAIR = 128 * 2 * (576 + 512)  # all heads, one (query, key) pair: QK over 576 + PV over 512
 KV_BYTES_PER_TOKEN = 576 * 2
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_paged_long_hbm_traffic.json")
+FP8_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_paged_fp8_long_hbm_traffic.json")
 
 
 def parse():
@@ -51,6 +52,9 @@ def parse():
                    help="run mla_combine_splits and mla_up_proj as two kernels instead of mla_combine_up_proj")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle time for the baseline")
     p.add_argument("--no-fp8", action="store_true", help="skip the 8-bit cache leg")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only copy 1 GiB device to device three times (the known-size reference for "
+                        "rocprofv3 FETCH_SIZE / WRITE_SIZE) and exit")
     return p.parse_args()
 
 
@@ -63,23 +67,24 @@ def visible_pairs(seqlens, s_q):
     return tot
 
 
-def kernel_source_digest():
+def kernel_source_digest(fp8=False):
     h = hashlib.sha256()
-    for f in ("decode.hip", "mla_device.hpp", "decode.hpp"):
+    for f in ("decode.hip", "mla_device.hpp", "decode.hpp") + (("fp8_cache.hpp",) if fp8 else ()):
         with open(os.path.join(ROOT, "mla_latent_kv_06_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload, splits):
+def measured_traffic(workload, splits, fp8=False):
     """HBM bytes per decode launch from committed rocprofv3 counter runs, if they
     were taken on the current kernel source and launch configuration."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(FP8_TRAFFIC_FILE if fp8 else TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_digest") != kernel_source_digest() or t.get("workload") != workload or t.get("splits") != splits:
+    if (t.get("kernel_digest") != kernel_source_digest(fp8) or t.get("workload") != workload
+            or t.get("splits") != splits):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -207,7 +212,7 @@ FP8_BYTES_PER_TOKEN = 512 + 64 * 2 + 4   # E4M3 codes, bf16 k_R, fp32 scale
 
 
 def time_fp8_cache(M, torch, kv, tables, seqlens, lens, q_c, q_r, w_uk, w_uv, S, layers, steps, warmup,
-                   flop_step, flop_attn, q_bytes, olat_bytes):
+                   flop_step, flop_attn, q_bytes, olat_bytes, workload):
     """The same step over the 8-bit cache: every resident layer converted once
     (mla_quantize_cache_fp8), then absorb -> mla_decode_paged_fp8 ->
     mla_combine_up_proj, rotating through the layers as the main loop does."""
@@ -263,6 +268,7 @@ def time_fp8_cache(M, torch, kv, tables, seqlens, lens, q_c, q_r, w_uk, w_uv, S,
         "decode_roofline": {"bound": "hbm", "achieved": round(dec_bytes / (dec_ms * 1e-3) / 1e9, 1),
                             "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": round(dec_bytes / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                            "traffic": measured_traffic(workload, S, fp8=True),
                             "algorithmic_bytes_per_launch": dec_bytes,
                             "decode_tflops": round(flop_attn / (dec_ms * 1e-3) / 1e12, 1),
                             "mfma_frac": round(flop_attn / (dec_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
@@ -277,6 +283,17 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        n = 1 << 30
+        a = torch.empty(n // 4, dtype=torch.float32, device="cuda")
+        a.fill_(1.0)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(f"[bench] copied {n} bytes three times", file=sys.stderr, flush=True)
+        return
     import mla_latent_kv_06_amd as M
     from mla_inputs import CONFIGS, make_inputs, make_structure, make_cache_on_device
 
@@ -407,7 +424,7 @@ def main():
         print("[bench] 8-bit cache: convert the resident layers, time the same steps", file=sys.stderr, flush=True)
         result["next_rows"]["fp8_cache"] = time_fp8_cache(
             M, torch, kv, tables, seqlens, lens, q_c, q_r, w_uk, w_uv, S, layers, args.steps, args.warmup,
-            flop_step, flop_attn, q_bytes, olat_bytes)
+            flop_step, flop_attn, q_bytes, olat_bytes, cfg.name)
     if s_q > 1:
         # the decompressed branch the dispatch rule would take above 256 new
         # tokens, timed at this chunk length for comparison with the step
