@@ -370,6 +370,24 @@ def main():
     names = (["mla_absorb_q", "mla_decode_paged", "mla_combine_splits", "mla_up_proj"] if sep else
              ["mla_absorb_q", "mla_decode_paged", "mla_combine_up_proj"])
 
+    # the same steps launched from a HIP graph (one captured step per resident
+    # layer, replayed): the step without host launch overhead, as a serving
+    # loop that captures it would run it
+    n_cap = min(layers, 64)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for k in range(n_cap):
+            step(k)
+    graph.replay()
+    torch.cuda.synchronize()
+    reps = max(1, -(-args.steps // n_cap))
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        graph.replay()
+    torch.cuda.synchronize()
+    graph_ms = (time.perf_counter() - t0) / (reps * n_cap) * 1e3
+    del graph
+
     pairs = visible_pairs(lens, s_q)
     flop_attn = pairs * FLOP_PER_PAIR
     flop_proj = 2 * (2 * T * 128 * 128 * 512)
@@ -402,6 +420,7 @@ def main():
                    "heads": 128, "d_c": 512, "d_R": 64, "page": 64, "num_splits": S,
                    "resident_layers": layers, "cache_gb": round(layers * layer_bytes / 1e9, 2)},
         "kv_gbps": round(kv_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "graph_ms_per_step": round(graph_ms, 4),
         "step_roofline_frac": round(t_roof / (ms_step * 1e-3), 4),
         "kernels_ms": {n: round(a, 4) for n, a in zip(names, avg)},
         "roofline": {

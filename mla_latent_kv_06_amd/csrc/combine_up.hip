@@ -7,15 +7,17 @@
 // Workgroup = (head h, tile of R = 8 or 16 query rows t), 8 waves:
 //   * merge: wave w merges rows t0 + w (and t0 + w + 8 when R = 16) as
 //     combine_kernel does (split weights by readlane, the loads of up to 24
-//     splits in flight, empty splits never read) into an fp32 tile in LDS.
+//     splits in flight (16 with 8-row tiles), empty splits never read) into an
+//     fp32 tile in LDS; the split LSEs are read once.
 //     Lane l owns
 //     latent columns 4l..4l+3 and 256+4l..+3, so every load instruction covers
 //     1 KiB of contiguous memory;
-//   * W_UV[h] fragments (output rows 16w..16w+15, all 512 latent columns) are
-//     requested after the merge loads, so the merge waits only on its own
-//     data and the weight loads overlap the LDS write and the barrier (the
-//     workgroups of one head are 128 apart in the grid, hence on the same
-//     XCD, and share W_UV[h] through its L2);
+//   * W_UV[h] fragments (output rows 16w..16w+15, all 512 latent columns):
+//     with 16-row tiles requested after the merge loads, so the merge waits
+//     only on its own data and the weight loads overlap the LDS write and the
+//     barrier; with 8-row tiles (few rows, latency-bound) requested first.
+//     The workgroups of one head are 128 apart in the grid, hence on the same
+//     XCD, and share W_UV[h] through its L2;
 //   * up-projection: out^T[d, t] = sum_c W_UV[h][d][c] o_lat[t][c] on
 //     v_mfma_f32_16x16x32_bf16 (16 rows d x 16 columns t, of which the tile's
 //     R are real, x 32 latent columns c), the fp32 o_lat fed as a bf16 high
@@ -65,6 +67,18 @@ __global__ __launch_bounds__(512) void combine_up_kernel(const float* __restrict
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q = lane >> 4, r = lane & 15;
 
+  // W_UV[h] rows d = 16w + r, columns 32ks + 8q .. +7 for k-steps ks = 0..15.
+  // With 8-row tiles (few rows: each load round is latency, not bandwidth)
+  // they are requested first, so their latency overlaps the merge's; with
+  // 16-row tiles after the merge loads, so the merge waits only on its own data.
+  bf16x8 a[16];
+  auto load_w = [&]() {
+    const bf16x8* wp = reinterpret_cast<const bf16x8*>(w_uv + ((int64_t)h * kDhc + 16 * wave + r) * kDc + 8 * q);
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) a[ks] = wp[4 * ks];
+  };
+  if constexpr (kRows == 8) load_w();
+
   // ---- merge rows t0 + w (+ 8) into LDS rows w (+ 8); zeros past the end,
   // never stored
   for (int rr = wave; rr < kTileCols; rr += 8) {
@@ -74,31 +88,37 @@ __global__ __launch_bounds__(512) void combine_up_kernel(const float* __restrict
       const int64_t row = (int64_t)tm * kH + h;
       const float* lp = lse_part + row * num_splits;
       const float* op = o_part + row * num_splits * kDc + 4 * lane;
-      float M = -INFINITY;
-      for (int s = lane; s < num_splits; s += 64) M = fmaxf(M, lp[s]);
+      // up to 64 splits: one load round, lane s holding lse_s for the max, the
+      // sum and the weights
+      const float l0 = lane < num_splits ? lp[lane] : -INFINITY;
+      float M = l0;
+      for (int s = lane + 64; s < num_splits; s += 64) M = fmaxf(M, lp[s]);
       M = wave_max_f(M);
       float L = -INFINITY;
       if (M != -INFINITY) {
-        float tot = 0.f;
-        for (int s = lane; s < num_splits; s += 64) tot += expf(lp[s] - M);
+        float tot = expf(l0 - M);
+        for (int s = lane + 64; s < num_splits; s += 64) tot += expf(lp[s] - M);
         L = M + logf(wave_sum_f(tot));
-        f32x4v v0[kMergeChunk], v1[kMergeChunk];
+        // 8-row tiles hold W_UV's fragments during the merge: 16 splits in flight
+        constexpr int kChunk = kRows == 8 ? 16 : kMergeChunk;
+        f32x4v v0[kChunk], v1[kChunk];
         for (int b0 = 0; b0 < num_splits; b0 += 64) {  // blocks of 64 splits: lane k holds the weight of b0 + k
           const int b1 = min(num_splits, b0 + 64);
-          const float wl = b0 + lane < num_splits ? expf(lp[b0 + lane] - L) : 0.f;  // 0 when lse = -inf
+          const float lb = b0 == 0 ? l0 : (b0 + lane < num_splits ? lp[b0 + lane] : -INFINITY);
+          const float wl = expf(lb - L);  // 0 when lse = -inf
           auto weight = [&](int s) {
             return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), s - b0));
           };
-          for (int s0 = b0; s0 < b1; s0 += kMergeChunk) {
+          for (int s0 = b0; s0 < b1; s0 += kChunk) {
 #pragma unroll
-            for (int k = 0; k < kMergeChunk; ++k) {
+            for (int k = 0; k < kChunk; ++k) {
               if (s0 + k < b1 && weight(s0 + k) > 0.f) {
                 v0[k] = *reinterpret_cast<const f32x4v*>(op + (int64_t)(s0 + k) * kDc);
                 v1[k] = *reinterpret_cast<const f32x4v*>(op + (int64_t)(s0 + k) * kDc + kDc / 2);
               }
             }
 #pragma unroll
-            for (int k = 0; k < kMergeChunk; ++k) {
+            for (int k = 0; k < kChunk; ++k) {
               if (s0 + k < b1) {
                 const float w = weight(s0 + k);
                 if (w > 0.f) {
@@ -117,13 +137,7 @@ __global__ __launch_bounds__(512) void combine_up_kernel(const float* __restrict
     *reinterpret_cast<f32x4v*>(dst + kDc / 2) = a1;
   }
 
-  // W_UV[h] rows d = 16w + r, columns 32ks + 8q .. +7 for k-steps ks = 0..15
-  bf16x8 a[16];
-  {
-    const bf16x8* wp = reinterpret_cast<const bf16x8*>(w_uv + ((int64_t)h * kDhc + 16 * wave + r) * kDc + 8 * q);
-#pragma unroll
-    for (int ks = 0; ks < 16; ++ks) a[ks] = wp[4 * ks];
-  }
+  if constexpr (kRows == 16) load_w();
 
   __syncthreads();
 
