@@ -12,7 +12,8 @@ Prints one JSON line (rank 0):
   roofline         the dominant kernel (mla_decode_paged) against HBM
   cpu_baseline     the fp64 CPU oracle on a bounded sample of the workload
 plus effective KV GB/s, per-kernel times and, under next_rows, the cache
-append and query rotation, the same step over the 8-bit cache
+append and query rotation, the step as one launch (mla_decode_step) against
+the four kernels it fuses, the same step over the 8-bit cache
 (mla_decode_paged_fp8), and for chunks of s_q > 1 the decompressed branch.
 """
 from __future__ import annotations
@@ -275,6 +276,44 @@ def time_fp8_cache(M, torch, kv, tables, seqlens, lens, q_c, q_r, w_uk, w_uv, S,
     }
 
 
+def time_one_launch_step(M, torch, kv, tables, seqlens, q_c, q_r, w_uk, w_uv, S, layers, steps, warmup):
+    """mla_decode_step (one cooperative launch) against the four kernels it
+    fuses (mla_absorb_q, mla_decode_paged, mla_combine_splits, mla_up_proj),
+    same buffers, same layer rotation; wall-clock per step."""
+    B, s_q = q_c.shape[0], q_c.shape[1]
+    dev = q_c.device
+    buf = dict(q_abs=torch.empty((B, s_q, 128, 512), dtype=torch.bfloat16, device=dev),
+               o_part=torch.empty((B, s_q, 128, S, 512), dtype=torch.float32, device=dev),
+               lse_part=torch.empty((B, s_q, 128, S), dtype=torch.float32, device=dev),
+               o_lat=torch.empty((B, s_q, 128, 512), dtype=torch.float32, device=dev),
+               lse=torch.empty((B, s_q, 128), dtype=torch.float32, device=dev),
+               out=torch.empty((B, s_q, 128, 128), dtype=torch.bfloat16, device=dev))
+    def fused(k):
+        l = k % layers
+        M.mla_decode_step(q_c, q_r, kv[l], tables[l], seqlens, w_uk, w_uv, S, buffers=buf)
+
+    def four(k):
+        l = k % layers
+        M.mla_absorb_q(q_c, w_uk, buf["q_abs"])
+        M.mla_decode_paged(buf["q_abs"], q_r, kv[l], tables[l], seqlens, S, o_part=buf["o_part"],
+                           lse_part=buf["lse_part"])
+        M.mla_combine_splits(buf["o_part"], buf["lse_part"], buf["o_lat"], buf["lse"])
+        M.mla_up_proj(buf["o_lat"], w_uv, buf["out"])
+
+    res = {}
+    for name, fn in (("four_kernels_ms", four), ("one_launch_ms", fused)):
+        for k in range(warmup):
+            fn(k)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(steps):
+            fn(warmup + k)
+        torch.cuda.synchronize()
+        res[name] = round((time.perf_counter() - t0) / steps * 1e3, 4)
+    res["speedup"] = round(res["four_kernels_ms"] / res["one_launch_ms"], 3)
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -439,6 +478,9 @@ def main():
     # cache append + query rotation, timed after the step (they write into the
     # cache rows the step has already read)
     result["next_rows"] = time_next_rows(M, torch, kv, tables, seqlens, lens, B, s_q, layers)
+    print("[bench] one-launch step against the four kernels it fuses", file=sys.stderr, flush=True)
+    result["next_rows"]["one_launch_step"] = time_one_launch_step(
+        M, torch, kv, tables, seqlens, q_c, q_r, w_uk, w_uv, S, layers, args.steps, args.warmup)
     if not args.no_fp8:
         print("[bench] 8-bit cache: convert the resident layers, time the same steps", file=sys.stderr, flush=True)
         result["next_rows"]["fp8_cache"] = time_fp8_cache(

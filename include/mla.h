@@ -321,6 +321,39 @@ mla_status mla_decode_paged_fp8(const void* q_abs, const void* q_r,
                                 float softmax_scale, int num_splits,
                                 float* o_part, float* lse_part, void* stream);
 
+/* ---- the whole step in one launch ---------------------------------------
+ * mla_absorb_q -> mla_decode_paged -> mla_combine_splits -> mla_up_proj as the
+ * four phases of one cooperative kernel (256 workgroups, one per CU, separated
+ * by grid-wide barriers), for short contexts where the step is a chain of
+ * small dependent kernels. Results are bit-identical to that sequence of
+ * calls with the same arguments: q_abs, o_part/lse_part, o_lat/lse and out are
+ * all written.
+ *   q_c bf16 [B, s_q, H, 128], q_r bf16 [B, s_q, H, 64] (rotated)
+ *   kv_cache, num_pages, block_table, max_pages, seqlens, softmax_scale,
+ *       num_splits: as mla_decode_paged
+ *   w_uk, w_uv bf16 [H, 128, 512]
+ *   q_abs bf16 [B, s_q, H, 512], o_part fp32 [B, s_q, H, num_splits, 512],
+ *   lse_part fp32 [B, s_q, H, num_splits], o_lat fp32 [B, s_q, H, 512]:
+ *       caller-owned intermediates (written)
+ *   out bf16 [B, s_q, H, 128], lse fp32 [B, s_q, H]: the step's outputs
+ * Argument rules as mla_decode_paged, and B * s_q <= 2^20. Returns MLA_ERR_HIP
+ * if the device cannot hold all 256 workgroups at once (the launch is refused,
+ * nothing runs). */
+mla_status mla_decode_step(const void* q_c, const void* q_r, const void* kv_cache, int64_t num_pages,
+                           const int32_t* block_table, int max_pages, const int32_t* seqlens, int B, int s_q,
+                           int H, const void* w_uk, const void* w_uv, float softmax_scale, int num_splits,
+                           void* q_abs, float* o_part, float* lse_part, float* o_lat, void* out, float* lse,
+                           void* stream);
+
+/* mla_decode_step over the 8-bit cache (kv_fp8 uint8 [num_pages, 41216]);
+ * bit-identical to mla_absorb_q -> mla_decode_paged_fp8 -> mla_combine_splits
+ * -> mla_up_proj. */
+mla_status mla_decode_step_fp8(const void* q_c, const void* q_r, const void* kv_fp8, int64_t num_pages,
+                               const int32_t* block_table, int max_pages, const int32_t* seqlens, int B, int s_q,
+                               int H, const void* w_uk, const void* w_uv, float softmax_scale, int num_splits,
+                               void* q_abs, float* o_part, float* lse_part, float* o_lat, void* out, float* lse,
+                               void* stream);
+
 /* Test and debug aid: gather the logical cache rows of each sequence through
  * the block table with the same address arithmetic as mla_decode_paged.
  *   out bf16 [B, max_len, 576]: row t of sequence b is the cache row of token

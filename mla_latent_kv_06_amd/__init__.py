@@ -388,6 +388,46 @@ def decode_layer(q_c, q_r, kv_cache, block_table, seqlens, w_uk, w_uv, num_split
     return dict(q_abs=q_abs, o_part=o_part, lse_part=lse_part, o_lat=o_lat, lse=lse, out=out)
 
 
+def mla_decode_step(q_c, q_r, kv_cache, block_table, seqlens, w_uk, w_uv, num_splits: int,
+                    softmax_scale: float = DEFAULT_SCALE, buffers: dict | None = None, stream=None):
+    """The whole absorbed step in one launch (absorb -> scan -> merge -> up-projection),
+    bit-identical to decode_layer; kv_cache is the bf16 or the 8-bit cache.
+    Returns dict(q_abs, o_part, lse_part, o_lat, lse, out); ``buffers`` may
+    supply any of them preallocated."""
+    B, s_q = q_c.shape[0], q_c.shape[1]
+    S = int(num_splits)
+    dev = q_c.device
+    shapes = dict(q_abs=((B, s_q, H, D_C), torch.bfloat16), o_part=((B, s_q, H, S, D_C), torch.float32),
+                  lse_part=((B, s_q, H, S), torch.float32), o_lat=((B, s_q, H, D_C), torch.float32),
+                  lse=((B, s_q, H), torch.float32), out=((B, s_q, H, D_HC), torch.bfloat16))
+    buf = dict(buffers or {})
+    for k, (shape, dt) in shapes.items():
+        if k not in buf:
+            buf[k] = torch.empty(shape, dtype=dt, device=dev)
+        _need(buf[k], k, dt, shape)
+    _need(q_c, "q_c", torch.bfloat16, (B, s_q, H, D_HC))
+    _need(q_r, "q_r", torch.bfloat16, (B, s_q, H, D_R))
+    _need(w_uk, "w_uk", torch.bfloat16, (H, D_HC, D_C))
+    _need(w_uv, "w_uv", torch.bfloat16, (H, D_HC, D_C))
+    fp8 = is_fp8_cache(kv_cache)
+    if fp8:
+        _need_fp8_cache(kv_cache, "kv_cache")
+    else:
+        if kv_cache.dim() != 3 or kv_cache.shape[1:] != (PAGE, ROW):
+            raise ValueError(f"kv_cache must be [num_pages, 64, 576], got {tuple(kv_cache.shape)}")
+        _need(kv_cache, "kv_cache", torch.bfloat16)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError(f"block_table must be [B, max_pages], got {tuple(block_table.shape)}")
+    _need(block_table, "block_table", torch.int32)
+    _need(seqlens, "seqlens", torch.int32, (B,))
+    fn = _lib.LIB.mla_decode_step_fp8 if fp8 else _lib.LIB.mla_decode_step
+    _check(fn(_ptr(q_c), _ptr(q_r), _ptr(kv_cache), kv_cache.shape[0], _ptr(block_table), block_table.shape[1],
+              _ptr(seqlens), B, s_q, H, _ptr(w_uk), _ptr(w_uv), float(softmax_scale), S, _ptr(buf["q_abs"]),
+              _ptr(buf["o_part"]), _ptr(buf["lse_part"]), _ptr(buf["o_lat"]), _ptr(buf["out"]), _ptr(buf["lse"]),
+              _stream(stream)), "mla_decode_step_fp8" if fp8 else "mla_decode_step")
+    return buf
+
+
 def attention_layer(q_c, q_r, kv_cache, block_table, seqlens, w_uk, w_uv, max_len: int,
                     softmax_scale: float = DEFAULT_SCALE, num_splits: int | None = None, absorbed: bool | None = None,
                     stream=None):

@@ -12,6 +12,7 @@
 #include "decode.hpp"
 #include "fp8_cache.hpp"
 #include "prefill.hpp"
+#include "step.hpp"
 #include "validate.hpp"
 
 namespace {
@@ -54,6 +55,38 @@ mla_status decode_paged_any(const void* q_abs, const void* q_r, const void* kv_c
   p.lse_part = lse_part;
   if (fp8) return report_hip(mla::launch_decode_paged_fp8(p, as_stream(stream)), "mla_decode_paged_fp8 launch");
   return report_hip(mla::launch_decode_paged(p, as_stream(stream)), "mla_decode_paged launch");
+}
+
+mla_status decode_step_any(const void* q_c, const void* q_r, const void* kv_cache, int64_t num_pages,
+                           const int32_t* block_table, int max_pages, const int32_t* seqlens, int B, int s_q, int H,
+                           const void* w_uk, const void* w_uv, float softmax_scale, int num_splits, void* q_abs,
+                           float* o_part, float* lse_part, float* o_lat, void* out, float* lse, void* stream,
+                           bool fp8) {
+  const mla::Check c = mla::check_step(q_c, q_r, kv_cache, num_pages, block_table, max_pages, seqlens, B, s_q, H, w_uk,
+                                       w_uv, softmax_scale, num_splits, q_abs, o_part, lse_part, o_lat, out, lse);
+  if (!c.ok()) return report(c);
+  mla::StepParams p{};
+  p.d.q_abs = static_cast<const __bf16*>(q_abs);
+  p.d.q_r = static_cast<const __bf16*>(q_r);
+  p.d.kv = static_cast<const char*>(kv_cache);
+  p.d.num_pages = num_pages;
+  p.d.block_table = block_table;
+  p.d.max_pages = max_pages;
+  p.d.seqlens = seqlens;
+  p.d.B = B;
+  p.d.s_q = s_q;
+  p.d.num_splits = num_splits;
+  p.d.scale_log2 = softmax_scale * 1.44269504088896340736f;
+  p.d.o_part = o_part;
+  p.d.lse_part = lse_part;
+  p.q_c = static_cast<const __bf16*>(q_c);
+  p.w_uk = static_cast<const __bf16*>(w_uk);
+  p.w_uv = static_cast<const __bf16*>(w_uv);
+  p.o_lat = o_lat;
+  p.lse = lse;
+  p.out = static_cast<__bf16*>(out);
+  return report_hip(mla::launch_decode_step(p, fp8, as_stream(stream)),
+                    fp8 ? "mla_decode_step_fp8 launch" : "mla_decode_step launch");
 }
 
 }  // namespace
@@ -130,6 +163,23 @@ mla_status mla_append_latent_fp8(const void* c_new, const void* kr_new, const fl
                                                   static_cast<char*>(kv_fp8), num_pages, block_table, max_pages,
                                                   seqlens, B, s_q, as_stream(stream)),
                     "mla_append_latent_fp8 launch");
+}
+
+mla_status mla_decode_step(const void* q_c, const void* q_r, const void* kv_cache, int64_t num_pages,
+                           const int32_t* block_table, int max_pages, const int32_t* seqlens, int B, int s_q, int H,
+                           const void* w_uk, const void* w_uv, float softmax_scale, int num_splits, void* q_abs,
+                           float* o_part, float* lse_part, float* o_lat, void* out, float* lse, void* stream) {
+  return decode_step_any(q_c, q_r, kv_cache, num_pages, block_table, max_pages, seqlens, B, s_q, H, w_uk, w_uv,
+                         softmax_scale, num_splits, q_abs, o_part, lse_part, o_lat, out, lse, stream, false);
+}
+
+mla_status mla_decode_step_fp8(const void* q_c, const void* q_r, const void* kv_fp8, int64_t num_pages,
+                               const int32_t* block_table, int max_pages, const int32_t* seqlens, int B, int s_q,
+                               int H, const void* w_uk, const void* w_uv, float softmax_scale, int num_splits,
+                               void* q_abs, float* o_part, float* lse_part, float* o_lat, void* out, float* lse,
+                               void* stream) {
+  return decode_step_any(q_c, q_r, kv_fp8, num_pages, block_table, max_pages, seqlens, B, s_q, H, w_uk, w_uv,
+                         softmax_scale, num_splits, q_abs, o_part, lse_part, o_lat, out, lse, stream, true);
 }
 
 mla_status mla_combine_splits(const float* o_part, const float* lse_part, int B, int s_q, int H, int num_splits,

@@ -47,6 +47,15 @@ __device__ __forceinline__ const char* token_row(const char* __restrict__ kv, co
   return kv + page * kPageBytes + (int64_t)(t & (kPage - 1)) * kRowBytes;
 }
 
+// The lane id, recomputed where it is used: volatile asm, so the compiler
+// neither merges it with another lane-id computation (which would keep that
+// value live from one phase of a kernel into a much later one) nor hoists it.
+__device__ __forceinline__ int lane_opaque() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
 // vmcnt bits [3:0] and [15:14], expcnt [6:4] = 7, lgkmcnt [11:8] = 15).
 template <int N>

@@ -100,6 +100,22 @@ inline Check check_decode(const void* q_abs, const void* q_r, const void* kv, in
   return Check{};
 }
 
+inline Check check_step(const void* q_c, const void* q_r, const void* kv, int64_t num_pages, const void* bt,
+                        int max_pages, const void* seqlens, int B, int s_q, int H, const void* w_uk,
+                        const void* w_uv, float scale, int num_splits, const void* q_abs, const void* o_part,
+                        const void* lse_part, const void* o_lat, const void* out, const void* lse) {
+  MLA_TRY(need_ptr(q_c, "q_c"));
+  MLA_TRY(need_ptr(w_uk, "w_uk"));
+  MLA_TRY(need_ptr(w_uv, "w_uv"));
+  MLA_TRY(need_ptr(o_lat, "o_lat"));
+  MLA_TRY(need_ptr(out, "out"));
+  MLA_TRY(need_ptr(lse, "lse"));
+  MLA_TRY(check_decode(q_abs, q_r, kv, num_pages, bt, max_pages, seqlens, B, s_q, H, scale, num_splits, o_part,
+                       lse_part));
+  MLA_TRY(need_range((long long)B * s_q, 1, (1LL << 20), "B * s_q"));
+  return Check{};
+}
+
 inline Check check_combine(const void* o_part, const void* lse_part, int B, int s_q, int H,
                            int num_splits, const void* o_lat, const void* lse) {
   MLA_TRY(need_ptr(o_part, "o_part"));
