@@ -70,7 +70,7 @@ def visible_pairs(seqlens, s_q):
 
 def kernel_source_digest(fp8=False):
     h = hashlib.sha256()
-    for f in ("decode.hip", "mla_device.hpp", "decode.hpp") + (("fp8_cache.hpp",) if fp8 else ()):
+    for f in ("decode.hip", "decode_body.hpp", "mla_device.hpp", "decode.hpp") + (("fp8_cache.hpp",) if fp8 else ()):
         with open(os.path.join(ROOT, "mla_latent_kv_06_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
