@@ -132,16 +132,6 @@ __device__ __forceinline__ void mfma_qk_first(f32x16& d, const bf16x8& a, const 
 __device__ __forceinline__ void mfma_qk(f32x16& d, const bf16x8& a, const bf16x8& b) {
   asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
 }
-// The same chain when the A operand was just written by VALU (the 8-bit
-// path converts it in registers): an MFMA may read a VGPR that a VALU
-// instruction wrote only after 2 wait states, which the compiler does not
-// insert in front of inline asm; 3 are given.
-__device__ __forceinline__ void mfma_qk8_first(f32x16& d, const bf16x8& a, const bf16x8& b) {
-  asm("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma_qk8(f32x16& d, const bf16x8& a, const bf16x8& b) {
-  asm("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
-}
 // VALU may read an MFMA result only after the MFMA has drained (at most
 // 16 passes + 2 on CDNA; 24 wait states here). Tied to the value so no read
 // of it can be scheduled above the wait.
@@ -193,8 +183,99 @@ __device__ __forceinline__ void dma16(const char* sbase, unsigned voff, unsigned
 }
 
 typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2_t;
+
+// 8-bit path: one lane's 16 query values of a 32-dim block (the block's other
+// 16 are in lane l ^ 32) as two E4M3 terms with per-block power-of-two scales,
+// q = hi * 2^kh + lo * 2^kl. hi keeps the top 4 significant bits of each bf16
+// value (truncated, so the remainder has at most 4 significant bits and lo
+// holds it exactly unless it falls below lo's subnormal range, i.e. for
+// values under 2^-13 of the block's largest). Returns hi's 16 codes in h and
+// lo's in l (byte j of the 16 = value j) and the two scale exponents.
+__device__ __forceinline__ void split_block_fp8(const bf16x8& x0, const bf16x8& x1, u32x4& h, u32x4& l, int& kh,
+                                                int& kl) {
+  float v[16];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    v[j] = (float)x0[j];
+    v[8 + j] = (float)x1[j];
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) amax = fmaxf(amax, __builtin_fabsf(v[j]));
+  kh = fp8_scale_exponent(pair_max32(amax));
+  float r[16];
+#pragma unroll
+  for (int j = 0; j < 16; j += 2) {
+    const float t0 = __uint_as_float(__float_as_uint(v[j]) & 0xFFF00000u);
+    const float t1 = __uint_as_float(__float_as_uint(v[j + 1]) & 0xFFF00000u);
+    const int c = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_ldexpf(t0, -kh), __builtin_ldexpf(t1, -kh), 0, false);
+    const auto hv = __builtin_amdgcn_cvt_pk_f32_fp8(c, false);   // exact E4M3 values of the pair
+    r[j] = v[j] - __builtin_ldexpf(hv[0], kh);
+    r[j + 1] = v[j + 1] - __builtin_ldexpf(hv[1], kh);
+    const int w = (j >> 1);  // 16-bit piece of h
+    if ((w & 1) == 0)
+      h[w >> 1] = (unsigned)(c & 0xFFFF);
+    else
+      h[w >> 1] |= (unsigned)(c & 0xFFFF) << 16;
+  }
+  float rmax = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) rmax = fmaxf(rmax, __builtin_fabsf(r[j]));
+  kl = fp8_scale_exponent(pair_max32(rmax));
+#pragma unroll
+  for (int j = 0; j < 16; j += 4) {
+    int c = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_ldexpf(r[j], -kl), __builtin_ldexpf(r[j + 1], -kl), 0, false);
+    c = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_ldexpf(r[j + 2], -kl), __builtin_ldexpf(r[j + 3], -kl), c, true);
+    l[j >> 2] = (unsigned)c;
+  }
+}
+
+// E4M3 x E4M3 scaled MFMA (32x32x64) accumulating into d, which stays in
+// VGPRs (asm, as the bf16 QK chain): A's E8M0 scale is byte 0 of sa, B's is
+// byte kSel of sb (op_sel / op_sel_hi of the second scale operand). A comes
+// from LDS; the first MFMA of a tile carries the 2 wait states an MFMA needs
+// after a VALU write of a source (the tile's token scale), later ones chain on
+// the same d and need none.
+template <int kSel, bool kFirst>
+__device__ __forceinline__ void mfma_scaled_sel(f32x16& d, const i32x8& a, const i32x8& b, int sa, int sb) {
+  if constexpr (kFirst) {
+    if constexpr (kSel == 0)
+      asm("s_nop 1\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %3, %4" : "=&v"(d) : "v"(a), "v"(b), "v"(sa), "v"(sb));
+    else if constexpr (kSel == 1)
+      asm("s_nop 1\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %3, %4 op_sel:[0,1,0]"
+          : "=&v"(d) : "v"(a), "v"(b), "v"(sa), "v"(sb));
+    else if constexpr (kSel == 2)
+      asm("s_nop 1\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %3, %4 op_sel_hi:[0,1,0]"
+          : "=&v"(d) : "v"(a), "v"(b), "v"(sa), "v"(sb));
+    else
+      asm("s_nop 1\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %3, %4 op_sel:[0,1,0] op_sel_hi:[0,1,0]"
+          : "=&v"(d) : "v"(a), "v"(b), "v"(sa), "v"(sb));
+  } else {
+    if constexpr (kSel == 0)
+      asm("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4" : "+v"(d) : "v"(a), "v"(b), "v"(sa), "v"(sb));
+    else if constexpr (kSel == 1)
+      asm("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel:[0,1,0]"
+          : "+v"(d) : "v"(a), "v"(b), "v"(sa), "v"(sb));
+    else if constexpr (kSel == 2)
+      asm("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,1,0]"
+          : "+v"(d) : "v"(a), "v"(b), "v"(sa), "v"(sb));
+    else
+      asm("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel:[0,1,0] op_sel_hi:[0,1,0]"
+          : "+v"(d) : "v"(a), "v"(b), "v"(sa), "v"(sb));
+  }
+}
+template <bool kFirst>
+__device__ __forceinline__ void mfma_scaled(int sel, f32x16& d, const i32x8& a, const i32x8& b, int sa, int sb) {
+  switch (sel) {
+    case 0: mfma_scaled_sel<0, kFirst>(d, a, b, sa, sb); break;
+    case 1: mfma_scaled_sel<1, kFirst>(d, a, b, sa, sb); break;
+    case 2: mfma_scaled_sel<2, kFirst>(d, a, b, sa, sb); break;
+    default: mfma_scaled_sel<3, kFirst>(d, a, b, sa, sb); break;
+  }
+}
 
 __device__ __forceinline__ bf16x8 cat8(const i16x4& v0, const i16x4& v1) {
   const bf16x4 b0 = __builtin_bit_cast(bf16x4, v0);
@@ -237,10 +318,13 @@ __device__ __forceinline__ int wave_incl_scan32(int v, int lane) {
 }  // namespace
 
 // kFp8: the cache is the 8-bit layout of fp8_cache.hpp instead of bf16 rows.
-// Its codes are turned into bf16 operands in registers: a K fragment with the
-// lane's token scale in the same conversion, a V^T fragment (8 tokens of one
-// column, read transposed) at scale 1 with the tokens' scales folded into P
-// (P' = P * 2^k_t is exact), so the matrix work is the bf16 kernel's.
+// QK over the latent runs on the E4M3 block-scaled MFMA straight from the
+// codes (the token's scale as A's block scale); the query is held as two E4M3
+// terms, hi (each bf16 value truncated to 4 significant bits) and lo (the
+// remainder), with per-32-dim block scales, which reproduce it exactly except
+// for values under 2^-13 of their block's largest. PV converts a V^T fragment
+// (8 tokens of one column, read transposed) to bf16 at scale 1 and folds the
+// tokens' scales into P (P' = P * 2^k_t is exact).
 // The body of one scan workgroup (blockIdx.x is its range); lds points at
 // decode_lds_bytes<kFp8>() bytes of LDS aligned to 1024. It runs as its own
 // kernel (decode.hip) and as a phase of the fused step (step.hip).
@@ -346,11 +430,14 @@ __device__ __forceinline__ void decode_paged_body(
   int qk_off[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) qk_off[r] = lo * kRowBytes + (((2 * r + g) ^ swz(lo)) << 4);
-  // 8-bit: code chunk m = 4a + r (dims 32m + 16g .. +15, two MFMAs) of row lo
-  // at qk8_off[r] + 128a; k_R chunk 2r' + g at rope8_off + ((32 r') ^ rope8_x)
+  // 8-bit: the K operand of scaled MFMA m (latent dims 64m .. 64m + 63) is code
+  // chunks 4m + g (dims 64m + 16g .. +15, first K-block) and 4m + 2 + g (dims
+  // 64m + 32 + 16g .. +15, second K-block) of row lo, at
+  // qk8_off[2(m & 1) + p] + 128 (m >> 1) for p = 0, 1; k_R chunk 2r' + g at
+  // rope8_off + ((32 r') ^ rope8_x)
   int qk8_off[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) qk8_off[r] = lo * kDc + (((2 * r + g) ^ swz8(lo)) << 4);
+  for (int r = 0; r < 4; ++r) qk8_off[r] = lo * kDc + (((4 * (r >> 1) + 2 * (r & 1) + g) ^ swz8(lo)) << 4);
   const int rope8_off = kStage8Rope + lo * (kDr * 2);
   const int rope8_x = (g ^ (lo & 7)) << 4;
   // PV A operand (V^T) for this wave's columns 128w + 32c' through transposed
@@ -450,7 +537,11 @@ __device__ __forceinline__ void decode_paged_body(
     for (int k = 0; k < F::dma; ++k) dma_piece(t, k, tile);
   };
 
-  bf16x8 qf[36];  // queries of the current piece
+  bf16x8 qf[36];  // queries of the current piece (8-bit path: only the k_R part, qf[32..35])
+  // 8-bit: the B operands of scaled MFMA m, hi codes in qhl[2m] and lo codes in
+  // qhl[2m+1], and byte m & 3 of qsh / qsl [m >> 2] their E8M0 scales
+  i32x8 qhl[16];
+  int qsh[2] = {0, 0}, qsl[2] = {0, 0};
 
   const float c_log2 = a.scale_log2;
   f32x16 O[4][4];            // O^T tiles [column tile c'][head tile ht]
@@ -505,52 +596,54 @@ __device__ __forceinline__ void decode_paged_body(
     constexpr bool dma = decltype(dma_tag)::value;
     constexpr bool pv = decltype(pv_tag)::value;  // prefetch PV(it-1) operands
     if constexpr (kFp8) {
-      // 8-bit: MFMA kk < 32 takes half kk&1 of code chunk kk>>1, converted with
-      // the lane's token scale; MFMAs 32..35 take the bf16 k_R fragments.
-      // Chunk m >= 3 is read after MFMA 2m - 5 into slot m & 3 (free since its
-      // chunk m - 4 was converted), four MFMAs before its first conversion;
-      // k_R fragment r goes to slot r after MFMA 27 + r (r < 3) or 31 (r = 3).
+      // 8-bit: the latent part runs on v_mfma_scale_f32_32x32x64_f8f6f4 straight
+      // from the codes: A = 64 dims of the tile's K codes with the token's own
+      // E8M0 scale, B = the same dims of the query's hi and lo code terms with
+      // their per-32-dim block scales (two MFMAs per 64 dims, the time of the
+      // four bf16 MFMAs they replace, and no conversion of K); then the four
+      // bf16 MFMAs of k_R. K operands are read one MFMA pair ahead.
       const char* tb = lds + (it & (kStages - 1)) * F::bytes;
       DmaTarget t{nullptr, 0u};
       if constexpr (dma) t = dma_target(tile0 + it + 2, (it + 2) & (kStages - 1));
-      const float ksc = *reinterpret_cast<const float*>(tb + kStage8Scale + lo * 4);
-      u32x4 raw[4];
-#pragma unroll
-      for (int m = 0; m < 3; ++m) raw[m] = *reinterpret_cast<const u32x4*>(tb + qk8_off[m]);
+      // the token's scale 2^k as its E8M0 byte k + 127 (the exponent field)
+      const int kscale = (int)(__float_as_uint(*reinterpret_cast<const float*>(tb + kStage8Scale + lo * 4)) >> 23);
+      auto kread = [&](int m) -> i32x8 {
+        const u32x4 c0 = *reinterpret_cast<const u32x4*>(tb + qk8_off[2 * (m & 1)] + 128 * (m >> 1));
+        const u32x4 c1 = *reinterpret_cast<const u32x4*>(tb + qk8_off[2 * (m & 1) + 1] + 128 * (m >> 1));
+        return i32x8{(int)c0[0], (int)c0[1], (int)c0[2], (int)c0[3], (int)c1[0], (int)c1[1], (int)c1[2], (int)c1[3]};
+      };
+      i32x8 ka[2];
+      ka[0] = kread(0);
       __builtin_amdgcn_sched_barrier(0);
       mm4(3, va[1], pf);  // deferred tail of the previous PV
       __builtin_amdgcn_sched_barrier(0);
       f32x16 S;
-      bf16x8 af = fp8x8_to_bf16(raw[0][0], raw[0][1], ksc);
 #pragma unroll
-      for (int kk = 0; kk < 36; ++kk) {
-        if (kk == 0)
-          mfma_qk8_first(S, af, qf[0]);
+      for (int m = 0; m < 8; ++m) {
+        if (m + 1 < 8) ka[(m + 1) & 1] = kread(m + 1);  // one MFMA pair ahead
+        if (m == 0)
+          mfma_scaled<true>(m & 3, S, ka[m & 1], qhl[2 * m], kscale, qsh[m >> 2]);
         else
-          mfma_qk8(S, af, qf[kk]);
-        if ((kk & 1) && kk <= 25) {
-          const int m = (kk + 5) >> 1;
-          raw[m & 3] = *reinterpret_cast<const u32x4*>(tb + qk8_off[m & 3] + 128 * (m >> 2));
-        }
-        if (kk >= 27 && kk <= 29) {
-          const int r = kk - 27;
-          raw[r] = *reinterpret_cast<const u32x4*>(tb + rope8_off + ((32 * r) ^ rope8_x));
-        }
-        if (kk == 31) raw[3] = *reinterpret_cast<const u32x4*>(tb + rope8_off + (96 ^ rope8_x));
-        if constexpr (pv) {
-          if (kk == 33) { pf[0] = pfrag(it - 1, 0, 0); pf[1] = pfrag(it - 1, 0, 1); }
-          if (kk == 34) { pf[2] = pfrag(it - 1, 0, 2); pf[3] = pfrag(it - 1, 0, 3); }
-          if (kk == 35) { va[0] = vfrag(it - 1, 0, 0); va[1] = vfrag(it - 1, 0, 1); }
-        }
+          mfma_scaled<false>(m & 3, S, ka[m & 1], qhl[2 * m], kscale, qsh[m >> 2]);
+        mfma_scaled<false>(m & 3, S, ka[m & 1], qhl[2 * m + 1], kscale, qsl[m >> 2]);
         if constexpr (dma) {
-          if ((kk & 3) == 1 && (kk >> 2) < F::dma) dma_piece(t, kk >> 2, tile0 + it + 2);
+          if (m < F::dma) dma_piece(t, m, tile0 + it + 2);
         }
-        const int n = kk + 1;  // operand of the next MFMA
-        if (n < 32) {
-          const u32x4& c = raw[(n >> 1) & 3];
-          af = (n & 1) ? fp8x8_to_bf16(c[2], c[3], ksc) : fp8x8_to_bf16(c[0], c[1], ksc);
-        } else if (n < 36) {
-          af = __builtin_bit_cast(bf16x8, raw[n - 32]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      bf16x8 rf[2];
+      rf[0] = *reinterpret_cast<const bf16x8*>(tb + rope8_off + (0 ^ rope8_x));
+      // the bf16 MFMAs below take S as srcC from a different MFMA shape: drain first
+      mfma_result_fence(S);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (r + 1 < 4) rf[(r + 1) & 1] = *reinterpret_cast<const bf16x8*>(tb + rope8_off + ((32 * (r + 1)) ^ rope8_x));
+        mfma_qk(S, rf[r & 1], qf[32 + r]);
+        if constexpr (pv) {
+          if (r == 1) { pf[0] = pfrag(it - 1, 0, 0); pf[1] = pfrag(it - 1, 0, 1); }
+          if (r == 2) { pf[2] = pfrag(it - 1, 0, 2); pf[3] = pfrag(it - 1, 0, 3); }
+          if (r == 3) { va[0] = vfrag(it - 1, 0, 0); va[1] = vfrag(it - 1, 0, 1); }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -769,12 +862,41 @@ __device__ __forceinline__ void decode_paged_body(
         const int ql = lane_here();
         const bf16x8* qa = reinterpret_cast<const bf16x8*>(q_abs + (qbase + wave * 32 + (ql & 31)) * kDc);
         const bf16x8* qr = reinterpret_cast<const bf16x8*>(q_r + (qbase + wave * 32 + (ql & 31)) * kDr);
+        if constexpr (kFp8) {
+          // scaled MFMA m: dims 64m + 16g .. +15 (block 2m) and 64m + 32 + 16g
+          // .. +15 (block 2m + 1), held in qf[0..31] until they are split below
 #pragma unroll
-        for (int kk = 0; kk < 32; ++kk)  // 8-bit: dims 32(kk>>1) + 16g + 8(kk&1) .. +7, as the code reads
-          qf[kk] = kFp8 ? qa[4 * (kk >> 1) + 2 * (ql >> 5) + (kk & 1)] : qa[2 * kk + (ql >> 5)];
+          for (int m = 0; m < 8; ++m)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) qf[4 * m + j] = qa[8 * m + 4 * (j >> 1) + 2 * (ql >> 5) + (j & 1)];
+        } else {
+#pragma unroll
+          for (int kk = 0; kk < 32; ++kk) qf[kk] = qa[2 * kk + (ql >> 5)];
+        }
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) qf[32 + kk] = qr[2 * kk + (ql >> 5)];
         wait_vmcnt<0>();
+        if constexpr (kFp8) {
+          // each 32-dim block as hi + lo E4M3 codes; the MFMA operand takes
+          // block 2m's 16 dims in bytes 0..15 and block 2m+1's in 16..31, and
+          // this lane supplies the scale of block 2m + g
+          const int gq = ql >> 5;
+          qsh[0] = qsh[1] = qsl[0] = qsl[1] = 0;
+#pragma unroll
+          for (int m = 0; m < 8; ++m) {
+            u32x4 hA, lA, hB, lB;
+            int khA, klA, khB, klB;
+            split_block_fp8(qf[4 * m], qf[4 * m + 1], hA, lA, khA, klA);
+            split_block_fp8(qf[4 * m + 2], qf[4 * m + 3], hB, lB, khB, klB);
+            qhl[2 * m] = i32x8{(int)hA[0], (int)hA[1], (int)hA[2], (int)hA[3],
+                               (int)hB[0], (int)hB[1], (int)hB[2], (int)hB[3]};
+            qhl[2 * m + 1] = i32x8{(int)lA[0], (int)lA[1], (int)lA[2], (int)lA[3],
+                                   (int)lB[0], (int)lB[1], (int)lB[2], (int)lB[3]};
+            const int kh = gq ? khB : khA, kl = gq ? klB : klA;
+            qsh[m >> 2] |= (kh + 127) << (8 * (m & 3));
+            qsl[m >> 2] |= (kl + 127) << (8 * (m & 3));
+          }
+        }
       }
 
       for (int pass = 0; pass < 2; ++pass) {

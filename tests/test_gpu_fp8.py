@@ -3,8 +3,10 @@
 The conversion and the append are byte work and must match the oracle's
 quantizer bit for bit (a rotated k_R keeps the bf16 append's rounding bound).
 The 8-bit decode scan is judged against the oracle's attention over the stored
-values (E4M3 code times the token's scale) with the bar of the bf16 scan: the
-scan converts codes to bf16 exactly, so its own error is the bf16 scan's.
+values (E4M3 code times the token's scale) with the bar of the bf16 scan: it
+multiplies the codes exactly (block-scaled E4M3 MFMAs for QK, with the query as
+two E4M3 terms that reproduce it up to 2^-13 of each block's largest value;
+exact bf16 conversion for PV), so its own error is the bf16 scan's.
 """
 import math
 
@@ -254,3 +256,19 @@ def test_decode_fp8_long_config_sampled(M):
     o_lat, lse = r["o_lat"].cpu(), r["lse"].cpu()
     assert_bar(np.stack([o_lat[b, i, h].double().numpy() for b, i, h in picks]), ro, "fp8 long o_lat rows")
     assert_lse(np.array([float(lse[b, i, h]) for b, i, h in picks]), rl, "fp8 long lse rows")
+
+
+def test_decode_fp8_query_with_wide_range_inside_blocks(M):
+    """The scan holds the query as two E4M3 terms per 32-dim block: blocks that
+    mix one large value with values 10^4 to 2^20 times smaller, and blocks of
+    zeros, still meet the bar (the terms are exact down to 2^-13 of the block's
+    largest value, and what is lost below is smaller still)."""
+    lens = [900, 257]
+    q_abs, q_r, pages, bt, sl = _fp8_case(lens, 1, seed=23)
+    g = torch.Generator().manual_seed(24)
+    q = torch.randn((2, 1, 128, 512), generator=g) * 0.01
+    q[..., ::32] = 100.0 * torch.sign(torch.randn((2, 1, 128, 16), generator=g))   # one large value per block
+    q[..., 5::32] *= 2.0 ** -20 / 0.01                                              # and some far below it
+    q[:, :, :64, 64:128] = 0.0                                                      # all-zero blocks
+    q_abs = (q * 0.02).to(torch.bfloat16)
+    _decode8_check(M, q_abs, q_r, pages, bt, sl, 3, "fp8 wide-range query")
