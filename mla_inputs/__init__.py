@@ -193,6 +193,26 @@ def random_fp8_pages(num_pages: int, seed: int, k_lo: int = -10, k_hi: int = -6)
     return out
 
 
+MXFP4_PAGE_BYTES = PAGE * D_C // 2 + PAGE * D_R * 2 + PAGE * D_C // 32   # 25600: codes, bf16 k_R, E8M0 scales
+
+
+def random_mxfp4_pages(num_pages: int, seed: int, k_lo: int = -3, k_hi: int = -1) -> torch.Tensor:
+    """uint8 [num_pages, 25600] in the 4-bit cache layout, filled with seeded
+    data (no quantization happens here): packed E2M1 codes uniform over all
+    bytes (every nibble is a number), k_R ~ N(0, 1) rounded to bf16, and one
+    E8M0 scale byte k + 127 per token and 32-dim block, k uniform in
+    [k_lo, k_hi]."""
+    g = torch.Generator().manual_seed(seed)
+    out = torch.empty((num_pages, MXFP4_PAGE_BYTES), dtype=torch.uint8)
+    n_codes = PAGE * D_C // 2
+    out[:, :n_codes] = torch.randint(0, 256, (num_pages, n_codes), generator=g, dtype=torch.uint8)
+    rope = _randn_bf16((num_pages, PAGE * D_R), g)
+    out[:, n_codes:n_codes + PAGE * D_R * 2] = rope.view(torch.uint8).view(num_pages, -1)
+    k = torch.randint(k_lo, k_hi + 1, (num_pages, PAGE * D_C // 32), generator=g, dtype=torch.int32)
+    out[:, n_codes + PAGE * D_R * 2:] = (k + 127).to(torch.uint8)
+    return out
+
+
 def tiny_inputs(B: int, s_q: int, seqlens, h: int, d_hc: int, d_c: int, d_r: int,
                 page: int, seed: int = 7, pool_extra: int = 3):
     """Small float64 inputs of arbitrary dims for brute-force oracle checks.

@@ -20,7 +20,10 @@ Everything is float64 numpy, written from the definitions on the pages:
     (teardown page, section 3 threshold, section 4 path A in two stages);
   * an 8-bit latent cache (FP8 E4M3 codes with one power-of-two scale per
     token, k_R kept in bf16), the analog of the teardown page's quantized
-    latent gather (section 5), with the format readings stated beside it.
+    latent gather (section 5), with the format readings stated beside it;
+  * a 4-bit latent cache (OCP MXFP4: E2M1 codes with one E8M0 scale per 32
+    latent dims, k_R kept in bf16), the same analog in the microscaling form
+    the MI355X matrix cores read.
 
 Each function is pinned by tests under ``tests/test_oracle*.py`` against
 closed forms, brute-force loops, the pages' storage arithmetic and the
@@ -35,5 +38,8 @@ from .mla_oracle import (  # noqa: F401
     ROPE_BASE, rope_angles, rope_rotate, chunk_positions, append_latent,
     PREFILL_ABSORPTION_THRESHOLD, uses_absorption, decompress_kv, rope_keys, attend_mha,
     FP8_MAX, e4m3_value, e4m3_encode, fp8_scale_exponent, quantize_latent_fp8, dequantize_latent_fp8,
-    fp8_page_bytes, pack_fp8_cache, unpack_fp8_pages, dequantize_fp8_pages, PagedFp8Cache,
+    fp8_page_bytes, pack_fp8_cache, unpack_fp8_pages, dequantize_fp8_pages, PagedQuantCache, PagedFp8Cache,
+    E2M1_MAX, MX_BLOCK, e2m1_value, e2m1_encode, mx_scale_exponent, quantize_latent_mxfp4,
+    dequantize_latent_mxfp4, mxfp4_page_bytes, pack_mxfp4_cache, unpack_mxfp4_pages, dequantize_mxfp4_pages,
+    PagedMxfp4Cache,
 )

@@ -84,17 +84,18 @@ def gather_rows(kv_cache: np.ndarray, block_table_row: np.ndarray, n_tokens: int
     Token t lives in physical page block_table_row[t // page] at row t % page.
     Only the entries the sequence needs are read; they must be valid page ids.
     A uint16 cache is taken as bf16 bit patterns and decoded exactly after the
-    gather (so a large cache never has to exist in float64); a PagedFp8Cache
-    is dequantized after the gather in the same way.
+    gather (so a large cache never has to exist in float64); a quantized
+    cache (PagedFp8Cache, PagedMxfp4Cache) is dequantized after the gather in
+    the same way.
     """
-    fp8 = isinstance(kv_cache, PagedFp8Cache)
+    fp8 = isinstance(kv_cache, PagedQuantCache)
     kv = kv_cache if fp8 else np.asarray(kv_cache)
     page = kv.shape[1]
     n_pages = -(-int(n_tokens) // page)
     ids = np.asarray(block_table_row[:n_pages], dtype=np.int64)
     if n_pages and (ids.min() < 0 or ids.max() >= kv.shape[0]):
         raise ValueError("block table entry out of range")
-    if fp8:   # an 8-bit cache is dequantized after the gather
+    if fp8:   # a quantized cache is dequantized after the gather
         return kv.rows_of_pages(ids).reshape(n_pages * page, kv.shape[2])[:n_tokens]
     rows = kv[ids].reshape(n_pages * page, kv.shape[2])[:n_tokens]
     if rows.dtype == np.uint16:
@@ -270,7 +271,7 @@ def decode_split(q_abs, q_r, kv_cache, block_table, seqlens, scale: float, num_s
     q_abs = np.asarray(q_abs, np.float64)
     q_r = np.asarray(q_r, np.float64)
     B, s_q, Hn, d_c = q_abs.shape
-    page = (kv_cache.shape if isinstance(kv_cache, PagedFp8Cache) else np.asarray(kv_cache).shape)[1]
+    page = (kv_cache.shape if isinstance(kv_cache, PagedQuantCache) else np.asarray(kv_cache).shape)[1]
     o = np.zeros((B, s_q, Hn, num_splits, d_c))
     lse = np.full((B, s_q, Hn, num_splits), -np.inf)
     vis = [[max(visible_len(int(seqlens[b]), s_q, i), 0) for i in range(s_q)] for b in range(B)]
@@ -457,7 +458,7 @@ def decompress_kv(kv_cache, block_table, seqlens, w_uk, w_uv, max_len: int):
 
 def rope_keys(kv_cache, block_table, seqlens, max_len: int, d_c: int = 512):
     """k_R of every cached token, [B, max_len, d_R] (zero past L_b)."""
-    d_r = (kv_cache.shape if isinstance(kv_cache, PagedFp8Cache) else np.asarray(kv_cache).shape)[2] - d_c
+    d_r = (kv_cache.shape if isinstance(kv_cache, PagedQuantCache) else np.asarray(kv_cache).shape)[2] - d_c
     B = len(seqlens)
     R = np.zeros((B, max_len, d_r))
     for b in range(B):
@@ -615,21 +616,166 @@ def dequantize_fp8_pages(pages, page: int = 64, d_c: int = 512, d_r: int = 64) -
     return np.concatenate([c, bf16_bits_to_f64(rope)], axis=-1)
 
 
-class PagedFp8Cache:
-    """An 8-bit paged cache (uint8 pages [P, fp8_page_bytes]) as the decode
+class PagedQuantCache:
+    """A quantized paged cache (uint8 pages [P, page_bytes]) as the decode
     oracles read it: gather_rows dequantizes only the pages a sequence uses,
-    and np.asarray gives the whole cache in float64 (small caches only)."""
+    and np.asarray gives the whole cache in float64 (small caches only).
+    Subclasses name the page size and the dequantization of a page."""
+
+    page_bytes = None   # (page, d_c, d_r) -> bytes of one page
+    dequantize = None   # (pages, page, d_c, d_r) -> float64 rows [n, page, d_c + d_r]
 
     def __init__(self, pages, page: int = 64, d_c: int = 512, d_r: int = 64):
         self.pages = np.asarray(pages, np.uint8)
         self.page, self.d_c, self.d_r = page, d_c, d_r
-        if self.pages.ndim != 2 or self.pages.shape[1] != fp8_page_bytes(page, d_c, d_r):
-            raise ValueError("expected uint8 pages [P, fp8_page_bytes]")
+        nbytes = type(self).page_bytes(page, d_c, d_r)
+        if self.pages.ndim != 2 or self.pages.shape[1] != nbytes:
+            raise ValueError(f"expected uint8 pages [P, {nbytes}]")
         self.shape = (self.pages.shape[0], page, d_c + d_r)
 
     def rows_of_pages(self, ids) -> np.ndarray:
-        return dequantize_fp8_pages(self.pages[np.asarray(ids, np.int64)], self.page, self.d_c, self.d_r)
+        return type(self).dequantize(self.pages[np.asarray(ids, np.int64)], self.page, self.d_c, self.d_r)
 
     def __array__(self, dtype=None, copy=None):
-        out = dequantize_fp8_pages(self.pages, self.page, self.d_c, self.d_r)
+        out = type(self).dequantize(self.pages, self.page, self.d_c, self.d_r)
         return out if dtype is None else out.astype(dtype)
+
+
+class PagedFp8Cache(PagedQuantCache):
+    """The 8-bit cache: pages [P, fp8_page_bytes]."""
+    page_bytes = staticmethod(fp8_page_bytes)
+    dequantize = staticmethod(dequantize_fp8_pages)
+
+
+# --------------------------------------------------------------------------
+# 4-bit latent cache: c_KV in MXFP4 (E2M1 elements, one E8M0 scale per 32)
+# --------------------------------------------------------------------------
+# The NVFP4 gather of the teardown page (section 5) names a 4-bit latent
+# cache; MI355X's matrix cores read the OCP microscaling form of one (MXFP4)
+# directly. Readings taken here:
+#   * an element is OCP E2M1: sign, 2 exponent bits with bias 1, 1 mantissa
+#     bit; exponent 0 holds 0 and the subnormal 0.5; the magnitudes are
+#     0, 0.5, 1, 1.5, 2, 3, 4, 6; there are no infinities or NaN;
+#   * each block of 32 consecutive c_KV dims of a token (16 blocks per row)
+#     shares one scale 2^k, stored as the E8M0 byte k + 127, with k the
+#     smallest integer such that max|block| <= 6 * 2^k, clamped to
+#     [-126, 127] (-126 for a zero block): no element saturates (the OCP
+#     rule k = floor(log2 max|block|) - 2 would clip values above 6 * 2^k);
+#   * an element's code is c / 2^k rounded to the nearest E2M1 value, ties
+#     to the even mantissa, with the sign bit of c (a negative value that
+#     rounds to zero is stored as -0);
+#   * two elements per byte, the even dim in the low nibble;
+#   * k_R keeps its bf16 bits;
+#   * a page of 64 tokens is three arrays, each starting on a 16-byte
+#     boundary: 64 x 256 code bytes, then 64 x 64 bf16 k_R, then 64 x 16
+#     scale bytes (25600 bytes).
+
+E2M1_MAX = 6.0
+MX_BLOCK = 32
+MX_SCALE_EXP_MIN = -126
+MX_SCALE_EXP_MAX = 127
+
+
+def e2m1_value(codes) -> np.ndarray:
+    """Exact float64 value of E2M1 codes (4-bit, 0..15)."""
+    c = np.asarray(codes).astype(np.int64)
+    e = (c >> 1) & 3
+    m = c & 1
+    mag = np.where(e == 0, 0.5 * m, np.ldexp(1.0 + 0.5 * m, e - 1))
+    return np.where(c & 8, -mag, mag)
+
+
+def e2m1_encode(v) -> np.ndarray:
+    """Nearest E2M1 code of exact values with |v| <= 6, ties to the even code, sign kept."""
+    v = np.asarray(v, np.float64)
+    a = np.abs(v)
+    if not np.all(a <= E2M1_MAX):
+        raise ValueError("E2M1 encode: value outside [-6, 6] or NaN")
+    mags = e2m1_value(np.arange(8))                       # the 8 magnitudes, in code order
+    d = np.abs(a[..., None] - mags)
+    near = d == d.min(axis=-1, keepdims=True)             # one code, or two adjacent ones on a tie
+    even = near & (np.arange(8) % 2 == 0)
+    code = np.where(even.any(axis=-1), even.argmax(axis=-1), near.argmax(axis=-1))
+    return ((np.signbit(v).astype(np.int64) << 3) | code).astype(np.uint8)
+
+
+def mx_scale_exponent(amax) -> np.ndarray:
+    """k of a block's scale: the smallest integer with amax <= 6 * 2^k, clamped."""
+    a = np.asarray(amax, np.float64)
+    f, x = np.frexp(a)                      # 6 * 2^k = 0.75 * 2^(k + 3)
+    k = x - 3 + (f > 0.75)
+    k = np.clip(k, MX_SCALE_EXP_MIN, MX_SCALE_EXP_MAX)
+    return np.where(a == 0, MX_SCALE_EXP_MIN, k).astype(np.int64)
+
+
+def quantize_latent_mxfp4(c):
+    """(codes uint8 [..., d_c], one E2M1 code per element; k int64 [..., d_c / 32])."""
+    c = np.asarray(c, np.float64)
+    blocks = c.reshape(c.shape[:-1] + (c.shape[-1] // MX_BLOCK, MX_BLOCK))
+    k = mx_scale_exponent(np.abs(blocks).max(axis=-1))
+    codes = e2m1_encode(np.ldexp(blocks, -k[..., None]))
+    return codes.reshape(c.shape), k
+
+
+def dequantize_latent_mxfp4(codes, k) -> np.ndarray:
+    """Stored values: E2M1 value of each code times 2^k of its block."""
+    codes = np.asarray(codes)
+    k = np.asarray(k, np.int64)
+    v = e2m1_value(codes).reshape(codes.shape[:-1] + (k.shape[-1], MX_BLOCK))
+    return np.ldexp(v, k[..., None]).reshape(codes.shape)
+
+
+def mxfp4_page_bytes(page: int = 64, d_c: int = 512, d_r: int = 64) -> int:
+    """Bytes of one page of the 4-bit cache: packed codes, bf16 k_R and E8M0 scales."""
+    return page * d_c // 2 + page * d_r * 2 + page * d_c // MX_BLOCK
+
+
+def pack_mxfp4_cache(kv_bits, d_c: int = 512, chunk_pages: int = 256) -> np.ndarray:
+    """4-bit pages [P, mxfp4_page_bytes] of a bf16 cache given as bit patterns [P, page, d_c + d_R]."""
+    kv_bits = np.asarray(kv_bits)
+    if kv_bits.dtype != np.uint16:
+        raise ValueError("pack_mxfp4_cache takes the bf16 bit patterns (uint16)")
+    P, page, row = kv_bits.shape
+    d_r = row - d_c
+    out = np.zeros((P, mxfp4_page_bytes(page, d_c, d_r)), np.uint8)
+    o_rope = page * d_c // 2
+    o_scale = o_rope + page * d_r * 2
+    for p0 in range(0, P, chunk_pages):
+        blk = kv_bits[p0:p0 + chunk_pages]
+        n = blk.shape[0]
+        codes, k = quantize_latent_mxfp4(bf16_bits_to_f64(blk[..., :d_c]))
+        packed = codes[..., 0::2] | (codes[..., 1::2] << 4)
+        out[p0:p0 + n, :o_rope] = packed.reshape(n, -1)
+        out[p0:p0 + n, o_rope:o_scale] = np.ascontiguousarray(blk[..., d_c:]).view(np.uint8).reshape(n, -1)
+        out[p0:p0 + n, o_scale:] = (k + 127).astype(np.uint8).reshape(n, -1)
+    return out
+
+
+def unpack_mxfp4_pages(pages, page: int = 64, d_c: int = 512, d_r: int = 64):
+    """(codes [n, page, d_c] uint8 one per element, k_R bits [n, page, d_R] uint16,
+    scale exponents k [n, page, d_c / 32] int64)."""
+    pages = np.ascontiguousarray(pages, np.uint8)
+    n = pages.shape[0]
+    if pages.shape[1] != mxfp4_page_bytes(page, d_c, d_r):
+        raise ValueError("page size does not match the 4-bit layout")
+    o_rope = page * d_c // 2
+    o_scale = o_rope + page * d_r * 2
+    packed = pages[:, :o_rope].reshape(n, page, d_c // 2)
+    codes = np.empty((n, page, d_c), np.uint8)
+    codes[..., 0::2] = packed & 15
+    codes[..., 1::2] = packed >> 4
+    rope = pages[:, o_rope:o_scale].copy().view("<u2").reshape(n, page, d_r)
+    k = pages[:, o_scale:].reshape(n, page, d_c // MX_BLOCK).astype(np.int64) - 127
+    return codes, rope, k
+
+
+def dequantize_mxfp4_pages(pages, page: int = 64, d_c: int = 512, d_r: int = 64) -> np.ndarray:
+    """float64 rows [n, page, d_c + d_R] stored by 4-bit pages."""
+    codes, rope, k = unpack_mxfp4_pages(pages, page, d_c, d_r)
+    return np.concatenate([dequantize_latent_mxfp4(codes, k), bf16_bits_to_f64(rope)], axis=-1)
+
+
+class PagedMxfp4Cache(PagedQuantCache):
+    """The 4-bit cache: pages [P, mxfp4_page_bytes]."""
+    page_bytes = staticmethod(mxfp4_page_bytes)
+    dequantize = staticmethod(dequantize_mxfp4_pages)

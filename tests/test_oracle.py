@@ -716,3 +716,124 @@ def test_fp8_cache_decode_is_attention_over_stored_values():
     # and the attention result stays close to the bf16 cache's
     o16, l16 = O.decode_absorbed(qa, qr, kvb, bt, sl, O.default_scale())
     assert np.abs(o8 - o16).max() < 0.05 * np.abs(o16).max()
+
+
+# --------------------------------------------------------------------------
+# 4-bit latent cache (OCP MXFP4: E2M1 codes, one E8M0 scale per 32 dims)
+# --------------------------------------------------------------------------
+# torch has an E2M1 storage type but no conversion for it, so the value table
+# is pinned to the magnitudes the OCP microscaling format lists for E2M1,
+# rounding to a brute-force nearest search with the ties worked out by hand,
+# the block scale rule to a search, the page layout to byte offsets worked
+# out by hand, and the 4-bit decode to the definition "attention over the
+# stored values".
+
+OCP_E2M1_MAGNITUDES = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]   # codes 0..7; bit 3 is the sign
+
+
+def test_e2m1_values_match_the_ocp_table():
+    v = O.e2m1_value(np.arange(16))
+    assert v[:8].tolist() == OCP_E2M1_MAGNITUDES
+    assert (-v[8:]).tolist() == OCP_E2M1_MAGNITUDES
+    assert np.signbit(v[8])                       # code 0x8 is -0
+    assert O.E2M1_MAX == 6.0
+
+
+def test_e2m1_encode_is_nearest_with_ties_to_even_by_brute_force():
+    grid = np.arange(-6 * 64, 6 * 64 + 1) / 64.0      # every multiple of 1/64 in [-6, 6]
+    codes = O.e2m1_encode(grid)
+    ties = {0.25: 0, 0.75: 2, 1.25: 2, 1.75: 4, 2.5: 4, 3.5: 6, 5.0: 6}   # to the even code
+    for x, c in zip(grid, codes):
+        a = abs(x)
+        if a in ties:
+            want = ties[a]
+        else:
+            dist = [abs(a - m) for m in OCP_E2M1_MAGNITUDES]
+            want = dist.index(min(dist))
+        assert (int(c) & 7) == want, (x, c)
+        assert (int(c) >> 3) == (1 if np.signbit(x) else 0)
+    assert O.e2m1_encode([-0.1])[0] == 0x8          # a negative value that rounds to zero keeps its sign
+    with pytest.raises(ValueError):
+        O.e2m1_encode([6.01])
+
+
+def test_mx_scale_exponent_is_the_smallest_that_fits_by_search():
+    rng = np.random.default_rng(5)
+    amax = np.concatenate([
+        np.exp2(rng.uniform(-120, 120, 400)),
+        6.0 * np.exp2(np.arange(-20, 21)),                       # exactly 6 * 2^k
+        np.nextafter(6.0 * np.exp2(np.arange(-20, 21)), np.inf),  # just above
+        [0.0, 2.0 ** -140, 3.0e38]])
+    k = O.mx_scale_exponent(amax)
+    for a, kk in zip(amax, k):
+        if a == 0:
+            assert kk == -126
+            continue
+        want = next(j for j in range(-140, 140) if a <= 6.0 * 2.0 ** j)
+        assert kk == min(max(want, -126), 127), (a, kk, want)
+
+
+def test_quantize_latent_mxfp4_error_bound_and_no_saturation():
+    rng = np.random.default_rng(6)
+    c = rng.standard_normal((40, 512)) * np.exp2(rng.integers(-20, 20, (40, 1)))
+    c[3, 64:96] = 0.0                                   # one zero block
+    codes, k = O.quantize_latent_mxfp4(c)
+    assert codes.shape == (40, 512) and k.shape == (40, 16)
+    q = O.dequantize_latent_mxfp4(codes, k)
+    blocks = np.abs(c).reshape(40, 16, 32)
+    scaled_max = blocks.max(axis=-1) / np.exp2(k)
+    nz = blocks.max(axis=-1) > 0
+    assert np.all(scaled_max[nz] <= 6.0) and np.all(scaled_max[nz] > 3.0)   # smallest k: no clip, no waste
+    assert k[3, 2] == -126 and not np.any(q[3, 64:96])
+    # within half an E2M1 spacing (0.5 below 2, 1 below 4, 2 above) of the value
+    a = np.abs(c) / np.repeat(np.exp2(k), 32, axis=1)
+    half = np.where(a < 2, 0.25, np.where(a < 4, 0.5, 1.0)) * np.repeat(np.exp2(k), 32, axis=1)
+    assert np.all(np.abs(q - c) <= half)
+    # values on the grid come back exactly
+    exact = np.repeat(np.exp2(k), 32, axis=1) * O.e2m1_value(codes)
+    assert np.array_equal(O.dequantize_latent_mxfp4(*O.quantize_latent_mxfp4(exact)), exact)
+
+
+def test_mxfp4_page_layout_by_hand():
+    P, page, d_c, d_r = 2, 64, 512, 64
+    kv = torch.zeros((P, page, d_c + d_r), dtype=torch.bfloat16)
+    kv[1, 5, 0] = 1.0
+    kv[1, 5, 1] = -6.0        # block 0: max 6 -> k = 0
+    kv[1, 5, 40] = 0.75       # block 1: max 0.75 = 6 * 2^-3 -> k = -3
+    kv[1, 5, 41] = -0.1       # bf16 -0.10009765625 * 8 = -0.80078 -> -1.0
+    kv[1, 5, d_c + 3] = 1.25
+    pages = O.pack_mxfp4_cache(O.bf16_bits(kv))
+    assert pages.shape == (P, 64 * 256 + 64 * 128 + 64 * 16) == (P, 25600)
+    row = 5 * 256
+    assert pages[1, row + 0] == 0xF2                     # dim 0: 1.0 = 0.01.0 (low), dim 1: -6 = 1.11.1 (high)
+    assert pages[1, row + 20] == 0xA7                    # dim 40: 6 = 0.11.1, dim 41: -1.0 = 1.01.0
+    assert not pages[1, row + 1: row + 20].any() and not pages[1, row + 21: row + 256].any()
+    assert pages[1, 16384 + 5 * 128 + 6] == 0xA0 and pages[1, 16384 + 5 * 128 + 7] == 0x3F   # bf16 1.25, LE
+    sc = pages[1, 24576 + 5 * 16: 24576 + 6 * 16]
+    assert sc[0] == 127 and sc[1] == 124 and np.all(sc[2:] == 1)          # E8M0 k + 127; zero blocks 2^-126
+    assert np.all(pages[0, 24576:] == 1) and not pages[0, :24576].any()   # zero page
+
+
+def test_mxfp4_cache_decode_is_attention_over_stored_values():
+    inp = tiny_inputs(B=3, s_q=2, seqlens=[70, 9, 130], h=4, d_hc=128, d_c=512, d_r=64, page=64, seed=22)
+    kv16 = inp["kv_cache"].to(torch.bfloat16)
+    pages = O.pack_mxfp4_cache(O.bf16_bits(kv16))
+    cache4 = O.PagedMxfp4Cache(pages)
+    stored = O.dequantize_mxfp4_pages(pages)
+    assert np.array_equal(np.asarray(cache4), stored)
+    bt, sl = inp["block_table"].numpy(), inp["seqlens"].numpy()
+    qa = O.absorb(O.as_f64(inp["q_c"]), O.as_f64(inp["w_uk"]))
+    qr = O.as_f64(inp["q_r"])
+    o4, l4 = O.decode_absorbed(qa, qr, cache4, bt, sl, O.default_scale())
+    o_ref, l_ref = O.decode_absorbed(qa, qr, stored, bt, sl, O.default_scale())
+    assert np.array_equal(o4, o_ref) and np.array_equal(l4, l_ref)
+    # the split oracle reads the 4-bit cache the same way
+    os_, ls_ = O.decode_split(qa, qr, cache4, bt, sl, O.default_scale(), 3)
+    oc, lc = O.combine(os_, ls_)
+    assert np.allclose(oc, o_ref, rtol=0, atol=1e-12) and np.allclose(lc, l_ref, rtol=0, atol=1e-12)
+    # k_R is stored exactly; c_KV within half the coarsest E2M1 spacing of its block
+    kvb = O.as_f64(kv16)
+    assert np.array_equal(stored[..., 512:], kvb[..., 512:])
+    blk_max = np.abs(kvb[..., :512]).reshape(kvb.shape[0], 64, 16, 32).max(axis=-1)
+    # (half the top spacing is 2^k, and 2^k < max|block| / 3 by the scale rule)
+    assert np.all(np.abs(stored[..., :512] - kvb[..., :512]) < np.repeat(blk_max, 32, axis=-1) / 3.0 + 1e-300)

@@ -224,3 +224,62 @@ def test_fp8_page_with_swapped_rope_and_scale_is_caught(monkeypatch):
         return fixed
     _patch(monkeypatch, "pack_fp8_cache", swapped)
     _expect_fail(pins.test_fp8_page_layout_by_hand)
+
+
+def test_e2m1_ties_away_from_zero_is_caught(monkeypatch):
+    real = M.e2m1_encode
+
+    def half_up(v):
+        v = np.asarray(v, np.float64)
+        c = real(v)
+        a = np.abs(v)
+        tie_down = np.isin(a, [0.25, 1.25, 2.5, 5.0])       # ties that went to the smaller even code
+        return np.where(tie_down, c + 1, c).astype(np.uint8)
+    _patch(monkeypatch, "e2m1_encode", half_up)
+    _expect_fail(pins.test_e2m1_encode_is_nearest_with_ties_to_even_by_brute_force)
+
+
+def test_e2m1_subnormal_value_is_caught(monkeypatch):
+    real = M.e2m1_value
+
+    def wrong(codes):
+        c = np.asarray(codes).astype(np.int64)
+        v = real(c)
+        return np.where((c & 7) == 1, v / 2, v)             # 0.25 instead of 0.5
+    _patch(monkeypatch, "e2m1_value", wrong)
+    _expect_fail(pins.test_e2m1_values_match_the_ocp_table)
+
+
+def test_mx_scale_ocp_floor_rule_is_caught(monkeypatch):
+    # k = floor(log2 amax) - 2, which clips amax in (6, 8) * 2^k
+    def floor_rule(a):
+        a = np.asarray(a, np.float64)
+        _, x = np.frexp(a)
+        return np.where(a == 0, -126, np.clip(x - 3, -126, 127)).astype(np.int64)
+    _patch(monkeypatch, "mx_scale_exponent", floor_rule)
+    _expect_fail(pins.test_mx_scale_exponent_is_the_smallest_that_fits_by_search,
+                 pins.test_quantize_latent_mxfp4_error_bound_and_no_saturation)
+
+
+def test_mxfp4_nibble_order_is_caught(monkeypatch):
+    real = M.pack_mxfp4_cache
+
+    def swapped(kv_bits, d_c=512, chunk_pages=256):
+        out = real(kv_bits, d_c, chunk_pages)
+        page = np.asarray(kv_bits).shape[1]
+        n = page * d_c // 2
+        out[:, :n] = (out[:, :n] >> 4) | (out[:, :n] << 4)
+        return out
+    _patch(monkeypatch, "pack_mxfp4_cache", swapped)
+    _expect_fail(pins.test_mxfp4_page_layout_by_hand)
+
+
+def test_mxfp4_one_scale_per_token_is_caught(monkeypatch):
+    def per_token(c):
+        c = np.asarray(c, np.float64)
+        k1 = M.mx_scale_exponent(np.abs(c).max(axis=-1))
+        k = np.repeat(k1[..., None], c.shape[-1] // M.MX_BLOCK, axis=-1)
+        return M.e2m1_encode(np.ldexp(c, -k1[..., None])), k
+    _patch(monkeypatch, "quantize_latent_mxfp4", per_token)
+    _expect_fail(pins.test_mxfp4_page_layout_by_hand,
+                 pins.test_quantize_latent_mxfp4_error_bound_and_no_saturation)
