@@ -321,6 +321,57 @@ mla_status mla_decode_paged_fp8(const void* q_abs, const void* q_r,
                                 float softmax_scale, int num_splits,
                                 float* o_part, float* lse_part, void* stream);
 
+/* ---- 4-bit latent cache ---------------------------------------------------
+ * The teardown page's quantized gather is of a 4-bit (NVFP4) cache (section
+ * 5). This library's 4-bit cache is the OCP microscaling form that the gfx950
+ * matrix cores read directly, MXFP4: c_KV as E2M1 elements (1 sign, 2
+ * exponent bits with bias 1, 1 mantissa bit; magnitudes 0, 0.5, 1, 1.5, 2,
+ * 3, 4, 6; no infinities or NaN) with one E8M0 scale per 32 consecutive dims
+ * of a token (16 per row), and k_R kept in bf16:
+ *   block scale 2^k, k the smallest integer with max over the block of
+ *     |c_KV[c]| <= 6 * 2^k, clamped to [-126, 127] (a zero block gets 2^-126),
+ *     so nothing saturates; stored as the byte k + 127;
+ *   code[c] = c_KV[c] / 2^k rounded to the nearest E2M1 value, ties to the
+ *     even code, with the sign of c_KV[c] (a negative value that rounds to 0
+ *     becomes -0); two codes per byte, the even dim in the low nibble;
+ *   stored value = E2M1(code[c]) * 2^k.
+ * A page of 64 tokens is MLA_MXFP4_PAGE_BYTES = 25600 bytes, three arrays:
+ *   bytes [0, 16384)      uint8 codes [64][256]  (block u of a row = bytes 16u .. 16u+15)
+ *   bytes [16384, 24576)  bf16 k_R [64][64]
+ *   bytes [24576, 25600)  uint8 scales [64][16] (E8M0, k + 127)
+ * The cache holds 400 bytes per token instead of 1152. Decoding over it gives
+ * the attention of mla_decode_paged over the stored values: scores on the
+ * block-scaled matrix-core instruction straight from the codes (the query as
+ * two E4M3 terms, exact except for values under 2^-13 of their 32-dim block's
+ * largest), V dequantized to bf16 exactly. Scale bytes 0 and 255 never occur
+ * in pages this library writes and are not valid input. c_KV inputs must be
+ * finite. */
+enum { MLA_MXFP4_PAGE_BYTES = 25600 };
+
+/* Convert a bf16 cache to the 4-bit layout page for page (page p of kv_fp4
+ * holds the 64 rows of page p of kv_cache).
+ *   kv_cache bf16 [num_pages, 64, 576];  kv_fp4 uint8 [num_pages, 25600] output
+ * 1 <= num_pages <= 2^26. */
+mla_status mla_quantize_cache_mxfp4(const void* kv_cache, int64_t num_pages, void* kv_fp4, void* stream);
+
+/* mla_append_latent into the 4-bit cache: c_new[b, i] quantized as above
+ * (one scale per 32-dim block), kr_new[b, i] rotated in fp32 and rounded to
+ * bf16. kv_fp4 uint8 [num_pages, 25600], updated in place; all other
+ * arguments and rules as mla_append_latent. */
+mla_status mla_append_latent_mxfp4(const void* c_new, const void* kr_new, const float* rope, int max_pos,
+                                   void* kv_fp4, int64_t num_pages, const int32_t* block_table, int max_pages,
+                                   const int32_t* seqlens, int B, int s_q, void* stream);
+
+/* mla_decode_paged over the 4-bit cache: kv_fp4 uint8 [num_pages, 25600];
+ * every other argument, rule and output as mla_decode_paged (feed o_part and
+ * lse_part to mla_combine_splits or mla_combine_up_proj). */
+mla_status mla_decode_paged_mxfp4(const void* q_abs, const void* q_r,
+                                  const void* kv_fp4, int64_t num_pages,
+                                  const int32_t* block_table, int max_pages,
+                                  const int32_t* seqlens, int B, int s_q, int H,
+                                  float softmax_scale, int num_splits,
+                                  float* o_part, float* lse_part, void* stream);
+
 /* ---- the whole step in one launch ---------------------------------------
  * mla_absorb_q -> mla_decode_paged -> mla_combine_splits -> mla_up_proj as the
  * four phases of one cooperative kernel (256 workgroups, one per CU, separated

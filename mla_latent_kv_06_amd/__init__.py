@@ -133,24 +133,54 @@ def mla_decode_paged(q_abs, q_r, kv_cache, block_table, seqlens, num_splits: int
 FP8_PAGE_BYTES = 41216  # MLA_FP8_PAGE_BYTES: 64 x 512 E4M3 codes, 64 x 64 bf16 k_R, 64 fp32 scales
 
 
+MXFP4_PAGE_BYTES = 25600  # MLA_MXFP4_PAGE_BYTES: 64 x 256 E2M1 code bytes, 64 x 64 bf16 k_R, 64 x 16 E8M0 scales
+
+
 def is_fp8_cache(kv_cache) -> bool:
     """Whether kv_cache is the 8-bit layout (uint8 [num_pages, 41216])."""
-    return kv_cache.dtype == torch.uint8
+    return kv_cache.dtype == torch.uint8 and kv_cache.dim() == 2 and kv_cache.shape[1] == FP8_PAGE_BYTES
+
+
+def is_mxfp4_cache(kv_cache) -> bool:
+    """Whether kv_cache is the 4-bit layout (uint8 [num_pages, 25600])."""
+    return kv_cache.dtype == torch.uint8 and kv_cache.dim() == 2 and kv_cache.shape[1] == MXFP4_PAGE_BYTES
+
+
+def _need_paged_bytes(kv, name, page_bytes):
+    if kv.dim() != 2 or kv.shape[1] != page_bytes:
+        raise ValueError(f"{name} must be [num_pages, {page_bytes}] uint8, got {tuple(kv.shape)}")
+    _need(kv, name, torch.uint8)
 
 
 def _need_fp8_cache(kv_fp8, name="kv_fp8"):
-    if kv_fp8.dim() != 2 or kv_fp8.shape[1] != FP8_PAGE_BYTES:
-        raise ValueError(f"{name} must be [num_pages, {FP8_PAGE_BYTES}] uint8, got {tuple(kv_fp8.shape)}")
-    _need(kv_fp8, name, torch.uint8)
+    _need_paged_bytes(kv_fp8, name, FP8_PAGE_BYTES)
+
+
+def _need_mxfp4_cache(kv_fp4, name="kv_fp4"):
+    _need_paged_bytes(kv_fp4, name, MXFP4_PAGE_BYTES)
 
 
 def mla_decode_paged_fp8(q_abs, q_r, kv_fp8, block_table, seqlens, num_splits: int,
                          softmax_scale: float = DEFAULT_SCALE, o_part=None, lse_part=None, stream=None):
     """mla_decode_paged over the 8-bit cache (uint8 [num_pages, 41216]); same outputs."""
+    _need_fp8_cache(kv_fp8)
+    return _decode_quantized("mla_decode_paged_fp8", q_abs, q_r, kv_fp8, block_table, seqlens, num_splits,
+                             softmax_scale, o_part, lse_part, stream)
+
+
+def mla_decode_paged_mxfp4(q_abs, q_r, kv_fp4, block_table, seqlens, num_splits: int,
+                           softmax_scale: float = DEFAULT_SCALE, o_part=None, lse_part=None, stream=None):
+    """mla_decode_paged over the 4-bit cache (uint8 [num_pages, 25600]); same outputs."""
+    _need_mxfp4_cache(kv_fp4)
+    return _decode_quantized("mla_decode_paged_mxfp4", q_abs, q_r, kv_fp4, block_table, seqlens, num_splits,
+                             softmax_scale, o_part, lse_part, stream)
+
+
+def _decode_quantized(fn, q_abs, q_r, kv, block_table, seqlens, num_splits, softmax_scale, o_part, lse_part,
+                      stream):
     B, s_q = q_abs.shape[0], q_abs.shape[1]
     _need(q_abs, "q_abs", torch.bfloat16, (B, s_q, H, D_C))
     _need(q_r, "q_r", torch.bfloat16, (B, s_q, H, D_R))
-    _need_fp8_cache(kv_fp8)
     if block_table.dim() != 2 or block_table.shape[0] != B:
         raise ValueError(f"block_table must be [B, max_pages], got {tuple(block_table.shape)}")
     _need(block_table, "block_table", torch.int32)
@@ -162,24 +192,32 @@ def mla_decode_paged_fp8(q_abs, q_r, kv_fp8, block_table, seqlens, num_splits: i
         lse_part = torch.empty((B, s_q, H, S), dtype=torch.float32, device=q_abs.device)
     _need(o_part, "o_part", torch.float32, (B, s_q, H, S, D_C))
     _need(lse_part, "lse_part", torch.float32, (B, s_q, H, S))
-    _check(_lib.LIB.mla_decode_paged_fp8(
-        _ptr(q_abs), _ptr(q_r), _ptr(kv_fp8), kv_fp8.shape[0], _ptr(block_table), block_table.shape[1],
-        _ptr(seqlens), B, s_q, H, float(softmax_scale), S, _ptr(o_part), _ptr(lse_part), _stream(stream)),
-        "mla_decode_paged_fp8")
+    _check(getattr(_lib.LIB, fn)(
+        _ptr(q_abs), _ptr(q_r), _ptr(kv), kv.shape[0], _ptr(block_table), block_table.shape[1],
+        _ptr(seqlens), B, s_q, H, float(softmax_scale), S, _ptr(o_part), _ptr(lse_part), _stream(stream)), fn)
     return o_part, lse_part
 
 
-def mla_quantize_cache_fp8(kv_cache, out=None, stream=None):
-    """bf16 cache [P, 64, 576] -> 8-bit cache uint8 [P, 41216], page for page."""
+def _quantize_cache(fn, page_bytes, kv_cache, out, stream):
     if kv_cache.dim() != 3 or kv_cache.shape[1:] != (PAGE, ROW):
         raise ValueError(f"kv_cache must be [num_pages, 64, 576], got {tuple(kv_cache.shape)}")
     _need(kv_cache, "kv_cache", torch.bfloat16)
     P = kv_cache.shape[0]
     if out is None:
-        out = torch.empty((P, FP8_PAGE_BYTES), dtype=torch.uint8, device=kv_cache.device)
-    _need(out, "out", torch.uint8, (P, FP8_PAGE_BYTES))
-    _check(_lib.LIB.mla_quantize_cache_fp8(_ptr(kv_cache), P, _ptr(out), _stream(stream)), "mla_quantize_cache_fp8")
+        out = torch.empty((P, page_bytes), dtype=torch.uint8, device=kv_cache.device)
+    _need(out, "out", torch.uint8, (P, page_bytes))
+    _check(getattr(_lib.LIB, fn)(_ptr(kv_cache), P, _ptr(out), _stream(stream)), fn)
     return out
+
+
+def mla_quantize_cache_fp8(kv_cache, out=None, stream=None):
+    """bf16 cache [P, 64, 576] -> 8-bit cache uint8 [P, 41216], page for page."""
+    return _quantize_cache("mla_quantize_cache_fp8", FP8_PAGE_BYTES, kv_cache, out, stream)
+
+
+def mla_quantize_cache_mxfp4(kv_cache, out=None, stream=None):
+    """bf16 cache [P, 64, 576] -> 4-bit cache uint8 [P, 25600], page for page."""
+    return _quantize_cache("mla_quantize_cache_mxfp4", MXFP4_PAGE_BYTES, kv_cache, out, stream)
 
 
 def mla_combine_splits(o_part, lse_part, o_lat=None, lse=None, stream=None):
@@ -281,21 +319,32 @@ def mla_append_latent(kv_cache, block_table, seqlens, c_new, kr_new, rope, strea
 def mla_append_latent_fp8(kv_fp8, block_table, seqlens, c_new, kr_new, rope, stream=None):
     """mla_append_latent into the 8-bit cache (c_new quantized per token, kr_new
     rotated); returns kv_fp8."""
+    _need_fp8_cache(kv_fp8)
+    return _append_quantized("mla_append_latent_fp8", kv_fp8, block_table, seqlens, c_new, kr_new, rope, stream)
+
+
+def mla_append_latent_mxfp4(kv_fp4, block_table, seqlens, c_new, kr_new, rope, stream=None):
+    """mla_append_latent into the 4-bit cache (c_new quantized per 32-dim block,
+    kr_new rotated); returns kv_fp4."""
+    _need_mxfp4_cache(kv_fp4)
+    return _append_quantized("mla_append_latent_mxfp4", kv_fp4, block_table, seqlens, c_new, kr_new, rope, stream)
+
+
+def _append_quantized(fn, kv, block_table, seqlens, c_new, kr_new, rope, stream):
     B, s_q = c_new.shape[0], c_new.shape[1]
     _need(c_new, "c_new", torch.bfloat16, (B, s_q, D_C))
     _need(kr_new, "kr_new", torch.bfloat16, (B, s_q, D_R))
     if rope.dim() != 3 or rope.shape[1:] != (D_R // 2, 2):
         raise ValueError(f"rope must be [max_pos, 32, 2], got {tuple(rope.shape)}")
     _need(rope, "rope", torch.float32)
-    _need_fp8_cache(kv_fp8)
     if block_table.dim() != 2 or block_table.shape[0] != B:
         raise ValueError(f"block_table must be [B, max_pages], got {tuple(block_table.shape)}")
     _need(block_table, "block_table", torch.int32)
     _need(seqlens, "seqlens", torch.int32, (B,))
-    _check(_lib.LIB.mla_append_latent_fp8(_ptr(c_new), _ptr(kr_new), _ptr(rope), rope.shape[0], _ptr(kv_fp8),
-                                          kv_fp8.shape[0], _ptr(block_table), block_table.shape[1], _ptr(seqlens),
-                                          B, s_q, _stream(stream)), "mla_append_latent_fp8")
-    return kv_fp8
+    _check(getattr(_lib.LIB, fn)(_ptr(c_new), _ptr(kr_new), _ptr(rope), rope.shape[0], _ptr(kv),
+                                 kv.shape[0], _ptr(block_table), block_table.shape[1], _ptr(seqlens),
+                                 B, s_q, _stream(stream)), fn)
+    return kv
 
 
 def mla_rope_q(q_r, seqlens, rope, stream=None):
@@ -374,14 +423,16 @@ def decode_layer(q_c, q_r, kv_cache, block_table, seqlens, w_uk, w_uv, num_split
 
     Returns a dict with every intermediate (q_abs, o_part, lse_part, o_lat, lse, out).
     ``max_len`` (longest sequence, host int) only feeds the split heuristic.
-    ``kv_cache`` is the bf16 cache [P, 64, 576] or the 8-bit one (uint8 [P, 41216]).
+    ``kv_cache`` is the bf16 cache [P, 64, 576], the 8-bit one (uint8 [P, 41216]) or
+    the 4-bit one (uint8 [P, 25600]).
     """
     B, s_q = q_c.shape[0], q_c.shape[1]
     if num_splits is None:
         ml = int(max_len) if max_len is not None else block_table.shape[1] * PAGE
         num_splits = mla_recommended_splits(B, s_q, ml)
     q_abs = mla_absorb_q(q_c, w_uk, stream=stream)
-    scan = mla_decode_paged_fp8 if is_fp8_cache(kv_cache) else mla_decode_paged
+    scan = (mla_decode_paged_fp8 if is_fp8_cache(kv_cache) else
+            mla_decode_paged_mxfp4 if is_mxfp4_cache(kv_cache) else mla_decode_paged)
     o_part, lse_part = scan(q_abs, q_r, kv_cache, block_table, seqlens, num_splits, softmax_scale, stream=stream)
     o_lat, lse = mla_combine_splits(o_part, lse_part, stream=stream)
     out = mla_up_proj(o_lat, w_uv, stream=stream)
@@ -409,6 +460,8 @@ def mla_decode_step(q_c, q_r, kv_cache, block_table, seqlens, w_uk, w_uv, num_sp
     _need(q_r, "q_r", torch.bfloat16, (B, s_q, H, D_R))
     _need(w_uk, "w_uk", torch.bfloat16, (H, D_HC, D_C))
     _need(w_uv, "w_uv", torch.bfloat16, (H, D_HC, D_C))
+    if is_mxfp4_cache(kv_cache):
+        raise ValueError("the one-launch step reads the bf16 or the 8-bit cache; use decode_layer for the 4-bit one")
     fp8 = is_fp8_cache(kv_cache)
     if fp8:
         _need_fp8_cache(kv_cache, "kv_cache")
@@ -444,8 +497,8 @@ def attention_layer(q_c, q_r, kv_cache, block_table, seqlens, w_uk, w_uv, max_le
                          max_len, stream)
         r["path"] = "absorbed"
         return r
-    if is_fp8_cache(kv_cache):
-        raise ValueError("the decompressed branch reads the bf16 cache; the 8-bit cache serves the absorbed path")
+    if kv_cache.dtype == torch.uint8:
+        raise ValueError("the decompressed branch reads the bf16 cache; the quantized caches serve the absorbed path")
     ml = -(-int(max_len) // PAGE) * PAGE
     k_nope, v = mla_decompress_kv(kv_cache, block_table, seqlens, w_uk, w_uv, ml, stream=stream)
     out, lse = mla_prefill_mha(q_c, q_r, k_nope, v, kv_cache, block_table, seqlens, softmax_scale, stream=stream)

@@ -46,6 +46,11 @@ SIGNATURES = {
                                       c_void_p, c_int, c_int, c_void_p]),
     "mla_decode_paged_fp8": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_int, c_void_p, c_int, c_int,
                                      c_int, c_float, c_int, c_void_p, c_void_p, c_void_p]),
+    "mla_quantize_cache_mxfp4": (c_int, [c_void_p, c_int64, c_void_p, c_void_p]),
+    "mla_append_latent_mxfp4": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_int64, c_void_p, c_int,
+                                        c_void_p, c_int, c_int, c_void_p]),
+    "mla_decode_paged_mxfp4": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_int, c_void_p, c_int, c_int,
+                                       c_int, c_float, c_int, c_void_p, c_void_p, c_void_p]),
     "mla_decode_step": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_int, c_void_p, c_int, c_int, c_int,
                                 c_void_p, c_void_p, c_float, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                 c_void_p, c_void_p]),

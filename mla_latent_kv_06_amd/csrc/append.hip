@@ -14,6 +14,7 @@
 #include "mla_device.hpp"
 #include "append.hpp"
 #include "fp8_cache.hpp"
+#include "mxfp4_cache.hpp"
 
 namespace mla {
 
@@ -116,6 +117,58 @@ __global__ __launch_bounds__(256) void quantize_cache_fp8_kernel(const char* __r
   if (lane == 0) reinterpret_cast<float*>(base + kFp8ScaleOffset)[r] = fp8_scale_value(k);
 }
 
+// The append into the 4-bit cache: one wave per chunk token, c_KV quantized
+// per 32-dim block, k_R rotated as in the bf16 cache.
+__global__ __launch_bounds__(256) void append_latent_mxfp4_kernel(const __bf16* __restrict__ c_new,
+                                                                  const __bf16* __restrict__ kr_new,
+                                                                  const float2* __restrict__ rope, int max_pos,
+                                                                  char* __restrict__ kv, int64_t num_pages,
+                                                                  const int32_t* __restrict__ block_table,
+                                                                  int max_pages, const int32_t* __restrict__ seqlens,
+                                                                  int T, int s_q) {
+  const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
+  if (t >= T) return;
+  const int b = t / s_q, i = t - b * s_q;
+  const int64_t cap = (int64_t)max_pages * kPage < max_pos ? (int64_t)max_pages * kPage : max_pos;
+  const int p = chunk_position(seqlens, b, i, s_q, cap);
+  if (p < 0) return;
+  const int64_t page = physical_page(block_table, max_pages, b, p >> 6, num_pages);
+  char* base = kv + page * kFp4PageBytes;
+  const int r = p & (kPage - 1);
+  int k;
+  const unsigned codes = quantize_row_mxfp4(reinterpret_cast<const bf16x8*>(c_new + (int64_t)t * kDc)[lane], k);
+  reinterpret_cast<unsigned*>(base + r * kFp4RowBytes)[lane] = codes;
+  if (lane < kDr / 2) {
+    const bf16x2 x = reinterpret_cast<const bf16x2*>(kr_new + (int64_t)t * kDr)[lane];
+    const float2 cs = rope[(int64_t)p * (kDr / 2) + lane];
+    reinterpret_cast<bf16x2*>(base + kFp4RopeOffset + r * kDr * 2)[lane] = rotate_pair(x, cs);
+  }
+  if ((lane & 3) == 0) reinterpret_cast<unsigned char*>(base + kFp4ScaleOffset + r * (kDc / kMxBlock))[lane >> 2] =
+      (unsigned char)(k + 127);
+}
+
+// bf16 pages [num_pages, 64, 576] -> 4-bit pages [num_pages, 25600 bytes],
+// page for page: one wave per token row.
+__global__ __launch_bounds__(256) void quantize_cache_mxfp4_kernel(const char* __restrict__ kv, int64_t num_pages,
+                                                                   char* __restrict__ out) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= num_pages * kPage) return;
+  const int64_t page = row >> 6;
+  const int r = (int)(row & (kPage - 1));
+  const char* src = kv + page * kPageBytes + (int64_t)r * kRowBytes;
+  char* base = out + page * kFp4PageBytes;
+  int k;
+  const unsigned codes = quantize_row_mxfp4(reinterpret_cast<const bf16x8*>(src)[lane], k);
+  reinterpret_cast<unsigned*>(base + r * kFp4RowBytes)[lane] = codes;
+  if (lane < kDr * 2 / 16)
+    reinterpret_cast<f32x4*>(base + kFp4RopeOffset + r * kDr * 2)[lane] =
+        reinterpret_cast<const f32x4*>(src + kDc * 2)[lane];
+  if ((lane & 3) == 0) reinterpret_cast<unsigned char*>(base + kFp4ScaleOffset + r * (kDc / kMxBlock))[lane >> 2] =
+      (unsigned char)(k + 127);
+}
+
 // q_R [T, H, 64] rotated in place: one thread per 4 pairs (16 bytes). Rows of
 // tokens without a position below max_pos are left as they are.
 __global__ __launch_bounds__(256) void rope_q_kernel(__bf16* __restrict__ q_r, const float2* __restrict__ rope,
@@ -165,6 +218,22 @@ hipError_t launch_append_latent_fp8(const __bf16* c_new, const __bf16* kr_new, c
 hipError_t launch_quantize_cache_fp8(const char* kv, int64_t num_pages, char* out, hipStream_t stream) {
   const int64_t blocks = num_pages * (kPage / 4);
   hipLaunchKernelGGL(quantize_cache_fp8_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, kv, num_pages, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_latent_mxfp4(const __bf16* c_new, const __bf16* kr_new, const float* rope, int max_pos,
+                                      char* kv, int64_t num_pages, const int32_t* block_table, int max_pages,
+                                      const int32_t* seqlens, int B, int s_q, hipStream_t stream) {
+  const int T = B * s_q;
+  hipLaunchKernelGGL(append_latent_mxfp4_kernel, dim3((T + 3) / 4), dim3(256), 0, stream, c_new, kr_new,
+                     reinterpret_cast<const float2*>(rope), max_pos, kv, num_pages, block_table, max_pages, seqlens,
+                     T, s_q);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_cache_mxfp4(const char* kv, int64_t num_pages, char* out, hipStream_t stream) {
+  const int64_t blocks = num_pages * (kPage / 4);
+  hipLaunchKernelGGL(quantize_cache_mxfp4_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, kv, num_pages, out);
   return hipGetLastError();
 }
 

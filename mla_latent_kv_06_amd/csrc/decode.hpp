@@ -9,7 +9,7 @@ namespace mla {
 struct DecodeParams {
   const __bf16* q_abs;        // [B, s_q, 128, 512]
   const __bf16* q_r;          // [B, s_q, 128, 64]
-  const char* kv;             // [num_pages, 64, 576] bf16, or 8-bit pages (launch_decode_paged_fp8)
+  const char* kv;             // [num_pages, 64, 576] bf16, or 8-bit / 4-bit pages (launch_decode_paged_fp8 / _mxfp4)
   int64_t num_pages;
   const int32_t* block_table; // [B, max_pages]
   int max_pages;
@@ -22,10 +22,19 @@ struct DecodeParams {
   float* lse_part;            // [B, s_q, 128, num_splits]
 };
 
+// cache formats of the scan: bf16 rows, the 8-bit pages of fp8_cache.hpp,
+// the 4-bit pages of mxfp4_cache.hpp
+constexpr int kFmtBf16 = 0;
+constexpr int kFmtFp8 = 1;
+constexpr int kFmtMxfp4 = 2;
+
 hipError_t launch_decode_paged(const DecodeParams& p, hipStream_t stream);
 
 // The same scan over the 8-bit cache of fp8_cache.hpp (p.kv: pages of 41216 bytes).
 hipError_t launch_decode_paged_fp8(const DecodeParams& p, hipStream_t stream);
+
+// The same scan over the 4-bit cache of mxfp4_cache.hpp (p.kv: pages of 25600 bytes).
+hipError_t launch_decode_paged_mxfp4(const DecodeParams& p, hipStream_t stream);
 
 hipError_t launch_combine(const float* o_part, const float* lse_part, int rows, int num_splits,
                           float* o_lat, float* lse, hipStream_t stream);

@@ -44,6 +44,7 @@
 #include "mla_device.hpp"
 #include "decode.hpp"
 #include "fp8_cache.hpp"
+#include "mxfp4_cache.hpp"
 
 namespace mla {
 
@@ -72,13 +73,31 @@ static_assert(4 * kThreads * 16 == kStage8Rope && kThreads * 16 == kTok * kDr * 
               "8-bit stage must split into 16-byte loads");
 static_assert(kStage8Bytes % 16 == 0, "8-bit stages start on 16-byte boundaries");
 
-template <bool kFp8>
+// 4-bit cache: a stage holds the tile's 32 rows of 256 code bytes (16-byte
+// chunk u of a row = MX block u, at chunk slot u ^ (row & 7)), then its 32 k_R
+// rows, then its 32 rows of 16 scale bytes; a thread issues 4 loads per tile
+// (2 code chunks, 1 k_R chunk, and in lanes 0-7 of every wave 1 scale chunk).
+// V is dequantized once per tile into one of two bf16 tiles in the bf16
+// stage layout, which PV reads as in the bf16 scan.
+constexpr int kStage4Rope = kTok * kFp4RowBytes;             // 8192
+constexpr int kStage4Scale = kStage4Rope + kTok * kDr * 2;   // 12288
+constexpr int kStage4Bytes = kStage4Scale + kTok * (kDc / kMxBlock);  // 12800
+constexpr int kDma4PerThread = 4;
+static_assert(2 * kThreads * 16 == kStage4Rope && kThreads * 16 == kTok * kDr * 2 &&
+                  32 * 16 == kTok * (kDc / kMxBlock),
+              "4-bit stage must split into 16-byte loads");
+static_assert(kStage4Bytes % 16 == 0, "4-bit stages start on 16-byte boundaries");
+
+template <int kFmt>
 struct StageFmt {
-  static constexpr int bytes = kFp8 ? kStage8Bytes : kStageBytes;
-  static constexpr int dma = kFp8 ? kDma8PerThread : kDmaPerThread;
-  static constexpr int lds = kStages * bytes + kPBytes;
+  static constexpr int bytes = kFmt == kFmtFp8 ? kStage8Bytes : (kFmt == kFmtMxfp4 ? kStage4Bytes : kStageBytes);
+  static constexpr int dma = kFmt == kFmtFp8 ? kDma8PerThread : (kFmt == kFmtMxfp4 ? kDma4PerThread : kDmaPerThread);
+  static constexpr int rope = kFmt == kFmtFp8 ? kStage8Rope : kStage4Rope;    // k_R rows (quantized formats)
+  static constexpr int vbuf = kStages * bytes;                                // dequantized V tiles (4-bit)
+  static constexpr int pbuf = vbuf + (kFmt == kFmtMxfp4 ? 2 * kStageBytes : 0);
+  static constexpr int lds = pbuf + kPBytes;
 };
-static_assert(StageFmt<true>::lds <= 163840, "LDS budget");
+static_assert(StageFmt<kFmtFp8>::lds <= 163840 && StageFmt<kFmtMxfp4>::lds <= 163840, "LDS budget");
 
 __device__ __forceinline__ int swz(int t) { return ((t & 3) << 1) ^ ((t >> 2) & 7); }
 // 8-bit stage: chunk c of code row t sits at c ^ swz8(t) (low 3 bits). Rows
@@ -277,6 +296,36 @@ __device__ __forceinline__ void mfma_scaled(int sel, f32x16& d, const i32x8& a, 
   }
 }
 
+// E2M1 x E4M3 scaled MFMA (32x32x64, cbsz 4: A is 4-bit) accumulating into d
+// in VGPRs. A = 32 tokens x 64 latent dims of 4-bit codes: lane half g holds
+// all 32 values of the MFMA's K-block g (byte j = K values 2j, 2j+1, low
+// nibble first), with that block's E8M0 scale; B as in the 8-bit scan. Both
+// scales are byte kSel of their registers. kInit: d = A.B (srcC 0); kNop: two
+// wait states first, for a source written by the VALU just before.
+template <int kSel, bool kInit, bool kNop>
+__device__ __forceinline__ void mfma_scaled4_sel(f32x16& d, const u32x4& a, const i32x8& b, int sa, int sb) {
+#define MLA_SEL4(OPS) \
+  if constexpr (kInit) \
+    asm("s_nop 1\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %3, %4" OPS " cbsz:4" \
+        : "=&v"(d) : "v"(a), "v"(b), "v"(sa), "v"(sb)); \
+  else if constexpr (kNop) \
+    asm("s_nop 1\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4" OPS " cbsz:4" \
+        : "+v"(d) : "v"(a), "v"(b), "v"(sa), "v"(sb)); \
+  else \
+    asm("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4" OPS " cbsz:4" \
+        : "+v"(d) : "v"(a), "v"(b), "v"(sa), "v"(sb));
+  if constexpr (kSel == 0) {
+    MLA_SEL4("")
+  } else if constexpr (kSel == 1) {
+    MLA_SEL4(" op_sel:[1,1,0]")
+  } else if constexpr (kSel == 2) {
+    MLA_SEL4(" op_sel_hi:[1,1,0]")
+  } else {
+    MLA_SEL4(" op_sel:[1,1,0] op_sel_hi:[1,1,0]")
+  }
+#undef MLA_SEL4
+}
+
 __device__ __forceinline__ bf16x8 cat8(const i16x4& v0, const i16x4& v1) {
   const bf16x4 b0 = __builtin_bit_cast(bf16x4, v0);
   const bf16x4 b1 = __builtin_bit_cast(bf16x4, v1);
@@ -317,7 +366,9 @@ __device__ __forceinline__ int wave_incl_scan32(int v, int lane) {
 
 }  // namespace
 
-// kFp8: the cache is the 8-bit layout of fp8_cache.hpp instead of bf16 rows.
+// kFmt: the cache is bf16 rows (kFmtBf16), the 8-bit layout of fp8_cache.hpp
+// (kFmtFp8) or the 4-bit layout of mxfp4_cache.hpp (kFmtMxfp4).
+// 8-bit:
 // QK over the latent runs on the E4M3 block-scaled MFMA straight from the
 // codes (the token's scale as A's block scale); the query is held as two E4M3
 // terms, hi (each bf16 value truncated to 4 significant bits) and lo (the
@@ -326,15 +377,19 @@ __device__ __forceinline__ int wave_incl_scan32(int v, int lane) {
 // (8 tokens of one column, read transposed) to bf16 at scale 1 and folds the
 // tokens' scales into P (P' = P * 2^k_t is exact).
 // The body of one scan workgroup (blockIdx.x is its range); lds points at
-// decode_lds_bytes<kFp8>() bytes of LDS aligned to 1024. It runs as its own
+// decode_lds_bytes<kFmt>() bytes of LDS aligned to 1024. It runs as its own
 // kernel (decode.hip) and as a phase of the fused step (step.hip).
-template <bool kStream, bool kFp8>
+template <bool kStream, int kFmt>
 __device__ __forceinline__ void decode_paged_body(
     char* __restrict__ lds, const __bf16* __restrict__ q_abs, const __bf16* __restrict__ q_r,
     const char* __restrict__ kv, const int32_t* __restrict__ block_table, const int32_t* __restrict__ seqlens,
     float* __restrict__ o_part, float* __restrict__ lse_part, DecodeParams a) {
-  using F = StageFmt<kFp8>;
-  char* const pbuf = lds + kStages * F::bytes;
+  constexpr bool kFp8 = kFmt == kFmtFp8;
+  constexpr bool kFp4 = kFmt == kFmtMxfp4;
+  constexpr bool kScaled = kFp8 || kFp4;  // QK over the latent on the block-scaled MFMA
+  using F = StageFmt<kFmt>;
+  char* const pbuf = lds + F::pbuf;
+  char* const vbuf = lds + F::vbuf;  // 4-bit cache: two dequantized V tiles
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -438,7 +493,14 @@ __device__ __forceinline__ void decode_paged_body(
   int qk8_off[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) qk8_off[r] = lo * kDc + (((4 * (r >> 1) + 2 * (r & 1) + g) ^ swz8(lo)) << 4);
-  const int rope8_off = kStage8Rope + lo * (kDr * 2);
+  // 4-bit: the A operand of scaled MFMA m is code chunk 2m + g of row lo (all
+  // of MX block 2m + g), at chunk slot (2m + g) ^ (lo & 7) =
+  // 2((m & 3) ^ ((lo >> 1) & 3)) + (g ^ (lo & 1)) + 8 (m >> 2): qk4_off[m & 3] + 128 (m >> 2)
+  int qk4_off[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    qk4_off[r] = lo * kFp4RowBytes + (((2 * (r ^ ((lo >> 1) & 3))) + (g ^ (lo & 1))) << 4);
+  const int rope8_off = F::rope + lo * (kDr * 2);
   const int rope8_x = (g ^ (lo & 7)) << 4;
   // PV A operand (V^T) for this wave's columns 128w + 32c' through transposed
   // reads; group G = lane>>4, ii = lane&15 fetches row 4(G>>1) + (ii>>2)
@@ -476,7 +538,18 @@ __device__ __forceinline__ void decode_paged_body(
   // DMA: thread tid fills chunk slot q = k*256 + tid of a stage; the matching
   // source chunk of the 32-row half page is (row q/72, chunk (q%72) ^ swz(row))
   unsigned dma_off[F::dma];
-  if constexpr (kFp8) {
+  if constexpr (kFp4) {
+    // code slot q = k*256 + tid (k < 2): row q/16, source chunk (q%16) ^ (row&7);
+    // k_R slot tid as in the 8-bit stage; scale slot 8*wave + lane (lanes 0-7)
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const unsigned q = k * kThreads + tid;
+      const unsigned t = q >> 4;
+      dma_off[k] = t * kFp4RowBytes + (((q & 15) ^ (t & 7)) << 4);
+    }
+    dma_off[2] = (tid >> 3) * (kDr * 2) + (((tid & 7) ^ ((tid >> 3) & 7)) << 4);
+    dma_off[3] = (8 * wave + (tid & 7)) * 16;
+  } else if constexpr (kFp8) {
     // code slot q = k*256 + tid (k < 4): row q/32, source chunk (q%32) ^ swz8(row);
     // k_R slot tid: row tid/8, source chunk (tid%8) ^ (row&7); scale slot
     // 2*wave + lane (lanes 0-1)
@@ -507,7 +580,10 @@ __device__ __forceinline__ void decode_paged_body(
   // 8-bit: src is the page's first byte, dst the stage's wave slice
   auto dma_target = [&](int tile, int stage) -> DmaTarget {
     const int64_t page = physical_page(block_table, a.max_pages, b, tile >> 1, a.num_pages);
-    if constexpr (kFp8)
+    if constexpr (kFp4)
+      return DmaTarget{kv + page * kFp4PageBytes,
+                       (unsigned)(uintptr_t)(lds_void_t*)(lds + stage * F::bytes + wave * 1024)};
+    else if constexpr (kFp8)
       return DmaTarget{kv + page * kFp8PageBytes,
                        (unsigned)(uintptr_t)(lds_void_t*)(lds + stage * F::bytes + wave * 1024)};
     else
@@ -517,7 +593,17 @@ __device__ __forceinline__ void decode_paged_body(
   // load k of a tile (k is a compile-time constant at every call); the 8-bit
   // tile is half `tile & 1` of its page in each of the page's three arrays
   auto dma_piece = [&](const DmaTarget& t, int k, int tile) {
-    if constexpr (kFp8) {
+    if constexpr (kFp4) {
+      const int half = tile & 1;
+      if (k < 2) {
+        dma16<kStream>(t.src + half * (kTok * kFp4RowBytes), dma_off[k], t.dst + k * (kThreads * 16));
+      } else if (k == 2) {
+        dma16<kStream>(t.src + kFp4RopeOffset + half * (kTok * kDr * 2), dma_off[2], t.dst + kStage4Rope);
+      } else if ((tid & 63) < 8) {
+        dma16<kStream>(t.src + kFp4ScaleOffset + half * (kTok * (kDc / kMxBlock)), dma_off[3],
+                       t.dst - wave * 1024 + kStage4Scale + wave * 128);
+      }
+    } else if constexpr (kFp8) {
       const int half = tile & 1;
       if (k < 4) {
         dma16<kStream>(t.src + half * (kTok * kDc), dma_off[k], t.dst + k * (kThreads * 16));
@@ -565,7 +651,8 @@ __device__ __forceinline__ void decode_paged_body(
       const char* tv = lds + (ip & (kStages - 1)) * F::bytes + pv8_off[cp] + ks * (16 * kDc);
       return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)tv);
     } else {
-      const char* tv = lds + (ip & (kStages - 1)) * kStageBytes + (cp >> 1) * 128;
+      const char* tv = (kFp4 ? vbuf + (ip & 1) * kStageBytes : lds + (ip & (kStages - 1)) * kStageBytes) +
+                       (cp >> 1) * 128;
       return cat8(__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(tv + pv_off[cp & 1][0][ks])),
                   __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(tv + pv_off[cp & 1][1][ks])));
     }
@@ -595,7 +682,102 @@ __device__ __forceinline__ void decode_paged_body(
   auto qk = [&](int it, auto dma_tag, auto pv_tag) -> f32x16 {
     constexpr bool dma = decltype(dma_tag)::value;
     constexpr bool pv = decltype(pv_tag)::value;  // prefetch PV(it-1) operands
-    if constexpr (kFp8) {
+    if constexpr (kFp4) {
+      // 4-bit: the latent part on v_mfma_scale_f32_32x32x64_f8f6f4 with A =
+      // the tile's E2M1 codes and their per-token, per-block E8M0 scales
+      // (lane half g supplies K-block g: all of MX block 2m + g), B = the
+      // query's E4M3 hi and lo terms as in the 8-bit scan; then the four bf16
+      // MFMAs of k_R. Between the MFMA pairs every thread dequantizes its
+      // eighth of V(it) (token tid & 31, dims 64 (tid >> 5) .. +63) into the
+      // bf16 tile vbuf[it & 1], one 16-byte chunk per pair, zero past the
+      // visible length.
+      const char* tb = lds + (it & (kStages - 1)) * F::bytes;
+      DmaTarget t{nullptr, 0u};
+      if constexpr (dma) t = dma_target(tile0 + it + 2, (it + 2) & (kStages - 1));
+      // A scales: byte m & 3 of sa[m >> 2] = scale of MX block 2m + g of token lo
+      int sa[2];
+      {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(tb + kStage4Scale + lo * 16);
+        const unsigned sel = 0x06040200u + 0x01010101u * (unsigned)g;
+        sa[0] = (int)__builtin_amdgcn_perm(w[1], w[0], sel);
+        sa[1] = (int)__builtin_amdgcn_perm(w[3], w[2], sel);
+      }
+      auto kread = [&](int m) -> u32x4 {
+        return *reinterpret_cast<const u32x4*>(tb + qk4_off[m & 3] + 128 * (m >> 2));
+      };
+      // V dequantization of this thread's token dt and dims 64 ds .. 64 ds + 63
+      const int dl = lane_here();
+      const int dt = dl & 31;
+      const int ds = 2 * wave + (dl >> 5);
+      const u32x4 dc0 = *reinterpret_cast<const u32x4*>(tb + dt * kFp4RowBytes + (((2 * ds) ^ (dt & 7)) << 4));
+      const u32x4 dc1 = *reinterpret_cast<const u32x4*>(tb + dt * kFp4RowBytes + (((2 * ds + 1) ^ (dt & 7)) << 4));
+      const unsigned de = *reinterpret_cast<const unsigned short*>(tb + kStage4Scale + dt * 16 + 2 * ds);
+      const bool dok = (tile0 + it) * kTok + dt < t_end;
+      char* const vrow = vbuf + (it & 1) * kStageBytes + dt * kRowBytes;
+      auto dequant = [&](int j) {  // output chunk 8 ds + j (dims 64 ds + 8j .. +7)
+        const unsigned w = (j < 4 ? dc0 : dc1)[j & 3];
+        const float sc = __uint_as_float(((j < 4 ? de : de >> 8) & 255u) << 23);
+        const bf16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0);
+        const bf16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1);
+        const bf16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2);
+        const bf16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3);
+        bf16x8 v = bf16x8{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+        if (!dok) v = bf16x8{};
+        *reinterpret_cast<bf16x8*>(vrow + (((8 * ds + j) ^ swz(dt)) << 4)) = v;
+      };
+      u32x4 ka[2];
+      ka[0] = kread(0);
+      __builtin_amdgcn_sched_barrier(0);
+      mm4(3, va[1], pf);  // deferred tail of the previous PV
+      __builtin_amdgcn_sched_barrier(0);
+      f32x16 S;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        if (m + 1 < 8) ka[(m + 1) & 1] = kread(m + 1);  // one MFMA pair ahead
+        if (m == 0)
+          mfma_scaled4_sel<0, true, true>(S, ka[0], qhl[0], sa[0], qsh[0]);
+        else if (m == 4)
+          mfma_scaled4_sel<0, false, true>(S, ka[0], qhl[8], sa[1], qsh[1]);
+        else if ((m & 3) == 1)
+          mfma_scaled4_sel<1, false, false>(S, ka[m & 1], qhl[2 * m], sa[m >> 2], qsh[m >> 2]);
+        else if ((m & 3) == 2)
+          mfma_scaled4_sel<2, false, false>(S, ka[m & 1], qhl[2 * m], sa[m >> 2], qsh[m >> 2]);
+        else
+          mfma_scaled4_sel<3, false, false>(S, ka[m & 1], qhl[2 * m], sa[m >> 2], qsh[m >> 2]);
+        if ((m & 3) == 0)
+          mfma_scaled4_sel<0, false, false>(S, ka[m & 1], qhl[2 * m + 1], sa[m >> 2], qsl[m >> 2]);
+        else if ((m & 3) == 1)
+          mfma_scaled4_sel<1, false, false>(S, ka[m & 1], qhl[2 * m + 1], sa[m >> 2], qsl[m >> 2]);
+        else if ((m & 3) == 2)
+          mfma_scaled4_sel<2, false, false>(S, ka[m & 1], qhl[2 * m + 1], sa[m >> 2], qsl[m >> 2]);
+        else
+          mfma_scaled4_sel<3, false, false>(S, ka[m & 1], qhl[2 * m + 1], sa[m >> 2], qsl[m >> 2]);
+        if constexpr (dma) {
+          if (m < F::dma) dma_piece(t, m, tile0 + it + 2);
+        }
+        dequant(m);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      bf16x8 rf[2];
+      rf[0] = *reinterpret_cast<const bf16x8*>(tb + rope8_off + (0 ^ rope8_x));
+      // the bf16 MFMAs below take S as srcC from a different MFMA shape: drain first
+      mfma_result_fence(S);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (r + 1 < 4) rf[(r + 1) & 1] = *reinterpret_cast<const bf16x8*>(tb + rope8_off + ((32 * (r + 1)) ^ rope8_x));
+        mfma_qk(S, rf[r & 1], qf[32 + r]);
+        if constexpr (pv) {
+          if (r == 1) { pf[0] = pfrag(it - 1, 0, 0); pf[1] = pfrag(it - 1, 0, 1); }
+          if (r == 2) { pf[2] = pfrag(it - 1, 0, 2); pf[3] = pfrag(it - 1, 0, 3); }
+          if (r == 3) { va[0] = vfrag(it - 1, 0, 0); va[1] = vfrag(it - 1, 0, 1); }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      mfma_result_fence(S);
+      __builtin_amdgcn_sched_barrier(0);
+      return S;
+    } else if constexpr (kFp8) {
       // 8-bit: the latent part runs on v_mfma_scale_f32_32x32x64_f8f6f4 straight
       // from the codes: A = 64 dims of the tile's K codes with the token's own
       // E8M0 scale, B = the same dims of the query's hi and lo code terms with
@@ -814,6 +996,7 @@ __device__ __forceinline__ void decode_paged_body(
   // rows past the visible length may hold anything (even NaN); P is 0 there,
   // so make those rows exactly 0 as well before PV reads them
   auto zero_tail = [&](int it) {
+    if constexpr (kFp4) return;  // the dequantized V rows past the end are written as zeros
     const int valid = t_end - (tile0 + it) * kTok;
     if (valid < kTok) {
       char* tb = lds + (it & (kStages - 1)) * F::bytes;
@@ -862,7 +1045,7 @@ __device__ __forceinline__ void decode_paged_body(
         const int ql = lane_here();
         const bf16x8* qa = reinterpret_cast<const bf16x8*>(q_abs + (qbase + wave * 32 + (ql & 31)) * kDc);
         const bf16x8* qr = reinterpret_cast<const bf16x8*>(q_r + (qbase + wave * 32 + (ql & 31)) * kDr);
-        if constexpr (kFp8) {
+        if constexpr (kScaled) {
           // scaled MFMA m: dims 64m + 16g .. +15 (block 2m) and 64m + 32 + 16g
           // .. +15 (block 2m + 1), held in qf[0..31] until they are split below
 #pragma unroll
@@ -876,7 +1059,7 @@ __device__ __forceinline__ void decode_paged_body(
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) qf[32 + kk] = qr[2 * kk + (ql >> 5)];
         wait_vmcnt<0>();
-        if constexpr (kFp8) {
+        if constexpr (kScaled) {
           // each 32-dim block as hi + lo E4M3 codes; the MFMA operand takes
           // block 2m's 16 dims in bytes 0..15 and block 2m+1's in 16..31, and
           // this lane supplies the scale of block 2m + g
@@ -1028,8 +1211,8 @@ __device__ __forceinline__ void decode_paged_body(
   }
 }
 
-template <bool kFp8>
-constexpr int decode_lds_bytes() { return StageFmt<kFp8>::lds; }
+template <int kFmt>
+constexpr int decode_lds_bytes() { return StageFmt<kFmt>::lds; }
 constexpr int kDecodeThreads = kThreads;
 constexpr int kDecodeGroups = kScanGroups;
 

@@ -35,7 +35,7 @@ inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s);
 mla_status decode_paged_any(const void* q_abs, const void* q_r, const void* kv_cache, int64_t num_pages,
                             const int32_t* block_table, int max_pages, const int32_t* seqlens, int B, int s_q, int H,
                             float softmax_scale, int num_splits, float* o_part, float* lse_part, void* stream,
-                            bool fp8) {
+                            int fmt) {
   const mla::Check c = mla::check_decode(q_abs, q_r, kv_cache, num_pages, block_table, max_pages, seqlens, B, s_q, H,
                                          softmax_scale, num_splits, o_part, lse_part);
   if (!c.ok()) return report(c);
@@ -53,7 +53,10 @@ mla_status decode_paged_any(const void* q_abs, const void* q_r, const void* kv_c
   p.scale_log2 = softmax_scale * 1.44269504088896340736f;
   p.o_part = o_part;
   p.lse_part = lse_part;
-  if (fp8) return report_hip(mla::launch_decode_paged_fp8(p, as_stream(stream)), "mla_decode_paged_fp8 launch");
+  if (fmt == mla::kFmtFp8)
+    return report_hip(mla::launch_decode_paged_fp8(p, as_stream(stream)), "mla_decode_paged_fp8 launch");
+  if (fmt == mla::kFmtMxfp4)
+    return report_hip(mla::launch_decode_paged_mxfp4(p, as_stream(stream)), "mla_decode_paged_mxfp4 launch");
   return report_hip(mla::launch_decode_paged(p, as_stream(stream)), "mla_decode_paged launch");
 }
 
@@ -132,7 +135,7 @@ mla_status mla_decode_paged(const void* q_abs, const void* q_r, const void* kv_c
                             int H, float softmax_scale, int num_splits, float* o_part, float* lse_part,
                             void* stream) {
   return decode_paged_any(q_abs, q_r, kv_cache, num_pages, block_table, max_pages, seqlens, B, s_q, H, softmax_scale,
-                          num_splits, o_part, lse_part, stream, false);
+                          num_splits, o_part, lse_part, stream, mla::kFmtBf16);
 }
 
 
@@ -141,7 +144,7 @@ mla_status mla_decode_paged_fp8(const void* q_abs, const void* q_r, const void* 
                                 int H, float softmax_scale, int num_splits, float* o_part, float* lse_part,
                                 void* stream) {
   return decode_paged_any(q_abs, q_r, kv_fp8, num_pages, block_table, max_pages, seqlens, B, s_q, H, softmax_scale,
-                          num_splits, o_part, lse_part, stream, true);
+                          num_splits, o_part, lse_part, stream, mla::kFmtFp8);
 }
 
 mla_status mla_quantize_cache_fp8(const void* kv_cache, int64_t num_pages, void* kv_fp8, void* stream) {
@@ -163,6 +166,35 @@ mla_status mla_append_latent_fp8(const void* c_new, const void* kr_new, const fl
                                                   static_cast<char*>(kv_fp8), num_pages, block_table, max_pages,
                                                   seqlens, B, s_q, as_stream(stream)),
                     "mla_append_latent_fp8 launch");
+}
+
+mla_status mla_decode_paged_mxfp4(const void* q_abs, const void* q_r, const void* kv_fp4, int64_t num_pages,
+                                  const int32_t* block_table, int max_pages, const int32_t* seqlens, int B, int s_q,
+                                  int H, float softmax_scale, int num_splits, float* o_part, float* lse_part,
+                                  void* stream) {
+  return decode_paged_any(q_abs, q_r, kv_fp4, num_pages, block_table, max_pages, seqlens, B, s_q, H, softmax_scale,
+                          num_splits, o_part, lse_part, stream, mla::kFmtMxfp4);
+}
+
+mla_status mla_quantize_cache_mxfp4(const void* kv_cache, int64_t num_pages, void* kv_fp4, void* stream) {
+  const mla::Check c = mla::check_quantize_cache(kv_cache, num_pages, kv_fp4);
+  if (!c.ok()) return report(c);
+  return report_hip(mla::launch_quantize_cache_mxfp4(static_cast<const char*>(kv_cache), num_pages,
+                                                     static_cast<char*>(kv_fp4), as_stream(stream)),
+                    "mla_quantize_cache_mxfp4 launch");
+}
+
+mla_status mla_append_latent_mxfp4(const void* c_new, const void* kr_new, const float* rope, int max_pos,
+                                   void* kv_fp4, int64_t num_pages, const int32_t* block_table, int max_pages,
+                                   const int32_t* seqlens, int B, int s_q, void* stream) {
+  const mla::Check c = mla::check_append(c_new, kr_new, rope, max_pos, kv_fp4, num_pages, block_table, max_pages,
+                                         seqlens, B, s_q);
+  if (!c.ok()) return report(c);
+  return report_hip(mla::launch_append_latent_mxfp4(static_cast<const __bf16*>(c_new),
+                                                    static_cast<const __bf16*>(kr_new), rope, max_pos,
+                                                    static_cast<char*>(kv_fp4), num_pages, block_table, max_pages,
+                                                    seqlens, B, s_q, as_stream(stream)),
+                    "mla_append_latent_mxfp4 launch");
 }
 
 mla_status mla_decode_step(const void* q_c, const void* q_r, const void* kv_cache, int64_t num_pages,

@@ -27,7 +27,7 @@ namespace mla {
 
 namespace {
 
-static_assert(kAbsorbLdsBytes <= decode_lds_bytes<true>() && kUpProjLdsBytes <= decode_lds_bytes<true>(),
+static_assert(kAbsorbLdsBytes <= decode_lds_bytes<kFmtFp8>() && kUpProjLdsBytes <= decode_lds_bytes<kFmtFp8>(),
               "every phase fits in the scan's LDS");
 
 }  // namespace
@@ -44,7 +44,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seqlens, float* __restrict__ o_part,
     float* __restrict__ lse_part, float* __restrict__ o_lat, float* __restrict__ lse, __bf16* __restrict__ out,
     DecodeParams a) {
-  __shared__ __attribute__((aligned(1024))) char lds[decode_lds_bytes<kFp8>()];
+  constexpr int kFmt = kFp8 ? kFmtFp8 : kFmtBf16;
+  __shared__ __attribute__((aligned(1024))) char lds[decode_lds_bytes<kFmt>()];
   cooperative_groups::grid_group grid = cooperative_groups::this_grid();
   const int T = a.B * a.s_q;
 
@@ -60,7 +61,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
   wait_vmcnt<0>();
 
   // phase 2: the split scan, workgroup k scanning page range k
-  decode_paged_body<kStream, kFp8>(lds, q_abs, q_r, kv, block_table, seqlens, o_part, lse_part, a);
+  decode_paged_body<kStream, kFmt>(lds, q_abs, q_r, kv, block_table, seqlens, o_part, lse_part, a);
   grid.sync();
 
   // phase 3: merge the partials of each (token, head) row, four rows per item

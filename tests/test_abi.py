@@ -26,7 +26,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) == 23, names
+    assert len(names) == 26, names
     out = subprocess.run(["nm", "-D", "--defined-only", os.path.join(ROOT, "mla_latent_kv_06_amd", "libmla.so")],
                          capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\bT (mla_[a-z0-9_]+)\b", out))
@@ -64,7 +64,7 @@ def _decode(lib, fn="mla_decode_paged", **kw):
     (dict(S=5), 2), (dict(max_pages=0), 2), (dict(num_pages=0), 2), (dict(scale=float("nan")), 2),
     (dict(scale=float("inf")), 2), (dict(scale=0.0), 2), (dict(scale=-0.5), 2),
 ])
-@pytest.mark.parametrize("fn", ["mla_decode_paged", "mla_decode_paged_fp8"])
+@pytest.mark.parametrize("fn", ["mla_decode_paged", "mla_decode_paged_fp8", "mla_decode_paged_mxfp4"])
 def test_decode_validation(lib, kw, status, fn):
     assert _decode(lib, fn, **kw) == status
     assert lib.mla_last_error() != b""
@@ -90,6 +90,9 @@ def test_other_entry_validation(lib):
     assert lib.mla_append_latent_fp8(None, A, A, 64, A, 4, A, 2, A, 2, 1, None) == 1
     assert lib.mla_append_latent_fp8(A, A, A, 64, MIS, 4, A, 2, A, 2, 1, None) == 3
     assert lib.mla_append_latent_fp8(A, A, A, 64, A, 4, A, 2, A, 2, 5000, None) == 2
+    assert lib.mla_append_latent_mxfp4(None, A, A, 64, A, 4, A, 2, A, 2, 1, None) == 1
+    assert lib.mla_append_latent_mxfp4(A, A, A, 64, MIS, 4, A, 2, A, 2, 1, None) == 3
+    assert lib.mla_append_latent_mxfp4(A, A, A, 64, A, 4, A, 2, A, 2, 5000, None) == 2
     # one-launch step: q_c, q_r, kv, num_pages, bt, max_pages, seqlens, B, s_q, H, w_uk, w_uv, scale, S,
     # q_abs, o_part, lse_part, o_lat, out, lse
     for fn in (lib.mla_decode_step, lib.mla_decode_step_fp8):
@@ -104,6 +107,10 @@ def test_other_entry_validation(lib):
     assert lib.mla_quantize_cache_fp8(A, 4, MIS, None) == 3
     assert lib.mla_quantize_cache_fp8(A, 0, A, None) == 2
     assert lib.mla_quantize_cache_fp8(A, (1 << 26) + 1, A, None) == 2
+    assert lib.mla_quantize_cache_mxfp4(None, 4, A, None) == 1
+    assert lib.mla_quantize_cache_mxfp4(A, 4, MIS, None) == 3
+    assert lib.mla_quantize_cache_mxfp4(A, 0, A, None) == 2
+    assert lib.mla_quantize_cache_mxfp4(A, (1 << 26) + 1, A, None) == 2
     # query rotation: q_r, rope, max_pos, seqlens, B, s_q, H
     assert lib.mla_rope_q(None, A, 64, A, 2, 1, 128, None) == 1
     assert lib.mla_rope_q(A, A, 64, MIS, 2, 1, 128, None) == 3
