@@ -14,7 +14,8 @@ Prints one JSON line (rank 0):
 plus effective KV GB/s, per-kernel times and, under next_rows, the cache
 append and query rotation, the step as one launch (mla_decode_step) against
 the four kernels it fuses, the same step over the 8-bit cache
-(mla_decode_paged_fp8), and for chunks of s_q > 1 the decompressed branch.
+(mla_decode_paged_fp8) and over the 4-bit cache (mla_decode_paged_mxfp4), and
+for chunks of s_q > 1 the decompressed branch.
 """
 from __future__ import annotations
 
@@ -34,7 +35,12 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 FLOP_PER_PAIR = 128 * 2 * (576 + 512)  # all heads, one (query, key) pair: QK over 576 + PV over 512
 KV_BYTES_PER_TOKEN = 576 * 2
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_paged_long_hbm_traffic.json")
-FP8_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_paged_fp8_long_hbm_traffic.json")
+TRAFFIC_FILES = {
+    "bf16": TRAFFIC_FILE,
+    "fp8": os.path.join(ROOT, "profiles", "decode_paged_fp8_long_hbm_traffic.json"),
+    "mxfp4": os.path.join(ROOT, "profiles", "decode_paged_mxfp4_long_hbm_traffic.json"),
+}
+FORMAT_HEADERS = {"bf16": (), "fp8": ("fp8_cache.hpp",), "mxfp4": ("mxfp4_cache.hpp",)}
 
 
 def parse():
@@ -53,6 +59,7 @@ def parse():
                    help="run mla_combine_splits and mla_up_proj as two kernels instead of mla_combine_up_proj")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle time for the baseline")
     p.add_argument("--no-fp8", action="store_true", help="skip the 8-bit cache leg")
+    p.add_argument("--no-mxfp4", action="store_true", help="skip the 4-bit cache leg")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only copy 1 GiB device to device three times (the known-size reference for "
                         "rocprofv3 FETCH_SIZE / WRITE_SIZE) and exit")
@@ -68,23 +75,23 @@ def visible_pairs(seqlens, s_q):
     return tot
 
 
-def kernel_source_digest(fp8=False):
+def kernel_source_digest(fmt="bf16"):
     h = hashlib.sha256()
-    for f in ("decode.hip", "decode_body.hpp", "mla_device.hpp", "decode.hpp") + (("fp8_cache.hpp",) if fp8 else ()):
+    for f in ("decode.hip", "decode_body.hpp", "mla_device.hpp", "decode.hpp") + FORMAT_HEADERS[fmt]:
         with open(os.path.join(ROOT, "mla_latent_kv_06_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload, splits, fp8=False):
+def measured_traffic(workload, splits, fmt="bf16"):
     """HBM bytes per decode launch from committed rocprofv3 counter runs, if they
     were taken on the current kernel source and launch configuration."""
     try:
-        with open(FP8_TRAFFIC_FILE if fp8 else TRAFFIC_FILE) as f:
+        with open(TRAFFIC_FILES[fmt]) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if (t.get("kernel_digest") != kernel_source_digest(fp8) or t.get("workload") != workload
+    if (t.get("kernel_digest") != kernel_source_digest(fmt) or t.get("workload") != workload
             or t.get("splits") != splits):
         return None
     return t.get("hbm_bytes_per_launch")
@@ -209,20 +216,27 @@ def time_decompressed_branch(M, torch, kv, tables, seqlens, lens, q_c, q_r, w_uk
     }
 
 
-FP8_BYTES_PER_TOKEN = 512 + 64 * 2 + 4   # E4M3 codes, bf16 k_R, fp32 scale
+QUANT_FORMATS = {
+    # page bytes, bytes per token, what the cache holds
+    "fp8": (41216, 512 + 64 * 2 + 4, "c_KV in E4M3 with a power-of-two scale per token, k_R in bf16"),
+    "mxfp4": (25600, 256 + 64 * 2 + 16, "c_KV in MXFP4 (E2M1 with an E8M0 scale per 32 dims), k_R in bf16"),
+}
 
 
-def time_fp8_cache(M, torch, kv, tables, seqlens, lens, q_c, q_r, w_uk, w_uv, S, layers, steps, warmup,
-                   flop_step, flop_attn, q_bytes, olat_bytes, workload):
-    """The same step over the 8-bit cache: every resident layer converted once
-    (mla_quantize_cache_fp8), then absorb -> mla_decode_paged_fp8 ->
+def time_quantized_cache(M, torch, fmt, kv, tables, seqlens, lens, q_c, q_r, w_uk, w_uv, S, layers, steps, warmup,
+                         flop_step, flop_attn, q_bytes, olat_bytes, workload):
+    """The same step over a quantized cache: every resident layer converted once
+    (mla_quantize_cache_<fmt>), then absorb -> mla_decode_paged_<fmt> ->
     mla_combine_up_proj, rotating through the layers as the main loop does."""
+    page_bytes, per_token, what = QUANT_FORMATS[fmt]
+    quantize = getattr(M, f"mla_quantize_cache_{fmt}")
+    scan = getattr(M, f"mla_decode_paged_{fmt}")
     B, s_q = q_c.shape[0], q_c.shape[1]
     T = B * s_q
     dev = q_c.device
-    kv8 = torch.empty((layers, kv.shape[1], 41216), dtype=torch.uint8, device=dev)
+    kv8 = torch.empty((layers, kv.shape[1], page_bytes), dtype=torch.uint8, device=dev)
     for l in range(layers):
-        M.mla_quantize_cache_fp8(kv[l], kv8[l])
+        quantize(kv[l], kv8[l])
     torch.cuda.synchronize()
     q_abs = torch.empty((B, s_q, 128, 512), dtype=torch.bfloat16, device=dev)
     o_part = torch.empty((B, s_q, 128, S, 512), dtype=torch.float32, device=dev)
@@ -237,7 +251,7 @@ def time_fp8_cache(M, torch, kv, tables, seqlens, lens, q_c, q_r, w_uk, w_uv, S,
         if e: e[0].record(stream)
         M.mla_absorb_q(q_c, w_uk, q_abs)
         if e: e[1].record(stream)
-        M.mla_decode_paged_fp8(q_abs, q_r, kv8[layer], tables[layer], seqlens, S, o_part=o_part, lse_part=lse_part)
+        scan(q_abs, q_r, kv8[layer], tables[layer], seqlens, S, o_part=o_part, lse_part=lse_part)
         if e: e[2].record(stream)
         M.mla_combine_up_proj(o_part, lse_part, w_uv, out, lse)
         if e: e[3].record(stream)
@@ -255,21 +269,20 @@ def time_fp8_cache(M, torch, kv, tables, seqlens, lens, q_c, q_r, w_uk, w_uv, S,
     torch.cuda.synchronize()
     per = [sum(ev[k][j].elapsed_time(ev[k][j + 1]) for k in range(steps)) / steps for j in range(3)]
     ms_step = wall / steps * 1e3
-    kv_bytes = sum(lens) * FP8_BYTES_PER_TOKEN
+    kv_bytes = sum(lens) * per_token
     dec_bytes = kv_bytes + q_bytes + olat_bytes
     dec_ms = per[1]
     del kv8
     return {
-        "cache": "c_KV in E4M3 with a power-of-two scale per token, k_R in bf16: "
-                 f"{FP8_BYTES_PER_TOKEN} bytes per token instead of {KV_BYTES_PER_TOKEN}",
+        "cache": f"{what}: {per_token} bytes per token instead of {KV_BYTES_PER_TOKEN}",
         "ms_per_step": round(ms_step, 4),
         "value_tflops": round(flop_step / (ms_step * 1e-3) / 1e12, 2),
-        "kernels_ms": {"mla_absorb_q": round(per[0], 4), "mla_decode_paged_fp8": round(dec_ms, 4),
+        "kernels_ms": {"mla_absorb_q": round(per[0], 4), f"mla_decode_paged_{fmt}": round(dec_ms, 4),
                        "mla_combine_up_proj": round(per[2], 4)},
         "decode_roofline": {"bound": "hbm", "achieved": round(dec_bytes / (dec_ms * 1e-3) / 1e9, 1),
                             "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": round(dec_bytes / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                            "traffic": measured_traffic(workload, S, fp8=True),
+                            "traffic": measured_traffic(workload, S, fmt),
                             "algorithmic_bytes_per_launch": dec_bytes,
                             "decode_tflops": round(flop_attn / (dec_ms * 1e-3) / 1e12, 1),
                             "mfma_frac": round(flop_attn / (dec_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
@@ -481,10 +494,13 @@ def main():
     print("[bench] one-launch step against the four kernels it fuses", file=sys.stderr, flush=True)
     result["next_rows"]["one_launch_step"] = time_one_launch_step(
         M, torch, kv, tables, seqlens, q_c, q_r, w_uk, w_uv, S, layers, args.steps, args.warmup)
-    if not args.no_fp8:
-        print("[bench] 8-bit cache: convert the resident layers, time the same steps", file=sys.stderr, flush=True)
-        result["next_rows"]["fp8_cache"] = time_fp8_cache(
-            M, torch, kv, tables, seqlens, lens, q_c, q_r, w_uk, w_uv, S, layers, args.steps, args.warmup,
+    for fmt, bits in (("fp8", 8), ("mxfp4", 4)):
+        if getattr(args, f"no_{fmt}"):
+            continue
+        print(f"[bench] {bits}-bit cache: convert the resident layers, time the same steps", file=sys.stderr,
+              flush=True)
+        result["next_rows"][f"{fmt}_cache"] = time_quantized_cache(
+            M, torch, fmt, kv, tables, seqlens, lens, q_c, q_r, w_uk, w_uv, S, layers, args.steps, args.warmup,
             flop_step, flop_attn, q_bytes, olat_bytes, cfg.name)
     if s_q > 1:
         # the decompressed branch the dispatch rule would take above 256 new
