@@ -689,8 +689,8 @@ __device__ __forceinline__ void decode_paged_body(
       // query's E4M3 hi and lo terms as in the 8-bit scan; then the four bf16
       // MFMAs of k_R. Between the MFMA pairs every thread dequantizes its
       // eighth of V(it) (token tid & 31, dims 64 (tid >> 5) .. +63) into the
-      // bf16 tile vbuf[it & 1], one 16-byte chunk per pair, zero past the
-      // visible length.
+      // bf16 tile vbuf[it & 1], one 16-byte chunk per pair; in the tail tile
+      // the rows past the visible length are then overwritten with zeros.
       const char* tb = lds + (it & (kStages - 1)) * F::bytes;
       DmaTarget t{nullptr, 0u};
       if constexpr (dma) t = dma_target(tile0 + it + 2, (it + 2) & (kStages - 1));
@@ -712,7 +712,6 @@ __device__ __forceinline__ void decode_paged_body(
       const u32x4 dc0 = *reinterpret_cast<const u32x4*>(tb + dt * kFp4RowBytes + (((2 * ds) ^ (dt & 7)) << 4));
       const u32x4 dc1 = *reinterpret_cast<const u32x4*>(tb + dt * kFp4RowBytes + (((2 * ds + 1) ^ (dt & 7)) << 4));
       const unsigned de = *reinterpret_cast<const unsigned short*>(tb + kStage4Scale + dt * 16 + 2 * ds);
-      const bool dok = (tile0 + it) * kTok + dt < t_end;
       char* const vrow = vbuf + (it & 1) * kStageBytes + dt * kRowBytes;
       auto dequant = [&](int j) {  // output chunk 8 ds + j (dims 64 ds + 8j .. +7)
         const unsigned w = (j < 4 ? dc0 : dc1)[j & 3];
@@ -721,9 +720,8 @@ __device__ __forceinline__ void decode_paged_body(
         const bf16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1);
         const bf16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2);
         const bf16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3);
-        bf16x8 v = bf16x8{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
-        if (!dok) v = bf16x8{};
-        *reinterpret_cast<bf16x8*>(vrow + (((8 * ds + j) ^ swz(dt)) << 4)) = v;
+        *reinterpret_cast<bf16x8*>(vrow + (((8 * ds + j) ^ swz(dt)) << 4)) =
+            bf16x8{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
       };
       u32x4 ka[2];
       ka[0] = kread(0);
@@ -760,6 +758,12 @@ __device__ __forceinline__ void decode_paged_body(
       }
       bf16x8 rf[2];
       rf[0] = *reinterpret_cast<const bf16x8*>(tb + rope8_off + (0 ^ rope8_x));
+      // the tail tile: this thread's rows past the visible length become zeros
+      // (written after its own chunks, and LDS writes of a wave land in order)
+      if ((tile0 + it + 1) * kTok > t_end && (tile0 + it) * kTok + dt >= t_end) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) *reinterpret_cast<bf16x8*>(vrow + (((8 * ds + j) ^ swz(dt)) << 4)) = bf16x8{};
+      }
       // the bf16 MFMAs below take S as srcC from a different MFMA shape: drain first
       mfma_result_fence(S);
       __builtin_amdgcn_sched_barrier(0);
