@@ -405,6 +405,15 @@ mla_status mla_decode_step_fp8(const void* q_c, const void* q_r, const void* kv_
                                void* q_abs, float* o_part, float* lse_part, float* o_lat, void* out, float* lse,
                                void* stream);
 
+/* mla_decode_step over the 4-bit cache (kv_fp4 uint8 [num_pages, 25600]);
+ * bit-identical to mla_absorb_q -> mla_decode_paged_mxfp4 -> mla_combine_splits
+ * -> mla_up_proj. */
+mla_status mla_decode_step_mxfp4(const void* q_c, const void* q_r, const void* kv_fp4, int64_t num_pages,
+                                 const int32_t* block_table, int max_pages, const int32_t* seqlens, int B, int s_q,
+                                 int H, const void* w_uk, const void* w_uv, float softmax_scale, int num_splits,
+                                 void* q_abs, float* o_part, float* lse_part, float* o_lat, void* out, float* lse,
+                                 void* stream);
+
 /* Test and debug aid: gather the logical cache rows of each sequence through
  * the block table with the same address arithmetic as mla_decode_paged.
  *   out bf16 [B, max_len, 576]: row t of sequence b is the cache row of token

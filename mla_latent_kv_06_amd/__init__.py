@@ -442,7 +442,7 @@ def decode_layer(q_c, q_r, kv_cache, block_table, seqlens, w_uk, w_uv, num_split
 def mla_decode_step(q_c, q_r, kv_cache, block_table, seqlens, w_uk, w_uv, num_splits: int,
                     softmax_scale: float = DEFAULT_SCALE, buffers: dict | None = None, stream=None):
     """The whole absorbed step in one launch (absorb -> scan -> merge -> up-projection),
-    bit-identical to decode_layer; kv_cache is the bf16 or the 8-bit cache.
+    bit-identical to decode_layer; kv_cache is the bf16, the 8-bit or the 4-bit cache.
     Returns dict(q_abs, o_part, lse_part, o_lat, lse, out); ``buffers`` may
     supply any of them preallocated."""
     B, s_q = q_c.shape[0], q_c.shape[1]
@@ -460,12 +460,14 @@ def mla_decode_step(q_c, q_r, kv_cache, block_table, seqlens, w_uk, w_uv, num_sp
     _need(q_r, "q_r", torch.bfloat16, (B, s_q, H, D_R))
     _need(w_uk, "w_uk", torch.bfloat16, (H, D_HC, D_C))
     _need(w_uv, "w_uv", torch.bfloat16, (H, D_HC, D_C))
-    if is_mxfp4_cache(kv_cache):
-        raise ValueError("the one-launch step reads the bf16 or the 8-bit cache; use decode_layer for the 4-bit one")
-    fp8 = is_fp8_cache(kv_cache)
-    if fp8:
+    if is_fp8_cache(kv_cache):
+        fn = "mla_decode_step_fp8"
         _need_fp8_cache(kv_cache, "kv_cache")
+    elif is_mxfp4_cache(kv_cache):
+        fn = "mla_decode_step_mxfp4"
+        _need_mxfp4_cache(kv_cache, "kv_cache")
     else:
+        fn = "mla_decode_step"
         if kv_cache.dim() != 3 or kv_cache.shape[1:] != (PAGE, ROW):
             raise ValueError(f"kv_cache must be [num_pages, 64, 576], got {tuple(kv_cache.shape)}")
         _need(kv_cache, "kv_cache", torch.bfloat16)
@@ -473,11 +475,11 @@ def mla_decode_step(q_c, q_r, kv_cache, block_table, seqlens, w_uk, w_uv, num_sp
         raise ValueError(f"block_table must be [B, max_pages], got {tuple(block_table.shape)}")
     _need(block_table, "block_table", torch.int32)
     _need(seqlens, "seqlens", torch.int32, (B,))
-    fn = _lib.LIB.mla_decode_step_fp8 if fp8 else _lib.LIB.mla_decode_step
-    _check(fn(_ptr(q_c), _ptr(q_r), _ptr(kv_cache), kv_cache.shape[0], _ptr(block_table), block_table.shape[1],
-              _ptr(seqlens), B, s_q, H, _ptr(w_uk), _ptr(w_uv), float(softmax_scale), S, _ptr(buf["q_abs"]),
-              _ptr(buf["o_part"]), _ptr(buf["lse_part"]), _ptr(buf["o_lat"]), _ptr(buf["out"]), _ptr(buf["lse"]),
-              _stream(stream)), "mla_decode_step_fp8" if fp8 else "mla_decode_step")
+    _check(getattr(_lib.LIB, fn)(
+        _ptr(q_c), _ptr(q_r), _ptr(kv_cache), kv_cache.shape[0], _ptr(block_table), block_table.shape[1],
+        _ptr(seqlens), B, s_q, H, _ptr(w_uk), _ptr(w_uv), float(softmax_scale), S, _ptr(buf["q_abs"]),
+        _ptr(buf["o_part"]), _ptr(buf["lse_part"]), _ptr(buf["o_lat"]), _ptr(buf["out"]), _ptr(buf["lse"]),
+        _stream(stream)), fn)
     return buf
 
 

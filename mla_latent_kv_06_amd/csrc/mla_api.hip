@@ -64,7 +64,7 @@ mla_status decode_step_any(const void* q_c, const void* q_r, const void* kv_cach
                            const int32_t* block_table, int max_pages, const int32_t* seqlens, int B, int s_q, int H,
                            const void* w_uk, const void* w_uv, float softmax_scale, int num_splits, void* q_abs,
                            float* o_part, float* lse_part, float* o_lat, void* out, float* lse, void* stream,
-                           bool fp8) {
+                           int fmt) {
   const mla::Check c = mla::check_step(q_c, q_r, kv_cache, num_pages, block_table, max_pages, seqlens, B, s_q, H, w_uk,
                                        w_uv, softmax_scale, num_splits, q_abs, o_part, lse_part, o_lat, out, lse);
   if (!c.ok()) return report(c);
@@ -88,8 +88,10 @@ mla_status decode_step_any(const void* q_c, const void* q_r, const void* kv_cach
   p.o_lat = o_lat;
   p.lse = lse;
   p.out = static_cast<__bf16*>(out);
-  return report_hip(mla::launch_decode_step(p, fp8, as_stream(stream)),
-                    fp8 ? "mla_decode_step_fp8 launch" : "mla_decode_step launch");
+  return report_hip(mla::launch_decode_step(p, fmt, as_stream(stream)),
+                    fmt == mla::kFmtFp8     ? "mla_decode_step_fp8 launch"
+                    : fmt == mla::kFmtMxfp4 ? "mla_decode_step_mxfp4 launch"
+                                            : "mla_decode_step launch");
 }
 
 }  // namespace
@@ -202,7 +204,7 @@ mla_status mla_decode_step(const void* q_c, const void* q_r, const void* kv_cach
                            const void* w_uk, const void* w_uv, float softmax_scale, int num_splits, void* q_abs,
                            float* o_part, float* lse_part, float* o_lat, void* out, float* lse, void* stream) {
   return decode_step_any(q_c, q_r, kv_cache, num_pages, block_table, max_pages, seqlens, B, s_q, H, w_uk, w_uv,
-                         softmax_scale, num_splits, q_abs, o_part, lse_part, o_lat, out, lse, stream, false);
+                         softmax_scale, num_splits, q_abs, o_part, lse_part, o_lat, out, lse, stream, mla::kFmtBf16);
 }
 
 mla_status mla_decode_step_fp8(const void* q_c, const void* q_r, const void* kv_fp8, int64_t num_pages,
@@ -211,7 +213,16 @@ mla_status mla_decode_step_fp8(const void* q_c, const void* q_r, const void* kv_
                                void* q_abs, float* o_part, float* lse_part, float* o_lat, void* out, float* lse,
                                void* stream) {
   return decode_step_any(q_c, q_r, kv_fp8, num_pages, block_table, max_pages, seqlens, B, s_q, H, w_uk, w_uv,
-                         softmax_scale, num_splits, q_abs, o_part, lse_part, o_lat, out, lse, stream, true);
+                         softmax_scale, num_splits, q_abs, o_part, lse_part, o_lat, out, lse, stream, mla::kFmtFp8);
+}
+
+mla_status mla_decode_step_mxfp4(const void* q_c, const void* q_r, const void* kv_fp4, int64_t num_pages,
+                                 const int32_t* block_table, int max_pages, const int32_t* seqlens, int B, int s_q,
+                                 int H, const void* w_uk, const void* w_uv, float softmax_scale, int num_splits,
+                                 void* q_abs, float* o_part, float* lse_part, float* o_lat, void* out, float* lse,
+                                 void* stream) {
+  return decode_step_any(q_c, q_r, kv_fp4, num_pages, block_table, max_pages, seqlens, B, s_q, H, w_uk, w_uv,
+                         softmax_scale, num_splits, q_abs, o_part, lse_part, o_lat, out, lse, stream, mla::kFmtMxfp4);
 }
 
 mla_status mla_combine_splits(const float* o_part, const float* lse_part, int B, int s_q, int H, int num_splits,

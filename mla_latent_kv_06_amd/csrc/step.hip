@@ -27,8 +27,12 @@ namespace mla {
 
 namespace {
 
-static_assert(kAbsorbLdsBytes <= decode_lds_bytes<kFmtFp8>() && kUpProjLdsBytes <= decode_lds_bytes<kFmtFp8>(),
-              "every phase fits in the scan's LDS");
+template <int kFmt>
+constexpr bool phases_fit() {
+  return kAbsorbLdsBytes <= decode_lds_bytes<kFmt>() && kUpProjLdsBytes <= decode_lds_bytes<kFmt>();
+}
+static_assert(phases_fit<kFmtBf16>() && phases_fit<kFmtFp8>() && phases_fit<kFmtMxfp4>(),
+              "every phase fits in the scan's LDS, for every cache format");
 
 }  // namespace
 
@@ -37,14 +41,13 @@ static_assert(kAbsorbLdsBytes <= decode_lds_bytes<kFmtFp8>() && kUpProjLdsBytes 
 // or the lengths and keeps their uniform loads on the scalar path, as in the
 // scan kernel; q_abs and o_lat are written by one phase and read by a later
 // one through the same pointer, after a grid barrier.
-template <bool kStream, bool kFp8>
+template <bool kStream, int kFmt>
 __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
     const __bf16* __restrict__ q_c, const __bf16* __restrict__ w_uk, const __bf16* __restrict__ w_uv,
     __bf16* __restrict__ q_abs, const __bf16* __restrict__ q_r, const char* __restrict__ kv,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seqlens, float* __restrict__ o_part,
     float* __restrict__ lse_part, float* __restrict__ o_lat, float* __restrict__ lse, __bf16* __restrict__ out,
     DecodeParams a) {
-  constexpr int kFmt = kFp8 ? kFmtFp8 : kFmtBf16;
   __shared__ __attribute__((aligned(1024))) char lds[decode_lds_bytes<kFmt>()];
   cooperative_groups::grid_group grid = cooperative_groups::this_grid();
   const int T = a.B * a.s_q;
@@ -77,14 +80,18 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
   }
 }
 
-hipError_t launch_decode_step(const StepParams& p, bool fp8, hipStream_t stream) {
+hipError_t launch_decode_step(const StepParams& p, int fmt, hipStream_t stream) {
   const void* fn;
-  if (fp8)
-    fn = p.d.s_q == 1 ? reinterpret_cast<const void*>(&decode_step_kernel<true, true>)
-                      : reinterpret_cast<const void*>(&decode_step_kernel<false, true>);
+  const bool stream1 = p.d.s_q == 1;
+  if (fmt == kFmtFp8)
+    fn = stream1 ? reinterpret_cast<const void*>(&decode_step_kernel<true, kFmtFp8>)
+                 : reinterpret_cast<const void*>(&decode_step_kernel<false, kFmtFp8>);
+  else if (fmt == kFmtMxfp4)
+    fn = stream1 ? reinterpret_cast<const void*>(&decode_step_kernel<true, kFmtMxfp4>)
+                 : reinterpret_cast<const void*>(&decode_step_kernel<false, kFmtMxfp4>);
   else
-    fn = p.d.s_q == 1 ? reinterpret_cast<const void*>(&decode_step_kernel<true, false>)
-                      : reinterpret_cast<const void*>(&decode_step_kernel<false, false>);
+    fn = stream1 ? reinterpret_cast<const void*>(&decode_step_kernel<true, kFmtBf16>)
+                 : reinterpret_cast<const void*>(&decode_step_kernel<false, kFmtBf16>);
   const __bf16* q_c = p.q_c;
   const __bf16* w_uk = p.w_uk;
   const __bf16* w_uv = p.w_uv;

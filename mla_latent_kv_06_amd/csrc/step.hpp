@@ -19,6 +19,6 @@ struct StepParams {
 
 // Cooperative launch of 256 workgroups (one per CU); fails with the runtime's
 // error if they cannot all be resident.
-hipError_t launch_decode_step(const StepParams& p, bool fp8, hipStream_t stream);
+hipError_t launch_decode_step(const StepParams& p, int fmt, hipStream_t stream);  // fmt: kFmt* of decode.hpp
 
 }  // namespace mla

@@ -26,7 +26,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) == 26, names
+    assert len(names) == 27, names
     out = subprocess.run(["nm", "-D", "--defined-only", os.path.join(ROOT, "mla_latent_kv_06_amd", "libmla.so")],
                          capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\bT (mla_[a-z0-9_]+)\b", out))
@@ -95,7 +95,7 @@ def test_other_entry_validation(lib):
     assert lib.mla_append_latent_mxfp4(A, A, A, 64, A, 4, A, 2, A, 2, 5000, None) == 2
     # one-launch step: q_c, q_r, kv, num_pages, bt, max_pages, seqlens, B, s_q, H, w_uk, w_uv, scale, S,
     # q_abs, o_part, lse_part, o_lat, out, lse
-    for fn in (lib.mla_decode_step, lib.mla_decode_step_fp8):
+    for fn in (lib.mla_decode_step, lib.mla_decode_step_fp8, lib.mla_decode_step_mxfp4):
         assert fn(None, A, A, 10, A, 4, A, 2, 1, 128, A, A, 0.07, 2, A, A, A, A, A, A, None) == 1
         assert fn(A, A, A, 10, A, 4, A, 2, 1, 128, A, None, 0.07, 2, A, A, A, A, A, A, None) == 1
         assert fn(A, A, A, 10, A, 4, A, 2, 1, 128, A, A, 0.07, 2, A, A, A, MIS, A, A, None) == 3

@@ -1,4 +1,4 @@
-"""GPU: the one-launch step (mla_decode_step, mla_decode_step_fp8) against the
+"""GPU: the one-launch step (mla_decode_step over the bf16, 8-bit and 4-bit caches) against the
 same four kernels launched one after another (bit for bit: every phase runs
 the kernel's own workgroup body), and against the fp64 oracle."""
 import math
@@ -26,7 +26,7 @@ def _say(msg):
     print(f"[gpu] {msg}", flush=True)
 
 
-def _case(lens, s_q, seed, fp8=False):
+def _case(lens, s_q, seed, fmt="bf16"):
     g = torch.Generator().manual_seed(seed)
     need = [-(-int(L) // 64) for L in lens]
     pool = sum(need) + 3
@@ -42,32 +42,37 @@ def _case(lens, s_q, seed, fp8=False):
     kv = torch.randn((pool, 64, 576), generator=g).to(torch.bfloat16)
     w_uk = (torch.randn((128, 128, 512), generator=g) / math.sqrt(512)).to(torch.bfloat16)
     w_uv = (torch.randn((128, 128, 512), generator=g) / math.sqrt(512)).to(torch.bfloat16)
-    cache = torch.from_numpy(O.pack_fp8_cache(O.bf16_bits(kv))) if fp8 else kv
+    cache = {"bf16": lambda: kv, "fp8": lambda: torch.from_numpy(O.pack_fp8_cache(O.bf16_bits(kv))),
+             "mxfp4": lambda: torch.from_numpy(O.pack_mxfp4_cache(O.bf16_bits(kv)))}[fmt]()
     return dict(q_c=q_c, q_r=q_r, kv=cache, bt=bt, sl=torch.tensor(lens, dtype=torch.int32), w_uk=w_uk, w_uv=w_uv)
 
 
 def _sequence(M, d, S):
     """absorb -> scan -> merge -> up-projection as four launches."""
     q_abs = M.mla_absorb_q(d["q_c"], d["w_uk"])
-    scan = M.mla_decode_paged_fp8 if M.is_fp8_cache(d["kv"]) else M.mla_decode_paged
+    scan = (M.mla_decode_paged_fp8 if M.is_fp8_cache(d["kv"]) else
+            M.mla_decode_paged_mxfp4 if M.is_mxfp4_cache(d["kv"]) else M.mla_decode_paged)
     o_part, lse_part = scan(q_abs, d["q_r"], d["kv"], d["bt"], d["sl"], S, SCALE)
     o_lat, lse = M.mla_combine_splits(o_part, lse_part)
     out = M.mla_up_proj(o_lat, d["w_uv"])
     return dict(q_abs=q_abs, o_part=o_part, lse_part=lse_part, o_lat=o_lat, lse=lse, out=out)
 
 
-@pytest.mark.parametrize("lens,s_q,S,fp8", [
-    ([2048], 1, 32, False),               # one short sequence, many splits
-    ([700] * 16, 1, 9, False),            # a batch of short sequences
-    ([1, 130, 2047, 0, 64], 1, 5, False),  # ragged, with an empty row
-    ([300, 77], 3, 3, False),             # causal chunk
-    ([2048], 1, 32, True),                # the 8-bit cache
-    ([700] * 16, 1, 9, True),
+@pytest.mark.parametrize("lens,s_q,S,fmt", [
+    ([2048], 1, 32, "bf16"),               # one short sequence, many splits
+    ([700] * 16, 1, 9, "bf16"),            # a batch of short sequences
+    ([1, 130, 2047, 0, 64], 1, 5, "bf16"),  # ragged, with an empty row
+    ([300, 77], 3, 3, "bf16"),             # causal chunk
+    ([2048], 1, 32, "fp8"),                # the 8-bit cache
+    ([700] * 16, 1, 9, "fp8"),
+    ([2048], 1, 32, "mxfp4"),              # the 4-bit cache
+    ([1, 130, 2047, 0, 64], 1, 5, "mxfp4"),
+    ([300, 77], 3, 3, "mxfp4"),
 ])
-def test_step_is_bit_identical_to_the_kernel_sequence(M, lens, s_q, S, fp8):
-    c = _case(lens, s_q, seed=len(lens) * 7 + s_q + S, fp8=fp8)
+def test_step_is_bit_identical_to_the_kernel_sequence(M, lens, s_q, S, fmt):
+    c = _case(lens, s_q, seed=len(lens) * 7 + s_q + S, fmt=fmt)
     d = {k: v.to(DEV) for k, v in c.items()}
-    _say(f"step lens={lens[:6]} s_q={s_q} S={S} fp8={fp8}")
+    _say(f"step lens={lens[:6]} s_q={s_q} S={S} cache={fmt}")
     ref = _sequence(M, d, S)
     got = M.mla_decode_step(d["q_c"], d["q_r"], d["kv"], d["bt"], d["sl"], d["w_uk"], d["w_uv"], S, SCALE)
     torch.cuda.synchronize()
