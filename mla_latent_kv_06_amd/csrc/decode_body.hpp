@@ -687,10 +687,10 @@ __device__ __forceinline__ void decode_paged_body(
       // the tile's E2M1 codes and their per-token, per-block E8M0 scales
       // (lane half g supplies K-block g: all of MX block 2m + g), B = the
       // query's E4M3 hi and lo terms as in the 8-bit scan; then the four bf16
-      // MFMAs of k_R. Between the MFMA pairs every thread dequantizes its
-      // eighth of V(it) (token tid & 31, dims 64 (tid >> 5) .. +63) into the
-      // bf16 tile vbuf[it & 1], one 16-byte chunk per pair; in the tail tile
-      // the rows past the visible length are then overwritten with zeros.
+      // MFMAs of k_R. Inside every MFMA pair each thread dequantizes one
+      // 16-byte chunk of its eighth of V(it) (token tid & 31, dims
+      // 64 (tid >> 5) .. +63) into the bf16 tile vbuf[it & 1]; in the tail
+      // tile the rows past the visible length are then overwritten with zeros.
       const char* tb = lds + (it & (kStages - 1)) * F::bytes;
       DmaTarget t{nullptr, 0u};
       if constexpr (dma) t = dma_target(tile0 + it + 2, (it + 2) & (kStages - 1));
@@ -742,6 +742,13 @@ __device__ __forceinline__ void decode_paged_body(
           mfma_scaled4_sel<2, false, false>(S, ka[m & 1], qhl[2 * m], sa[m >> 2], qsh[m >> 2]);
         else
           mfma_scaled4_sel<3, false, false>(S, ka[m & 1], qhl[2 * m], sa[m >> 2], qsh[m >> 2]);
+        // The second MFMA of the pair accumulates onto the first, so the wave
+        // cannot issue it (or anything after it) until the first is done: VALU
+        // work placed here issues while the first MFMA runs, work placed after
+        // the second while the second runs.
+        __builtin_amdgcn_sched_barrier(0);
+        dequant(m);
+        __builtin_amdgcn_sched_barrier(0);
         if ((m & 3) == 0)
           mfma_scaled4_sel<0, false, false>(S, ka[m & 1], qhl[2 * m + 1], sa[m >> 2], qsl[m >> 2]);
         else if ((m & 3) == 1)
@@ -753,7 +760,6 @@ __device__ __forceinline__ void decode_paged_body(
         if constexpr (dma) {
           if (m < F::dma) dma_piece(t, m, tile0 + it + 2);
         }
-        dequant(m);
         __builtin_amdgcn_sched_barrier(0);
       }
       bf16x8 rf[2];
