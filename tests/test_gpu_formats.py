@@ -152,3 +152,49 @@ def test_quantized_scans_on_a_causal_chunk(M, fmt):
     ref_o, ref_l = O.decode_absorbed(O.as_f64(q_abs), O.as_f64(q_r), cache, bt.numpy(), np.array(lens), SCALE)
     assert_bar(o_lat.cpu().numpy(), ref_o, f"{fmt} chunk o_lat")
     assert_lse(lse.cpu().numpy(), ref_l, f"{fmt} chunk lse")
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "mxfp4"])
+def test_decode_layer_replays_in_a_graph(M, fmt):
+    """The whole layer (absorb -> scan -> merge -> up-projection) captured in
+    one HIP graph over each cache format and replayed three times with new
+    queries copied in between (eager work and synchronisations between the
+    replays): every replay equals the eager call on the same queries, bit for
+    bit (the kernels' results do not depend on how they were launched)."""
+    lens = [700, 64, 1500]
+    g = torch.Generator().manual_seed(70)
+    need = [-(-L // 64) for L in lens]
+    pool = sum(need) + 2
+    order = torch.randperm(pool, generator=g)
+    bt = torch.full((len(lens), max(need)), -1, dtype=torch.int32)
+    off = 0
+    for b, n in enumerate(need):
+        bt[b, :n] = order[off:off + n].to(torch.int32)
+        off += n
+    kv = torch.randn((pool, 64, 576), generator=g).to(torch.bfloat16).to(DEV)
+    cache = {"bf16": lambda: kv, "fp8": lambda: M.mla_quantize_cache_fp8(kv),
+             "mxfp4": lambda: M.mla_quantize_cache_mxfp4(kv)}[fmt]()
+    w_uk = (torch.randn((128, 128, 512), generator=g) / math.sqrt(512)).to(torch.bfloat16).to(DEV)
+    w_uv = (torch.randn((128, 128, 512), generator=g) / math.sqrt(512)).to(torch.bfloat16).to(DEV)
+    btd, sld = bt.to(DEV), torch.tensor(lens, dtype=torch.int32, device=DEV)
+    qs = [(torch.randn((3, 1, 128, 128), generator=g).to(torch.bfloat16).to(DEV),
+           torch.randn((3, 1, 128, 64), generator=g).to(torch.bfloat16).to(DEV)) for _ in range(3)]
+    _say(f"decode layer in a HIP graph, cache={fmt}")
+    q_c, q_r = qs[0][0].clone(), qs[0][1].clone()
+    M.decode_layer(q_c, q_r, cache, btd, sld, w_uk, w_uv, num_splits=4)   # warm the allocator outside capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        r = M.decode_layer(q_c, q_r, cache, btd, sld, w_uk, w_uv, num_splits=4)
+    for rep, (qc, qr) in enumerate(qs):
+        q_c.copy_(qc)
+        q_r.copy_(qr)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = M.decode_layer(qc, qr, cache, btd, sld, w_uk, w_uv, num_splits=4)
+        torch.cuda.synchronize()
+        assert torch.equal(r["out"].view(torch.int16), ref["out"].view(torch.int16)), f"replay {rep}: out"
+        assert torch.equal(r["lse"], ref["lse"]), f"replay {rep}: lse"
+        assert torch.equal(r["o_lat"], ref["o_lat"]), f"replay {rep}: o_lat"
+    del graph
