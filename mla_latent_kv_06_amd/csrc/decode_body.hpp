@@ -817,10 +817,13 @@ __device__ __forceinline__ void decode_paged_body(
           mfma_scaled<true>(m & 3, S, ka[m & 1], qhl[2 * m], kscale, qsh[m >> 2]);
         else
           mfma_scaled<false>(m & 3, S, ka[m & 1], qhl[2 * m], kscale, qsh[m >> 2]);
-        mfma_scaled<false>(m & 3, S, ka[m & 1], qhl[2 * m + 1], kscale, qsl[m >> 2]);
+        // the lo MFMA accumulates onto the hi one: the DMA issues while hi runs
+        __builtin_amdgcn_sched_barrier(0);
         if constexpr (dma) {
           if (m < F::dma) dma_piece(t, m, tile0 + it + 2);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_scaled<false>(m & 3, S, ka[m & 1], qhl[2 * m + 1], kscale, qsl[m >> 2]);
         __builtin_amdgcn_sched_barrier(0);
       }
       bf16x8 rf[2];
