@@ -13,6 +13,12 @@
  *   merged by their log-sum-exp (stage 1 scan and stage 2 reduction of the
  *   MI355X Kimi K3 time-share study, jinnpan.com, "Inside the blocks").
  *
+ * Sections below, in order: the absorbed path (absorb, split scan, merge,
+ *   up-projection, and the merge fused with the up-projection); the cache
+ *   append and RoPE; the decompressed branch for long chunks and its
+ *   dispatch rule; the 8-bit (E4M3) and 4-bit (MXFP4) latent caches; the
+ *   whole step in one launch; test aids.
+ *
  * Conventions for every function below:
  *   - Pointers are DEVICE pointers unless stated otherwise, must be non-NULL
  *     and 16-byte aligned. Tensors are dense, row-major, innermost last.
