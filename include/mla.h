@@ -104,6 +104,24 @@ int mla_recommended_splits(int B, int s_q, int max_len, int num_cus);
  * [1, min(max_pages, 256)]. */
 int mla_plan_splits(const int32_t* seqlens_host, int B, int s_q, int max_pages, int num_cus);
 
+/* HOST function (test and debug aid): check a block table and its lengths
+ * against the contract of mla_decode_paged and the other paged calls, which
+ * do not check it on the device (they clamp every entry into the cache, so a
+ * bad entry reads another page's rows instead of faulting; the teardown page,
+ * section 5, lists such address faults among the gather's failure modes).
+ *   block_table int32 [B, max_pages], seqlens int32 [B]: HOST pointers
+ *   bad_seq, bad_page: HOST pointers (either may be NULL) that receive the
+ *     first offending sequence and logical page in (b, p) order; page -1
+ *     when the sequence's length is out of range; both -1 if all is valid
+ * Returns MLA_OK when every length lies in [0, max_pages * 64] and every
+ * entry a decode reads (logical pages p < ceil(L_b / 64)) lies in
+ * [0, num_pages); MLA_ERR_SHAPE otherwise (mla_last_error() names the entry);
+ * MLA_ERR_NULL for a NULL table or length array; MLA_ERR_SHAPE for
+ * B, max_pages or num_pages out of the ranges mla_decode_paged accepts.
+ * Entries past a sequence's pages are not examined. Reads only. */
+mla_status mla_validate_block_table(const int32_t* block_table, int max_pages, const int32_t* seqlens, int B,
+                                    int64_t num_pages, int* bad_seq, int* bad_page);
+
 /* Stage 1: split scan of the paged latent cache, absorbed scores, online
  * softmax, P . c_KV on matrix cores (teardown page, section 4 absorbed
  * scores; K3 study "Inside the blocks" stage 1).

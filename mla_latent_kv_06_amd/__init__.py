@@ -86,6 +86,23 @@ def mla_plan_splits(seqlens, max_pages: int, s_q: int = 1, cus: int | None = Non
                                         int(cus or num_cus())))
 
 
+def mla_validate_block_table(block_table, seqlens, num_pages: int):
+    """Host check of a block table against the paged calls' contract (the C
+    function of the same name): returns None when every length lies in
+    [0, max_pages * 64] and every entry a decode reads lies in [0, num_pages);
+    otherwise raises MlaError naming the first bad (sequence, page). Tensors
+    on a GPU are copied to the host first."""
+    bt = torch.as_tensor(block_table).to(device="cpu", dtype=torch.int32).contiguous()
+    lens = torch.as_tensor(seqlens).to(device="cpu", dtype=torch.int32).contiguous()
+    if bt.dim() != 2 or lens.dim() != 1 or bt.shape[0] != lens.numel():
+        raise ValueError("block_table must be [B, max_pages] and seqlens [B]")
+    import ctypes
+    bad_seq, bad_page = ctypes.c_int(-1), ctypes.c_int(-1)
+    st = _lib.LIB.mla_validate_block_table(bt.data_ptr(), int(bt.shape[1]), lens.data_ptr(), int(lens.numel()),
+                                           int(num_pages), ctypes.addressof(bad_seq), ctypes.addressof(bad_page))
+    _check(st, "mla_validate_block_table")
+
+
 def mla_decode_workspace_bytes(B: int, s_q: int, num_splits: int, heads: int = H) -> int:
     return int(_lib.LIB.mla_decode_workspace_bytes(int(B), int(s_q), int(heads), int(num_splits)))
 

@@ -26,6 +26,7 @@ SIGNATURES = {
     "mla_decode_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int]),
     "mla_recommended_splits": (c_int, [c_int, c_int, c_int, c_int]),
     "mla_plan_splits": (c_int, [c_void_p, c_int, c_int, c_int, c_int]),
+    "mla_validate_block_table": (c_int, [c_void_p, c_int, c_void_p, c_int, c_int64, c_void_p, c_void_p]),
     "mla_decode_paged": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_int, c_void_p, c_int, c_int,
                                  c_int, c_float, c_int, c_void_p, c_void_p, c_void_p]),
     "mla_combine_splits": (c_int, [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p]),

@@ -33,6 +33,9 @@ def compile_command(out: str = LIB) -> list[str]:
         # packed fp32 VALU ops are kept out of the device code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-Wno-unused-command-line-argument",
+        # inline asm that touches a reserved register (M0, EXEC, ...) without
+        # telling the compiler fails the build
+        "-Werror=inline-asm",
         "-o", out,
     ] + [os.path.join(CSRC, s) for s in SOURCES]
 

@@ -47,11 +47,12 @@ __device__ __forceinline__ int swz64(int row, int chunk) { return (chunk ^ ((row
 // One 16-byte-per-lane direct-to-LDS load: lane l's 16 bytes from
 // sbase + voff land at LDS byte address lds_addr + 16 l (lds_addr and sbase
 // uniform). Written as asm so that later LDS reads are not treated as
-// overlapping it; completion is tracked with explicit vmcnt waits. An SALU
-// write of M0 needs one wait state before the LDS-DMA instruction reads it.
+// overlapping it; completion is tracked with explicit vmcnt waits. lds_addr
+// is an operand bound to M0, so the compiler writes M0 itself; the s_nop is
+// the wait state an LDS-DMA instruction needs after an SALU write of M0.
 __device__ __forceinline__ void dma16(const char* sbase, unsigned voff, unsigned lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_addr)
-               : "memory", "m0");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds_addr)
+               : "memory");
 }
 
 // Workgroup barrier after this wave's own loads of the chunk have been

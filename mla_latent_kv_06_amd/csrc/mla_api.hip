@@ -112,6 +112,11 @@ const char* mla_status_string(int status) {
 
 const char* mla_last_error(void) { return g_last_error.c_str(); }
 
+mla_status mla_validate_block_table(const int32_t* block_table, int max_pages, const int32_t* seqlens, int B,
+                                    int64_t num_pages, int* bad_seq, int* bad_page) {
+  return report(mla::validate_block_table(block_table, max_pages, seqlens, B, num_pages, bad_seq, bad_page));
+}
+
 size_t mla_decode_workspace_bytes(int B, int s_q, int H, int num_splits) {
   return mla::workspace_bytes(B, s_q, H, num_splits);
 }

@@ -236,6 +236,57 @@ inline Check check_gather(const void* kv, int64_t num_pages, const void* bt, int
   return Check{};
 }
 
+// ---- block-table contract ------------------------------------------------
+// The decode, gather, append and decompression kernels read entry
+// block_table[b, p] for the logical pages p < ceil(L_b / 64) of every
+// sequence and clamp each entry into [0, num_pages) on the device, so a bad
+// entry never leaves the cache but silently yields another page's rows. This
+// host check reports the first entry (in (b, p) order) that breaks the
+// contract instead, and lengths outside [0, max_pages * 64] (the kernels clamp
+// those too). Entries past a sequence's pages are never read and may hold
+// anything (-1 by convention). bad_seq / bad_page (either may be NULL)
+// receive the offending sequence and logical page, or page -1 when the length
+// itself is out of range; both are -1 when the table is valid.
+inline Check validate_block_table(const int32_t* bt, int max_pages, const int32_t* seqlens, int B,
+                                  int64_t num_pages, int* bad_seq, int* bad_page) {
+  if (bad_seq) *bad_seq = -1;
+  if (bad_page) *bad_page = -1;
+  if (bt == nullptr) return fail(MLA_ERR_NULL, "%s is NULL", "block_table");
+  if (seqlens == nullptr) return fail(MLA_ERR_NULL, "%s is NULL", "seqlens");
+  MLA_TRY(need_range(num_pages, 1, (1LL << 40), "num_pages"));
+  MLA_TRY(need_range(max_pages, 1, (1 << 24), "max_pages"));
+  MLA_TRY(need_range(B, 1, (1 << 20), "B"));
+  const long long cap = (long long)max_pages * MLA_PAGE;
+  for (int b = 0; b < B; ++b) {
+    const long long L = seqlens[b];
+    if (L < 0 || L > cap) {
+      if (bad_seq) *bad_seq = b;
+      Check c;
+      c.status = MLA_ERR_SHAPE;
+      char buf[256];
+      std::snprintf(buf, sizeof buf, "seqlens[%d] = %lld outside [0, %lld] (max_pages * 64)", b, L, cap);
+      c.detail = buf;
+      return c;
+    }
+    const long long n = (L + MLA_PAGE - 1) / MLA_PAGE;
+    const int32_t* row = bt + (size_t)b * (size_t)max_pages;
+    for (long long p = 0; p < n; ++p) {
+      if (row[p] < 0 || row[p] >= num_pages) {
+        if (bad_seq) *bad_seq = b;
+        if (bad_page) *bad_page = (int)p;
+        Check c;
+        c.status = MLA_ERR_SHAPE;
+        char buf[256];
+        std::snprintf(buf, sizeof buf, "block_table[%d, %lld] = %d outside [0, %lld) (sequence of %lld tokens)", b,
+                      p, (int)row[p], (long long)num_pages, L);
+        c.detail = buf;
+        return c;
+      }
+    }
+  }
+  return Check{};
+}
+
 inline size_t workspace_bytes(int B, int s_q, int H, int num_splits) {
   if (B < 1 || s_q < 1 || H < 1 || num_splits < 1) return 0;
   return (size_t)B * s_q * H * num_splits * (MLA_D_C + 1) * sizeof(float);

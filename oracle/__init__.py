@@ -33,7 +33,7 @@ absorption script are not reproducible and are not used as a pin.
 from .mla_oracle import (  # noqa: F401
     as_f64, bf16_bits, bf16_bits_to_f64, default_scale, gather_rows, absorb, visible_len,
     scores_absorbed, softmax_rows, attend_absorbed, decode_absorbed,
-    decode_naive, up_proj, SCAN_GROUPS, scan_plan, decode_split, combine, decode_rows,
+    decode_naive, up_proj, decode_split, combine, decode_rows,
     latent_row_elems, latent_row_bytes, mha_kv_bytes_per_token_layer,
     ROPE_BASE, rope_angles, rope_rotate, chunk_positions, append_latent,
     PREFILL_ABSORPTION_THRESHOLD, uses_absorption, decompress_kv, rope_keys, attend_mha,

@@ -228,61 +228,35 @@ def up_proj(o_lat, w_uv) -> np.ndarray:
 # --------------------------------------------------------------------------
 
 
-SCAN_GROUPS = 256  # equal page ranges of the library's split plan
+def decode_split(q_abs, q_r, kv_cache, block_table, seqlens, scale: float, pieces, num_splits: int):
+    """Partials of a given split: stage 1 of the K3 study's "Inside the blocks"
+    (each split scans a page range of one row and keeps its own normalised
+    output and log-sum-exp).
 
-
-def scan_plan(row_pages, num_splits: int, groups: int = SCAN_GROUPS):
-    """The library's split plan: for each row (in (b, i) order) its pieces as
-    (slot, first page, end page) within the row.
-
-    The pages of all rows, concatenated in order, are cut into ``groups``
-    ranges of W pages; range k holds one piece of every row it touches. With
-    S = num_splits > 1, W = max(ceil(P_tot/groups), ceil((n_max-1)/(S-1)), 1)
-    and a row starting at page P gets slot k - P // W for its piece in range k;
-    with S = 1 rows are not cut (one piece, slot 0). Slots a row does not use
-    are empty. The combined result does not depend on the plan.
+    pieces[r] for row r = b * s_q + i lists that row's splits as
+    (slot, first page, end page): pages [first, end) of the row's visible keys
+    go to partial slot `slot`. The caller chooses the partition (any set of
+    disjoint page ranges; the combined result does not depend on it). Returns
+    o_part [B, s_q, H, S, d_c] (zero for an unused slot) and lse_part
+    [B, s_q, H, S] (-inf for an unused slot or an empty range).
     """
-    n = [int(x) for x in row_pages]
-    p_tot = sum(n)
-    plan = [[] for _ in n]
-    if p_tot == 0:
-        return plan
-    S = int(num_splits)
-    W = -(-p_tot // groups)
-    if S > 1:
-        W = max(W, -(-(max(n) - 1) // (S - 1)), 1)
-    P = 0
-    for r, nr in enumerate(n):
-        if nr > 0:
-            if S == 1:
-                plan[r].append((0, 0, nr))
-            else:
-                for k in range(P // W, (P + nr - 1) // W + 1):
-                    a_, e_ = max(k * W, P) - P, min((k + 1) * W, P + nr) - P
-                    plan[r].append((k - P // W, a_, e_))
-        P += nr
-    return plan
-
-
-def decode_split(q_abs, q_r, kv_cache, block_table, seqlens, scale: float, num_splits: int):
-    """Per-split partials of the library's plan (scan_plan): o_part [B, s_q, H, S, d_c]
-    (each normalised; zero for an empty slot), lse_part [B, s_q, H, S] (-inf for an
-    empty slot)."""
     q_abs = np.asarray(q_abs, np.float64)
     q_r = np.asarray(q_r, np.float64)
     B, s_q, Hn, d_c = q_abs.shape
     page = (kv_cache.shape if isinstance(kv_cache, PagedQuantCache) else np.asarray(kv_cache).shape)[1]
+    if len(pieces) != B * s_q:
+        raise ValueError("one list of pieces per query row")
     o = np.zeros((B, s_q, Hn, num_splits, d_c))
     lse = np.full((B, s_q, Hn, num_splits), -np.inf)
-    vis = [[max(visible_len(int(seqlens[b]), s_q, i), 0) for i in range(s_q)] for b in range(B)]
-    plan = scan_plan([-(-v // page) for row in vis for v in row], num_splits)
     for b in range(B):
         L = int(seqlens[b])
         rows = np.asarray(gather_rows(kv_cache, block_table[b], max(L, 0)), np.float64)
         C, R = _split_row(rows, d_c)
         for i in range(s_q):
-            n = vis[b][i]
-            for s, p0, p1 in plan[b * s_q + i]:
+            n = max(visible_len(L, s_q, i), 0)
+            for s, p0, p1 in pieces[b * s_q + i]:
+                if not (0 <= s < num_splits and 0 <= p0 <= p1):
+                    raise ValueError(f"bad piece {(s, p0, p1)}")
                 t0, t1 = p0 * page, min(p1 * page, n)
                 o[b, i, :, s], lse[b, i, :, s] = attend_absorbed(
                     q_abs[b, i], q_r[b, i], C[t0:t1], R[t0:t1], scale)

@@ -26,7 +26,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) == 27, names
+    assert len(names) == 28, names
     out = subprocess.run(["nm", "-D", "--defined-only", os.path.join(ROOT, "mla_latent_kv_06_amd", "libmla.so")],
                          capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\bT (mla_[a-z0-9_]+)\b", out))
@@ -196,3 +196,34 @@ def test_plan_splits(lib):
     # degenerate inputs
     assert lib.mla_plan_splits(None, 4, 1, 8, 256) == 1
     assert plan([0, 0], 4) == 1
+
+
+def test_validate_block_table(lib):
+    """The host check of the block-table contract: first bad (sequence, page)
+    in order, lengths past the table, -1 tails ignored (teardown page,
+    section 5: the gather's address faults)."""
+    import numpy as np
+
+    def run(bt, lens, num_pages):
+        bt = np.ascontiguousarray(bt, np.int32)
+        lens = np.ascontiguousarray(lens, np.int32)
+        bs, bp = ctypes.c_int(7), ctypes.c_int(7)
+        st = lib.mla_validate_block_table(bt.ctypes.data, bt.shape[1], lens.ctypes.data, len(lens), num_pages,
+                                          ctypes.addressof(bs), ctypes.addressof(bp))
+        return st, bs.value, bp.value
+
+    bt = [[3, 0, -1, -1], [1, 2, 4, -5]]
+    assert run(bt, [65, 130], 5) == (0, -1, -1)          # tails past ceil(L/64) are not read
+    assert run(bt, [0, 1], 5) == (0, -1, -1)
+    assert run(bt, [129, 10], 5) == (2, 0, 2)            # sequence 0 needs page 2 (-1)
+    assert b"block_table[0, 2] = -1" in lib.mla_last_error()
+    assert run(bt, [65, 130], 4) == (2, 1, 2)            # entry 4 outside [0, 4)
+    assert run(bt, [65, 257], 5) == (2, 1, -1)           # length past max_pages * 64
+    assert run(bt, [-1, 3], 5) == (2, 0, -1)
+    assert run(bt, [65, 130], 0)[0] == 2
+    assert lib.mla_validate_block_table(None, 4, A, 1, 5, None, None) == 1
+    assert lib.mla_validate_block_table(A, 4, None, 1, 5, None, None) == 1
+    # NULL out-pointers are allowed
+    arr = np.zeros((1, 1), np.int32)
+    ln = np.array([64], np.int32)
+    assert lib.mla_validate_block_table(arr.ctypes.data, 1, ln.ctypes.data, 1, 1, None, None) == 0

@@ -17,6 +17,7 @@ import torch
 
 import oracle as O
 from mla_inputs import make_inputs, random_mxfp4_pages
+from tests._plan import header_pieces, row_pages
 from tests._bars import assert_bar, assert_lse
 
 pytestmark = pytest.mark.gpu
@@ -72,7 +73,8 @@ def _decode4_check(M, q_abs, q_r, pages, bt, sl, S, what, check_parts=True):
     assert_bar(o_lat.cpu().numpy(), ref_o, f"{what} o_lat")
     assert_lse(lse.cpu().numpy(), ref_l, f"{what} lse")
     if check_parts:
-        rp_o, rp_l = O.decode_split(O.as_f64(q_abs), O.as_f64(q_r), cache, bt.numpy(), sl.numpy(), SCALE, S)
+        rp_o, rp_l = O.decode_split(O.as_f64(q_abs), O.as_f64(q_r), cache, bt.numpy(), sl.numpy(), SCALE,
+                                    header_pieces(row_pages(sl.tolist(), q_abs.shape[1]), S), S)
         assert_lse(lse_part.cpu().numpy(), rp_l, f"{what} lse_part")
         live = np.isfinite(rp_l)
         assert_bar(o_part.cpu().numpy()[live], rp_o[live], f"{what} o_part")

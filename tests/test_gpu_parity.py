@@ -14,6 +14,7 @@ import torch
 
 import oracle as O
 from mla_inputs import CONFIGS, Config, make_inputs, make_structure
+from tests._plan import header_pieces, row_pages
 from tests._bars import assert_bar, assert_lse
 
 pytestmark = pytest.mark.gpu
@@ -71,7 +72,8 @@ def _decode_check(M, q_abs, q_r, kv, bt, sl, num_splits, what, check_parts=True)
     assert_bar(o_lat.cpu().numpy(), ref_o, f"{what} o_lat")
     assert_lse(lse.cpu().numpy(), ref_l, f"{what} lse")
     if check_parts:
-        rp_o, rp_l = O.decode_split(O.as_f64(q_abs), O.as_f64(q_r), kvb, bt.numpy(), sl.numpy(), SCALE, num_splits)
+        rp_o, rp_l = O.decode_split(O.as_f64(q_abs), O.as_f64(q_r), kvb, bt.numpy(), sl.numpy(), SCALE,
+                                    header_pieces(row_pages(sl.tolist(), q_abs.shape[1]), num_splits), num_splits)
         assert_lse(lse_part.cpu().numpy(), rp_l, f"{what} lse_part")
         # rows of empty splits are not written: compare the others only
         live = np.isfinite(rp_l)
@@ -244,11 +246,12 @@ def test_decode_ragged_plan_leaves_empty_splits_unwritten_and_unread(M):
     ref_o, ref_l = O.decode_absorbed(O.as_f64(q_abs), O.as_f64(q_r), kvb, bt.numpy(), sl.numpy(), SCALE)
     assert_bar(o_lat.cpu().numpy(), ref_o, "ragged plan o_lat")
     assert_lse(lse.cpu().numpy(), ref_l, "ragged plan lse")
-    rp_o, rp_l = O.decode_split(O.as_f64(q_abs), O.as_f64(q_r), kvb, bt.numpy(), sl.numpy(), SCALE, S)
+    plan = header_pieces(row_pages(sl.tolist(), 1), S)
+    rp_o, rp_l = O.decode_split(O.as_f64(q_abs), O.as_f64(q_r), kvb, bt.numpy(), sl.numpy(), SCALE, plan, S)
     assert_lse(lse_part.cpu().numpy(), rp_l, "ragged plan lse_part")
     live = np.isfinite(rp_l)
     used = live.reshape(B, 128, S)[:, 0, :].sum(1).tolist()
-    assert used == [len(p) for p in O.scan_plan([-(-L // 64) for L in lens], S)], used
+    assert used == [len(p) for p in plan], used
     assert min(used) < S
     op = o_part.cpu().numpy()
     assert_bar(op[live], rp_o[live], "ragged plan o_part")

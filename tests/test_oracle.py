@@ -303,49 +303,55 @@ def test_page_permutation_invariance():
 # split scan + combine
 # --------------------------------------------------------------------------
 
-def test_scan_plan_covers_rows_and_balances():
-    g = np.random.default_rng(5)
-    for rows in ([1024] * 16, [64] * 16, list(g.integers(0, 513, 64)), [0, 0, 3], [1], [260] * 1024,
-                 list(g.integers(0, 40, 300))):
-        p_tot, n_max = sum(rows), max(rows)
-        for S in (1, 2, 7, 16, 17, 64):
-            plan = O.scan_plan(rows, S)
-            W = -(-p_tot // O.SCAN_GROUPS) if p_tot else 1
-            if S > 1 and p_tot:
-                W = max(W, -(-(n_max - 1) // (S - 1)), 1)
-            load = {}
-            P = 0
-            for nr, pieces in zip(rows, plan):
-                # every page of the row exactly once, slots distinct and < S
-                covered = sorted(p for _, a, e in pieces for p in range(a, e))
-                assert covered == list(range(nr))
-                slots = [s_ for s_, _, _ in pieces]
-                assert len(set(slots)) == len(slots) and all(0 <= s_ < S for s_ in slots)
-                for s_, a, e in pieces:
-                    k = (P + a) // W if S > 1 else P // W
-                    assert k < O.SCAN_GROUPS
-                    if S > 1:
-                        assert (P + e - 1) // W == k  # a piece never crosses a range border
-                    load[k] = load.get(k, 0) + (e - a)
-                P += nr
-            if S > 1 and load:
-                assert max(load.values()) <= W
-    # equal rows that the ranges divide evenly: one piece per range
-    plan = O.scan_plan([1024] * 16, 17)
-    assert all(len(p) == 16 and [s for s, _, _ in p] == list(range(16)) for p in plan)
-    assert all(e - a == 64 for p in plan for _, a, e in p)
+def _random_pieces(row_pages, num_splits, rng):
+    """An arbitrary page-aligned partition of every row into at most num_splits
+    pieces (cut points drawn at random, empty pieces allowed, slots shuffled)."""
+    out = []
+    for n in row_pages:
+        k = int(rng.integers(1, num_splits + 1))
+        cuts = np.sort(rng.integers(0, n + 1, size=k - 1)) if k > 1 else np.array([], int)
+        edges = [0] + [int(c) for c in cuts] + [int(n)]
+        slots = rng.permutation(num_splits)[:k]
+        out.append([(int(s_), edges[j], edges[j + 1]) for j, s_ in enumerate(slots)])
+    return out
 
 
 @pytest.mark.parametrize("num_splits", [1, 2, 7, 20])
 def test_split_invariance(num_splits):
+    """Any page-aligned partition merges to the unsplit result (K3 study,
+    "Inside the blocks": stage 2 reduces the per-split partials exactly)."""
     inp = tiny_inputs(B=3, s_q=2, seqlens=[300, 64, 129], h=4, d_hc=8, d_c=32, d_r=8, page=16, seed=12)
     n = {k: v.numpy() for k, v in inp.items()}
     qa = O.absorb(n["q_c"], n["w_uk"])
     ref_o, ref_l = O.decode_absorbed(qa, n["q_r"], n["kv_cache"], n["block_table"], n["seqlens"], 0.25)
-    op, lp = O.decode_split(qa, n["q_r"], n["kv_cache"], n["block_table"], n["seqlens"], 0.25, num_splits)
-    o, l = O.combine(op, lp)
-    np.testing.assert_allclose(o, ref_o, rtol=1e-12, atol=1e-14)
-    np.testing.assert_allclose(l, ref_l, rtol=1e-13, atol=1e-13)
+    rows = [-(-max(int(L) - 2 + i + 1, 0) // 16) for L in n["seqlens"] for i in range(2)]
+    rng = np.random.default_rng(num_splits)
+    for _ in range(3):
+        pieces = _random_pieces(rows, num_splits, rng)
+        op, lp = O.decode_split(qa, n["q_r"], n["kv_cache"], n["block_table"], n["seqlens"], 0.25, pieces,
+                                num_splits)
+        o, l = O.combine(op, lp)
+        np.testing.assert_allclose(o, ref_o, rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(l, ref_l, rtol=1e-13, atol=1e-13)
+
+
+def test_split_piece_is_the_attention_over_its_range():
+    """One piece's partial is the plain softmax attention over its own keys:
+    brute force over the tokens of pages [1, 3) of a row."""
+    inp = tiny_inputs(B=1, s_q=1, seqlens=[70], h=2, d_hc=4, d_c=8, d_r=2, page=16, seed=21)
+    n = {k: v.numpy() for k, v in inp.items()}
+    qa = O.absorb(n["q_c"], n["w_uk"])
+    op, lp = O.decode_split(qa, n["q_r"], n["kv_cache"], n["block_table"], n["seqlens"], 0.5, [[(1, 1, 3)]], 3)
+    rows = O.gather_rows(n["kv_cache"], n["block_table"][0], 70)
+    for h in range(2):
+        s = [0.5 * (sum(qa[0, 0, h, c] * rows[t, c] for c in range(8)) +
+                    sum(n["q_r"][0, 0, h, d] * rows[t, 8 + d] for d in range(2))) for t in range(16, 48)]
+        m = max(s)
+        w = [math.exp(x - m) for x in s]
+        ref = [sum(w[k] * rows[16 + k, c] for k in range(32)) / sum(w) for c in range(8)]
+        np.testing.assert_allclose(op[0, 0, h, 1], ref, rtol=1e-12, atol=1e-14)
+        assert lp[0, 0, h, 1] == pytest.approx(m + math.log(sum(w)), abs=1e-12)
+        assert np.isneginf(lp[0, 0, h, [0, 2]]).all() and not op[0, 0, h, [0, 2]].any()
 
 
 def test_combine_closed_forms():
@@ -828,7 +834,9 @@ def test_mxfp4_cache_decode_is_attention_over_stored_values():
     o_ref, l_ref = O.decode_absorbed(qa, qr, stored, bt, sl, O.default_scale())
     assert np.array_equal(o4, o_ref) and np.array_equal(l4, l_ref)
     # the split oracle reads the 4-bit cache the same way
-    os_, ls_ = O.decode_split(qa, qr, cache4, bt, sl, O.default_scale(), 3)
+    rows = [-(-max(int(L) - 2 + i + 1, 0) // 64) for L in sl for i in range(2)]
+    pieces = _random_pieces(rows, 3, np.random.default_rng(4))
+    os_, ls_ = O.decode_split(qa, qr, cache4, bt, sl, O.default_scale(), pieces, 3)
     oc, lc = O.combine(os_, ls_)
     assert np.allclose(oc, o_ref, rtol=0, atol=1e-12) and np.allclose(lc, l_ref, rtol=0, atol=1e-12)
     # k_R is stored exactly; c_KV within half the coarsest E2M1 spacing of its block

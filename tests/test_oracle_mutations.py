@@ -45,14 +45,16 @@ def test_causal_off_by_one_is_caught(monkeypatch):
     _expect_fail(lambda: pins.test_brute_force_tiny([7, 10], 3))
 
 
-def test_split_plan_losing_last_page_is_caught(monkeypatch):
-    real = M.scan_plan
+def test_split_losing_last_page_is_caught(monkeypatch):
+    real = M.decode_split
 
-    def lossy(rows, S, groups=M.SCAN_GROUPS):
-        return [[(s, a, e - 1 if e == nr and e - 1 > a else e) for s, a, e in pieces]
-                for nr, pieces in zip(rows, real(rows, S, groups))]
-    _patch(monkeypatch, "scan_plan", lossy)
-    _expect_fail(lambda: pins.test_split_invariance(2), pins.test_scan_plan_covers_rows_and_balances)
+    def lossy(q_abs, q_r, kv, bt, sl, scale, pieces, num_splits):
+        # every piece that ends a row stops one page short
+        short = [[(s_, a, e - 1 if e - 1 > a and e == max(x[2] for x in row) else e) for s_, a, e in row]
+                 for row in pieces]
+        return real(q_abs, q_r, kv, bt, sl, scale, short, num_splits)
+    _patch(monkeypatch, "decode_split", lossy)
+    _expect_fail(lambda: pins.test_split_invariance(2))
 
 
 def test_gather_ignoring_block_table_is_caught(monkeypatch):
