@@ -1,26 +1,35 @@
 """Benchmark: absorbed MLA decode over a paged latent cache on one MI355X.
 
 A step is one pass of the whole hot path for one layer: mla_absorb_q ->
-mla_decode_paged -> stage 2 + up-projection (mla_combine_up_proj, one pass;
---separate-stage2 runs mla_combine_splits and mla_up_proj instead). The default workload is
-B=16 sequences of 65536 cached tokens with 60 layers of latent cache resident
-(72.5 GB); step k uses layer k mod 60, so every step reads its 1.2 GB of cache
-from HBM (it cannot be served by the 256 MB last-level cache).
+mla_decode_paged -> stage 2 fused with the up-projection (mla_combine_up_proj;
+--separate-stage2 runs mla_combine_splits and mla_up_proj instead). The
+headline workload (--workload, default "long") is B=16 sequences of 65536
+cached tokens with 60 layers of latent cache resident (72.5 GB); step k uses
+layer k mod 60, so every step reads its 1.2 GB of cache from HBM. The other
+four workloads are measured the same way, each rotating through enough
+resident layers (>= 2 GiB) that no step is served by the 256 MB last-level
+cache.
 
-Prints one JSON line (rank 0):
-  value            whole-step throughput, algorithmic TFLOP/s
-  roofline         the dominant kernel (mla_decode_paged) against HBM
-  cpu_baseline     the fp64 CPU oracle on a bounded sample of the workload
-plus effective KV GB/s, per-kernel times and, under next_rows, the cache
-append and query rotation, the step as one launch (mla_decode_step) against
-the four kernels it fuses, the same step over the 8-bit cache
-(mla_decode_paged_fp8) and over the 4-bit cache (mla_decode_paged_mxfp4), and
-for chunks of s_q > 1 the decompressed branch.
+Order of the run: every workload's inputs are built first; then the other
+workloads are measured and the headline last, back to back, so that its few
+warmup steps do not start from an idle board (this board's power controller
+runs the first ~40 launches of sustained load up to 1.5x slower); then the
+headline's next rows; then the CPU baseline.
+
+Prints one JSON line:
+  value         whole-step throughput of the headline workload, algorithmic TFLOP/s
+  roofline      mla_decode_paged on the headline workload against the roof its
+                arithmetic intensity selects (HBM below the ridge, bf16 MFMA above)
+  configs       every workload: decode and step times, intensity, binding roof, fraction
+  cpu_baseline  the fp64 CPU oracle on a bounded sample of every workload
+  next_rows     for the headline: cache append and query rotation, the scan over the
+                8-bit and 4-bit caches, the decompressed branch (chunks with s_q > 1)
+Per-kernel times come from HIP events recorded around each launch inside the K
+timed steps, on the stream the kernels run on.
 """
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -30,36 +39,42 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
-MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+RIDGE = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)   # 312.5 FLOP per byte
 FLOP_PER_PAIR = 128 * 2 * (576 + 512)  # all heads, one (query, key) pair: QK over 576 + PV over 512
 KV_BYTES_PER_TOKEN = 576 * 2
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_paged_long_hbm_traffic.json")
-TRAFFIC_FILES = {
-    "bf16": TRAFFIC_FILE,
-    "fp8": os.path.join(ROOT, "profiles", "decode_paged_fp8_long_hbm_traffic.json"),
-    "mxfp4": os.path.join(ROOT, "profiles", "decode_paged_mxfp4_long_hbm_traffic.json"),
-}
+WORKLOAD_ORDER = ("single", "uniform", "ragged", "prefill", "long")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 FORMAT_HEADERS = {"bf16": (), "fp8": ("fp8_cache.hpp",), "mxfp4": ("mxfp4_cache.hpp",)}
+QUANT_FORMATS = {
+    # page bytes, bytes per token, what the cache holds
+    "fp8": (41216, 512 + 64 * 2 + 4, "c_KV in E4M3 with a power-of-two scale per token, k_R in bf16"),
+    "mxfp4": (25600, 256 + 64 * 2 + 16, "c_KV in MXFP4 (E2M1 with an E8M0 scale per 32 dims), k_R in bf16"),
+}
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=100)
-    # the board's power controller overshoots during the first ~15 ms of
-    # sustained load (decode slows by up to 40%, then recovers); 100 warmup
-    # steps (~30 ms) start the timed region in the settled state
     p.add_argument("--warmup", type=int, default=100)
-    p.add_argument("--workload", default="long", choices=["single", "uniform", "ragged", "long", "prefill"])
-    p.add_argument("--layers", type=int, default=0, help="resident cache layers (0: workload default)")
-    p.add_argument("--splits", type=int, default=0, help="num_splits (0: library recommendation)")
+    p.add_argument("--workload", default="long", choices=list(WORKLOAD_ORDER),
+                   help="the headline workload (the JSON line's value and roofline)")
+    p.add_argument("--configs", default="all", choices=["all", "headline"],
+                   help="measure every workload (default) or the headline only")
+    p.add_argument("--layers", type=int, default=0, help="resident cache layers of the headline (0: default)")
+    p.add_argument("--splits", type=int, default=0, help="num_splits of the headline (0: mla_plan_splits)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--separate-stage2", action="store_true",
                    help="run mla_combine_splits and mla_up_proj as two kernels instead of mla_combine_up_proj")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle time for the baseline")
+    p.add_argument("--no-next", action="store_true", help="skip the next rows (append, quantized caches, ...)")
     p.add_argument("--no-fp8", action="store_true", help="skip the 8-bit cache leg")
     p.add_argument("--no-mxfp4", action="store_true", help="skip the 4-bit cache leg")
+    p.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay of the step")
+    p.add_argument("--one-launch", action="store_true",
+                   help="also time mla_decode_step (one cooperative launch) against the four kernels")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only copy 1 GiB device to device three times (the known-size reference for "
                         "rocprofv3 FETCH_SIZE / WRITE_SIZE) and exit")
@@ -75,7 +90,26 @@ def visible_pairs(seqlens, s_q):
     return tot
 
 
+def roof(flop, nbytes, seconds, peak_dtype="bf16"):
+    """The roof a kernel's arithmetic intensity selects, and its fraction.
+    Below the ridge (312.5 FLOP/byte) it is HBM bandwidth, above it the dense
+    bf16 MFMA rate; both fractions are given."""
+    intensity = flop / nbytes
+    gbs = nbytes / seconds / 1e9
+    tfs = flop / seconds / 1e12
+    hbm, mfma = gbs / HBM_PEAK_GBS, tfs / MFMA_BF16_PEAK_TFLOPS
+    if intensity > RIDGE:
+        r = {"bound": "mfma", "achieved": round(tfs, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+             "frac": round(mfma, 4), "peak_dtype": peak_dtype}
+    else:
+        r = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(hbm, 4)}
+    r.update({"intensity_flop_per_byte": round(intensity, 1), "ridge_flop_per_byte": RIDGE,
+              "hbm_frac": round(hbm, 4), "mfma_frac": round(mfma, 4), "tflops": round(tfs, 1), "gbps": round(gbs, 1)})
+    return r
+
+
 def kernel_source_digest(fmt="bf16"):
+    import hashlib
     h = hashlib.sha256()
     for f in ("decode.hip", "decode_body.hpp", "mla_device.hpp", "decode.hpp") + FORMAT_HEADERS[fmt]:
         with open(os.path.join(ROOT, "mla_latent_kv_06_amd", "csrc", f), "rb") as fh:
@@ -84,60 +118,151 @@ def kernel_source_digest(fmt="bf16"):
 
 
 def measured_traffic(workload, splits, fmt="bf16"):
-    """HBM bytes per decode launch from committed rocprofv3 counter runs, if they
-    were taken on the current kernel source and launch configuration."""
+    """HBM bytes (read + written) per decode launch from the committed rocprofv3
+    counter runs, if they were taken on the current kernel source and launch
+    configuration; None otherwise."""
     try:
-        with open(TRAFFIC_FILES[fmt]) as f:
-            t = json.load(f)
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f).get(f"{fmt}/{workload}")
     except (OSError, ValueError):
         return None
-    if (t.get("kernel_digest") != kernel_source_digest(fmt) or t.get("workload") != workload
-            or t.get("splits") != splits):
+    if not t or t.get("kernel_digest") != kernel_source_digest(fmt) or t.get("splits") != splits:
         return None
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(inp_cpu, q_abs_cpu, target_s):
-    """fp64 oracle (absorbed path) on whole sequences of the workload until ~target_s."""
-    import numpy as np
-    import oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:
-        threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
-    kvb = O.bf16_bits(inp_cpu["kv_cache"])
-    bt = inp_cpu["block_table"].numpy()
-    sl = inp_cpu["seqlens"].numpy()
-    qa = O.as_f64(q_abs_cpu)
-    qr = O.as_f64(inp_cpu["q_r"])
-    s_q = qa.shape[1]
-    scale = 1.0 / math.sqrt(192)
-    t0 = time.perf_counter()
-    done, flop = 0, 0.0
-    while time.perf_counter() - t0 < target_s:
-        b = done % qa.shape[0]
-        O.decode_absorbed(qa[b:b + 1], qr[b:b + 1], kvb, bt[b:b + 1], sl[b:b + 1], scale)
-        flop += visible_pairs([int(sl[b])], s_q) * FLOP_PER_PAIR
-        done += 1
-    dt = time.perf_counter() - t0
-    return {
-        "value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-        "sample": f"fp64 numpy absorbed path (gather, scores, softmax, P.c_KV) over {done} whole sequences "
-                  f"(cycling through the {qa.shape[0]} of layer 0), all 128 heads, {dt:.1f} s; "
-                  f"host logical CPUs {os.cpu_count()}, "
-                  f"affinity {len(os.sched_getaffinity(0))}",
-        "seconds": dt,
-    }
+class Workload:
+    """One workload's inputs resident on the device, its preallocated outputs
+    and the algorithmic work of one step."""
+
+    def __init__(self, M, torch, name, dev, layers=0, splits=0, separate=False):
+        from mla_inputs import CONFIGS, make_cache_on_device, make_inputs, make_structure
+        self.M, self.torch, self.name, self.separate = M, torch, name, separate
+        cfg = self.cfg = CONFIGS[name]
+        inp = make_inputs(cfg, seed=42, with_cache=False)
+        st0 = make_structure(cfg, seed=42)
+        self.layer_bytes = st0.num_pages * 64 * 576 * 2
+        self.layers = layers or max(cfg.layers, math.ceil(2 * 2**30 / self.layer_bytes))
+        self.kv = make_cache_on_device(st0.num_pages, self.layers, seed=1234, device=dev)
+        self.tables = torch.stack([make_structure(cfg, seed=42 + l).block_table
+                                   for l in range(self.layers)]).to(dev)
+        self.seqlens = st0.seqlens.to(dev)
+        self.seqlens_cpu = st0.seqlens
+        self.inp_cpu = inp
+        self.q_c, self.q_r = inp.q_c.to(dev), inp.q_r.to(dev)
+        self.w_uk, self.w_uv = inp.w_uk.to(dev), inp.w_uv.to(dev)
+        self.lens = [int(x) for x in st0.seqlens]
+        self.B, self.s_q = cfg.B, cfg.s_q
+        T = self.T = self.B * self.s_q
+        self.S = splits or M.mla_plan_splits(self.lens, self.tables.shape[2], self.s_q)
+        B, s_q, S = self.B, self.s_q, self.S
+        self.q_abs = torch.empty((B, s_q, 128, 512), dtype=torch.bfloat16, device=dev)
+        self.o_part = torch.empty((B, s_q, 128, S, 512), dtype=torch.float32, device=dev)
+        self.lse_part = torch.empty((B, s_q, 128, S), dtype=torch.float32, device=dev)
+        self.o_lat = torch.empty((B, s_q, 128, 512), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((B, s_q, 128), dtype=torch.float32, device=dev)
+        self.out = torch.empty((T, 128, 128), dtype=torch.bfloat16, device=dev)
+        # algorithmic work (the FLOP convention of the K3 study: 2 (Lq + Lv) per
+        # visible pair and head; bytes: cache rows, queries, fp32 o_lat and LSE)
+        self.pairs = visible_pairs(self.lens, s_q)
+        self.flop_attn = self.pairs * FLOP_PER_PAIR
+        self.flop_proj = 2 * (2 * T * 128 * 128 * 512)
+        self.flop_step = self.flop_attn + self.flop_proj
+        self.kv_bytes = sum(self.lens) * KV_BYTES_PER_TOKEN
+        self.q_bytes = T * 128 * 576 * 2
+        self.olat_bytes = T * 128 * (512 + 1) * 4
+        self.decode_bytes = self.kv_bytes + self.q_bytes + self.olat_bytes
+        self.step_bytes = self.decode_bytes + 2 * (128 * 128 * 512 * 2) + T * 128 * 128 * 2 * 2
+        self.names = (["mla_absorb_q", "mla_decode_paged", "mla_combine_splits", "mla_up_proj"] if separate else
+                      ["mla_absorb_q", "mla_decode_paged", "mla_combine_up_proj"])
+
+    def step(self, k, ev=None):
+        M, layer = self.M, k % self.layers
+        stream = self.torch.cuda.current_stream()
+        if ev: ev[0].record(stream)
+        M.mla_absorb_q(self.q_c, self.w_uk, self.q_abs)
+        if ev: ev[1].record(stream)
+        M.mla_decode_paged(self.q_abs, self.q_r, self.kv[layer], self.tables[layer], self.seqlens, self.S,
+                           o_part=self.o_part, lse_part=self.lse_part)
+        if ev: ev[2].record(stream)
+        if self.separate:
+            M.mla_combine_splits(self.o_part, self.lse_part, self.o_lat, self.lse)
+            if ev: ev[3].record(stream)
+            M.mla_up_proj(self.o_lat.view(self.T, 128, 512), self.w_uv, self.out)
+        else:
+            M.mla_combine_up_proj(self.o_part, self.lse_part, self.w_uv, self.out, self.lse)
+        if ev: ev[len(self.names)].record(stream)
+
+    def measure(self, warmup, steps):
+        """W untimed steps, then exactly K timed steps bracketed by synchronisations,
+        with HIP events around every kernel of every timed step."""
+        torch = self.torch
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(self.names) + 1)] for _ in range(steps)]
+        for k in range(warmup):
+            self.step(k)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(steps):
+            self.step(warmup + k, ev[k])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        per = [[e[j].elapsed_time(e[j + 1]) for e in ev] for j in range(len(self.names))]
+        self.kernel_ms = {n: sum(x) / len(x) for n, x in zip(self.names, per)}
+        self.kernel_min_ms = {n: min(x) for n, x in zip(self.names, per)}
+        self.ms_step = wall / steps * 1e3
+        return self
+
+    def graph_ms(self, steps):
+        """The same step launched from a HIP graph (one captured step per resident
+        layer, at most 64, replayed): the step without host launch overhead."""
+        torch = self.torch
+        n_cap = min(self.layers, 64)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for k in range(n_cap):
+                self.step(k)
+        graph.replay()
+        torch.cuda.synchronize()
+        reps = max(1, -(-steps // n_cap))
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            graph.replay()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) / (reps * n_cap) * 1e3
+        del graph
+        return ms
+
+    def summary(self):
+        dec_s = self.kernel_ms["mla_decode_paged"] * 1e-3
+        r = roof(self.flop_attn, self.decode_bytes, dec_s)
+        r.update({
+            "decode_us": round(self.kernel_ms["mla_decode_paged"] * 1e3, 2),
+            "decode_min_us": round(self.kernel_min_ms["mla_decode_paged"] * 1e3, 2),
+            "step_us": round(self.ms_step * 1e3, 2),
+            "graph_step_us": None if math.isnan(self.graph_step_ms) else round(self.graph_step_ms * 1e3, 2),
+            "kernels_us": {n: round(v * 1e3, 2) for n, v in self.kernel_ms.items()},
+            "num_splits": self.S, "B": self.B, "s_q": self.s_q, "max_ctx": max(self.lens),
+            "tokens": sum(self.lens), "visible_pairs": self.pairs,
+            "flop_per_launch": self.flop_attn, "algorithmic_bytes_per_launch": self.decode_bytes,
+            "roofline_time_us": round(max(self.flop_attn / (MFMA_BF16_PEAK_TFLOPS * 1e12),
+                                          self.decode_bytes / (HBM_PEAK_GBS * 1e9)) * 1e6, 2),
+            "step_tflops": round(self.flop_step / (self.ms_step * 1e-3) / 1e12, 2),
+            "kv_gbps_decode": round(self.kv_bytes / dec_s / 1e9, 1),
+            "resident_layers": self.layers,
+            "cache": f"cold: step k reads layer k mod {self.layers} ({self.layers * self.layer_bytes / 1e9:.1f} GB)",
+            "traffic": measured_traffic(self.name, self.S),
+        })
+        return r
 
 
-def time_next_rows(M, torch, kv, tables, seqlens, lens, B, s_q, layers, reps=200):
+def time_next_rows(M, torch, wl, reps=200):
     """The step before the path at this workload: writing the chunk's tokens
     into the cache (c_KV copied, k_R rotated) and rotating the queries' RoPE
     parts. Both are launch-bound at decode sizes, so `reps` launches are
     captured in one HIP graph and the replay is timed with HIP events: the
     per-launch time is the GPU's, without Python dispatch in between."""
-    dev = kv.device
+    dev, kv, tables, seqlens, lens, B, s_q, layers = (wl.kv.device, wl.kv, wl.tables, wl.seqlens, wl.lens, wl.B,
+                                                      wl.s_q, wl.layers)
     T = B * s_q
     g = torch.Generator(device=dev).manual_seed(77)
     c_new = torch.randn((B, s_q, 512), device=dev, generator=g).to(torch.bfloat16)
@@ -175,11 +300,11 @@ def time_next_rows(M, torch, kv, tables, seqlens, lens, B, s_q, layers, reps=200
     return res
 
 
-def time_decompressed_branch(M, torch, kv, tables, seqlens, lens, q_c, q_r, w_uk, w_uv, s_q, layers, reps=5):
+def time_decompressed_branch(M, torch, wl, reps=5):
     """The decompressed branch (per-head K/V, then causal MHA) at this
     workload, timed per kernel with HIP events, with its algorithmic FLOP
-    and bytes. The absorbed step above is the comparison the dispatch rule
-    makes."""
+    and bytes. The absorbed step is the comparison the dispatch rule makes."""
+    kv, tables, seqlens, lens, s_q, layers = wl.kv, wl.tables, wl.seqlens, wl.lens, wl.s_q, wl.layers
     B = len(lens)
     max_len = -(-max(lens) // 64) * 64
     shape = (B, 128, max_len, 128)
@@ -193,67 +318,52 @@ def time_decompressed_branch(M, torch, kv, tables, seqlens, lens, q_c, q_r, w_uk
         layer = k % layers
         e = ev[k - 2] if k >= 2 else None
         if e: e[0].record(stream)
-        M.mla_decompress_kv(kv[layer], tables[layer], seqlens, w_uk, w_uv, max_len, k_nope=k_nope, v=v)
+        M.mla_decompress_kv(kv[layer], tables[layer], seqlens, wl.w_uk, wl.w_uv, max_len, k_nope=k_nope, v=v)
         if e: e[1].record(stream)
-        M.mla_prefill_mha(q_c, q_r, k_nope, v, kv[layer], tables[layer], seqlens, out=out, lse=lse)
+        M.mla_prefill_mha(wl.q_c, wl.q_r, k_nope, v, kv[layer], tables[layer], seqlens, out=out, lse=lse)
         if e: e[2].record(stream)
     torch.cuda.synchronize()
     t_dec = sum(e[0].elapsed_time(e[1]) for e in ev) / reps
     t_mha = sum(e[1].elapsed_time(e[2]) for e in ev) / reps
     tokens = sum(lens)
     flop_dec = 2.0 * tokens * 512 * (2 * 128 * 128)
-    pairs = visible_pairs(lens, s_q)
-    flop_mha = 2.0 * pairs * 128 * (192 + 128)
+    flop_mha = 2.0 * visible_pairs(lens, s_q) * 128 * (192 + 128)
     bytes_dec = tokens * (1024 + 2 * 128 * 128 * 2) + 2 * 128 * 128 * 512 * 2
     del k_nope, v
     return {
-        "mla_decompress_kv": {"ms": round(t_dec, 4), "flop": flop_dec, "tflops": round(flop_dec / (t_dec * 1e-3) / 1e12, 1),
-                              "mfma_frac": round(flop_dec / (t_dec * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-                              "bytes": bytes_dec, "gbps": round(bytes_dec / (t_dec * 1e-3) / 1e9, 1)},
-        "mla_prefill_mha": {"ms": round(t_mha, 4), "flop": flop_mha, "tflops": round(flop_mha / (t_mha * 1e-3) / 1e12, 1),
-                            "mfma_frac": round(flop_mha / (t_mha * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "mla_decompress_kv": dict(ms=round(t_dec, 4), flop=flop_dec, bytes=bytes_dec,
+                                  roofline=roof(flop_dec, bytes_dec, t_dec * 1e-3)),
+        "mla_prefill_mha": dict(ms=round(t_mha, 4), flop=flop_mha,
+                                mfma_frac=round(flop_mha / (t_mha * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)),
         "branch_ms": round(t_dec + t_mha, 4),
     }
 
 
-QUANT_FORMATS = {
-    # page bytes, bytes per token, what the cache holds
-    "fp8": (41216, 512 + 64 * 2 + 4, "c_KV in E4M3 with a power-of-two scale per token, k_R in bf16"),
-    "mxfp4": (25600, 256 + 64 * 2 + 16, "c_KV in MXFP4 (E2M1 with an E8M0 scale per 32 dims), k_R in bf16"),
-}
-
-
-def time_quantized_cache(M, torch, fmt, kv, tables, seqlens, lens, q_c, q_r, w_uk, w_uv, S, layers, steps, warmup,
-                         flop_step, flop_attn, q_bytes, olat_bytes, workload):
+def time_quantized_cache(M, torch, fmt, wl, steps, warmup):
     """The same step over a quantized cache: every resident layer converted once
     (mla_quantize_cache_<fmt>), then absorb -> mla_decode_paged_<fmt> ->
-    mla_combine_up_proj, rotating through the layers as the main loop does."""
+    mla_combine_up_proj, rotating through the layers as the main loop does,
+    HIP events around every kernel of the timed steps."""
     page_bytes, per_token, what = QUANT_FORMATS[fmt]
     quantize = getattr(M, f"mla_quantize_cache_{fmt}")
     scan = getattr(M, f"mla_decode_paged_{fmt}")
-    B, s_q = q_c.shape[0], q_c.shape[1]
-    T = B * s_q
-    dev = q_c.device
-    kv8 = torch.empty((layers, kv.shape[1], page_bytes), dtype=torch.uint8, device=dev)
-    for l in range(layers):
-        quantize(kv[l], kv8[l])
+    dev = wl.q_c.device
+    kvq = torch.empty((wl.layers, wl.kv.shape[1], page_bytes), dtype=torch.uint8, device=dev)
+    for l in range(wl.layers):
+        quantize(wl.kv[l], kvq[l])
     torch.cuda.synchronize()
-    q_abs = torch.empty((B, s_q, 128, 512), dtype=torch.bfloat16, device=dev)
-    o_part = torch.empty((B, s_q, 128, S, 512), dtype=torch.float32, device=dev)
-    lse_part = torch.empty((B, s_q, 128, S), dtype=torch.float32, device=dev)
-    out = torch.empty((T, 128, 128), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((B, s_q, 128), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
 
     def step(k, e=None):
-        layer = k % layers
+        layer = k % wl.layers
         if e: e[0].record(stream)
-        M.mla_absorb_q(q_c, w_uk, q_abs)
+        M.mla_absorb_q(wl.q_c, wl.w_uk, wl.q_abs)
         if e: e[1].record(stream)
-        scan(q_abs, q_r, kv8[layer], tables[layer], seqlens, S, o_part=o_part, lse_part=lse_part)
+        scan(wl.q_abs, wl.q_r, kvq[layer], wl.tables[layer], wl.seqlens, wl.S, o_part=wl.o_part,
+             lse_part=wl.lse_part)
         if e: e[2].record(stream)
-        M.mla_combine_up_proj(o_part, lse_part, w_uv, out, lse)
+        M.mla_combine_up_proj(wl.o_part, wl.lse_part, wl.w_uv, wl.out, wl.lse)
         if e: e[3].record(stream)
 
     for k in range(warmup):
@@ -261,57 +371,44 @@ def time_quantized_cache(M, torch, fmt, kv, tables, seqlens, lens, q_c, q_r, w_u
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(steps):
-        step(warmup + k)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    for k in range(steps):
         step(warmup + k, ev[k])
     torch.cuda.synchronize()
-    per = [sum(ev[k][j].elapsed_time(ev[k][j + 1]) for k in range(steps)) / steps for j in range(3)]
+    wall = time.perf_counter() - t0
+    per = [sum(e[j].elapsed_time(e[j + 1]) for e in ev) / steps for j in range(3)]
     ms_step = wall / steps * 1e3
-    kv_bytes = sum(lens) * per_token
-    dec_bytes = kv_bytes + q_bytes + olat_bytes
+    dec_bytes = sum(wl.lens) * per_token + wl.q_bytes + wl.olat_bytes
     dec_ms = per[1]
-    del kv8
+    del kvq
+    r = roof(wl.flop_attn, dec_bytes, dec_ms * 1e-3)
+    r.update({"algorithmic_bytes_per_launch": dec_bytes, "traffic": measured_traffic(wl.name, wl.S, fmt),
+              "note": "the bf16 peak: the scan does the bf16 scan's arithmetic (the query as two E4M3 terms "
+                      "reproduces its bf16 value; V is dequantized to bf16)"})
     return {
         "cache": f"{what}: {per_token} bytes per token instead of {KV_BYTES_PER_TOKEN}",
         "ms_per_step": round(ms_step, 4),
-        "value_tflops": round(flop_step / (ms_step * 1e-3) / 1e12, 2),
+        "value_tflops": round(wl.flop_step / (ms_step * 1e-3) / 1e12, 2),
         "kernels_ms": {"mla_absorb_q": round(per[0], 4), f"mla_decode_paged_{fmt}": round(dec_ms, 4),
                        "mla_combine_up_proj": round(per[2], 4)},
-        "decode_roofline": {"bound": "hbm", "achieved": round(dec_bytes / (dec_ms * 1e-3) / 1e9, 1),
-                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                            "frac": round(dec_bytes / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                            "traffic": measured_traffic(workload, S, fmt),
-                            "algorithmic_bytes_per_launch": dec_bytes,
-                            "decode_tflops": round(flop_attn / (dec_ms * 1e-3) / 1e12, 1),
-                            "mfma_frac": round(flop_attn / (dec_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "decode_roofline": r,
     }
 
 
-def time_one_launch_step(M, torch, kv, tables, seqlens, q_c, q_r, w_uk, w_uv, S, layers, steps, warmup):
+def time_one_launch_step(M, torch, wl, steps, warmup):
     """mla_decode_step (one cooperative launch) against the four kernels it
-    fuses (mla_absorb_q, mla_decode_paged, mla_combine_splits, mla_up_proj),
-    same buffers, same layer rotation; wall-clock per step."""
-    B, s_q = q_c.shape[0], q_c.shape[1]
-    dev = q_c.device
-    buf = dict(q_abs=torch.empty((B, s_q, 128, 512), dtype=torch.bfloat16, device=dev),
-               o_part=torch.empty((B, s_q, 128, S, 512), dtype=torch.float32, device=dev),
-               lse_part=torch.empty((B, s_q, 128, S), dtype=torch.float32, device=dev),
-               o_lat=torch.empty((B, s_q, 128, 512), dtype=torch.float32, device=dev),
-               lse=torch.empty((B, s_q, 128), dtype=torch.float32, device=dev),
-               out=torch.empty((B, s_q, 128, 128), dtype=torch.bfloat16, device=dev))
+    fuses, same buffers, same layer rotation; wall-clock per step."""
     def fused(k):
-        l = k % layers
-        M.mla_decode_step(q_c, q_r, kv[l], tables[l], seqlens, w_uk, w_uv, S, buffers=buf)
+        l = k % wl.layers
+        M.mla_decode_step(wl.q_c, wl.q_r, wl.kv[l], wl.tables[l], wl.seqlens, wl.w_uk, wl.w_uv, wl.S,
+                          buffers=dict(q_abs=wl.q_abs, o_part=wl.o_part, lse_part=wl.lse_part, o_lat=wl.o_lat,
+                                       lse=wl.lse, out=wl.out.view(wl.B, wl.s_q, 128, 128)))
 
     def four(k):
-        l = k % layers
-        M.mla_absorb_q(q_c, w_uk, buf["q_abs"])
-        M.mla_decode_paged(buf["q_abs"], q_r, kv[l], tables[l], seqlens, S, o_part=buf["o_part"],
-                           lse_part=buf["lse_part"])
-        M.mla_combine_splits(buf["o_part"], buf["lse_part"], buf["o_lat"], buf["lse"])
-        M.mla_up_proj(buf["o_lat"], w_uv, buf["out"])
+        l = k % wl.layers
+        M.mla_absorb_q(wl.q_c, wl.w_uk, wl.q_abs)
+        M.mla_decode_paged(wl.q_abs, wl.q_r, wl.kv[l], wl.tables[l], wl.seqlens, wl.S, o_part=wl.o_part,
+                           lse_part=wl.lse_part)
+        M.mla_combine_splits(wl.o_part, wl.lse_part, wl.o_lat, wl.lse)
+        M.mla_up_proj(wl.o_lat.view(wl.T, 128, 512), wl.w_uv, wl.out)
 
     res = {}
     for name, fn in (("four_kernels_ms", four), ("one_launch_ms", fused)):
@@ -325,6 +422,93 @@ def time_one_launch_step(M, torch, kv, tables, seqlens, q_c, q_r, w_uk, w_uv, S,
         res[name] = round((time.perf_counter() - t0) / steps * 1e3, 4)
     res["speedup"] = round(res["four_kernels_ms"] / res["one_launch_ms"], 3)
     return res
+
+
+def _cpu_facts():
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        blas = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    affinity = len(os.sched_getaffinity(0))
+    return {"cpu_model": model, "logical_cpus": os.cpu_count(), "affinity": affinity, "blas_threads": int(blas),
+            "threads_used": int(min(blas, affinity))}
+
+
+def cpu_baseline(M, torch, workloads, headline, target_s):
+    """The fp64 oracle (test infrastructure, not the product path) on the host
+    cores, on a bounded sample of every workload: the absorbed path (gather,
+    scores, softmax, P.c_KV on the GPU's own q_abs) on whole sequences (query
+    rows for the chunked workload), and the naive path (decompressed per-head
+    K and V, then attention and the output) on the single and uniform ones."""
+    import oracle as O
+    facts = _cpu_facts()
+    scale = 1.0 / math.sqrt(192)
+    share = {"single": 0.05, "uniform": 0.1, "ragged": 0.15, "prefill": 0.2, "long": 0.3}
+    per = {}
+    for name, wl in workloads.items():
+        budget = target_s * share.get(name, 0.2)
+        M.mla_absorb_q(wl.q_c, wl.w_uk, wl.q_abs)
+        torch.cuda.synchronize()
+        qa = O.as_f64(wl.q_abs.cpu())
+        qr = O.as_f64(wl.inp_cpu.q_r)
+        kvb = O.bf16_bits(wl.kv[0].cpu())
+        bt = wl.tables[0].cpu().numpy()
+        sl = wl.seqlens_cpu.numpy()
+        t0, done, pairs = time.perf_counter(), 0, 0
+        if wl.s_q == 1:
+            while time.perf_counter() - t0 < budget and done < wl.B:
+                b = done
+                O.decode_absorbed(qa[b:b + 1], qr[b:b + 1], kvb, bt[b:b + 1], sl[b:b + 1], scale)
+                pairs += visible_pairs([int(sl[b])], 1)
+                done += 1
+            what = f"absorbed path, {done} of {wl.B} whole sequences, all 128 heads"
+        else:   # query rows of the first sequence, one by one (the chunk's causal rows)
+            L = int(sl[0])
+            while time.perf_counter() - t0 < budget and done < wl.s_q:
+                i = done
+                O.decode_absorbed(qa[0:1, i:i + 1], qr[0:1, i:i + 1], kvb, bt[0:1],
+                                  [L - wl.s_q + i + 1], scale)
+                pairs += L - wl.s_q + i + 1
+                done += 1
+            what = f"absorbed path, {done} of {wl.s_q} query rows of sequence 0, all 128 heads"
+        dt = time.perf_counter() - t0
+        entry = {"absorbed": {"seconds": round(dt, 3), "visible_pairs": pairs,
+                              "tflops": round(pairs * FLOP_PER_PAIR / dt / 1e12, 4), "sample": what}}
+        if name in ("single", "uniform"):
+            qc = O.as_f64(wl.inp_cpu.q_c)
+            wuk, wuv = O.as_f64(wl.inp_cpu.w_uk), O.as_f64(wl.inp_cpu.w_uv)
+            t0, done, flop = time.perf_counter(), 0, 0.0
+            while (done == 0 or time.perf_counter() - t0 < budget) and done < wl.B:
+                b = done
+                O.decode_naive(qc[b:b + 1], qr[b:b + 1], kvb, bt[b:b + 1], sl[b:b + 1], wuk, wuv, scale)
+                L = int(sl[b])
+                # per head: K and V decompression (2 L 512 128 each), scores and P.V
+                # (2 L (128 + 64) and 2 L 128), per query
+                flop += 128 * (2 * 2 * L * 512 * 128 + 2 * L * (192 + 128))
+                done += 1
+            dt = time.perf_counter() - t0
+            entry["naive"] = {"seconds": round(dt, 3), "tflops": round(flop / dt / 1e12, 4),
+                              "sample": f"naive path, {done} of {wl.B} whole sequences, all 128 heads"}
+        per[name] = entry
+    head = per[headline]["absorbed"]
+    return {
+        "value": head["tflops"], "unit": "TFLOP/s", "cores": facts["threads_used"], "kind": "oracle",
+        "sample": f"{head['sample']} of the {headline} workload (layer 0), {head['seconds']} s; "
+                  f"CPU {facts['cpu_model']}, {facts['logical_cpus']} logical CPUs, affinity {facts['affinity']}, "
+                  f"BLAS threads {facts['blas_threads']}",
+        "host": facts,
+        "configs": per,
+    }
 
 
 def main():
@@ -347,174 +531,90 @@ def main():
         print(f"[bench] copied {n} bytes three times", file=sys.stderr, flush=True)
         return
     import mla_latent_kv_06_amd as M
-    from mla_inputs import CONFIGS, make_inputs, make_structure, make_cache_on_device
 
-    cfg = CONFIGS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    head = args.workload
+    names = [n for n in WORKLOAD_ORDER if n != head] if args.configs == "all" else []
+    names.append(head)
 
-    # ---- inputs resident in HBM before timing
-    inp = make_inputs(cfg, seed=42, with_cache=False)
-    st0 = make_structure(cfg, seed=42)
-    layer_bytes = st0.num_pages * 64 * 576 * 2
-    layers = args.layers or max(cfg.layers, math.ceil(2 * 2**30 / layer_bytes))
-    print(f"[bench] workload={cfg.name} B={cfg.B} s_q={cfg.s_q} layers={layers} "
-          f"cache={layers * layer_bytes / 1e9:.1f} GB", file=sys.stderr, flush=True)
-    kv = make_cache_on_device(st0.num_pages, layers, seed=1234, device=dev)
-    tables = torch.stack([make_structure(cfg, seed=42 + l).block_table for l in range(layers)]).to(dev)
-    seqlens = st0.seqlens.to(dev)
-    q_c, q_r = inp.q_c.to(dev), inp.q_r.to(dev)
-    w_uk, w_uv = inp.w_uk.to(dev), inp.w_uv.to(dev)
-    lens = [int(x) for x in st0.seqlens]
-    S = args.splits or M.mla_plan_splits(lens, tables.shape[2], cfg.s_q)
-    B, s_q = cfg.B, cfg.s_q
-    T = B * s_q
-
-    # preallocated outputs: the timed loop allocates nothing
-    q_abs = torch.empty((B, s_q, 128, 512), dtype=torch.bfloat16, device=dev)
-    o_part = torch.empty((B, s_q, 128, S, 512), dtype=torch.float32, device=dev)
-    lse_part = torch.empty((B, s_q, 128, S), dtype=torch.float32, device=dev)
-    o_lat = torch.empty((B, s_q, 128, 512), dtype=torch.float32, device=dev)
-    lse = torch.empty((B, s_q, 128), dtype=torch.float32, device=dev)
-    out = torch.empty((B, s_q, 128, 128), dtype=torch.bfloat16, device=dev)
-
-    stream = torch.cuda.current_stream()
-    sep = args.separate_stage2
-    nev = 5 if sep else 4
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
-    out_rows = out.view(T, 128, 128)
-
-    def step(k, ev=None):
-        layer = k % layers
-        if ev: ev[0].record(stream)
-        M.mla_absorb_q(q_c, w_uk, q_abs)
-        if ev: ev[1].record(stream)
-        M.mla_decode_paged(q_abs, q_r, kv[layer], tables[layer], seqlens, S, o_part=o_part, lse_part=lse_part)
-        if ev: ev[2].record(stream)
-        if sep:
-            M.mla_combine_splits(o_part, lse_part, o_lat, lse)
-            if ev: ev[3].record(stream)
-            M.mla_up_proj(o_lat, w_uv, out)
-        else:
-            # stage 2 and the up-projection in one pass (o_lat stays on chip)
-            M.mla_combine_up_proj(o_part, lse_part, w_uv, out_rows, lse)
-        if ev: ev[nev - 1].record(stream)
-
-    for k in range(args.warmup):
-        step(k)
+    # ---- every workload's inputs resident in HBM before any timing
+    wls = {}
+    for n in names:
+        is_head = n == head
+        wls[n] = Workload(M, torch, n, dev, layers=args.layers if is_head else 0,
+                          splits=args.splits if is_head else 0, separate=args.separate_stage2)
+        w = wls[n]
+        print(f"[bench] {n}: B={w.B} s_q={w.s_q} layers={w.layers} cache={w.layers * w.layer_bytes / 1e9:.1f} GB "
+              f"splits={w.S}", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
-    print(f"[bench] warmup {args.warmup} done; timing {args.steps} steps (splits={S})", file=sys.stderr, flush=True)
 
-    # wall-clock over exactly K steps (no events inside, so nothing is added between kernels)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        step(args.warmup + k)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    # ---- measurements, back to back, the headline last
+    for n in names:
+        wls[n].measure(args.warmup, args.steps)
+        print(f"[bench] {n}: decode {wls[n].kernel_ms['mla_decode_paged'] * 1e3:.1f} us, "
+              f"step {wls[n].ms_step * 1e3:.1f} us", file=sys.stderr, flush=True)
+    for n in names:
+        wls[n].graph_step_ms = float("nan") if args.no_graph else wls[n].graph_ms(args.steps)
 
-    # the same K steps again with HIP events around each kernel (same stream)
-    for k in range(args.steps):
-        step(args.warmup + k, events[k])
-    torch.cuda.synchronize()
-    per = [[events[k][j].elapsed_time(events[k][j + 1]) for k in range(args.steps)] for j in range(nev - 1)]
-    avg = [sum(x) / len(x) for x in per]
-    names = (["mla_absorb_q", "mla_decode_paged", "mla_combine_splits", "mla_up_proj"] if sep else
-             ["mla_absorb_q", "mla_decode_paged", "mla_combine_up_proj"])
-
-    # the same steps launched from a HIP graph (one captured step per resident
-    # layer, replayed): the step without host launch overhead, as a serving
-    # loop that captures it would run it
-    n_cap = min(layers, 64)
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for k in range(n_cap):
-            step(k)
-    graph.replay()
-    torch.cuda.synchronize()
-    reps = max(1, -(-args.steps // n_cap))
-    t0 = time.perf_counter()
-    for _ in range(reps):
-        graph.replay()
-    torch.cuda.synchronize()
-    graph_ms = (time.perf_counter() - t0) / (reps * n_cap) * 1e3
-    del graph
-
-    pairs = visible_pairs(lens, s_q)
-    flop_attn = pairs * FLOP_PER_PAIR
-    flop_proj = 2 * (2 * T * 128 * 128 * 512)
-    flop_step = flop_attn + flop_proj
-    kv_bytes = sum(lens) * KV_BYTES_PER_TOKEN
-    q_bytes = T * 128 * 576 * 2
-    olat_bytes = T * 128 * (512 + 1) * 4
-    decode_bytes = kv_bytes + q_bytes + olat_bytes        # algorithmic bytes of the attention itself
-    step_bytes = decode_bytes + 2 * (128 * 128 * 512 * 2) + T * 128 * 128 * 2 * 2
-    ms_step = wall / args.steps * 1e3
-    dec_ms = avg[1]
-    achieved_gbs = decode_bytes / (dec_ms * 1e-3) / 1e9
-    t_roof = max(flop_step / (MFMA_BF16_PEAK_TFLOPS * 1e12), step_bytes / (HBM_PEAK_GBS * 1e9))
-    traffic = measured_traffic(cfg.name, S)
-
+    wl = wls[head]
+    dec_s = wl.kernel_ms["mla_decode_paged"] * 1e-3
+    r = roof(wl.flop_attn, wl.decode_bytes, dec_s)
+    roofline = {"kernel": "mla_decode_paged", "bound": r["bound"], "achieved": r["achieved"], "peak": r["peak"],
+                "unit": r["unit"], "frac": r["frac"], "traffic": measured_traffic(head, wl.S),
+                "algorithmic_bytes_per_launch": wl.decode_bytes, "algorithmic_flop_per_launch": wl.flop_attn,
+                "intensity_flop_per_byte": r["intensity_flop_per_byte"], "ridge_flop_per_byte": RIDGE,
+                "decode_tflops": r["tflops"], "mfma_frac": r["mfma_frac"], "hbm_frac": r["hbm_frac"],
+                "timing": f"HIP events around each launch inside the {args.steps} timed steps"}
+    t_roof = max(wl.flop_step / (MFMA_BF16_PEAK_TFLOPS * 1e12), wl.step_bytes / (HBM_PEAK_GBS * 1e9))
     result = {
         "metric": "MLA decode TFLOP/s + effective KV GB/s, B=16 ctx 64K, % of MI355X roofline",
-        "value": round(flop_step / (ms_step * 1e-3) / 1e12, 2),
+        "value": round(wl.flop_step / (wl.ms_step * 1e-3) / 1e12, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": round(wl.ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) bf16 cache and activations, N(0,1/512) weights)",
-        "config": {"workload": f"{cfg.name}: {cfg.notes}", "B": B, "s_q": s_q, "ctx": max(lens),
-                   "heads": 128, "d_c": 512, "d_R": 64, "page": 64, "num_splits": S,
-                   "resident_layers": layers, "cache_gb": round(layers * layer_bytes / 1e9, 2)},
-        "kv_gbps": round(kv_bytes / (ms_step * 1e-3) / 1e9, 1),
-        "graph_ms_per_step": round(graph_ms, 4),
-        "step_roofline_frac": round(t_roof / (ms_step * 1e-3), 4),
-        "kernels_ms": {n: round(a, 4) for n, a in zip(names, avg)},
-        "roofline": {
-            "kernel": "mla_decode_paged",
-            "bound": "hbm",
-            "achieved": round(achieved_gbs, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
-            "traffic": traffic,
-            "algorithmic_bytes_per_launch": decode_bytes,
-            "decode_tflops": round(flop_attn / (dec_ms * 1e-3) / 1e12, 1),
-            "mfma_frac": round(flop_attn / (dec_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-        },
+        "config": {"workload": f"{wl.cfg.name}: {wl.cfg.notes}", "B": wl.B, "s_q": wl.s_q, "ctx": max(wl.lens),
+                   "heads": 128, "d_c": 512, "d_R": 64, "page": 64, "num_splits": wl.S,
+                   "resident_layers": wl.layers, "cache_gb": round(wl.layers * wl.layer_bytes / 1e9, 2)},
+        "kv_gbps": round(wl.kv_bytes / (wl.ms_step * 1e-3) / 1e9, 1),
+        "graph_ms_per_step": None if math.isnan(wl.graph_step_ms) else round(wl.graph_step_ms, 4),
+        "step_roofline_frac": round(t_roof / (wl.ms_step * 1e-3), 4),
+        "kernels_ms": {n: round(a, 4) for n, a in wl.kernel_ms.items()},
+        "roofline": roofline,
+        "configs": {n: wls[n].summary() for n in names},
     }
-    # cache append + query rotation, timed after the step (they write into the
-    # cache rows the step has already read)
-    result["next_rows"] = time_next_rows(M, torch, kv, tables, seqlens, lens, B, s_q, layers)
-    print("[bench] one-launch step against the four kernels it fuses", file=sys.stderr, flush=True)
-    result["next_rows"]["one_launch_step"] = time_one_launch_step(
-        M, torch, kv, tables, seqlens, q_c, q_r, w_uk, w_uv, S, layers, args.steps, args.warmup)
-    for fmt, bits in (("fp8", 8), ("mxfp4", 4)):
-        if getattr(args, f"no_{fmt}"):
-            continue
-        print(f"[bench] {bits}-bit cache: convert the resident layers, time the same steps", file=sys.stderr,
-              flush=True)
-        result["next_rows"][f"{fmt}_cache"] = time_quantized_cache(
-            M, torch, fmt, kv, tables, seqlens, lens, q_c, q_r, w_uk, w_uv, S, layers, args.steps, args.warmup,
-            flop_step, flop_attn, q_bytes, olat_bytes, cfg.name)
-    if s_q > 1:
-        # the decompressed branch the dispatch rule would take above 256 new
-        # tokens, timed at this chunk length for comparison with the step
-        result["next_rows"]["decompressed_branch"] = time_decompressed_branch(
-            M, torch, kv, tables, seqlens, lens, q_c, q_r, w_uk, w_uv, s_q, layers)
-        result["next_rows"]["decompressed_branch"]["absorbed_step_ms"] = round(ms_step, 4)
+    # the headline's own order of runs: other workloads first (see the module docstring)
+    result["configs_order"] = names
+
+    if not args.no_next:
+        nxt = result["next_rows"] = {}
+        # cache append + query rotation, timed after the step (they write into the
+        # cache rows the step has already read)
+        nxt.update(time_next_rows(M, torch, wl))
+        for fmt, bits in (("fp8", 8), ("mxfp4", 4)):
+            if getattr(args, f"no_{fmt}"):
+                continue
+            print(f"[bench] {bits}-bit cache: convert the resident layers, time the same steps", file=sys.stderr,
+                  flush=True)
+            nxt[f"{fmt}_cache"] = time_quantized_cache(M, torch, fmt, wl, args.steps, args.warmup)
+        if wl.s_q > 1:
+            # the decompressed branch the dispatch rule would take above 256 new
+            # tokens, timed at this chunk length for comparison with the step
+            nxt["decompressed_branch"] = time_decompressed_branch(M, torch, wl)
+            nxt["decompressed_branch"]["absorbed_step_ms"] = round(wl.ms_step, 4)
+        if args.one_launch:
+            print("[bench] one-launch step against the four kernels it fuses", file=sys.stderr, flush=True)
+            nxt["one_launch_step"] = time_one_launch_step(M, torch, wl, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (fp64 oracle on host cores)", file=sys.stderr, flush=True)
-        layer0 = {"kv_cache": kv[0].cpu(), "block_table": tables[0].cpu(), "seqlens": st0.seqlens,
-                  "q_r": inp.q_r}
-        M.mla_absorb_q(q_c, w_uk, q_abs)
-        torch.cuda.synchronize()
-        result["cpu_baseline"] = cpu_baseline(layer0, q_abs.cpu(), args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(M, torch, wls, head, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 

@@ -27,28 +27,55 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libmla)")
 
 
-def compile_command(out: str = LIB) -> list[str]:
-    return [
-        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-        # packed fp32 VALU ops are kept out of the device code
-        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        "-Wno-unused-command-line-argument",
-        # inline asm that touches a reserved register (M0, EXEC, ...) without
-        # telling the compiler fails the build
-        "-Werror=inline-asm",
-        "-o", out,
-    ] + [os.path.join(CSRC, s) for s in SOURCES]
+FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    # packed fp32 VALU ops are kept out of the device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-command-line-argument",
+    # inline asm that touches a reserved register (M0, EXEC, ...) without
+    # telling the compiler fails the build
+    "-Werror=inline-asm",
+]
 
 
-def build_library(verbose: bool = False) -> str:
+def compile_command(src: str, obj: str) -> list[str]:
+    return [hipcc()] + FLAGS + ["-c", src, "-o", obj]
+
+
+def link_command(objs: list[str], out: str = LIB) -> list[str]:
+    return [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", out] + objs
+
+
+def build_library(verbose: bool = False, jobs: int | None = None) -> str:
+    """Compile every source to an object (in parallel) and link libmla.so."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    obj_dir = os.path.join(HERE, "_build")
+    os.makedirs(obj_dir, exist_ok=True)
+    jobs = jobs or min(len(SOURCES), max(1, min(16, int(os.environ.get("MAX_JOBS", os.cpu_count() or 1)))))
+
+    def one(src):
+        obj = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
+        cmd = compile_command(os.path.join(CSRC, src), obj)
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        return obj, subprocess.run(cmd, capture_output=True, text=True)
+
+    with ThreadPoolExecutor(jobs) as pool:
+        results = list(pool.map(one, SOURCES))
+    failed = [(o, r) for o, r in results if r.returncode != 0]
+    for _, r in failed:
+        sys.stderr.write(r.stdout + r.stderr)
+    if failed:
+        raise RuntimeError(f"hipcc failed on {', '.join(os.path.basename(o) for o, _ in failed)}")
     tmp = LIB + ".tmp"
-    cmd = compile_command(tmp)
+    cmd = link_command([o for o, _ in results], tmp)
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
+        raise RuntimeError(f"hipcc link failed with exit code {res.returncode}")
     os.replace(tmp, LIB)
     return LIB
 

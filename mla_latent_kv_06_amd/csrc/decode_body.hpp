@@ -885,12 +885,17 @@ __device__ __forceinline__ void decode_paged_body(
   float xs[16];
   float mx = 0.f;
   bf16x8 pb[2];
-  // xs = raw scores; the tail tile masks tokens past the visible length
-  auto sm_scale = [&](const f32x16& S, int it) {
+  // xs = raw scores; the tail tile masks tokens past the visible length.
+  // kMay (a compile-time flag) is false where the tile is known to be full
+  // (every tile at least two before the piece's last), so those tiles carry
+  // no masking code at all: as a uniform runtime branch the compiler turns it
+  // into 33 selects per tile.
+  auto sm_scale = [&](const f32x16& S, int it, auto may_tag) {
+    constexpr bool kMay = decltype(may_tag)::value;
     const int valid = t_end - (tile0 + it) * kTok;  // uniform; >= 32 for full tiles
 #pragma unroll
     for (int r = 0; r < 16; ++r) xs[r] = S[r];
-    if (valid < kTok) {
+    if (kMay && valid < kTok) {
       const int vlim = valid - 4 * g;
 #pragma unroll
       for (int r = 0; r < 16; ++r) xs[r] = (8 * (r >> 2) + (r & 3)) < vlim ? xs[r] : -INFINITY;
@@ -919,13 +924,14 @@ __device__ __forceinline__ void decode_paged_body(
   // 2h + 1 one phase before sm_exp(8h) uses them. Scales of rows past the
   // visible length are not data: in the tail tile they become 0 (P is 0 there).
   f32x4 psc[2];
-  auto sm_scales = [&](int it, int h) {
+  auto sm_scales = [&](int it, int h, auto may_tag) {
     if constexpr (kFp8) {
+      constexpr bool kMay = decltype(may_tag)::value;
       const char* sb = lds + (it & (kStages - 1)) * F::bytes + kStage8Scale + 16 * g + 64 * h;
       psc[0] = *reinterpret_cast<const f32x4*>(sb);
       psc[1] = *reinterpret_cast<const f32x4*>(sb + 32);
       const int vlim = t_end - (tile0 + it) * kTok - 4 * g;
-      if (vlim + 4 * g < kTok) {
+      if (kMay && vlim + 4 * g < kTok) {
 #pragma unroll
         for (int r = 0; r < 8; ++r)
           if ((16 * h + 8 * (r >> 2) + (r & 3)) >= vlim) psc[r >> 2][r & 3] = 0.f;
@@ -962,12 +968,12 @@ __device__ __forceinline__ void decode_paged_body(
   // tile `it` without PV (first tile of a pass)
   auto softmax_only = [&](int it, bool& over, auto dma_tag) {
     const f32x16 S = qk(it, dma_tag, std::false_type{});
-    sm_scales(it, 0);
-    sm_scale(S, it);
+    sm_scales(it, 0, std::true_type{});
+    sm_scale(S, it, std::true_type{});
     sm_localmax();
     sm_ref(over);
     sm_exp(0);
-    sm_scales(it, 1);
+    sm_scales(it, 1, std::true_type{});
     sm_exp(8);
     sm_pack();
     sm_publish(it);
@@ -975,15 +981,16 @@ __device__ __forceinline__ void decode_paged_body(
   };
 
   // tile `it`: QK(it), then softmax(it) chunks interleaved with PV(it-1),
-  // whose first operands QK(it) has already fetched
-  auto softmax_pv = [&](int it, bool& over, auto dma_tag) {
+  // whose first operands QK(it) has already fetched. may_tag: whether the
+  // tile can be the piece's partial last one (std::false_type: it is full).
+  auto softmax_pv = [&](int it, bool& over, auto dma_tag, auto may_tag) {
     const int ip = it - 1;
     const f32x16 S = qk(it, dma_tag, std::true_type{});
-    sm_scale(S, it);       mm4(0, va[0], pf); va[2] = vfrag(ip, 0, 2); interleave<8>(); MLA_FENCE();
-    sm_localmax();         mm4(1, va[1], pf); va[0] = vfrag(ip, 0, 3); sm_scales(it, 0); interleave<4>(); MLA_FENCE();
+    sm_scale(S, it, may_tag); mm4(0, va[0], pf); va[2] = vfrag(ip, 0, 2); interleave<8>(); MLA_FENCE();
+    sm_localmax();         mm4(1, va[1], pf); va[0] = vfrag(ip, 0, 3); sm_scales(it, 0, may_tag); interleave<4>(); MLA_FENCE();
     sm_ref(over);          mm4(2, va[2], pf); va[1] = vfrag(ip, 1, 0); interleave<2>(); MLA_FENCE();
     sm_exp(0);             mm4(3, va[0], pf); interleave<4>(); MLA_FENCE();
-    sm_scales(it, 1);
+    sm_scales(it, 1, may_tag);
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht) pf[ht] = pfrag(ip, 1, ht);
     va[2] = vfrag(ip, 1, 1);
@@ -1131,17 +1138,16 @@ __device__ __forceinline__ void decode_paged_body(
           // steady state: QK(it) + softmax(it) overlapped with PV(it - 1); the
           // last two tiles issue no further DMA
           int it = 1;
-          for (; it + 2 < n_tiles; ++it) {
+          for (; it + 2 < n_tiles; ++it) {  // full tiles: no tail handling
             wait_vmcnt<F::dma>();
             tile_barrier();
-            zero_tail(it);
-            softmax_pv(it, over, std::true_type{});
+            softmax_pv(it, over, std::true_type{}, std::false_type{});
           }
           for (; it < n_tiles; ++it) {
             if (it + 1 < n_tiles) wait_vmcnt<F::dma>(); else wait_vmcnt<0>();
             tile_barrier();
             zero_tail(it);
-            softmax_pv(it, over, std::false_type{});
+            softmax_pv(it, over, std::false_type{}, std::true_type{});
           }
           tile_barrier();
           mm4(3, va[1], pf);  // deferred tail of PV(n_tiles - 2)

@@ -367,49 +367,148 @@ def test_chain_single_vs_naive(M):
 
 
 # ---------------------------------------------------------------------------
-# full-size workloads on sampled rows, in the launch configuration the bench uses
+# full-size workloads, every output row, in the launch configuration the bench uses
 # ---------------------------------------------------------------------------
 
-def _sampled_check(M, inp, picks, what, num_splits=None):
+def _full_check(M, inp, what, num_splits=None):
+    """decode_layer at the workload's full size; every (b, i, h) row of o_lat
+    and lse against the fp64 oracle (decode_absorbed on the GPU's own q_abs),
+    absorb on the whole tensor and the up-projection on its own o_lat."""
     d = _to(inp)
     B, s_q = inp.cfg.B, inp.cfg.s_q
-    S = num_splits or M.mla_recommended_splits(B, s_q, int(inp.seqlens.max()))
-    _say(f"{what}: B={B} s_q={s_q} pages={inp.kv_cache.shape[0]} splits={S} rows={len(picks)}")
+    S = num_splits or M.mla_plan_splits(inp.seqlens.tolist(), inp.block_table.shape[1], s_q)
+    _say(f"{what}: B={B} s_q={s_q} pages={inp.kv_cache.shape[0]} splits={S} (all rows)")
     r = M.decode_layer(d["q_c"], d["q_r"], d["kv_cache"], d["block_table"], d["seqlens"], d["w_uk"], d["w_uv"],
                        num_splits=S)
     torch.cuda.synchronize()
     q_abs = r["q_abs"].cpu()
-    ro, rl = O.decode_rows(O.as_f64(q_abs), O.as_f64(inp.q_r), O.bf16_bits(inp.kv_cache), inp.block_table.numpy(),
-                           inp.seqlens.numpy(), SCALE, picks)
-    o_lat = r["o_lat"].cpu()
-    lse = r["lse"].cpu()
-    go = np.stack([o_lat[b, i, h].double().numpy() for b, i, h in picks])
-    gl = np.array([float(lse[b, i, h]) for b, i, h in picks])
-    assert_bar(go, ro, f"{what} o_lat rows")
-    assert_lse(gl, rl, f"{what} lse rows")
-    # absorb and up-projection on their own inputs, full tensors
+    ref_o, ref_l = O.decode_absorbed(O.as_f64(q_abs), O.as_f64(inp.q_r), O.bf16_bits(inp.kv_cache),
+                                     inp.block_table.numpy(), inp.seqlens.numpy(), SCALE)
+    assert_bar(r["o_lat"].cpu().double().numpy(), ref_o, f"{what} o_lat (all rows)")
+    assert_lse(r["lse"].cpu().numpy(), ref_l, f"{what} lse (all rows)")
     assert_bar(O.as_f64(q_abs), O.absorb(O.as_f64(inp.q_c), O.as_f64(inp.w_uk)), f"{what} absorb")
-    sel = slice(0, min(B, 4))
-    assert_bar(O.as_f64(r["out"][sel].cpu()), O.up_proj(r["o_lat"][sel].cpu().double().numpy(), O.as_f64(inp.w_uv)),
-               f"{what} up_proj")
+    w_uv = O.as_f64(inp.w_uv)
+    o_lat = r["o_lat"].cpu().double().numpy().reshape(B * s_q, 128, 512)
+    assert_bar(O.as_f64(r["out"].cpu()).reshape(B * s_q, 128, 128), O.up_proj(o_lat, w_uv), f"{what} up_proj")
+    # the bench's stage 2 (merge fused with the up-projection) on the same partials,
+    # against the oracle's merge of those partials (unwritten empty slots zeroed)
+    out2, lse2 = M.mla_combine_up_proj(r["o_part"], r["lse_part"], d["w_uv"])
+    torch.cuda.synchronize()
+    out2 = O.as_f64(out2.cpu()).reshape(B, s_q, 128, 128)
+    lp = r["lse_part"].cpu().double().numpy()
+    ref_out2, ref_lse2 = [], []
+    for b in range(B):
+        op = r["o_part"][b].cpu().double().numpy()
+        op[np.isneginf(lp[b])] = 0.0
+        mo, ml = O.combine(op, lp[b])
+        ref_out2.append(O.up_proj(mo, w_uv))
+        ref_lse2.append(ml)
+    assert_bar(out2, np.stack(ref_out2), f"{what} combine_up_proj")
+    assert_lse(lse2.cpu().numpy(), np.stack(ref_lse2), f"{what} combine_up_proj lse")
 
 
-def test_ragged_config_sampled(M):
-    inp = make_inputs("ragged")
-    rng = np.random.default_rng(0)
-    picks = [(b, 0, int(h)) for b in range(inp.cfg.B) for h in rng.choice(128, 3, replace=False)]
-    _sampled_check(M, inp, picks, "ragged")
+def test_ragged_config_full(M):
+    _full_check(M, make_inputs("ragged"), "ragged")
 
 
-def test_long_config_sampled(M):
-    inp = make_inputs("long")
-    rng = np.random.default_rng(1)
-    picks = [(b, 0, int(h)) for b in range(inp.cfg.B) for h in rng.choice(128, 2, replace=False)]
-    _sampled_check(M, inp, picks, "long 64K")
+def test_long_config_full(M):
+    _full_check(M, make_inputs("long"), "long 64K")
 
 
-def test_prefill_config_sampled(M):
-    inp = make_inputs("prefill")
-    rng = np.random.default_rng(2)
-    picks = [(b, i, int(rng.integers(128))) for b in range(inp.cfg.B) for i in (0, 1, 100, 254, 255)]
-    _sampled_check(M, inp, picks, "prefill 256 over 16K")
+def test_prefill_config_full(M):
+    _full_check(M, make_inputs("prefill"), "prefill 256 over 16K")
+
+
+# ---------------------------------------------------------------------------
+# pools larger than 2^31 bytes: page offsets need 64 bits
+# ---------------------------------------------------------------------------
+
+def _top_pool(page_bytes, num_pages, pages_cpu, seed):
+    """A device pool of num_pages pages of page_bytes bytes, all 0xFF (NaN in
+    bf16, NaN scales in the quantized layouts) except for the given pages,
+    which land at the top ids in a seeded order. Returns the pool and the
+    physical id of each given page."""
+    n = pages_cpu.shape[0]
+    assert num_pages * page_bytes > 2**31 and n < num_pages
+    pool = torch.full((num_pages, page_bytes), 0xFF, dtype=torch.uint8, device=DEV)
+    ids = num_pages - n + torch.randperm(n, generator=torch.Generator().manual_seed(seed))
+    assert int(ids.max()) == num_pages - 1
+    pool[ids.to(DEV)] = pages_cpu.reshape(n, page_bytes).to(DEV)
+    return pool, ids
+
+
+def _large_case(lens, seed):
+    need = [-(-L // 64) for L in lens]
+    n = sum(need)
+    g = torch.Generator().manual_seed(seed)
+    local = torch.full((len(lens), max(need) + 3), -1, dtype=torch.int32)
+    off = 0
+    for b, k in enumerate(need):
+        local[b, :k] = torch.arange(off, off + k, dtype=torch.int32)
+        off += k
+    q_abs = (torch.randn((len(lens), 1, 128, 512), generator=g) * 0.05).to(torch.bfloat16)
+    q_r = torch.randn((len(lens), 1, 128, 64), generator=g).to(torch.bfloat16)
+    return n, local, q_abs, q_r, torch.tensor(lens, dtype=torch.int32)
+
+
+def _remap(local, ids):
+    return torch.where(local >= 0, ids[local.clamp(min=0).long()].to(torch.int32), local)
+
+
+LARGE_LENS = [1, 4000, 9000, 64 * 30]
+
+
+def test_large_bf16_pool_gather_and_decode(M):
+    """A 2.21 GB bf16 pool (30000 pages; page ids >= 29128 start past 2^31
+    bytes) whose sequences live in its top pages: the gather is bit-exact and
+    the decode meets the bar against the oracle on the same rows."""
+    n, local, q_abs, q_r, sl = _large_case(LARGE_LENS, 31)
+    pages = torch.randn((n, 64, 576), generator=torch.Generator().manual_seed(32)).to(torch.bfloat16)
+    pool_u8, ids = _top_pool(73728, 30000, pages.view(torch.uint8), 33)
+    assert int(ids.min()) * 73728 > 2**31
+    pool = pool_u8.view(torch.bfloat16).view(30000, 64, 576)
+    bt = _remap(local, ids)
+    _say(f"large bf16 pool: 30000 pages, ids {int(ids.min())}..{int(ids.max())}, lens={LARGE_LENS}")
+    out = M.mla_debug_gather(pool, bt.to(DEV), sl.to(DEV), max(LARGE_LENS))
+    o_part, lse_part = M.mla_decode_paged(q_abs.to(DEV), q_r.to(DEV), pool, bt.to(DEV), sl.to(DEV), 5, SCALE)
+    o_lat, lse = M.mla_combine_splits(o_part, lse_part)
+    torch.cuda.synchronize()
+    got = out.cpu().view(torch.int16).numpy().view(np.uint16)
+    bits = O.bf16_bits(pages)
+    for b, L in enumerate(LARGE_LENS):
+        ref = np.zeros((max(LARGE_LENS), 576), np.uint16)
+        ref[:L] = bits[local[b, :-(-L // 64)].numpy().astype(np.int64)].reshape(-1, 576)[:L]
+        assert np.array_equal(got[b], ref), f"gather, sequence {b}"
+    ref_o, ref_l = O.decode_absorbed(O.as_f64(q_abs), O.as_f64(q_r), bits, local.numpy(), sl.numpy(), SCALE)
+    assert_bar(o_lat.cpu().numpy(), ref_o, "large bf16 pool o_lat")
+    assert_lse(lse.cpu().numpy(), ref_l, "large bf16 pool lse")
+    del pool, pool_u8
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+def test_large_quantized_pool_decode(M, fmt):
+    """The 8-bit (53000 pages of 41216 bytes; ids >= 52104 start past 2^31)
+    and 4-bit (85000 pages of 25600 bytes; ids >= 83887) caches, sequences in
+    the top pages, against the oracle over the stored values."""
+    from mla_inputs import random_fp8_pages, random_mxfp4_pages
+    n, local, q_abs, q_r, sl = _large_case(LARGE_LENS, 41)
+    if fmt == "fp8":
+        pages, num_pages, page_bytes, scan, cache_cls = (random_fp8_pages(n, 42), 53000, 41216,
+                                                         M.mla_decode_paged_fp8, O.PagedFp8Cache)
+    else:
+        pages, num_pages, page_bytes, scan, cache_cls = (random_mxfp4_pages(n, 42), 85000, 25600,
+                                                         M.mla_decode_paged_mxfp4, O.PagedMxfp4Cache)
+    pool, ids = _top_pool(page_bytes, num_pages, pages, 43)
+    assert int(ids.min()) * page_bytes > 2**31
+    bt = _remap(local, ids)
+    _say(f"large {fmt} pool: {num_pages} pages, ids {int(ids.min())}..{int(ids.max())}, lens={LARGE_LENS}")
+    o_part, lse_part = scan(q_abs.to(DEV), q_r.to(DEV), pool, bt.to(DEV), sl.to(DEV), 5, SCALE)
+    o_lat, lse = M.mla_combine_splits(o_part, lse_part)
+    torch.cuda.synchronize()
+    cache = cache_cls(pages.numpy())
+    ref_o, ref_l = O.decode_absorbed(O.as_f64(q_abs), O.as_f64(q_r), cache, local.numpy(), sl.numpy(), SCALE)
+    assert_bar(o_lat.cpu().numpy(), ref_o, f"large {fmt} pool o_lat")
+    assert_lse(lse.cpu().numpy(), ref_l, f"large {fmt} pool lse")
+    del pool
+    torch.cuda.empty_cache()
