@@ -438,6 +438,35 @@ mla_status mla_decode_step_mxfp4(const void* q_c, const void* q_r, const void* k
                                  void* q_abs, float* o_part, float* lse_part, float* o_lat, void* out, float* lse,
                                  void* stream);
 
+/* ---- the step without caller workspace -----------------------------------
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.
+ * mla_decode_step_static computes what mla_decode_step computes (out and lse)
+ * without the caller-owned intermediates: q_abs and the split partials live in
+ * one static device array of MLA_STATIC_SCRATCH_BYTES (96 MiB), which the
+ * library holds on every GPU it runs on until the process ends. It launches
+ * mla_absorb_q -> mla_decode_paged -> mla_combine_up_proj (the fast kernels of
+ * the step, not the cooperative one), so out and lse equal those three calls
+ * bit for bit, and meet mla_decode_step's within rounding of the fused merge.
+ * It allocates nothing (no hipMalloc, hipFree or allocating library call).
+ *   q_c, q_r, kv_cache, num_pages, block_table, max_pages, seqlens, B, s_q, H,
+ *   w_uk, w_uv, softmax_scale, num_splits: as mla_decode_step
+ *   out bf16 [B * s_q, H, 128], lse fp32 [B, s_q, H]: outputs
+ * Needs the scratch layout q_abs [B*s_q, H, 512] bf16, o_part
+ * [B*s_q, H, num_splits, 512] fp32 and lse_part [B*s_q, H, num_splits] fp32,
+ * each rounded up to 256 bytes, to fit in the array: otherwise
+ * MLA_ERR_WORKSPACE and nothing is enqueued (B = 16, num_splits = 17 needs
+ * about 70 MiB). `stream` must belong to the current device (MLA_ERR_HIP
+ * otherwise). Calls on one GPU share its array: two calls whose executions
+ * overlap on that GPU (different streams, or host threads) race and give
+ * undefined results; calls ordered on one stream are safe. The array keeps
+ * the last call's contents; nothing in it needs clearing between calls. */
+enum { MLA_STATIC_SCRATCH_BYTES = 96 * 1024 * 1024 };
+mla_status mla_decode_step_static(const void* q_c, const void* q_r, const void* kv_cache, int64_t num_pages,
+                                  const int32_t* block_table, int max_pages, const int32_t* seqlens, int B, int s_q,
+                                  int H, const void* w_uk, const void* w_uv, float softmax_scale, int num_splits,
+                                  void* out, float* lse, void* stream);
+
 /* Test and debug aid: gather the logical cache rows of each sequence through
  * the block table with the same address arithmetic as mla_decode_paged.
  *   out bf16 [B, max_len, 576]: row t of sequence b is the cache row of token

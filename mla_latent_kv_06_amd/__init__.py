@@ -500,6 +500,38 @@ def mla_decode_step(q_c, q_r, kv_cache, block_table, seqlens, w_uk, w_uv, num_sp
     return buf
 
 
+STATIC_SCRATCH_BYTES = 96 * 1024 * 1024
+
+
+def mla_decode_step_static(q_c, q_r, kv_cache, block_table, seqlens, w_uk, w_uv, num_splits: int,
+                           softmax_scale: float = DEFAULT_SCALE, out=None, lse=None, stream=None):
+    """The decode step with no caller workspace (bf16 cache): q_abs and the
+    split partials live in the library's static device array. Returns
+    (out [B*s_q, H, 128] bf16, lse [B, s_q, H] fp32); allocates them through
+    torch only when they are not given."""
+    B, s_q = q_c.shape[0], q_c.shape[1]
+    _need(q_c, "q_c", torch.bfloat16, (B, s_q, H, D_HC))
+    _need(q_r, "q_r", torch.bfloat16, (B, s_q, H, D_R))
+    _need(w_uk, "w_uk", torch.bfloat16, (H, D_HC, D_C))
+    _need(w_uv, "w_uv", torch.bfloat16, (H, D_HC, D_C))
+    _need(kv_cache, "kv_cache", torch.bfloat16)
+    if kv_cache.dim() != 3 or kv_cache.shape[1:] != (PAGE, ROW):
+        raise ValueError(f"kv_cache must be [P, {PAGE}, {ROW}], got {tuple(kv_cache.shape)}")
+    _need(block_table, "block_table", torch.int32)
+    _need(seqlens, "seqlens", torch.int32, (B,))
+    if out is None:
+        out = torch.empty((B * s_q, H, D_HC), dtype=torch.bfloat16, device=q_c.device)
+    if lse is None:
+        lse = torch.empty((B, s_q, H), dtype=torch.float32, device=q_c.device)
+    _need(out, "out", torch.bfloat16, (B * s_q, H, D_HC))
+    _need(lse, "lse", torch.float32, (B, s_q, H))
+    _check(_lib.LIB.mla_decode_step_static(_ptr(q_c), _ptr(q_r), _ptr(kv_cache), kv_cache.shape[0],
+                                           _ptr(block_table), block_table.shape[1], _ptr(seqlens), B, s_q, H,
+                                           _ptr(w_uk), _ptr(w_uv), float(softmax_scale), int(num_splits), _ptr(out),
+                                           _ptr(lse), _stream(stream)), "mla_decode_step_static")
+    return out, lse
+
+
 def attention_layer(q_c, q_r, kv_cache, block_table, seqlens, w_uk, w_uv, max_len: int,
                     softmax_scale: float = DEFAULT_SCALE, num_splits: int | None = None, absorbed: bool | None = None,
                     stream=None):

@@ -61,6 +61,8 @@ SIGNATURES = {
     "mla_decode_step_mxfp4": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_int, c_void_p, c_int, c_int,
                                     c_int, c_void_p, c_void_p, c_float, c_int, c_void_p, c_void_p, c_void_p, c_void_p,
                                     c_void_p, c_void_p, c_void_p]),
+    "mla_decode_step_static": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_int, c_void_p, c_int, c_int,
+                                       c_int, c_void_p, c_void_p, c_float, c_int, c_void_p, c_void_p, c_void_p]),
     "mla_prefill_mha": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_int64, c_void_p, c_int,
                                 c_void_p, c_int, c_int, c_int, c_float, c_void_p, c_void_p, c_void_p]),
 }

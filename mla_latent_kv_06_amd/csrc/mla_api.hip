@@ -96,6 +96,9 @@ mla_status decode_step_any(const void* q_c, const void* q_r, const void* kv_cach
 
 }  // namespace
 
+// detail for mla_last_error from entry points defined in other sources
+void mla_set_last_error(const std::string& s) { g_last_error = s; }
+
 extern "C" {
 
 const char* mla_status_string(int status) {

@@ -116,6 +116,55 @@ inline Check check_step(const void* q_c, const void* q_r, const void* kv, int64_
   return Check{};
 }
 
+// The allocation-free step keeps q_abs and the split partials in a static
+// device array of kStaticScratchBytes; scratch_layout gives each region's
+// byte offset (each 256-byte aligned) and the total.
+constexpr size_t kStaticScratchBytes = size_t(96) << 20;
+
+struct ScratchLayout {
+  size_t q_abs = 0, o_part = 0, lse_part = 0, total = 0;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+inline ScratchLayout scratch_layout(int B, int s_q, int num_splits) {
+  ScratchLayout L;
+  const size_t rows = (size_t)B * (size_t)s_q * MLA_HEADS;
+  L.q_abs = 0;
+  L.o_part = align256(rows * MLA_D_C * 2);
+  L.lse_part = L.o_part + align256(rows * (size_t)num_splits * MLA_D_C * 4);
+  L.total = L.lse_part + align256(rows * (size_t)num_splits * 4);
+  return L;
+}
+
+inline Check check_step_static(const void* q_c, const void* q_r, const void* kv, int64_t num_pages, const void* bt,
+                               int max_pages, const void* seqlens, int B, int s_q, int H, const void* w_uk,
+                               const void* w_uv, float scale, int num_splits, const void* out, const void* lse) {
+  MLA_TRY(need_ptr(q_c, "q_c"));
+  MLA_TRY(need_ptr(w_uk, "w_uk"));
+  MLA_TRY(need_ptr(w_uv, "w_uv"));
+  MLA_TRY(need_ptr(out, "out"));
+  MLA_TRY(need_ptr(lse, "lse"));
+  // q_abs and the partials live in the scratch array; any aligned stand-in
+  // passes the pointer checks of the scan
+  const void* const inside = reinterpret_cast<const void*>(uintptr_t(256));
+  MLA_TRY(check_decode(inside, q_r, kv, num_pages, bt, max_pages, seqlens, B, s_q, H, scale, num_splits, inside,
+                       inside));
+  MLA_TRY(need_range((long long)B * s_q, 1, (1LL << 20), "B * s_q"));
+  const ScratchLayout L = scratch_layout(B, s_q, num_splits);
+  if (L.total > kStaticScratchBytes) {
+    Check c;
+    c.status = MLA_ERR_WORKSPACE;
+    char buf[256];
+    std::snprintf(buf, sizeof buf,
+                  "B * s_q = %lld with num_splits = %d needs %zu bytes of scratch; the static array holds %zu",
+                  (long long)B * s_q, num_splits, L.total, kStaticScratchBytes);
+    c.detail = buf;
+    return c;
+  }
+  return Check{};
+}
+
 inline Check check_combine(const void* o_part, const void* lse_part, int B, int s_q, int H,
                            int num_splits, const void* o_lat, const void* lse) {
   MLA_TRY(need_ptr(o_part, "o_part"));

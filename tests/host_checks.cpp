@@ -60,6 +60,22 @@ static void status_codes() {
   EXPECT(!mla::check_decode(nullptr, A, A, 10, A, 4, A, 2, 1, 128, 0.07f, 2, A, A).detail.empty());
 }
 
+static void static_scratch() {
+  // the long workload (B = 16, 17 splits) fits; 64 splits do not
+  const mla::ScratchLayout L = mla::scratch_layout(16, 1, 17);
+  EXPECT(L.q_abs == 0 && L.o_part == (size_t)16 * 128 * 512 * 2);
+  EXPECT(L.lse_part == L.o_part + (size_t)16 * 128 * 17 * 512 * 4);
+  EXPECT(L.total % 256 == 0 && L.total <= mla::kStaticScratchBytes);
+  auto st = [](int B, int s_q, int S, const void* out) {
+    return mla::check_step_static(A, A, A, 10, A, 1024, A, B, s_q, 128, A, A, 0.07f, S, out, A).status;
+  };
+  EXPECT(st(16, 1, 17, A) == MLA_OK);
+  EXPECT(st(16, 1, 64, A) == MLA_ERR_WORKSPACE);
+  EXPECT(st(16, 1, 17, nullptr) == MLA_ERR_NULL);
+  EXPECT(st(16, 1, 17, MIS) == MLA_ERR_ALIGN);
+  EXPECT(st(1 << 20, 2, 1, A) == MLA_ERR_SHAPE);
+}
+
 static void block_tables() {
   const int32_t bt[2][4] = {{3, 0, -1, -1}, {1, 2, 4, -5}};
   int bs = 7, bp = 7;
@@ -124,6 +140,7 @@ static void planning() {
 
 int main() {
   status_codes();
+  static_scratch();
   block_tables();
   planning();
   if (g_fail) {
