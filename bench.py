@@ -144,8 +144,12 @@ class Workload:
         self.layer_bytes = st0.num_pages * 64 * 576 * 2
         self.layers = layers or max(cfg.layers, math.ceil(2 * 2**30 / self.layer_bytes))
         self.kv = make_cache_on_device(st0.num_pages, self.layers, seed=1234, device=dev)
-        self.tables = torch.stack([make_structure(cfg, seed=42 + l).block_table
-                                   for l in range(self.layers)]).to(dev)
+        # every layer holds the same sequences (lengths of seed 42) at another
+        # physical page layout; each table is checked against its cache
+        tabs = [make_structure(cfg, seed=42, layout_seed=42 + l).block_table for l in range(self.layers)]
+        for t in tabs:
+            M.mla_validate_block_table(t, st0.seqlens, st0.num_pages)
+        self.tables = torch.stack(tabs).to(dev)
         self.seqlens = st0.seqlens.to(dev)
         self.seqlens_cpu = st0.seqlens
         self.inp_cpu = inp

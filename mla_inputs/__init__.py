@@ -99,7 +99,10 @@ def pages_for(n_tokens: int) -> int:
     return -(-int(n_tokens) // PAGE)
 
 
-def make_structure(cfg: Config, seed: int = 42) -> Structure:
+def make_structure(cfg: Config, seed: int = 42, layout_seed: int | None = None) -> Structure:
+    """Sequence lengths drawn from ``seed``; the physical page layout from the
+    same generator, or, with another ``layout_seed``, from a generator of its
+    own (the lengths stay those of ``seed``: several layers of one batch)."""
     g = torch.Generator().manual_seed(seed ^ STRUCT_SEED_XOR)
     if cfg.seqlen_rule == "fixed":
         seqlens = torch.full((cfg.B,), cfg.ctx, dtype=torch.int32)
@@ -107,6 +110,8 @@ def make_structure(cfg: Config, seed: int = 42) -> Structure:
         seqlens = torch.randint(1, cfg.max_ctx + 1, (cfg.B,), generator=g, dtype=torch.int64).to(torch.int32)
     else:
         raise ValueError(cfg.seqlen_rule)
+    if layout_seed is not None and layout_seed != seed:
+        g = torch.Generator().manual_seed(layout_seed ^ STRUCT_SEED_XOR)
     need = [pages_for(int(L)) for L in seqlens]
     total = sum(need)
     pool = cfg.pool_pages or total

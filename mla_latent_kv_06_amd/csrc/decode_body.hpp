@@ -59,6 +59,10 @@ constexpr int kPBytes = 2 * 4 * 2 * 1024;         // [slot][wave][k-step][64 lan
 constexpr int kLdsBytes = kStages * kStageBytes + kPBytes;   // 163840 = all of it
 constexpr float kRefSlack = 64.0f;                // log2 headroom above the reference max
 constexpr int kScanGroups = 256;                  // workgroups of a scan (one per MI355X CU)
+#ifndef MLA_DMA_GAP
+#define MLA_DMA_GAP 4
+#endif
+constexpr int kDmaGap = MLA_DMA_GAP;              // QK MFMAs between two of the next tile's loads (bf16)
 static_assert(kDmaPerThread * kThreads * 16 == kStageBytes, "stage must split into 16-byte loads");
 static_assert(kLdsBytes <= 163840, "LDS budget");
 
@@ -871,7 +875,7 @@ __device__ __forceinline__ void decode_paged_body(
         if (kk == 35) { va[0] = vfrag(it - 1, 0, 0); va[1] = vfrag(it - 1, 0, 1); }
       }
       if constexpr (dma) {
-        if ((kk & 3) == 1) dma_piece(t, kk >> 2, tile0 + it + 2);
+        if (kk % kDmaGap == kDmaGap - 1 && kk / kDmaGap < kDmaPerThread) dma_piece(t, kk / kDmaGap, tile0 + it + 2);
       }
       __builtin_amdgcn_sched_barrier(0);
     }

@@ -7,10 +7,11 @@
 // heads, read from the paged cache) and 128-dim values.
 //
 // Workgroup = (sequence b, head h, block of 128 queries), 4 waves of 32
-// queries. The keys stream in tiles of 64 (one page) through a ring of three
-// LDS stages filled with 16-byte direct-to-LDS loads, two tiles ahead of the
-// one being computed (the per-tile compute is shorter than a memory round
-// trip, so one tile of lookahead would leave each tile waiting on memory):
+// queries. The keys stream in tiles of 64 (one page) through two LDS stages
+// filled with 16-byte direct-to-LDS loads: tile it+1 is requested right after
+// the barrier that starts tile it, into the stage tile it-1 has released. One
+// tile of lookahead is shorter than a memory round trip; the second
+// workgroup on the CU (80 KiB of LDS each) computes while this one waits:
 //   * QK: S^T[32 tokens, 32 queries] per token half on v_mfma_f32_32x32x16_bf16,
 //     A = key rows from LDS, B = the wave's queries held in 48 VGPRs; a lane
 //     owns one query and 16 of each 32 tokens;
