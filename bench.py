@@ -10,11 +10,12 @@ four workloads are measured the same way, each rotating through enough
 resident layers (>= 2 GiB) that no step is served by the 256 MB last-level
 cache.
 
-Order of the run: every workload's inputs are built first; then the other
-workloads are measured and the headline last, back to back, so that its few
-warmup steps do not start from an idle board (this board's power controller
-runs the first ~40 launches of sustained load up to 1.5x slower); then the
-headline's next rows; then the CPU baseline.
+Order of the run: every workload's inputs are built first; then the
+workloads are measured back to back, the two short ones first, then the
+prefill chunk, the ragged batch and the headline last, so that the few warmup
+steps of the long scans do not start from an idle board (this board's power
+controller runs the first ~40 launches of sustained load up to 1.5x slower);
+then the headline's next rows; then the CPU baseline.
 
 Prints one JSON line:
   value         whole-step throughput of the headline workload, algorithmic TFLOP/s
@@ -44,7 +45,10 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 RIDGE = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)   # 312.5 FLOP per byte
 FLOP_PER_PAIR = 128 * 2 * (576 + 512)  # all heads, one (query, key) pair: QK over 576 + PV over 512
 KV_BYTES_PER_TOKEN = 576 * 2
-WORKLOAD_ORDER = ("single", "uniform", "ragged", "prefill", "long")
+# measurement order: the two short workloads are latency-bound and never reach
+# the board's power limit; the MFMA-heavy prefill step then runs the power
+# controller through its settling transient before the ragged and long scans
+WORKLOAD_ORDER = ("single", "uniform", "prefill", "ragged", "long")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 FORMAT_HEADERS = {"bf16": (), "fp8": ("fp8_cache.hpp",), "mxfp4": ("mxfp4_cache.hpp",)}
 QUANT_FORMATS = {

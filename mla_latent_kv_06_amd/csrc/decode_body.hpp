@@ -63,11 +63,6 @@ constexpr int kScanGroups = 256;                  // workgroups of a scan (one p
 #define MLA_DMA_GAP 4
 #endif
 constexpr int kDmaGap = MLA_DMA_GAP;              // QK MFMAs between two of the next tile's loads (bf16)
-#ifndef MLA_NT_PARTIALS
-#define MLA_NT_PARTIALS 1
-#endif
-// partial rows are stored non-temporally (they are read once, by stage 2)
-constexpr bool kNtPartials = MLA_NT_PARTIALS != 0;
 static_assert(kDmaPerThread * kThreads * 16 == kStageBytes, "stage must split into 16-byte loads");
 static_assert(kLdsBytes <= 163840, "LDS budget");
 
@@ -1213,10 +1208,7 @@ __device__ __forceinline__ void decode_paged_body(
           const int r = 2 * j + eg;
           const f32x4 v = *reinterpret_cast<const f32x4*>(ebuf + r * kEpiStride + elo * 16);
           float* orow = o_part + ((qbase + ht * 32 + r) * a.num_splits + split) * kDc + wave * 128 + elo * 4;
-          if constexpr (kNtPartials)
-            __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(orow));
-          else
-            *reinterpret_cast<f32x4*>(orow) = v;
+          *reinterpret_cast<f32x4*>(orow) = v;
         }
         asm volatile("" ::: "memory");
       }
