@@ -506,6 +506,17 @@ def e4m3_value(codes) -> np.ndarray:
     return np.where(c & 0x80, -mag, mag)
 
 
+def _e4m3_table() -> np.ndarray:
+    """e4m3_value of every code 0..255, indexed by the code."""
+    global _E4M3_TABLE
+    if _E4M3_TABLE is None:
+        _E4M3_TABLE = e4m3_value(np.arange(256))
+    return _E4M3_TABLE
+
+
+_E4M3_TABLE = None
+
+
 def e4m3_encode(v) -> np.ndarray:
     """Nearest E4M3 code of exact values with |v| <= 448, ties to even, sign kept."""
     v = np.asarray(v, np.float64)
@@ -584,9 +595,11 @@ def unpack_fp8_pages(pages, page: int = 64, d_c: int = 512, d_r: int = 64):
 
 
 def dequantize_fp8_pages(pages, page: int = 64, d_c: int = 512, d_r: int = 64) -> np.ndarray:
-    """float64 rows [n, page, d_c + d_R] stored by 8-bit pages."""
+    """float64 rows [n, page, d_c + d_R] stored by 8-bit pages. Codes are looked
+    up in the table of e4m3_value over all 256 codes (the same values, without
+    evaluating the format's formula once per element of a large cache)."""
     codes, rope, scale = unpack_fp8_pages(pages, page, d_c, d_r)
-    c = e4m3_value(codes) * scale.astype(np.float64)[..., None]
+    c = np.take(_e4m3_table(), codes.astype(np.intp)) * scale.astype(np.float64)[..., None]
     return np.concatenate([c, bf16_bits_to_f64(rope)], axis=-1)
 
 
@@ -695,8 +708,11 @@ def dequantize_latent_mxfp4(codes, k) -> np.ndarray:
     """Stored values: E2M1 value of each code times 2^k of its block."""
     codes = np.asarray(codes)
     k = np.asarray(k, np.int64)
-    v = e2m1_value(codes).reshape(codes.shape[:-1] + (k.shape[-1], MX_BLOCK))
-    return np.ldexp(v, k[..., None]).reshape(codes.shape)
+    v = np.take(e2m1_value(np.arange(16)), np.asarray(codes).astype(np.intp))
+    v = v.reshape(codes.shape[:-1] + (k.shape[-1], MX_BLOCK))
+    # 2^k of each block times its values: exact in float64 (E2M1 values have two
+    # significant bits and 2^k, |k| <= 127, is a float64 power of two)
+    return (v * np.ldexp(1.0, k)[..., None]).reshape(codes.shape)
 
 
 def mxfp4_page_bytes(page: int = 64, d_c: int = 512, d_r: int = 64) -> int:

@@ -244,25 +244,23 @@ def test_decode_mxfp4_uniform_config_full(M):
     assert_lse(r["lse"].cpu().numpy(), ref_l, "mxfp4 uniform lse")
 
 
-def test_decode_mxfp4_long_config_sampled(M):
+def test_decode_mxfp4_long_config_full(M):
     """The 64K-context workload (B = 16) over a seeded 4-bit cache, in the
-    launch configuration of the benchmark, on rows the oracle computes one by one."""
+    launch configuration of the benchmark: every (b, h) row of o_lat and lse
+    against the oracle over the stored values."""
     inp = make_inputs("long", with_cache=False)
     P = int(inp.block_table.max()) + 1
     pages = random_mxfp4_pages(P, seed=78)
     d = {k: getattr(inp, k).to(DEV) for k in ("q_c", "q_r", "w_uk", "w_uv", "block_table", "seqlens")}
-    S = M.mla_recommended_splits(inp.cfg.B, 1, int(inp.seqlens.max()))
-    _say(f"mxfp4 long config: pages={P} splits={S}")
+    S = M.mla_plan_splits(inp.seqlens.tolist(), inp.block_table.shape[1], 1)
+    _say(f"mxfp4 long config: pages={P} splits={S} (all rows)")
     r = M.decode_layer(d["q_c"], d["q_r"], pages.to(DEV), d["block_table"], d["seqlens"], d["w_uk"], d["w_uv"],
                        num_splits=S)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(2)
-    picks = [(b, 0, int(h)) for b in range(inp.cfg.B) for h in rng.choice(128, 2, replace=False)]
-    ro, rl = O.decode_rows(O.as_f64(r["q_abs"].cpu()), O.as_f64(inp.q_r), O.PagedMxfp4Cache(pages.numpy()),
-                           inp.block_table.numpy(), inp.seqlens.numpy(), SCALE, picks)
-    o_lat, lse = r["o_lat"].cpu(), r["lse"].cpu()
-    assert_bar(np.stack([o_lat[b, i, h].double().numpy() for b, i, h in picks]), ro, "mxfp4 long o_lat rows")
-    assert_lse(np.array([float(lse[b, i, h]) for b, i, h in picks]), rl, "mxfp4 long lse rows")
+    ro, rl = O.decode_absorbed(O.as_f64(r["q_abs"].cpu()), O.as_f64(inp.q_r), O.PagedMxfp4Cache(pages.numpy()),
+                               inp.block_table.numpy(), inp.seqlens.numpy(), SCALE)
+    assert_bar(r["o_lat"].cpu().numpy(), ro, "mxfp4 long o_lat (all rows)")
+    assert_lse(r["lse"].cpu().numpy(), rl, "mxfp4 long lse (all rows)")
 
 
 def test_decode_mxfp4_query_with_wide_range_inside_blocks(M):
