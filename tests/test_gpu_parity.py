@@ -207,7 +207,7 @@ def test_decode_uniform_config(M):
     d = _to(inp)
     S = M.mla_recommended_splits(16, 1, 4096)
     q_abs = M.mla_absorb_q(d["q_c"], d["w_uk"]).cpu()
-    _decode_check(M, q_abs, inp.q_r, inp.kv_cache, inp.block_table, inp.seqlens, S, "uniform", check_parts=False)
+    _decode_check(M, q_abs, inp.q_r, inp.kv_cache, inp.block_table, inp.seqlens, S, "uniform")
 
 
 @pytest.mark.parametrize("lens,s_q,S", [
