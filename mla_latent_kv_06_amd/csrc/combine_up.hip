@@ -5,26 +5,29 @@
 // page, section 4) in one pass, so the fp32 o_lat tile never leaves LDS.
 //
 // Workgroup = (head h, tile of R = 8 or 16 query rows t), 8 waves:
-//   * merge: wave w merges rows t0 + w (and t0 + w + 8 when R = 16) as
+//   * merge, R = 16: wave w merges rows t0 + w and t0 + w + 8 as
 //     combine_kernel does (split weights by readlane, the loads of up to 24
-//     splits in flight (16 with 8-row tiles), empty splits never read) into an
-//     fp32 tile in LDS; the split LSEs are read once.
-//     Lane l owns
-//     latent columns 4l..4l+3 and 256+4l..+3, so every load instruction covers
-//     1 KiB of contiguous memory;
-//   * W_UV[h] fragments (output rows 16w..16w+15, all 512 latent columns):
-//     with 16-row tiles requested after the merge loads, so the merge waits
-//     only on its own data and the weight loads overlap the LDS write and the
-//     barrier; with 8-row tiles (few rows, latency-bound) requested first.
-//     The workgroups of one head are 128 apart in the grid, hence on the same
-//     XCD, and share W_UV[h] through its L2;
+//     splits in flight, empty splits never read) into an fp32 tile in LDS;
+//   * merge, R = 8 (at most 32 rows in all: few rows, latency-bound): the
+//     rows of the tile share the 8 waves (8, 4, 2 or 1 waves per row for
+//     1, 2, 3-4 or 5-8 rows), each wave merging a contiguous range of the
+//     row's splits with up to 16 in flight; the waves' sums are added in LDS
+//     in wave order, so the result does not depend on timing. A single row's
+//     32 splits thus take one round of loads instead of two in one wave.
+//     Lane l owns latent columns 4l..4l+3 and 256+4l..+3, so every load
+//     instruction covers 1 KiB of contiguous memory; the split LSEs are read
+//     first, on their own;
+//   * W_UV[h] fragments (output rows 16w..16w+15, all 512 latent columns) are
+//     requested after the merge's first loads, so the merge waits only on its
+//     own data and the weight loads overlap it, the LDS writes and the
+//     barrier. The workgroups of one head are 128 apart in the grid, hence on
+//     the same XCD, and share W_UV[h] through its L2;
 //   * up-projection: out^T[d, t] = sum_c W_UV[h][d][c] o_lat[t][c] on
 //     v_mfma_f32_16x16x32_bf16 (16 rows d x 16 columns t, of which the tile's
 //     R are real, x 32 latent columns c), the fp32 o_lat fed as a bf16 high
 //     part plus a bf16 remainder (two MFMAs per step, ~16 significant bits).
-// R = 8 keeps every merge concurrent and spreads few rows over more
-// workgroups; R = 16 halves the W_UV reads per row where there are rows
-// enough to fill the chip.
+// R = 8 spreads few rows over more workgroups; R = 16 halves the W_UV reads
+// per row where there are rows enough to fill the chip.
 // In k-step ks, lane quad q holds latent columns 32ks + 8q .. +7 of both
 // operands, so one instruction reads 64 contiguous bytes of each W_UV row.
 #include "mla_device.hpp"
@@ -54,6 +57,68 @@ __device__ __forceinline__ float wave_sum_f(float v) {
 
 }  // namespace
 
+// The merge of one row: the split weights w_s = exp(lse_s - L) of the row's
+// LSE L (empty splits, lse = -inf, weigh 0 and are never read), then
+// sum_s w_s o_s over the splits [sa, sb) into a0 (columns 4l..4l+3) and a1
+// (columns 256 + 4l..+3). l0 = lse of split `lane` (-inf past the end), M the
+// row maximum. before_wait runs once, right after the first loads of
+// partials are issued (the W_UV fragments are requested there, so the merge
+// waits only on its own data).
+template <int kChunk, class F>
+__device__ __forceinline__ void merge_range(const float* __restrict__ lp, const float* __restrict__ op, int num_splits,
+                                            float l0, float L, int sa, int sb, int lane, f32x4v& a0, f32x4v& a1,
+                                            F&& before_wait) {
+  f32x4v v0[kChunk], v1[kChunk];
+  bool first = true;
+  for (int b0 = sa & ~63; b0 < sb; b0 += 64) {  // blocks of 64 splits: lane k holds the weight of b0 + k
+    const float lb = b0 == 0 ? l0 : (b0 + lane < num_splits ? lp[b0 + lane] : -INFINITY);
+    const float wl = expf(lb - L);  // 0 when lse = -inf
+    auto weight = [&](int s) {
+      return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), s - b0));
+    };
+    const int e = min(b0 + 64, sb);
+    for (int s0 = max(b0, sa); s0 < e; s0 += kChunk) {
+#pragma unroll
+      for (int k = 0; k < kChunk; ++k) {
+        if (s0 + k < e && weight(s0 + k) > 0.f) {
+          v0[k] = *reinterpret_cast<const f32x4v*>(op + (int64_t)(s0 + k) * kDc);
+          v1[k] = *reinterpret_cast<const f32x4v*>(op + (int64_t)(s0 + k) * kDc + kDc / 2);
+        }
+      }
+      if (first) {
+        before_wait();
+        first = false;
+      }
+#pragma unroll
+      for (int k = 0; k < kChunk; ++k) {
+        if (s0 + k < e) {
+          const float w = weight(s0 + k);
+          if (w > 0.f) {
+            a0 += w * v0[k];
+            a1 += w * v1[k];
+          }
+        }
+      }
+    }
+  }
+  if (first) before_wait();
+}
+
+// The row's LSE statistics: l0 = lse of split `lane`, M = max, L = M + log sum exp
+// (-inf when every split is empty).
+__device__ __forceinline__ void row_lse(const float* __restrict__ lp, int num_splits, int lane, float& l0, float& L) {
+  l0 = lane < num_splits ? lp[lane] : -INFINITY;
+  float M = l0;
+  for (int s = lane + 64; s < num_splits; s += 64) M = fmaxf(M, lp[s]);
+  M = wave_max_f(M);
+  L = -INFINITY;
+  if (M != -INFINITY) {
+    float tot = expf(l0 - M);
+    for (int s = lane + 64; s < num_splits; s += 64) tot += expf(lp[s] - M);
+    L = M + logf(wave_sum_f(tot));
+  }
+}
+
 template <int kRows>
 __global__ __launch_bounds__(512) void combine_up_kernel(const float* __restrict__ o_part,
                                                          const float* __restrict__ lse_part,
@@ -61,83 +126,92 @@ __global__ __launch_bounds__(512) void combine_up_kernel(const float* __restrict
                                                          __bf16* __restrict__ out, float* __restrict__ lse_out) {
   static_assert(kRows == 8 || kRows == 16, "one or two rows per wave");
   __shared__ __attribute__((aligned(16))) float olat[kTileCols * kOlatStride];
+  // per-wave sums of a row merged by several waves: [wave][column half][lane]
+  __shared__ f32x4v wsum[kRows == 8 ? 8 : 1][2][64];
   const int h = blockIdx.x % kH;
   const int t0 = (blockIdx.x / kH) * kRows;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q = lane >> 4, r = lane & 15;
+  const int rows_here = min(kRows, T - t0);
 
-  // W_UV[h] rows d = 16w + r, columns 32ks + 8q .. +7 for k-steps ks = 0..15.
-  // With 8-row tiles (few rows: each load round is latency, not bandwidth)
-  // they are requested first, so their latency overlaps the merge's; with
-  // 16-row tiles after the merge loads, so the merge waits only on its own data.
+  // W_UV[h] rows d = 16w + r, columns 32ks + 8q .. +7 for k-steps ks = 0..15,
+  // requested once the merge's own loads are under way
   bf16x8 a[16];
   auto load_w = [&]() {
     const bf16x8* wp = reinterpret_cast<const bf16x8*>(w_uv + ((int64_t)h * kDhc + 16 * wave + r) * kDc + 8 * q);
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks) a[ks] = wp[4 * ks];
   };
-  if constexpr (kRows == 8) load_w();
 
-  // ---- merge rows t0 + w (+ 8) into LDS rows w (+ 8); zeros past the end,
-  // never stored
-  for (int rr = wave; rr < kTileCols; rr += 8) {
-    f32x4v a0 = f32x4v{}, a1 = f32x4v{};
-    const int tm = t0 + rr;
-    if (rr < kRows && tm < T) {
-      const int64_t row = (int64_t)tm * kH + h;
-      const float* lp = lse_part + row * num_splits;
-      const float* op = o_part + row * num_splits * kDc + 4 * lane;
-      // up to 64 splits: one load round, lane s holding lse_s for the max, the
-      // sum and the weights
-      const float l0 = lane < num_splits ? lp[lane] : -INFINITY;
-      float M = l0;
-      for (int s = lane + 64; s < num_splits; s += 64) M = fmaxf(M, lp[s]);
-      M = wave_max_f(M);
-      float L = -INFINITY;
-      if (M != -INFINITY) {
-        float tot = expf(l0 - M);
-        for (int s = lane + 64; s < num_splits; s += 64) tot += expf(lp[s] - M);
-        L = M + logf(wave_sum_f(tot));
-        // 8-row tiles hold W_UV's fragments during the merge: 16 splits in flight
-        constexpr int kChunk = kRows == 8 ? 16 : kMergeChunk;
-        f32x4v v0[kChunk], v1[kChunk];
-        for (int b0 = 0; b0 < num_splits; b0 += 64) {  // blocks of 64 splits: lane k holds the weight of b0 + k
-          const int b1 = min(num_splits, b0 + 64);
-          const float lb = b0 == 0 ? l0 : (b0 + lane < num_splits ? lp[b0 + lane] : -INFINITY);
-          const float wl = expf(lb - L);  // 0 when lse = -inf
-          auto weight = [&](int s) {
-            return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), s - b0));
-          };
-          for (int s0 = b0; s0 < b1; s0 += kChunk) {
-#pragma unroll
-            for (int k = 0; k < kChunk; ++k) {
-              if (s0 + k < b1 && weight(s0 + k) > 0.f) {
-                v0[k] = *reinterpret_cast<const f32x4v*>(op + (int64_t)(s0 + k) * kDc);
-                v1[k] = *reinterpret_cast<const f32x4v*>(op + (int64_t)(s0 + k) * kDc + kDc / 2);
-              }
-            }
-#pragma unroll
-            for (int k = 0; k < kChunk; ++k) {
-              if (s0 + k < b1) {
-                const float w = weight(s0 + k);
-                if (w > 0.f) {
-                  a0 += w * v0[k];
-                  a1 += w * v1[k];
-                }
-              }
-            }
-          }
-        }
+  if constexpr (kRows == 16) {
+    // ---- merge rows t0 + w and t0 + w + 8 into LDS rows w and w + 8; zeros
+    // past the end, never stored. W_UV is requested after both rows' loads.
+    for (int rr = wave; rr < kTileCols; rr += 8) {
+      f32x4v a0 = f32x4v{}, a1 = f32x4v{};
+      if (rr < rows_here) {
+        const int64_t row = (int64_t)(t0 + rr) * kH + h;
+        const float* lp = lse_part + row * num_splits;
+        float l0, L;
+        row_lse(lp, num_splits, lane, l0, L);
+        if (L != -INFINITY)
+          merge_range<kMergeChunk>(lp, o_part + row * num_splits * kDc + 4 * lane, num_splits, l0, L, 0, num_splits,
+                                   lane, a0, a1, [] {});
+        if (lane == 0) lse_out[row] = L;
       }
-      if (lane == 0) lse_out[row] = L;
+      float* dst = olat + rr * kOlatStride + 4 * lane;
+      *reinterpret_cast<f32x4v*>(dst) = a0;
+      *reinterpret_cast<f32x4v*>(dst + kDc / 2) = a1;
     }
-    float* dst = olat + rr * kOlatStride + 4 * lane;
-    *reinterpret_cast<f32x4v*>(dst) = a0;
-    *reinterpret_cast<f32x4v*>(dst + kDc / 2) = a1;
+    load_w();
+  } else {
+    // ---- few rows: a row's splits are dealt to wpr waves (8 / 4 / 2 / 1 for
+    // 1 / 2 / 3-4 / 5-8 rows), each wave merging a contiguous range; the wave
+    // sums are then added in wave order, so the result does not depend on timing
+    const int wpr_log = rows_here == 1 ? 3 : rows_here == 2 ? 2 : rows_here <= 4 ? 1 : 0;
+    const int rr = wave >> wpr_log, j = wave & ((1 << wpr_log) - 1);
+    f32x4v a0 = f32x4v{}, a1 = f32x4v{};
+    bool requested = false;
+    if (rr < rows_here) {
+      const int64_t row = (int64_t)(t0 + rr) * kH + h;
+      const float* lp = lse_part + row * num_splits;
+      float l0, L;
+      row_lse(lp, num_splits, lane, l0, L);
+      if (L != -INFINITY) {
+        const int cnt = (num_splits + (1 << wpr_log) - 1) >> wpr_log;
+        const int sa = min(num_splits, j * cnt), sb = min(num_splits, sa + cnt);
+        merge_range<16>(lp, o_part + row * num_splits * kDc + 4 * lane, num_splits, l0, L, sa, sb, lane, a0, a1, [&] {
+          if (!requested) load_w();
+          requested = true;
+        });
+      }
+      if (j == 0 && lane == 0) lse_out[row] = L;
+    }
+    if (!requested) load_w();
+    if (wpr_log == 0) {
+      // one wave per row: rows w and w + 8 (zeros past the tile's rows)
+      float* dst = olat + wave * kOlatStride + 4 * lane;
+      *reinterpret_cast<f32x4v*>(dst) = a0;
+      *reinterpret_cast<f32x4v*>(dst + kDc / 2) = a1;
+      dst += 8 * kOlatStride;
+      *reinterpret_cast<f32x4v*>(dst) = f32x4v{};
+      *reinterpret_cast<f32x4v*>(dst + kDc / 2) = f32x4v{};
+    } else {
+      wsum[wave][0][lane] = a0;
+      wsum[wave][1][lane] = a1;
+      __syncthreads();
+      // 16 rows x 128 column quads, four per thread
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = tid + 512 * i, row = e >> 7, c4 = e & 127;
+        f32x4v v = f32x4v{};
+        if (row < rows_here) {
+          for (int jj = 0; jj < (1 << wpr_log); ++jj) v += wsum[(row << wpr_log) + jj][c4 >> 6][c4 & 63];
+        }
+        *reinterpret_cast<f32x4v*>(olat + row * kOlatStride + 4 * c4) = v;
+      }
+    }
   }
-
-  if constexpr (kRows == 16) load_w();
 
   __syncthreads();
 
