@@ -582,8 +582,7 @@ __device__ __forceinline__ void decode_paged_body(
     unsigned dst;
   };
   // 8-bit: src is the page's first byte, dst the stage's wave slice
-  auto dma_target = [&](int tile, int stage) -> DmaTarget {
-    const int64_t page = physical_page(block_table, a.max_pages, b, tile >> 1, a.num_pages);
+  auto page_target = [&](int64_t page, int tile, int stage) -> DmaTarget {
     if constexpr (kFp4)
       return DmaTarget{kv + page * kFp4PageBytes,
                        (unsigned)(uintptr_t)(lds_void_t*)(lds + stage * F::bytes + wave * 1024)};
@@ -593,6 +592,9 @@ __device__ __forceinline__ void decode_paged_body(
     else
       return DmaTarget{kv + page * kPageBytes + (tile & 1) * kStageBytes,
                        (unsigned)(uintptr_t)(lds_void_t*)(lds + stage * kStageBytes + wave * 1024)};
+  };
+  auto dma_target = [&](int tile, int stage) -> DmaTarget {
+    return page_target(physical_page(block_table, a.max_pages, b, tile >> 1, a.num_pages), tile, stage);
   };
   // load k of a tile (k is a compile-time constant at every call); the 8-bit
   // tile is half `tile & 1` of its page in each of the page's three arrays
@@ -1058,12 +1060,11 @@ __device__ __forceinline__ void decode_paged_body(
       m_ref = -INFINITY;
       m_seen = -INFINITY;
 
-      // The first two tiles are requested before the queries so that the cache
-      // latency and the query loads overlap; all of them land before the tile loop
-      // (otherwise the compiler re-waits for the queries inside the loop, where the
-      // wait would also drain cache DMA).
-      if (n_tiles > 0) issue(tile0, 0);
-      if (n_tiles > 1) issue(tile0 + 1, 1);
+      // The queries are requested first, so that the page lookups of the first
+      // two tiles overlap their transfer; then the two tiles' DMA. Queries and
+      // tiles all land before the tile loop (otherwise the compiler re-waits
+      // for the queries inside the loop, where the wait would also drain cache
+      // DMA).
       // queries: B operand of S^T = K . Q^T; lane (g, lo) holds dims 16kk+8g..+7 of head h_own
       if (n_tiles > 0) {
         const int ql = lane_here();
@@ -1082,6 +1083,16 @@ __device__ __forceinline__ void decode_paged_body(
         }
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) qf[32 + kk] = qr[2 * kk + (ql >> 5)];
+        {
+          const DmaTarget d0 = dma_target(tile0, 0);
+#pragma unroll
+          for (int k = 0; k < F::dma; ++k) dma_piece(d0, k, tile0);
+        }
+        if (n_tiles > 1) {
+          const DmaTarget d1 = dma_target(tile0 + 1, 1);
+#pragma unroll
+          for (int k = 0; k < F::dma; ++k) dma_piece(d1, k, tile0 + 1);
+        }
         wait_vmcnt<0>();
         if constexpr (kScaled) {
           // each 32-dim block as hi + lo E4M3 codes; the MFMA operand takes
