@@ -3,7 +3,7 @@
 // K3 time-share study, "Inside the blocks").
 //
 // One wave per row: lane k holds the LSE of split k (of each block of 64),
-// max and sum come from wave reductions, and each split's weight is
+// max and sum come from DPP wave reductions, and each split's weight is
 // broadcast with readlane. Lane l owns latent columns 4l..4l+3 and
 // 256+4l..+3, so each load instruction covers 1 KiB of contiguous memory; up
 // to 16 splits' loads are in flight. Splits with LSE = -inf
@@ -14,21 +14,6 @@
 #include "decode.hpp"
 
 namespace mla {
-
-namespace {
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-
-}  // namespace
 
 constexpr int kCombineChunk = 16;  // splits whose loads are in flight together
 
@@ -45,7 +30,7 @@ __device__ __forceinline__ void combine_body(int item, const float* __restrict__
 
   float M = -INFINITY;
   for (int s = lane; s < num_splits; s += 64) M = fmaxf(M, lp[s]);
-  M = wave_max(M);
+  M = wave_max_dpp(M);
   if (M == -INFINITY) {  // every split empty
     *reinterpret_cast<f32x4*>(orow) = f32x4{};
     *reinterpret_cast<f32x4*>(orow + kDc / 2) = f32x4{};
@@ -54,7 +39,7 @@ __device__ __forceinline__ void combine_body(int item, const float* __restrict__
   }
   float tot = 0.f;
   for (int s = lane; s < num_splits; s += 64) tot += expf(lp[s] - M);
-  tot = wave_sum(tot);
+  tot = wave_sum_dpp(tot);
   const float L = M + logf(tot);
 
   f32x4 a0 = f32x4{}, a1 = f32x4{};

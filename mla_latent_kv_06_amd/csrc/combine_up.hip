@@ -44,17 +44,6 @@ constexpr int kMergeChunk = 24;       // splits whose loads are in flight togeth
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ float wave_max_f(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
-__device__ __forceinline__ float wave_sum_f(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-
 }  // namespace
 
 // The merge of one row: the split weights w_s = exp(lse_s - L) of the row's
@@ -110,12 +99,12 @@ __device__ __forceinline__ void row_lse(const float* __restrict__ lp, int num_sp
   l0 = lane < num_splits ? lp[lane] : -INFINITY;
   float M = l0;
   for (int s = lane + 64; s < num_splits; s += 64) M = fmaxf(M, lp[s]);
-  M = wave_max_f(M);
+  M = wave_max_dpp(M);
   L = -INFINITY;
   if (M != -INFINITY) {
     float tot = expf(l0 - M);
     for (int s = lane + 64; s < num_splits; s += 64) tot += expf(lp[s] - M);
-    L = M + logf(wave_sum_f(tot));
+    L = M + logf(wave_sum_dpp(tot));
   }
 }
 

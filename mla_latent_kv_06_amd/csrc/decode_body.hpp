@@ -349,24 +349,27 @@ __device__ __forceinline__ int pages_prefix(int x) {
 __device__ __forceinline__ int rows_pages(int L, int s_q, int i) {
   return pages_prefix(L - s_q + i) - pages_prefix(L - s_q);
 }
-__device__ __forceinline__ int wave_sum32(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return __builtin_amdgcn_readfirstlane(v);
-}
-__device__ __forceinline__ int wave_max32(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
-  return __builtin_amdgcn_readfirstlane(v);
-}
-__device__ __forceinline__ int wave_incl_scan32(int v, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(v, o, 64);
-    if (lane >= o) v += u;
-  }
+// Inclusive prefix sum (or running max) over the 64 lanes on DPP: shifts by 1,
+// 2, 4 and 8 lanes inside each 16-lane row, then lane 15's value into rows 1
+// and 3 and lane 31's into rows 2 and 3 (the two row broadcasts of the GFX9
+// DPP set). Six dependent VALU steps and no LDS round trip, where a __shfl
+// ladder costs one ds_bpermute round trip per step; the plan runs three of
+// these before a piece can start. Lanes shifted in read 0, so v must be >= 0
+// (page counts).
+template <bool kMax>
+__device__ __forceinline__ int wave_scan_dpp(int v) {
+  auto step = [&](int u) { v = kMax ? max(v, u) : v + u; };
+  step(__builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true));   // row_shr:1
+  step(__builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true));   // row_shr:2
+  step(__builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true));   // row_shr:4
+  step(__builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true));   // row_shr:8
+  step(__builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  step(__builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false));  // row_bcast:31
   return v;
 }
+__device__ __forceinline__ int wave_sum32(int v) { return __builtin_amdgcn_readlane(wave_scan_dpp<false>(v), 63); }
+__device__ __forceinline__ int wave_max32(int v) { return __builtin_amdgcn_readlane(wave_scan_dpp<true>(v), 63); }
+__device__ __forceinline__ int wave_incl_scan32(int v) { return wave_scan_dpp<false>(v); }
 
 }  // namespace
 
@@ -458,7 +461,7 @@ __device__ __forceinline__ void decode_paged_body(
     const int bb = b0 + lane;
     const int L = b0 == 0 ? L0 : (bb < a.B ? clamp_len(seqlens[bb], a.max_pages) : 0);
     const int t = b0 == 0 ? T0 : (bb < a.B ? rows_pages(L, a.s_q, a.s_q) : 0);
-    const int incl = wave_incl_scan32(t, lane);
+    const int incl = wave_incl_scan32(t);
     const uint64_t hit = __ballot(cp + incl > r_lo);
     if (hit) {
       const int f = __builtin_ctzll(hit);

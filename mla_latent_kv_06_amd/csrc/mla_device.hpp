@@ -56,6 +56,30 @@ __device__ __forceinline__ int lane_opaque() {
   return l;
 }
 
+// Max and sum of a float over the 64 lanes, returned to every lane: an
+// inclusive scan on DPP (shifts by 1, 2, 4 and 8 inside each 16-lane row, then
+// lane 15's value into rows 1 and 3 and lane 31's into rows 2 and 3), read at
+// lane 63. Lanes shifted in read the identity (-inf, resp. 0). Six dependent
+// VALU steps with a fixed order, where a __shfl ladder waits on six
+// ds_bpermute round trips.
+template <bool kMax>
+__device__ __forceinline__ float wave_reduce_dpp(float v) {
+  const int id = kMax ? __builtin_bit_cast(int, -INFINITY) : 0;
+  auto step = [&](int u) {
+    const float f = __builtin_bit_cast(float, u);
+    v = kMax ? fmaxf(v, f) : v + f;
+  };
+  step(__builtin_amdgcn_update_dpp(id, __builtin_bit_cast(int, v), 0x111, 0xf, 0xf, false));  // row_shr:1
+  step(__builtin_amdgcn_update_dpp(id, __builtin_bit_cast(int, v), 0x112, 0xf, 0xf, false));  // row_shr:2
+  step(__builtin_amdgcn_update_dpp(id, __builtin_bit_cast(int, v), 0x114, 0xf, 0xf, false));  // row_shr:4
+  step(__builtin_amdgcn_update_dpp(id, __builtin_bit_cast(int, v), 0x118, 0xf, 0xf, false));  // row_shr:8
+  step(__builtin_amdgcn_update_dpp(id, __builtin_bit_cast(int, v), 0x142, 0xa, 0xf, false));  // row_bcast:15
+  step(__builtin_amdgcn_update_dpp(id, __builtin_bit_cast(int, v), 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+__device__ __forceinline__ float wave_max_dpp(float v) { return wave_reduce_dpp<true>(v); }
+__device__ __forceinline__ float wave_sum_dpp(float v) { return wave_reduce_dpp<false>(v); }
+
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
 // vmcnt bits [3:0] and [15:14], expcnt [6:4] = 7, lgkmcnt [11:8] = 15).
 template <int N>
