@@ -25,6 +25,9 @@ Prints one JSON line:
   cpu_baseline  the fp64 CPU oracle on a bounded sample of every workload
   next_rows     for the headline: cache append and query rotation, the scan over the
                 8-bit and 4-bit caches, the decompressed branch (chunks with s_q > 1)
+  ceilings      the streaming-read rate and the sustained dense bf16 MFMA rate this
+                board reaches with nothing else to do, and the headline decode's
+                fractions of them (beside its fractions of the published peaks)
 Per-kernel times come from HIP events recorded around each launch inside the K
 timed steps, on the stream the kernels run on.
 """
@@ -77,6 +80,8 @@ def parse():
     p.add_argument("--no-fp8", action="store_true", help="skip the 8-bit cache leg")
     p.add_argument("--no-mxfp4", action="store_true", help="skip the 4-bit cache leg")
     p.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay of the step")
+    p.add_argument("--no-ceilings", action="store_true",
+                   help="skip the achievable streaming-read and sustained MFMA measurements")
     p.add_argument("--one-launch", action="store_true",
                    help="also time mla_decode_step (one cooperative launch) against the four kernels")
     p.add_argument("--copy-calibration", action="store_true",
@@ -432,6 +437,45 @@ def time_one_launch_step(M, torch, wl, steps, warmup):
     return res
 
 
+def time_ceilings(M, torch, wl, reads=10, mfma_launches=20, mfma_iters=100_000):
+    """What this board achieves with nothing else to do, for setting the decode's
+    fractions of the published peaks beside it: the streaming-read rate (one
+    non-temporal read of up to 4 GiB of the resident cache per launch) and the
+    sustained dense bf16 matrix rate (the register-only MFMA loop, after as many
+    warmup launches as timed ones so the board's power controller has settled).
+    HIP events on the stream the kernels run on, around all timed launches."""
+    stream = torch.cuda.current_stream()
+    flat = wl.kv.view(-1)
+    n = min(flat.numel(), (4 << 30) // 2) // 8 * 8  # bf16 elements, whole 16-byte chunks
+    buf = flat[:n]
+    sink = torch.empty(M.BENCH_SINK_FLOATS, dtype=torch.float32, device=buf.device)
+
+    def per_launch(fn, launches, warmup):
+        for _ in range(warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(launches):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / launches
+
+    nbytes = n * 2
+    s_read = per_launch(lambda: M.mla_bench_stream_read(buf, sink), reads, 3)
+    flop = 256 * 4 * 4 * mfma_iters * 32768
+    s_mfma = per_launch(lambda: M.mla_bench_mfma(mfma_iters, sink), mfma_launches, mfma_launches)
+    gbps, tfs = nbytes / s_read / 1e9, flop / s_mfma / 1e12
+    return {
+        "stream_read": {"gbps": round(gbps, 1), "frac_of_peak": round(gbps / HBM_PEAK_GBS, 4),
+                        "bytes_per_launch": nbytes, "us_per_launch": round(s_read * 1e6, 1), "launches": reads,
+                        "kernel": "mla_bench_stream_read (non-temporal 16-byte loads, 2048 x 256 threads)"},
+        "mfma_bf16": {"tflops": round(tfs, 1), "frac_of_peak": round(tfs / MFMA_BF16_PEAK_TFLOPS, 4),
+                      "flop_per_launch": flop, "us_per_launch": round(s_mfma * 1e6, 1), "launches": mfma_launches,
+                      "kernel": "mla_bench_mfma (v_mfma_f32_32x32x16_bf16, 256 x 4 waves, register operands)"},
+    }
+
+
 def _cpu_facts():
     model = "unknown"
     try:
@@ -620,6 +664,11 @@ def main():
         if args.one_launch:
             print("[bench] one-launch step against the four kernels it fuses", file=sys.stderr, flush=True)
             nxt["one_launch_step"] = time_one_launch_step(M, torch, wl, args.steps, args.warmup)
+    if not args.no_ceilings:
+        print("[bench] ceilings: streaming read and dense bf16 MFMA on this board", file=sys.stderr, flush=True)
+        c = result["ceilings"] = time_ceilings(M, torch, wl)
+        c["headline_decode"] = {"gbps_frac_of_stream_read": round(r["gbps"] / c["stream_read"]["gbps"], 4),
+                                "tflops_frac_of_sustained_mfma": round(r["tflops"] / c["mfma_bf16"]["tflops"], 4)}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (fp64 oracle on host cores)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(M, torch, wls, head, args.cpu_seconds)

@@ -477,6 +477,28 @@ mla_status mla_debug_gather(const void* kv_cache, int64_t num_pages,
                             const int32_t* seqlens, int B, int max_len,
                             void* out, void* stream);
 
+/* Measurement aids for reports that set a kernel's roofline fractions (taken
+ * against the published peaks) beside what this board achieves with nothing
+ * else to do; not part of the decode path. Both enqueue one kernel on
+ * `stream` and write to `sink` (device, 16-byte aligned, at least
+ * MLA_BENCH_SINK_FLOATS floats) only values of no meaning, which keep the work
+ * from being optimised away. MLA_ERR_NULL / MLA_ERR_ALIGN / MLA_ERR_SHAPE as
+ * for the other calls.
+ *
+ * mla_bench_stream_read: reads each 16-byte chunk of buf (device, 16-byte
+ * aligned, `bytes` a positive multiple of 16) once, with non-temporal vector
+ * loads (the scan's cache policy), from 2048 workgroups of 256 threads: the
+ * achievable streaming-read rate is bytes / duration.
+ *
+ * mla_bench_mfma: 256 workgroups of 4 waves (one wave per SIMD, the scan's
+ * launch shape); each wave runs `iters` (>= 1) rounds of four independent
+ * chains of v_mfma_f32_32x32x16_bf16 on register-resident pseudo-random bf16
+ * operands, i.e. 256 * 4 * 4 * iters * 32768 FLOP with no memory traffic: the
+ * sustained dense bf16 matrix rate is that over the duration. */
+enum { MLA_BENCH_SINK_FLOATS = 4096 };
+mla_status mla_bench_stream_read(const void* buf, int64_t bytes, float* sink, void* stream);
+mla_status mla_bench_mfma(int64_t iters, float* sink, void* stream);
+
 #ifdef __cplusplus
 } /* extern "C" */
 #endif

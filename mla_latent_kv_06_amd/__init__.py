@@ -283,6 +283,32 @@ def mla_up_proj(o_lat, w_uv, out=None, stream=None):
     return out
 
 
+BENCH_SINK_FLOATS = 4096
+
+
+def _bench_sink(device):
+    return torch.empty(BENCH_SINK_FLOATS, dtype=torch.float32, device=device)
+
+
+def mla_bench_stream_read(buf, sink=None, stream=None):
+    """Enqueue one streaming read of every byte of the device tensor buf
+    (contiguous, a whole number of 16-byte chunks); returns the bytes read."""
+    if not (buf.is_cuda and buf.is_contiguous()):
+        raise ValueError("buf must be a contiguous device tensor")
+    nbytes = buf.numel() * buf.element_size()
+    sink = _bench_sink(buf.device) if sink is None else sink
+    _check(_lib.LIB.mla_bench_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(stream)), "mla_bench_stream_read")
+    return nbytes
+
+
+def mla_bench_mfma(iters: int, sink=None, stream=None, device="cuda"):
+    """Enqueue one dense bf16 MFMA loop (256 x 4 waves, `iters` rounds of four
+    32x32x16 MFMAs each); returns its FLOP count."""
+    sink = _bench_sink(device) if sink is None else sink
+    _check(_lib.LIB.mla_bench_mfma(int(iters), _ptr(sink), _stream(stream)), "mla_bench_mfma")
+    return 256 * 4 * 4 * int(iters) * 32768
+
+
 def mla_debug_gather(kv_cache, block_table, seqlens, max_len: int, out=None, stream=None):
     """Logical rows [B, max_len, 576] gathered through the block table (zeros past L_b)."""
     B = block_table.shape[0]

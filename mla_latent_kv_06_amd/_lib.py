@@ -34,6 +34,8 @@ SIGNATURES = {
     "mla_combine_up_proj": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_void_p,
                                     c_void_p]),
     "mla_debug_gather": (c_int, [c_void_p, c_int64, c_void_p, c_int, c_void_p, c_int, c_int, c_void_p, c_void_p]),
+    "mla_bench_stream_read": (c_int, [c_void_p, c_int64, c_void_p, c_void_p]),
+    "mla_bench_mfma": (c_int, [c_int64, c_void_p, c_void_p]),
     "mla_rope_table": (c_int, [ctypes.c_double, c_int, c_void_p]),
     "mla_append_latent": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_int64, c_void_p, c_int, c_void_p,
                                   c_int, c_int, c_void_p]),

@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmla.so")
 ARCH = "gfx950"
 
-SOURCES = ["mla_api.hip", "decode.hip", "combine.hip", "combine_up.hip", "gemm.hip", "gather.hip", "append.hip", "decompress.hip", "prefill_mha.hip", "step.hip", "static_step.hip"]
+SOURCES = ["mla_api.hip", "decode.hip", "combine.hip", "combine_up.hip", "gemm.hip", "gather.hip", "append.hip", "decompress.hip", "prefill_mha.hip", "step.hip", "static_step.hip", "ceilings.hip"]
 
 
 def hipcc() -> str:

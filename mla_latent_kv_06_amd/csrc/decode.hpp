@@ -48,5 +48,7 @@ hipError_t launch_up_proj(const float* o_lat, const __bf16* w_uv, __bf16* out, i
 
 hipError_t launch_gather(const char* kv, int64_t num_pages, const int32_t* block_table, int max_pages,
                          const int32_t* seqlens, int B, int max_len, __bf16* out, hipStream_t stream);
+hipError_t launch_stream_read(const void* buf, int64_t bytes, float* sink, hipStream_t stream);
+hipError_t launch_mfma_loop(int64_t iters, float* sink, hipStream_t stream);
 
 }  // namespace mla

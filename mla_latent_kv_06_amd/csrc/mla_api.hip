@@ -329,4 +329,16 @@ mla_status mla_debug_gather(const void* kv_cache, int64_t num_pages, const int32
                     "mla_debug_gather launch");
 }
 
+mla_status mla_bench_stream_read(const void* buf, int64_t bytes, float* sink, void* stream) {
+  const mla::Check c = mla::check_bench_stream_read(buf, bytes, sink);
+  if (!c.ok()) return report(c);
+  return report_hip(mla::launch_stream_read(buf, bytes, sink, as_stream(stream)), "mla_bench_stream_read launch");
+}
+
+mla_status mla_bench_mfma(int64_t iters, float* sink, void* stream) {
+  const mla::Check c = mla::check_bench_mfma(iters, sink);
+  if (!c.ok()) return report(c);
+  return report_hip(mla::launch_mfma_loop(iters, sink, as_stream(stream)), "mla_bench_mfma launch");
+}
+
 }  // extern "C"

@@ -285,6 +285,20 @@ inline Check check_gather(const void* kv, int64_t num_pages, const void* bt, int
   return Check{};
 }
 
+inline Check check_bench_stream_read(const void* buf, int64_t bytes, const void* sink) {
+  MLA_TRY(need_ptr(buf, "buf"));
+  MLA_TRY(need_ptr(sink, "sink"));
+  MLA_TRY(need_range(bytes, 16, (1LL << 46), "bytes"));
+  if (bytes % 16 != 0) return fail(MLA_ERR_SHAPE, "%s = %lld is not a multiple of 16", "bytes", (long long)bytes);
+  return Check{};
+}
+
+inline Check check_bench_mfma(int64_t iters, const void* sink) {
+  MLA_TRY(need_ptr(sink, "sink"));
+  MLA_TRY(need_range(iters, 1, (1LL << 40), "iters"));
+  return Check{};
+}
+
 // ---- block-table contract ------------------------------------------------
 // The decode, gather, append and decompression kernels read entry
 // block_table[b, p] for the logical pages p < ceil(L_b / 64) of every

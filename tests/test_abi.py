@@ -26,7 +26,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) == 29, names
+    assert len(names) == 31, names
     out = subprocess.run(["nm", "-D", "--defined-only", os.path.join(ROOT, "mla_latent_kv_06_amd", "libmla.so")],
                          capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\bT (mla_[a-z0-9_]+)\b", out))
@@ -128,6 +128,21 @@ def test_other_entry_validation(lib):
     assert lib.mla_prefill_mha(A, A, A, A, 128, A, 4, A, 2, A, 2, 300, 64, 0.07, A, A, None) == 2
     assert lib.mla_prefill_mha(A, A, A, A, 128, A, 4, A, 2, A, 2, 300, 128, 0.0, A, A, None) == 2
     assert lib.mla_prefill_mha(A, A, A, A, 128, A, 4, A, 2, A, 2, 0, 128, 0.07, A, A, None) == 2
+
+
+def test_measurement_aid_validation(lib):
+    # mla_bench_stream_read(buf, bytes, sink, stream), mla_bench_mfma(iters, sink, stream):
+    # every rejection happens on the host, before any launch
+    assert lib.mla_bench_stream_read(None, 1024, A, None) == 1
+    assert lib.mla_bench_stream_read(A, 1024, None, None) == 1
+    assert lib.mla_bench_stream_read(MIS, 1024, A, None) == 3
+    assert lib.mla_bench_stream_read(A, 1024, MIS, None) == 3
+    assert lib.mla_bench_stream_read(A, 0, A, None) == 2
+    assert lib.mla_bench_stream_read(A, 1000, A, None) == 2
+    assert b"multiple of 16" in lib.mla_last_error()
+    assert lib.mla_bench_mfma(0, A, None) == 2
+    assert lib.mla_bench_mfma(-5, A, None) == 2
+    assert lib.mla_bench_mfma(10, None, None) == 1
 
 
 def test_host_helpers(lib):
