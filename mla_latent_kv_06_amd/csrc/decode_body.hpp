@@ -410,7 +410,10 @@ __device__ __forceinline__ void decode_paged_body(
   // k - floor(P_r / W) of row r (P_r = the row's first page in the
   // concatenation). W is at least ceil((n_max - 1) / (num_splits - 1)), so a
   // row never needs more than num_splits slots; with num_splits = 1 rows are
-  // not cut and each row goes whole to the range holding its first page.
+  // not cut and each row goes whole to the range holding its middle page
+  // (first page + floor(n / 2)): rows of nearly equal length then spread
+  // evenly, and the workgroups of an XCD start their rows at the same page,
+  // so a chunk's query rows, which all rescan one prefix, share it in L2.
   const int S = a.num_splits;
   // the first 64 sequences stay in registers (lane = sequence); larger
   // batches are read in further blocks of 64
@@ -1048,7 +1051,8 @@ __device__ __forceinline__ void decode_paged_body(
   while (cb < a.B && cp < r_hi) {
     const int v = cL - a.s_q + ci + 1;          // keys visible to query ci
     const int n_row = v > 0 ? (v + kPage - 1) / kPage : 0;
-    const bool mine = n_row > 0 && (S > 1 ? cp + n_row > r_lo : cp >= r_lo);
+    const int mid = cp + n_row / 2;  // with S = 1 the row belongs to the range of its middle page
+    const bool mine = n_row > 0 && (S > 1 ? cp + n_row > r_lo : (mid >= r_lo && mid < r_hi));
     if (mine) {
       const int pa = S > 1 ? max(r_lo, cp) - cp : 0;
       const int pe = S > 1 ? min(r_hi, cp + n_row) - cp : n_row;

@@ -362,7 +362,8 @@ inline size_t workspace_bytes(int B, int s_q, int H, int num_splits) {
 //     W = max(ceil(P_tot / kScanGroups), ceil((n_max - 1) / (S - 1)), 1),
 // which bounds any row to S pieces; with S = 1 rows are not cut, W is
 // ceil(P_tot / kScanGroups) and a row goes whole to the range holding its
-// first page. The planner below evaluates that plan for every distinct W.
+// middle page (first page + floor(n / 2)). The planner below evaluates that
+// plan for every distinct W.
 constexpr int kScanGroups = 256;
 
 // Visible pages of every row (b, i), lengths clamped like the kernel does.
@@ -402,8 +403,9 @@ inline long long scan_cost(const std::vector<int64_t>& n, int64_t W, bool cut, l
         }
         total += k1 - k0 + 1;
       } else {
-        pages[P / W] += nr;
-        ++pieces[P / W];
+        const int64_t k = (P + nr / 2) / W;
+        pages[k] += nr;
+        ++pieces[k];
         ++total;
       }
     }
