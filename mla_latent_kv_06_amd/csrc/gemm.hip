@@ -6,7 +6,10 @@ namespace mla {
 __global__ __launch_bounds__(256) void absorb_kernel(const __bf16* __restrict__ q_c, const __bf16* __restrict__ w_uk,
                                                      __bf16* __restrict__ q_abs, int T) {
   __shared__ __attribute__((aligned(16))) char lds[kAbsorbLdsBytes];
-  absorb_body(lds, blockIdx.x, q_c, w_uk, q_abs, T);
+  // workgroup x: item x mod 512 (so all token blocks of an item run on one XCD
+  // and share its W_UK block in L2), tokens of block x / 512
+  const int t_begin = (blockIdx.x / kAbsorbItems) * kAbsorbTokens;
+  absorb_body(lds, blockIdx.x % kAbsorbItems, q_c, w_uk, q_abs, t_begin, min(T, t_begin + kAbsorbTokens));
 }
 
 __global__ __launch_bounds__(256) void up_proj_kernel(const float* __restrict__ o_lat, const __bf16* __restrict__ w_uv,
@@ -16,7 +19,8 @@ __global__ __launch_bounds__(256) void up_proj_kernel(const float* __restrict__ 
 }
 
 hipError_t launch_absorb(const __bf16* q_c, const __bf16* w_uk, __bf16* q_abs, int T, hipStream_t stream) {
-  hipLaunchKernelGGL(absorb_kernel, dim3(kAbsorbItems), dim3(256), 0, stream, q_c, w_uk, q_abs, T);
+  const int blocks = (T + kAbsorbTokens - 1) / kAbsorbTokens;
+  hipLaunchKernelGGL(absorb_kernel, dim3(kAbsorbItems * blocks), dim3(256), 0, stream, q_c, w_uk, q_abs, T);
   return hipGetLastError();
 }
 

@@ -26,15 +26,17 @@ constexpr int kAbsLdsStride = kAbsCols * 2 + 16;  // padded W row in LDS (bytes)
 constexpr int kAbsorbLdsBytes = kDhc * kAbsLdsStride;
 constexpr int kUpProjLdsBytes = 4 * 4 * 64 * 16;
 constexpr int kAbsorbItems = kH * (kDc / kAbsCols);  // 512
+constexpr int kAbsorbTokens = 128;  // tokens per absorb workgroup: longer chunks spread over more workgroups
 constexpr int kUpProjItems = kH * 4;                 // 512
 
-// Workgroup = (head h, 128-column block cb). W_UK[h][:, cb*128 .. +128] is
-// staged in LDS once; the A operand (W^T: 32 columns c x 16 dims d per lane
-// group) is then read with transposed LDS reads and kept in registers for all
-// token tiles.
+// Workgroup = (head h, 128-column block cb, tokens [t_begin, t_end)).
+// W_UK[h][:, cb*128 .. +128] is staged in LDS once; the A operand (W^T: 32
+// columns c x 16 dims d per lane group) is then read with transposed LDS reads
+// and kept in registers for the workgroup's token tiles.
 // item = (head, column block) = h * 4 + cb; lds: kAbsorbLdsBytes, 16-byte aligned
 __device__ __forceinline__ void absorb_body(char* __restrict__ lds, int item, const __bf16* __restrict__ q_c,
-                                            const __bf16* __restrict__ w_uk, __bf16* __restrict__ q_abs, int T) {
+                                            const __bf16* __restrict__ w_uk, __bf16* __restrict__ q_abs, int t_begin,
+                                            int t_end) {
   const int h = item >> 2;
   const int cb = item & 3;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -46,12 +48,12 @@ __device__ __forceinline__ void absorb_body(char* __restrict__ lds, int item, co
   bf16x8 bq[8];
   auto load_q = [&](int t0) {
     const int t = t0 + lo;
-    const bool tv = t < T;
+    const bool tv = t < t_end;
     const bf16x8* qrow = reinterpret_cast<const bf16x8*>(q_c + ((int64_t)(tv ? t : 0) * kH + h) * kDhc);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) bq[ks] = tv ? qrow[2 * ks + g] : bf16x8{};
   };
-  load_q(0);
+  load_q(t_begin);
 
   // stage W rows d = 0..127, columns cb*128 .. +128 (256 bytes per row)
   const char* wsrc = reinterpret_cast<const char*>(w_uk + ((int64_t)h * kDhc) * kDc + cb * kAbsCols);
@@ -86,13 +88,13 @@ __device__ __forceinline__ void absorb_body(char* __restrict__ lds, int item, co
   }
 
   const int c0 = cb * kAbsCols + wave * 32;
-  for (int t0 = 0; t0 < T; t0 += 32) {
+  for (int t0 = t_begin; t0 < t_end; t0 += 32) {
     f32x16 acc = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], bq[ks], acc, 0, 0, 0);
-    if (t0 + 32 < T) load_q(t0 + 32);
+    if (t0 + 32 < t_end) load_q(t0 + 32);
     const int t = t0 + lo;
-    if (t < T) {
+    if (t < t_end) {
       __bf16* orow = q_abs + ((int64_t)t * kH + h) * kDc + c0;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {

@@ -54,7 +54,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
 
   // phase 1: q_abs = q_c . W_UK, work items (head, 128-column block)
   for (int item = blockIdx.x; item < kAbsorbItems; item += gridDim.x) {
-    absorb_body(lds, item, q_c, w_uk, q_abs, T);
+    absorb_body(lds, item, q_c, w_uk, q_abs, 0, T);
     __syncthreads();  // the next item restages the weights in LDS
   }
   grid.sync();

@@ -119,8 +119,9 @@ def test_gather_ragged_lengths_bit_exact(M):
 # absorb and up-projection
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("T", [1, 16, 45, 1024])
+@pytest.mark.parametrize("T", [1, 16, 45, 128, 129, 300, 1024])
 def test_absorb_parity(M, T):
+    """Token counts on and around the 128-token blocks the absorb splits a chunk into."""
     g = torch.Generator().manual_seed(100 + T)
     q_c = torch.randn((T, 128, 128), generator=g).to(torch.bfloat16)
     w_uk = (torch.randn((128, 128, 512), generator=g) / math.sqrt(512)).to(torch.bfloat16)
