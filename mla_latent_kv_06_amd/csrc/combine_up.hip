@@ -26,6 +26,10 @@
 //     v_mfma_f32_16x16x32_bf16 (16 rows d x 16 columns t, of which the tile's
 //     R are real, x 32 latent columns c), the fp32 o_lat fed as a bf16 high
 //     part plus a bf16 remainder (two MFMAs per step, ~16 significant bits).
+//     Each merged row is split into the two parts once, as it is written to
+//     LDS, so the 8 waves read bf16 operands instead of each converting the
+//     whole tile again. The partials are loaded non-temporally (each is read
+//     once), which keeps the shared W_UV fragments in L2.
 // R = 8 spreads few rows over more workgroups; R = 16 halves the W_UV reads
 // per row where there are rows enough to fill the chip.
 // In k-step ks, lane quad q holds latent columns 32ks + 8q .. +7 of both
@@ -39,7 +43,7 @@ namespace {
 
 constexpr int kTileCols = 16;     // MFMA columns: the tile's rows, then zero rows
 constexpr int kSmallTileMaxRows = 32;  // T up to this: 8-row tiles, else 16-row tiles
-constexpr int kOlatStride = kDc + 4;  // floats; the pad spreads the 16 rows of an MFMA read over the banks
+constexpr int kTileStride = kDc + 8;  // bf16 per tile row; the pad spreads the 16 rows of an MFMA read over the banks
 constexpr int kMergeChunk = 24;       // splits whose loads are in flight together
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
@@ -70,8 +74,9 @@ __device__ __forceinline__ void merge_range(const float* __restrict__ lp, const 
 #pragma unroll
       for (int k = 0; k < kChunk; ++k) {
         if (s0 + k < e && weight(s0 + k) > 0.f) {
-          v0[k] = *reinterpret_cast<const f32x4v*>(op + (int64_t)(s0 + k) * kDc);
-          v1[k] = *reinterpret_cast<const f32x4v*>(op + (int64_t)(s0 + k) * kDc + kDc / 2);
+          // partials are read once: non-temporal, so they do not push W_UV out of L2
+          v0[k] = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(op + (int64_t)(s0 + k) * kDc));
+          v1[k] = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(op + (int64_t)(s0 + k) * kDc + kDc / 2));
         }
       }
       if (first) {
@@ -114,7 +119,19 @@ __global__ __launch_bounds__(512) void combine_up_kernel(const float* __restrict
                                                          const __bf16* __restrict__ w_uv, int T, int num_splits,
                                                          __bf16* __restrict__ out, float* __restrict__ lse_out) {
   static_assert(kRows == 8 || kRows == 16, "one or two rows per wave");
-  __shared__ __attribute__((aligned(16))) float olat[kTileCols * kOlatStride];
+  // the merged o_lat tile as the MFMA's B operand: bf16 high parts (tile[0]) and
+  // bf16 remainders (tile[1]), split once as each row is merged
+  __shared__ __attribute__((aligned(16))) __bf16 tile[2][kTileCols * kTileStride];
+  auto put4 = [&](int row, int col, const f32x4v& v) {
+    bf16x4 hi, lw;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      hi[j] = (__bf16)v[j];
+      lw[j] = (__bf16)(v[j] - (float)hi[j]);
+    }
+    *reinterpret_cast<bf16x4*>(&tile[0][row * kTileStride + col]) = hi;
+    *reinterpret_cast<bf16x4*>(&tile[1][row * kTileStride + col]) = lw;
+  };
   // per-wave sums of a row merged by several waves: [wave][column half][lane]
   __shared__ f32x4v wsum[kRows == 8 ? 8 : 1][2][64];
   const int h = blockIdx.x % kH;
@@ -148,9 +165,8 @@ __global__ __launch_bounds__(512) void combine_up_kernel(const float* __restrict
                                    lane, a0, a1, [] {});
         if (lane == 0) lse_out[row] = L;
       }
-      float* dst = olat + rr * kOlatStride + 4 * lane;
-      *reinterpret_cast<f32x4v*>(dst) = a0;
-      *reinterpret_cast<f32x4v*>(dst + kDc / 2) = a1;
+      put4(rr, 4 * lane, a0);
+      put4(rr, kDc / 2 + 4 * lane, a1);
     }
     load_w();
   } else {
@@ -179,12 +195,10 @@ __global__ __launch_bounds__(512) void combine_up_kernel(const float* __restrict
     if (!requested) load_w();
     if (wpr_log == 0) {
       // one wave per row: rows w and w + 8 (zeros past the tile's rows)
-      float* dst = olat + wave * kOlatStride + 4 * lane;
-      *reinterpret_cast<f32x4v*>(dst) = a0;
-      *reinterpret_cast<f32x4v*>(dst + kDc / 2) = a1;
-      dst += 8 * kOlatStride;
-      *reinterpret_cast<f32x4v*>(dst) = f32x4v{};
-      *reinterpret_cast<f32x4v*>(dst + kDc / 2) = f32x4v{};
+      put4(wave, 4 * lane, a0);
+      put4(wave, kDc / 2 + 4 * lane, a1);
+      put4(wave + 8, 4 * lane, f32x4v{});
+      put4(wave + 8, kDc / 2 + 4 * lane, f32x4v{});
     } else {
       wsum[wave][0][lane] = a0;
       wsum[wave][1][lane] = a1;
@@ -197,7 +211,7 @@ __global__ __launch_bounds__(512) void combine_up_kernel(const float* __restrict
         if (row < rows_here) {
           for (int jj = 0; jj < (1 << wpr_log); ++jj) v += wsum[(row << wpr_log) + jj][c4 >> 6][c4 & 63];
         }
-        *reinterpret_cast<f32x4v*>(olat + row * kOlatStride + 4 * c4) = v;
+        put4(row, 4 * c4, v);
       }
     }
   }
@@ -208,16 +222,9 @@ __global__ __launch_bounds__(512) void combine_up_kernel(const float* __restrict
   f32x4 acc = f32x4{};
 #pragma unroll
   for (int ks = 0; ks < 16; ++ks) {
-    const float* src = olat + r * kOlatStride + 32 * ks + 8 * q;
-    const f32x4v x0 = *reinterpret_cast<const f32x4v*>(src);
-    const f32x4v x1 = *reinterpret_cast<const f32x4v*>(src + 4);
-    bf16x8 hi, lw;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float v = j < 4 ? x0[j] : x1[j - 4];
-      hi[j] = (__bf16)v;
-      lw[j] = (__bf16)(v - (float)hi[j]);
-    }
+    const int off = r * kTileStride + 32 * ks + 8 * q;
+    const bf16x8 hi = *reinterpret_cast<const bf16x8*>(&tile[0][off]);
+    const bf16x8 lw = *reinterpret_cast<const bf16x8*>(&tile[1][off]);
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], hi, acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], lw, acc, 0, 0, 0);
   }
