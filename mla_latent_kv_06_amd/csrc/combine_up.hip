@@ -44,7 +44,9 @@ namespace {
 constexpr int kTileCols = 16;     // MFMA columns: the tile's rows, then zero rows
 constexpr int kSmallTileMaxRows = 32;  // T up to this: 8-row tiles, else 16-row tiles
 constexpr int kTileStride = kDc + 8;  // bf16 per tile row; the pad spreads the 16 rows of an MFMA read over the banks
-constexpr int kMergeChunk = 24;       // splits whose loads are in flight together
+constexpr int kMergeChunk = 24;       // splits whose loads are in flight together (16-row tiles)
+constexpr int kFewChunk = 4;          // the same with few splits per row (see launch_combine_up)
+constexpr int kFewSplits16 = 16;      // 16-row tiles use kFewChunk up to this many splits
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
@@ -113,7 +115,7 @@ __device__ __forceinline__ void row_lse(const float* __restrict__ lp, int num_sp
   }
 }
 
-template <int kRows>
+template <int kRows, int kChunk>
 __global__ __launch_bounds__(512) void combine_up_kernel(const float* __restrict__ o_part,
                                                          const float* __restrict__ lse_part,
                                                          const __bf16* __restrict__ w_uv, int T, int num_splits,
@@ -161,7 +163,7 @@ __global__ __launch_bounds__(512) void combine_up_kernel(const float* __restrict
         float l0, L;
         row_lse(lp, num_splits, lane, l0, L);
         if (L != -INFINITY)
-          merge_range<kMergeChunk>(lp, o_part + row * num_splits * kDc + 4 * lane, num_splits, l0, L, 0, num_splits,
+          merge_range<kChunk>(lp, o_part + row * num_splits * kDc + 4 * lane, num_splits, l0, L, 0, num_splits,
                                    lane, a0, a1, [] {});
         if (lane == 0) lse_out[row] = L;
       }
@@ -185,7 +187,7 @@ __global__ __launch_bounds__(512) void combine_up_kernel(const float* __restrict
       if (L != -INFINITY) {
         const int cnt = (num_splits + (1 << wpr_log) - 1) >> wpr_log;
         const int sa = min(num_splits, j * cnt), sb = min(num_splits, sa + cnt);
-        merge_range<16>(lp, o_part + row * num_splits * kDc + 4 * lane, num_splits, l0, L, sa, sb, lane, a0, a1, [&] {
+        merge_range<kChunk>(lp, o_part + row * num_splits * kDc + 4 * lane, num_splits, l0, L, sa, sb, lane, a0, a1, [&] {
           if (!requested) load_w();
           requested = true;
         });
@@ -237,12 +239,28 @@ __global__ __launch_bounds__(512) void combine_up_kernel(const float* __restrict
 
 hipError_t launch_combine_up(const float* o_part, const float* lse_part, const __bf16* w_uv, int T, int num_splits,
                              __bf16* out, float* lse, hipStream_t stream) {
+  // With few splits per row the merge keeps loads of only kFewChunk splits in
+  // flight per wave: the 16-row kernel then needs 128 registers, so two
+  // 512-thread workgroups share a CU (one with the deep chunk: 222 registers).
+  // The 8-row kernel holds W_UV's fragments through the merge and stays at one
+  // workgroup per CU either way, so it takes the short chunk only where that
+  // costs no extra round of loads.
   if (T <= kSmallTileMaxRows) {
-    hipLaunchKernelGGL(combine_up_kernel<8>, dim3(kH * ((T + 7) / 8)), dim3(512), 0, stream, o_part, lse_part, w_uv,
-                       T, num_splits, out, lse);
+    const dim3 grid(kH * ((T + 7) / 8));
+    if (num_splits <= kFewChunk)
+      hipLaunchKernelGGL((combine_up_kernel<8, kFewChunk>), grid, dim3(512), 0, stream, o_part, lse_part, w_uv, T,
+                         num_splits, out, lse);
+    else
+      hipLaunchKernelGGL((combine_up_kernel<8, 16>), grid, dim3(512), 0, stream, o_part, lse_part, w_uv, T, num_splits,
+                         out, lse);
   } else {
-    hipLaunchKernelGGL(combine_up_kernel<16>, dim3(kH * ((T + 15) / 16)), dim3(512), 0, stream, o_part, lse_part,
-                       w_uv, T, num_splits, out, lse);
+    const dim3 grid(kH * ((T + 15) / 16));
+    if (num_splits <= kFewSplits16)
+      hipLaunchKernelGGL((combine_up_kernel<16, kFewChunk>), grid, dim3(512), 0, stream, o_part, lse_part, w_uv, T,
+                         num_splits, out, lse);
+    else
+      hipLaunchKernelGGL((combine_up_kernel<16, kMergeChunk>), grid, dim3(512), 0, stream, o_part, lse_part, w_uv, T,
+                         num_splits, out, lse);
   }
   return hipGetLastError();
 }
