@@ -7,7 +7,8 @@
 // Workgroup = (head h, tile of R = 8 or 16 query rows t), 8 waves:
 //   * merge, R = 16: wave w merges rows t0 + w and t0 + w + 8 as
 //     combine_kernel does (split weights by readlane, the loads of up to 24
-//     splits in flight, empty splits never read) into an fp32 tile in LDS;
+//     splits in flight, or 4 when rows have at most 16 splits so that two
+//     workgroups fit on a CU; empty splits never read) into the LDS tile;
 //   * merge, R = 8 (at most 32 rows in all: few rows, latency-bound): the
 //     rows of the tile share the 8 waves (8, 4, 2 or 1 waves per row for
 //     1, 2, 3-4 or 5-8 rows), each wave merging a contiguous range of the
@@ -18,9 +19,9 @@
 //     instruction covers 1 KiB of contiguous memory; the split LSEs are read
 //     first, on their own;
 //   * W_UV[h] fragments (output rows 16w..16w+15, all 512 latent columns) are
-//     requested after the merge's first loads, so the merge waits only on its
-//     own data and the weight loads overlap it, the LDS writes and the
-//     barrier. The workgroups of one head are 128 apart in the grid, hence on
+//     requested after the merge's loads (R = 8: its first ones; R = 16: both
+//     rows'), so the merge waits only on its own data and the weight loads
+//     overlap it, the LDS writes and the barrier. The workgroups of one head are 128 apart in the grid, hence on
 //     the same XCD, and share W_UV[h] through its L2;
 //   * up-projection: out^T[d, t] = sum_c W_UV[h][d][c] o_lat[t][c] on
 //     v_mfma_f32_16x16x32_bf16 (16 rows d x 16 columns t, of which the tile's
@@ -55,8 +56,8 @@ typedef float f32x4v __attribute__((ext_vector_type(4)));
 // The merge of one row: the split weights w_s = exp(lse_s - L) of the row's
 // LSE L (empty splits, lse = -inf, weigh 0 and are never read), then
 // sum_s w_s o_s over the splits [sa, sb) into a0 (columns 4l..4l+3) and a1
-// (columns 256 + 4l..+3). l0 = lse of split `lane` (-inf past the end), M the
-// row maximum. before_wait runs once, right after the first loads of
+// (columns 256 + 4l..+3). l0 = lse of split `lane` (-inf past the end).
+// before_wait runs once, right after the first loads of
 // partials are issued (the W_UV fragments are requested there, so the merge
 // waits only on its own data).
 template <int kChunk, class F>
