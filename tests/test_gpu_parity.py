@@ -229,6 +229,21 @@ def test_decode_edge_lengths(M, lens, s_q, S):
     _decode_check(M, q_abs, q_r, kv, bt, sl, S, f"edge lens={lens} s_q={s_q}")
 
 
+@pytest.mark.parametrize("B,s_q,S", [(150, 1, 1), (150, 1, 3), (130, 1, 7), (70, 3, 2), (200, 1, 256)])
+def test_decode_many_sequences(M, B, s_q, S):
+    """More than 64 sequences: the split plan reads the lengths in several blocks
+    of 64 (wave-wide sums, maximum and scan per block) and its row search walks
+    past the first block. Lengths 0..300 with zeros and one-token rows mixed in;
+    every row and every partial slot against the oracle."""
+    g = torch.Generator().manual_seed(1000 + B + s_q + S)
+    lens = torch.randint(0, 301, (B,), generator=g)
+    lens[::17] = 0
+    lens[5::19] = 1
+    q_abs, q_r, kv, bt, sl = _random_case(lens.tolist(), s_q, seed=2000 + B + S)
+    S = min(S, bt.shape[1])
+    _decode_check(M, q_abs, q_r, kv, bt, sl, S, f"{B} sequences s_q={s_q}")
+
+
 def test_decode_zero_length_rows(M):
     q_abs, q_r, kv, bt, sl = _random_case([0, 70], 1, seed=9)
     o_lat, lse = _decode_check(M, q_abs, q_r, kv, bt, sl, 2, "zero length", check_parts=True)
