@@ -223,6 +223,7 @@ def test_decode_uniform_config(M):
     ([5, 300, 1000], 1, 17),      # more splits than pages of short rows: empty splits
     ([300, 77], 2, 2),
     ([100, 400], 37, 3),          # causal chunk
+    ([700, 300], 512, 2),         # a long chunk: deep row search, the first 212 rows of sequence 1 see no key
 ])
 def test_decode_edge_lengths(M, lens, s_q, S):
     q_abs, q_r, kv, bt, sl = _random_case(lens, s_q, seed=sum(lens) + s_q)
