@@ -6,9 +6,8 @@
 // up-proj:  out[t, h, d]   = sum_c o_lat[t, h, c] W_UV[h, d, c]  (c: 512, d: 128)
 //
 // Both are computed transposed, D^T = W^T-ish . X^T, so that each lane of the
-// 32x32 accumulator owns one token and 4-runs of consecutive output columns,
-// which become 8-byte bf16 stores. At decode sizes both are bound by reading
-// the 16 MiB weight once.
+// 32x32 accumulator owns one token and 4-runs of consecutive output columns.
+// At decode sizes both are bound by reading the 16 MiB weight once.
 #pragma once
 
 #include "mla_device.hpp"
@@ -32,7 +31,13 @@ constexpr int kUpProjItems = kH * 4;                 // 512
 // Workgroup = (head h, 128-column block cb, tokens [t_begin, t_end)).
 // W_UK[h][:, cb*128 .. +128] is staged in LDS once; the A operand (W^T: 32
 // columns c x 16 dims d per lane group) is then read with transposed LDS reads
-// and kept in registers for the workgroup's token tiles.
+// and kept in registers for the workgroup's token tiles. The LDS then stages
+// each 32-token tile both ways: the queries arrive as whole 256-byte rows
+// (q_c[t][h], 16 lanes per row) and are read back in the MFMA's layout, and the
+// 32 x 128 output tile is written to LDS and stored as whole 256-byte rows of
+// q_abs. Loaded or stored straight in the MFMA layout, every instruction would
+// touch 32 token rows 32 KB (q_c) or 128 KB (q_abs) apart in 16-32 byte pieces;
+// staged, the 1024-token absorb takes 54 us instead of 96.
 // item = (head, column block) = h * 4 + cb; lds: kAbsorbLdsBytes, 16-byte aligned
 __device__ __forceinline__ void absorb_body(char* __restrict__ lds, int item, const __bf16* __restrict__ q_c,
                                             const __bf16* __restrict__ w_uk, __bf16* __restrict__ q_abs, int t_begin,
@@ -43,15 +48,30 @@ __device__ __forceinline__ void absorb_body(char* __restrict__ lds, int item, co
   const int g = lane >> 5, lo = lane & 31;
 
   // B operand (q_c^T: dims d = 16ks + 8g + 0..7 of token t0 + lo) of a token
-  // tile; the first tile is requested before the weights so both latencies
-  // overlap
+  // tile: loaded as whole rows (thread tid: 16-byte chunks tid and tid + 256
+  // of the tile, i.e. token chunk >> 4, bytes 16 (chunk & 15)), staged in LDS,
+  // read back per lane; the first tile is requested before the weights so
+  // both latencies overlap
   bf16x8 bq[8];
+  f32x4 qraw[2];
   auto load_q = [&](int t0) {
-    const int t = t0 + lo;
-    const bool tv = t < t_end;
-    const bf16x8* qrow = reinterpret_cast<const bf16x8*>(q_c + ((int64_t)(tv ? t : 0) * kH + h) * kDhc);
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) bq[ks] = tv ? qrow[2 * ks + g] : bf16x8{};
+    for (int k = 0; k < 2; ++k) {
+      const int c = k * 256 + tid, t = t0 + (c >> 4);
+      qraw[k] = t < t_end ? *reinterpret_cast<const f32x4*>(q_c + ((int64_t)t * kH + h) * kDhc + (c & 15) * 8) : f32x4{};
+    }
+  };
+  char* const qst = lds + 32 * kAbsLdsStride;  // query tile: 32 rows of 256 bytes (+16 padding)
+  auto stage_q = [&]() {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int c = k * 256 + tid;
+      *reinterpret_cast<f32x4*>(qst + (c >> 4) * kAbsLdsStride + (c & 15) * 16) = qraw[k];
+    }
+  };
+  auto read_q = [&]() {
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) bq[ks] = *reinterpret_cast<const bf16x8*>(qst + lo * kAbsLdsStride + (2 * ks + g) * 16);
   };
   load_q(t_begin);
 
@@ -87,20 +107,28 @@ __device__ __forceinline__ void absorb_body(char* __restrict__ lds, int item, co
     }
   }
 
-  const int c0 = cb * kAbsCols + wave * 32;
+  __syncthreads();  // every wave has its A fragments: the LDS now stages query and output tiles
   for (int t0 = t_begin; t0 < t_end; t0 += 32) {
+    if (t0 > t_begin) __syncthreads();  // the previous tile has been read and stored
+    stage_q();
+    __syncthreads();
+    read_q();
     f32x16 acc = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], bq[ks], acc, 0, 0, 0);
     if (t0 + 32 < t_end) load_q(t0 + 32);
-    const int t = t0 + lo;
-    if (t < t_end) {
-      __bf16* orow = q_abs + ((int64_t)t * kH + h) * kDc + c0;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const bf16x4 o = {(__bf16)acc[4 * q], (__bf16)acc[4 * q + 1], (__bf16)acc[4 * q + 2], (__bf16)acc[4 * q + 3]};
-        *reinterpret_cast<bf16x4*>(orow + 8 * q + 4 * g) = o;
-      }
+    for (int q = 0; q < 4; ++q) {
+      const bf16x4 o = {(__bf16)acc[4 * q], (__bf16)acc[4 * q + 1], (__bf16)acc[4 * q + 2], (__bf16)acc[4 * q + 3]};
+      *reinterpret_cast<bf16x4*>(lds + lo * kAbsLdsStride + (wave * 32 + 8 * q + 4 * g) * 2) = o;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int c = k * 256 + tid, row = c >> 4, ch = c & 15;
+      if (t0 + row < t_end)
+        *reinterpret_cast<f32x4*>(q_abs + ((int64_t)(t0 + row) * kH + h) * kDc + cb * kAbsCols + ch * 8) =
+            *reinterpret_cast<const f32x4*>(lds + row * kAbsLdsStride + ch * 16);
     }
   }
 }
