@@ -1047,6 +1047,45 @@ __device__ __forceinline__ void decode_paged_body(
   float* const lbuf = reinterpret_cast<float*>(pbuf);   // end-of-pass exchange (reuses the P slots)
   int* const flag = reinterpret_cast<int*>(pbuf + 1024);
 
+  // bf16 query staging (see the piece prologue). Round 0 moves q_abs chunks
+  // 0..31 (16-byte chunks, dims 8c..8c+7) of the wave's 32 heads, round 1
+  // chunks 32..63 and the q_R rows. Chunk c of head n sits at slot
+  // c ^ (n & 15) of the head's 512-byte row, q_R chunk c at c ^ ((n >> 1) & 7)
+  // of its 128-byte row, so the MFMA-layout reads (16 heads per 256 bytes of
+  // banks) are conflict-free; load j of a round moves heads 2j and 2j + 1.
+  constexpr int kQRegion = 20 * 1024;
+  static_assert(kScaled || 2 * kStageBytes + 4 * kQRegion <= F::lds, "query staging fits behind stage 1");
+  auto q_round = [&](int round) {
+    const int ql = lane_here();
+    const char* qa_w = reinterpret_cast<const char*>(q_abs + (qbase + wave * 32) * kDc) + round * 512;
+    const unsigned reg = (unsigned)(uintptr_t)(lds_void_t*)(lds + 2 * kStageBytes + wave * kQRegion);
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      dma16<false>(qa_w + j * 2048, (unsigned)((ql >> 5) * 1024 + (((ql & 31) ^ ((2 * j + (ql >> 5)) & 15)) << 4)),
+                   reg + j * 1024);
+    if (round == 1) {
+      const char* qr_w = reinterpret_cast<const char*>(q_r + (qbase + wave * 32) * kDr);
+      const int n = ql >> 3;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        dma16<false>(qr_w + j * 1024, (unsigned)(n * 128 + (((ql & 7) ^ (((8 * j + n) >> 1) & 7)) << 4)),
+                     reg + 16 * 1024 + j * 1024);
+    }
+  };
+  auto q_read = [&](int round) {
+    const int ql = lane_here();
+    const int n = ql & 31, gq = ql >> 5;
+    const char* qs = lds + 2 * kStageBytes + wave * kQRegion;
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk)
+      qf[16 * round + kk] = *reinterpret_cast<const bf16x8*>(qs + n * 512 + (((2 * kk + gq) ^ (n & 15)) << 4));
+    if (round == 1) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        qf[32 + kk] = *reinterpret_cast<const bf16x8*>(qs + 16 * 1024 + n * 128 + (((2 * kk + gq) ^ ((n >> 1) & 7)) << 4));
+    }
+  };
+
   // ---- piece loop: rows touching [r_lo, r_hi), in order
   while (cb < a.B && cp < r_hi) {
     const int v = cL - a.s_q + ci + 1;          // keys visible to query ci
@@ -1084,12 +1123,17 @@ __device__ __forceinline__ void decode_paged_body(
           for (int m = 0; m < 8; ++m)
 #pragma unroll
             for (int j = 0; j < 4; ++j) qf[4 * m + j] = qa[8 * m + 4 * (j >> 1) + 2 * (ql >> 5) + (j & 1)];
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) qf[32 + kk] = qr[2 * kk + (ql >> 5)];
         } else {
-#pragma unroll
-          for (int kk = 0; kk < 32; ++kk) qf[kk] = qa[2 * kk + (ql >> 5)];
+          // bf16 cache: the query goes through LDS (stages 2 and 3 and the P
+          // slots, idle until tile 2's DMA) so that every load covers whole
+          // rows; direct loads in the MFMA layout give each instruction 32-byte
+          // pieces of 32 rows 1 KiB apart. Two rounds per wave in a 20 KiB region
+          // of its own: q_abs dims 0..255 now, next to the first tiles' DMA; dims
+          // 256..511 and q_R once the first half is read.
+          q_round(0);
         }
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) qf[32 + kk] = qr[2 * kk + (ql >> 5)];
         {
           const DmaTarget d0 = dma_target(tile0, 0);
 #pragma unroll
@@ -1100,7 +1144,16 @@ __device__ __forceinline__ void decode_paged_body(
 #pragma unroll
           for (int k = 0; k < F::dma; ++k) dma_piece(d1, k, tile0 + 1);
         }
-        wait_vmcnt<0>();
+        if constexpr (!kScaled) {
+          if (n_tiles > 1) wait_vmcnt<2 * F::dma>(); else wait_vmcnt<F::dma>();
+          q_read(0);
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read before the region is refilled
+          q_round(1);
+          wait_vmcnt<0>();
+          q_read(1);
+        } else {
+          wait_vmcnt<0>();
+        }
         if constexpr (kScaled) {
           // each 32-dim block as hi + lo E4M3 codes; the MFMA operand takes
           // block 2m's 16 dims in bytes 0..15 and block 2m+1's in 16..31, and
