@@ -32,7 +32,11 @@
 //     whole tile again. The partials are loaded non-temporally (each is read
 //     once), which keeps the shared W_UV fragments in L2.
 // R = 8 spreads few rows over more workgroups; R = 16 halves the W_UV reads
-// per row where there are rows enough to fill the chip.
+// per row where there are rows enough to fill the chip. With more 16-row tiles
+// than kRowTileGroups per head, a workgroup takes every kRowTileGroups-th tile
+// of its head and keeps W_UV[h]'s fragments in registers across them; with one
+// split per row the merge is the identity and up_one_split_kernel (below)
+// streams the partials instead.
 // In k-step ks, lane quad q holds latent columns 32ks + 8q .. +7 of both
 // operands, so one instruction reads 64 contiguous bytes of each W_UV row.
 #include "mla_device.hpp"
@@ -48,6 +52,10 @@ constexpr int kTileStride = kDc + 8;  // bf16 per tile row; the pad spreads the 
 constexpr int kMergeChunk = 24;       // splits whose loads are in flight together (16-row tiles)
 constexpr int kFewChunk = 4;          // the same with few splits per row (see launch_combine_up)
 constexpr int kFewSplits16 = 16;      // 16-row tiles use kFewChunk up to this many splits
+// 16-row tiles with 2..16 splits: at most this many workgroups per head, each
+// looping over tiles (1024 rows, one split: 165 us against 178 us with a
+// workgroup per tile, which rereads the head's 128 KiB of W_UV for 16 rows)
+constexpr int kRowTileGroups = 4;
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
@@ -116,7 +124,7 @@ __device__ __forceinline__ void row_lse(const float* __restrict__ lp, int num_sp
   }
 }
 
-template <int kRows, int kChunk>
+template <int kRows, int kChunk, bool kLoop = false>
 __global__ __launch_bounds__(512) void combine_up_kernel(const float* __restrict__ o_part,
                                                          const float* __restrict__ lse_part,
                                                          const __bf16* __restrict__ w_uv, int T, int num_splits,
@@ -138,11 +146,9 @@ __global__ __launch_bounds__(512) void combine_up_kernel(const float* __restrict
   // per-wave sums of a row merged by several waves: [wave][column half][lane]
   __shared__ f32x4v wsum[kRows == 8 ? 8 : 1][2][64];
   const int h = blockIdx.x % kH;
-  const int t0 = (blockIdx.x / kH) * kRows;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q = lane >> 4, r = lane & 15;
-  const int rows_here = min(kRows, T - t0);
 
   // W_UV[h] rows d = 16w + r, columns 32ks + 8q .. +7 for k-steps ks = 0..15,
   // requested once the merge's own loads are under way
@@ -153,88 +159,243 @@ __global__ __launch_bounds__(512) void combine_up_kernel(const float* __restrict
     for (int ks = 0; ks < 16; ++ks) a[ks] = wp[4 * ks];
   };
 
-  if constexpr (kRows == 16) {
-    // ---- merge rows t0 + w and t0 + w + 8 into LDS rows w and w + 8; zeros
-    // past the end, never stored. W_UV is requested after both rows' loads.
-    for (int rr = wave; rr < kTileCols; rr += 8) {
+  // Workgroup x handles row tiles x / kH, x / kH + gridDim.x / kH, ... of head
+  // x mod kH, holding W_UV[h]'s fragments in registers from its first tile on
+  // (a workgroup per tile would read the head's 128 KiB of W_UV for 16 rows).
+  bool first = true;
+  for (int t0 = (blockIdx.x / kH) * kRows; t0 < T; t0 += (gridDim.x / kH) * kRows) {
+    const int rows_here = min(kRows, T - t0);
+    if (!first) __syncthreads();  // every wave has read the previous tile
+    if constexpr (kRows == 16) {
+      // ---- merge rows t0 + w and t0 + w + 8 into LDS rows w and w + 8; zeros
+      // past the end, never stored. W_UV is requested after both rows' loads.
+      for (int rr = wave; rr < kTileCols; rr += 8) {
+        f32x4v a0 = f32x4v{}, a1 = f32x4v{};
+        if (rr < rows_here) {
+          const int64_t row = (int64_t)(t0 + rr) * kH + h;
+          const float* lp = lse_part + row * num_splits;
+          float l0, L;
+          row_lse(lp, num_splits, lane, l0, L);
+          if (L != -INFINITY)
+            merge_range<kChunk>(lp, o_part + row * num_splits * kDc + 4 * lane, num_splits, l0, L, 0, num_splits,
+                                     lane, a0, a1, [] {});
+          if (lane == 0) lse_out[row] = L;
+        }
+        put4(rr, 4 * lane, a0);
+        put4(rr, kDc / 2 + 4 * lane, a1);
+      }
+      if (first) load_w();
+    } else {
+      // ---- few rows: a row's splits are dealt to wpr waves (8 / 4 / 2 / 1 for
+      // 1 / 2 / 3-4 / 5-8 rows), each wave merging a contiguous range; the wave
+      // sums are then added in wave order, so the result does not depend on timing
+      const int wpr_log = rows_here == 1 ? 3 : rows_here == 2 ? 2 : rows_here <= 4 ? 1 : 0;
+      const int rr = wave >> wpr_log, j = wave & ((1 << wpr_log) - 1);
       f32x4v a0 = f32x4v{}, a1 = f32x4v{};
+      bool requested = false;
       if (rr < rows_here) {
         const int64_t row = (int64_t)(t0 + rr) * kH + h;
         const float* lp = lse_part + row * num_splits;
         float l0, L;
         row_lse(lp, num_splits, lane, l0, L);
-        if (L != -INFINITY)
-          merge_range<kChunk>(lp, o_part + row * num_splits * kDc + 4 * lane, num_splits, l0, L, 0, num_splits,
-                                   lane, a0, a1, [] {});
-        if (lane == 0) lse_out[row] = L;
-      }
-      put4(rr, 4 * lane, a0);
-      put4(rr, kDc / 2 + 4 * lane, a1);
-    }
-    load_w();
-  } else {
-    // ---- few rows: a row's splits are dealt to wpr waves (8 / 4 / 2 / 1 for
-    // 1 / 2 / 3-4 / 5-8 rows), each wave merging a contiguous range; the wave
-    // sums are then added in wave order, so the result does not depend on timing
-    const int wpr_log = rows_here == 1 ? 3 : rows_here == 2 ? 2 : rows_here <= 4 ? 1 : 0;
-    const int rr = wave >> wpr_log, j = wave & ((1 << wpr_log) - 1);
-    f32x4v a0 = f32x4v{}, a1 = f32x4v{};
-    bool requested = false;
-    if (rr < rows_here) {
-      const int64_t row = (int64_t)(t0 + rr) * kH + h;
-      const float* lp = lse_part + row * num_splits;
-      float l0, L;
-      row_lse(lp, num_splits, lane, l0, L);
-      if (L != -INFINITY) {
-        const int cnt = (num_splits + (1 << wpr_log) - 1) >> wpr_log;
-        const int sa = min(num_splits, j * cnt), sb = min(num_splits, sa + cnt);
-        merge_range<kChunk>(lp, o_part + row * num_splits * kDc + 4 * lane, num_splits, l0, L, sa, sb, lane, a0, a1, [&] {
-          if (!requested) load_w();
-          requested = true;
-        });
-      }
-      if (j == 0 && lane == 0) lse_out[row] = L;
-    }
-    if (!requested) load_w();
-    if (wpr_log == 0) {
-      // one wave per row: rows w and w + 8 (zeros past the tile's rows)
-      put4(wave, 4 * lane, a0);
-      put4(wave, kDc / 2 + 4 * lane, a1);
-      put4(wave + 8, 4 * lane, f32x4v{});
-      put4(wave + 8, kDc / 2 + 4 * lane, f32x4v{});
-    } else {
-      wsum[wave][0][lane] = a0;
-      wsum[wave][1][lane] = a1;
-      __syncthreads();
-      // 16 rows x 128 column quads, four per thread
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e = tid + 512 * i, row = e >> 7, c4 = e & 127;
-        f32x4v v = f32x4v{};
-        if (row < rows_here) {
-          for (int jj = 0; jj < (1 << wpr_log); ++jj) v += wsum[(row << wpr_log) + jj][c4 >> 6][c4 & 63];
+        if (L != -INFINITY) {
+          const int cnt = (num_splits + (1 << wpr_log) - 1) >> wpr_log;
+          const int sa = min(num_splits, j * cnt), sb = min(num_splits, sa + cnt);
+          merge_range<kChunk>(lp, o_part + row * num_splits * kDc + 4 * lane, num_splits, l0, L, sa, sb, lane, a0, a1, [&] {
+            if (!requested && first) load_w();
+            requested = true;
+          });
         }
-        put4(row, 4 * c4, v);
+        if (j == 0 && lane == 0) lse_out[row] = L;
+      }
+      if (!requested && first) load_w();
+      if (wpr_log == 0) {
+        // one wave per row: rows w and w + 8 (zeros past the tile's rows)
+        put4(wave, 4 * lane, a0);
+        put4(wave, kDc / 2 + 4 * lane, a1);
+        put4(wave + 8, 4 * lane, f32x4v{});
+        put4(wave + 8, kDc / 2 + 4 * lane, f32x4v{});
+      } else {
+        wsum[wave][0][lane] = a0;
+        wsum[wave][1][lane] = a1;
+        __syncthreads();
+        // 16 rows x 128 column quads, four per thread
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = tid + 512 * i, row = e >> 7, c4 = e & 127;
+          f32x4v v = f32x4v{};
+          if (row < rows_here) {
+            for (int jj = 0; jj < (1 << wpr_log); ++jj) v += wsum[(row << wpr_log) + jj][c4 >> 6][c4 & 63];
+          }
+          put4(row, 4 * c4, v);
+        }
       }
     }
-  }
 
-  __syncthreads();
+    __syncthreads();
 
-  // ---- up-projection of the tile: D[d][t], d = 16w + 4q + i, t = t0 + r
-  f32x4 acc = f32x4{};
+    // ---- up-projection of the tile: D[d][t], d = 16w + 4q + i, t = t0 + r
+    f32x4 acc = f32x4{};
 #pragma unroll
-  for (int ks = 0; ks < 16; ++ks) {
-    const int off = r * kTileStride + 32 * ks + 8 * q;
-    const bf16x8 hi = *reinterpret_cast<const bf16x8*>(&tile[0][off]);
-    const bf16x8 lw = *reinterpret_cast<const bf16x8*>(&tile[1][off]);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], hi, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], lw, acc, 0, 0, 0);
+    for (int ks = 0; ks < 16; ++ks) {
+      const int off = r * kTileStride + 32 * ks + 8 * q;
+      const bf16x8 hi = *reinterpret_cast<const bf16x8*>(&tile[0][off]);
+      const bf16x8 lw = *reinterpret_cast<const bf16x8*>(&tile[1][off]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], hi, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], lw, acc, 0, 0, 0);
+    }
+    const int t = t0 + r;
+    if (r < kRows && t < T) {
+      const bf16x4 o = {(__bf16)acc[0], (__bf16)acc[1], (__bf16)acc[2], (__bf16)acc[3]};
+      *reinterpret_cast<bf16x4*>(out + ((int64_t)t * kH + h) * kDhc + 16 * wave + 4 * q) = o;
+    }
+    if constexpr (!kLoop) break;
+    first = false;
   }
-  const int t = t0 + r;
-  if (r < kRows && t < T) {
-    const bf16x4 o = {(__bf16)acc[0], (__bf16)acc[1], (__bf16)acc[2], (__bf16)acc[3]};
-    *reinterpret_cast<bf16x4*>(out + ((int64_t)t * kH + h) * kDhc + 16 * wave + 4 * q) = o;
+}
+
+// ---- one split per row (a chunk of query rows whose pieces were not cut):
+// the merge is the identity (weight exp(lse - lse) = 1, LSE unchanged), so
+// the kernel streams the partial rows through LDS and only up-projects.
+// Workgroup = (head h, every kOneSplitGroups-th 16-row tile), W_UV[h]'s
+// fragments in registers for all its tiles. Tiles reach LDS through
+// direct-to-LDS loads (each load instruction moves 1 KiB of one partial row;
+// each wave also moves the tile's 16 LSEs) into a ring of two stages, so one
+// tile is in flight while the previous one is split and multiplied; two
+// workgroups share a CU and fill each other's gaps. A tile is read into
+// registers, split into bf16 high parts and remainders, and written back over
+// its own stage as the MFMA operand, then multiplied as in combine_up_kernel.
+// At 1024 rows: 69 us, where one workgroup per 16-row tile (combine_up_kernel)
+// took 178 us and a ring of four stages with one workgroup per CU 76 us.
+namespace {
+
+constexpr int kOneSplitGroups = 4;                      // workgroups per head: 512 in all, two per CU
+constexpr int kOneSplitRing = 2;                        // LDS stages per workgroup
+constexpr int kOneSplitTileBytes = 16 * kDc * 4;        // 16 fp32 partial rows
+constexpr int kOneSplitStageBytes = kOneSplitTileBytes + 8 * 64 * 4;  // + each wave's copy of the 16 LSEs (x4)
+constexpr int kSplitTileBytes = 2 * kTileCols * kTileStride * 2;      // bf16 high parts, then remainders
+static_assert(kSplitTileBytes <= kOneSplitStageBytes, "the split tile fits in its stage");
+static_assert(kOneSplitRing >= 2 && kOneSplitRing <= 4, "at most two tiles issued after the one waited for");
+static_assert(2 * kOneSplitRing * kOneSplitStageBytes <= 160 * 1024, "two workgroups per CU");
+
+// lane l's 16 (4) bytes from sbase + voff land at LDS byte address
+// lds_addr + 16 l (4 l); lds_addr is bound to M0, and the s_nop is the wait
+// state an LDS-DMA instruction needs after an SALU write of M0. Completion is
+// tracked with explicit vmcnt waits.
+__device__ __forceinline__ void lds_dma_x4(const void* sbase, unsigned voff, unsigned lds_addr) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds_addr) : "memory");
+}
+__device__ __forceinline__ void lds_dma_x1(const void* sbase, unsigned voff, unsigned lds_addr) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds_addr) : "memory");
+}
+__device__ __forceinline__ unsigned lds_address(const void* p) {
+  return (unsigned)(uintptr_t)(const lds_void_t*)p;
+}
+// all LDS operations of this wave are done, then the workgroup barrier; unlike
+// __syncthreads() it leaves the tile loads in flight
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+}  // namespace
+
+__global__ __launch_bounds__(512) void up_one_split_kernel(const float* __restrict__ o_part,
+                                                           const float* __restrict__ lse_part,
+                                                           const __bf16* __restrict__ w_uv, int T,
+                                                           __bf16* __restrict__ out, float* __restrict__ lse_out) {
+  __shared__ __attribute__((aligned(16))) char ring[kOneSplitRing * kOneSplitStageBytes];
+  const int h = blockIdx.x % kH, grp = blockIdx.x / kH, groups = gridDim.x / kH;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q = lane >> 4, r = lane & 15;
+  const int n_tiles = (T + 15) / 16;
+  const int mine = n_tiles > grp ? (n_tiles - grp + groups - 1) / groups : 0;  // this workgroup's tiles
+
+  // tile i of this workgroup (rows t0 .. t0 + 15) into stage i % kOneSplitRing:
+  // load k moves chunk c = 512k + tid (row c >> 7, 16-byte column chunk
+  // c & 127); rows past T re-read row T - 1 and are never used
+  auto issue = [&](int i) {
+    const int t0 = (grp + i * groups) * 16;
+    const int last = min(16, T - t0) - 1;
+    char* st = ring + (i % kOneSplitRing) * kOneSplitStageBytes;
+    const float* base = o_part + ((int64_t)t0 * kH + h) * kDc;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int c = 512 * k + tid;
+      lds_dma_x4(base, (unsigned)(min(c >> 7, last) * (kH * kDc * 4) + (c & 127) * 16),
+                 lds_address(st + (512 * k + 64 * wave) * 16));
+    }
+    lds_dma_x1(lse_part + (int64_t)t0 * kH + h, (unsigned)(min(lane & 15, last) * (kH * 4)),
+               lds_address(st + kOneSplitTileBytes + wave * 256));
+  };
+  constexpr int kPerTile = 5;  // load instructions per wave and tile
+
+  bf16x8 a[16];  // W_UV[h] rows d = 16w + r, columns 32ks + 8q .. +7
+  {
+    const bf16x8* wp = reinterpret_cast<const bf16x8*>(w_uv + ((int64_t)h * kDhc + 16 * wave + r) * kDc + 8 * q);
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) a[ks] = wp[4 * ks];
+  }
+#pragma unroll
+  for (int i = 0; i < kOneSplitRing - 1; ++i)
+    if (i < mine) issue(i);
+
+  for (int i = 0; i < mine; ++i) {
+    // tile i has landed once at most the loads issued after it (up to
+    // kOneSplitRing - 2 tiles, and the stores of earlier tiles) are
+    // outstanding; waiting for fewer is also safe
+    const int after = min(kOneSplitRing - 2, mine - 1 - i);  // tiles issued after tile i
+    if (after >= 2)
+      wait_vmcnt<2 * kPerTile>();
+    else if (after == 1)
+      wait_vmcnt<kPerTile>();
+    else
+      wait_vmcnt<0>();
+    // every wave's loads of tile i are in LDS, and every wave has finished the
+    // MFMAs of tile i - 1, whose stage is refilled now
+    lds_barrier();
+    if (i + kOneSplitRing - 1 < mine) issue(i + kOneSplitRing - 1);
+
+    const int t0 = (grp + i * groups) * 16;
+    const int rows_here = min(16, T - t0);
+    char* const st = ring + (i % kOneSplitRing) * kOneSplitStageBytes;
+    __bf16* const hi_t = reinterpret_cast<__bf16*>(st);
+    __bf16* const lo_t = hi_t + kTileCols * kTileStride;
+    // thread: row tid >> 5, columns 4 cg + 128 j .. +3 (j < 4), cg = tid & 31
+    const int row = tid >> 5, cg = tid & 31;
+    f32x4v v[4];
+    const float l = *reinterpret_cast<const float*>(st + kOneSplitTileBytes + wave * 256 + row * 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = *reinterpret_cast<const f32x4v*>(st + row * (kDc * 4) + (4 * cg + 128 * j) * 4);
+    if (row < rows_here && cg == 0) lse_out[(int64_t)(t0 + row) * kH + h] = l;
+    lds_barrier();  // the whole stage is in registers: its bytes take the split tile
+    const bool live = row < rows_here && l != -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // 0 + v: a merged row starts from +0, so -0 becomes +0 here as well
+      const f32x4v m = live ? f32x4v{} + v[j] : f32x4v{};
+      bf16x4 hi, lw;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        hi[e] = (__bf16)m[e];
+        lw[e] = (__bf16)(m[e] - (float)hi[e]);
+      }
+      *reinterpret_cast<bf16x4*>(&hi_t[row * kTileStride + 4 * cg + 128 * j]) = hi;
+      *reinterpret_cast<bf16x4*>(&lo_t[row * kTileStride + 4 * cg + 128 * j]) = lw;
+    }
+    lds_barrier();
+
+    f32x4 acc = f32x4{};
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) {
+      const int off = r * kTileStride + 32 * ks + 8 * q;
+      const bf16x8 hi = *reinterpret_cast<const bf16x8*>(&hi_t[off]);
+      const bf16x8 lw = *reinterpret_cast<const bf16x8*>(&lo_t[off]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], hi, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], lw, acc, 0, 0, 0);
+    }
+    if (r < rows_here) {
+      const bf16x4 o = {(__bf16)acc[0], (__bf16)acc[1], (__bf16)acc[2], (__bf16)acc[3]};
+      *reinterpret_cast<bf16x4*>(out + ((int64_t)(t0 + r) * kH + h) * kDhc + 16 * wave + 4 * q) = o;
+    }
   }
 }
 
@@ -255,13 +416,19 @@ hipError_t launch_combine_up(const float* o_part, const float* lse_part, const _
       hipLaunchKernelGGL((combine_up_kernel<8, 16>), grid, dim3(512), 0, stream, o_part, lse_part, w_uv, T, num_splits,
                          out, lse);
   } else {
-    const dim3 grid(kH * ((T + 15) / 16));
-    if (num_splits <= kFewSplits16)
-      hipLaunchKernelGGL((combine_up_kernel<16, kFewChunk>), grid, dim3(512), 0, stream, o_part, lse_part, w_uv, T,
-                         num_splits, out, lse);
+    const int tiles = (T + 15) / 16;
+    if (tiles > kRowTileGroups && num_splits == 1)
+      hipLaunchKernelGGL(up_one_split_kernel, dim3(kH * kOneSplitGroups), dim3(512), 0, stream, o_part, lse_part,
+                         w_uv, T, out, lse);
+    else if (tiles > kRowTileGroups && num_splits <= kFewSplits16)
+      hipLaunchKernelGGL((combine_up_kernel<16, kFewChunk, true>), dim3(kH * kRowTileGroups), dim3(512), 0, stream,
+                         o_part, lse_part, w_uv, T, num_splits, out, lse);
+    else if (num_splits <= kFewSplits16)
+      hipLaunchKernelGGL((combine_up_kernel<16, kFewChunk>), dim3(kH * tiles), dim3(512), 0, stream, o_part, lse_part,
+                         w_uv, T, num_splits, out, lse);
     else
-      hipLaunchKernelGGL((combine_up_kernel<16, kMergeChunk>), grid, dim3(512), 0, stream, o_part, lse_part, w_uv, T,
-                         num_splits, out, lse);
+      hipLaunchKernelGGL((combine_up_kernel<16, kMergeChunk>), dim3(kH * tiles), dim3(512), 0, stream, o_part,
+                         lse_part, w_uv, T, num_splits, out, lse);
   }
   return hipGetLastError();
 }

@@ -171,13 +171,15 @@ def test_combine_parity(M, S):
 
 @pytest.mark.parametrize("B,s_q,S", [(1, 1, 1), (16, 1, 17), (3, 15, 3), (2, 512, 2), (2, 1, 70), (1, 1, 130), (3, 11, 5),
                                      (1, 1, 32), (3, 1, 7), (1, 4, 9), (5, 1, 3), (9, 1, 4), (2, 13, 6),
-                                     (37, 16, 1), (1, 1000, 2), (3, 12, 20)])
+                                     (37, 16, 1), (1, 1000, 2), (3, 12, 20), (1, 1000, 1), (5, 13, 1)])
 def test_combine_up_proj_parity(M, B, s_q, S):
     """Merge + up-projection in one pass against the oracle's combine then up_proj.
     Row counts 1 to 9 and 26 take every way the merge deals a tile's rows to its
     waves (8, 4, 2 or 1 waves per row, ranges crossing a block of 64 splits);
     the rest cover the 16-row tiles with few splits (loads of 4 splits in flight)
-    and with many (36 rows, 20 splits), and ragged last tiles."""
+    and with many (36 rows, 20 splits), ragged last tiles, workgroups looping
+    over several tiles of a head (1000 rows, 2 splits) and the one-split kernel
+    that streams the partials (592, 1000 and 65 rows)."""
     g = torch.Generator().manual_seed(400 + B + s_q + S)
     o_part = torch.randn((B, s_q, 128, S, 512), generator=g)
     lse_part = torch.randn((B, s_q, 128, S), generator=g) * 5
