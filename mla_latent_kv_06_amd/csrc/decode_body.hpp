@@ -209,6 +209,8 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2_t;
+typedef short v2i16 __attribute__((ext_vector_type(2)));
+typedef float v2f32 __attribute__((ext_vector_type(2)));
 
 // 8-bit path: one lane's 16 query values of a 32-dim block (the block's other
 // 16 are in lane l ^ 32) as two E4M3 terms with per-block power-of-two scales,
@@ -229,30 +231,40 @@ __device__ __forceinline__ void split_block_fp8(const bf16x8& x0, const bf16x8& 
 #pragma unroll
   for (int j = 0; j < 16; ++j) amax = fmaxf(amax, __builtin_fabsf(v[j]));
   kh = fp8_scale_exponent(pair_max32(amax));
+  // the scaled conversions divide by the scale on the way to E4M3 and multiply
+  // on the way back; with a power of two both are exact, so the codes are those
+  // of the value times 2^-kh (and the value back is hi * 2^kh), without the
+  // separate ldexp of each element
+  const float sh = __builtin_ldexpf(1.0f, kh);
   float r[16];
 #pragma unroll
-  for (int j = 0; j < 16; j += 2) {
-    const float t0 = __uint_as_float(__float_as_uint(v[j]) & 0xFFF00000u);
-    const float t1 = __uint_as_float(__float_as_uint(v[j + 1]) & 0xFFF00000u);
-    const int c = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_ldexpf(t0, -kh), __builtin_ldexpf(t1, -kh), 0, false);
-    const auto hv = __builtin_amdgcn_cvt_pk_f32_fp8(c, false);   // exact E4M3 values of the pair
-    r[j] = v[j] - __builtin_ldexpf(hv[0], kh);
-    r[j + 1] = v[j + 1] - __builtin_ldexpf(hv[1], kh);
-    const int w = (j >> 1);  // 16-bit piece of h
-    if ((w & 1) == 0)
-      h[w >> 1] = (unsigned)(c & 0xFFFF);
-    else
-      h[w >> 1] |= (unsigned)(c & 0xFFFF) << 16;
+  for (int j = 0; j < 16; j += 4) {
+    float t[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) t[e] = __uint_as_float(__float_as_uint(v[j + e]) & 0xFFF00000u);
+    v2i16 c = {0, 0};
+    c = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(c, t[0], t[1], sh, false);
+    c = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(c, t[2], t[3], sh, true);
+    const unsigned cw = __builtin_bit_cast(unsigned, c);
+    const v2f32 h0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(cw, sh, false);  // exact hi * 2^kh of the pairs
+    const v2f32 h1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(cw, sh, true);
+    r[j] = v[j] - h0[0];
+    r[j + 1] = v[j + 1] - h0[1];
+    r[j + 2] = v[j + 2] - h1[0];
+    r[j + 3] = v[j + 3] - h1[1];
+    h[j >> 2] = cw;
   }
   float rmax = 0.f;
 #pragma unroll
   for (int j = 0; j < 16; ++j) rmax = fmaxf(rmax, __builtin_fabsf(r[j]));
   kl = fp8_scale_exponent(pair_max32(rmax));
+  const float sl = __builtin_ldexpf(1.0f, kl);
 #pragma unroll
   for (int j = 0; j < 16; j += 4) {
-    int c = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_ldexpf(r[j], -kl), __builtin_ldexpf(r[j + 1], -kl), 0, false);
-    c = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_ldexpf(r[j + 2], -kl), __builtin_ldexpf(r[j + 3], -kl), c, true);
-    l[j >> 2] = (unsigned)c;
+    v2i16 c = {0, 0};
+    c = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(c, r[j], r[j + 1], sl, false);
+    c = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(c, r[j + 2], r[j + 3], sl, true);
+    l[j >> 2] = __builtin_bit_cast(unsigned, c);
   }
 }
 
