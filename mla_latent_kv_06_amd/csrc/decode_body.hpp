@@ -696,6 +696,18 @@ __device__ __forceinline__ void decode_paged_body(
   // zero operands (a no-op MFMA) when there is no earlier tile
   bf16x8 pf[4];
   VFrag va[3];
+  // Block-table entry of the page that QK(it) streams in (tile it + 2), loaded
+  // during the P publish of tile it - 1, so the scalar load has returned by
+  // the tile barrier; looked up right after the barrier, its latency and the
+  // clamp stood between the barrier and the tile's first MFMA (A/B,
+  // bit-identical: long 267.7 -> 266.1 us, 8-bit 262.3 -> 258.5 us). The
+  // clamp is physical_page's, on 32-bit scalar min/max (ids are 32-bit).
+  int pref_id = 0;
+  const int last_page = (int)(a.num_pages - 1 < (int64_t)0x7fffffff ? a.num_pages - 1 : (int64_t)0x7fffffff);
+  auto load_id = [&](int tile) { return block_table[(int64_t)b * a.max_pages + (tile >> 1)]; };
+  auto pref_target = [&](int tile, int stage) {
+    return page_target((int64_t)min(max(pref_id, 0), last_page), tile, stage);
+  };
 
   // ---- phase A: S^T[token, head] = K(it) . Q^T over 576 dims, pinned in
   // program order: the K fragment for MFMA kk+3 is read right after MFMA kk,
@@ -717,7 +729,7 @@ __device__ __forceinline__ void decode_paged_body(
       // tile the rows past the visible length are then overwritten with zeros.
       const char* tb = lds + (it & (kStages - 1)) * F::bytes;
       DmaTarget t{nullptr, 0u};
-      if constexpr (dma) t = dma_target(tile0 + it + 2, (it + 2) & (kStages - 1));
+      if constexpr (dma) t = pref_target(tile0 + it + 2, (it + 2) & (kStages - 1));
       // A scales: byte m & 3 of sa[m >> 2] = scale of MX block 2m + g of token lo
       int sa[2];
       {
@@ -820,7 +832,7 @@ __device__ __forceinline__ void decode_paged_body(
       // bf16 MFMAs of k_R. K operands are read one MFMA pair ahead.
       const char* tb = lds + (it & (kStages - 1)) * F::bytes;
       DmaTarget t{nullptr, 0u};
-      if constexpr (dma) t = dma_target(tile0 + it + 2, (it + 2) & (kStages - 1));
+      if constexpr (dma) t = pref_target(tile0 + it + 2, (it + 2) & (kStages - 1));
       // the token's scale 2^k as its E8M0 byte k + 127 (the exponent field)
       const int kscale = (int)(__float_as_uint(*reinterpret_cast<const float*>(tb + kStage8Scale + lo * 4)) >> 23);
       auto kread = [&](int m) -> i32x8 {
@@ -872,7 +884,7 @@ __device__ __forceinline__ void decode_paged_body(
     }
     const char* tb = lds + (it & (kStages - 1)) * kStageBytes;
     DmaTarget t{nullptr, 0u};
-    if constexpr (dma) t = dma_target(tile0 + it + 2, (it + 2) & (kStages - 1));
+    if constexpr (dma) t = pref_target(tile0 + it + 2, (it + 2) & (kStages - 1));
     f32x16 S;
     bf16x8 kf[4];
 #pragma unroll
@@ -1000,6 +1012,7 @@ __device__ __forceinline__ void decode_paged_body(
     sm_scales(it, 1, std::true_type{});
     sm_exp(8);
     sm_pack();
+    pref_id = load_id(tile0 + min(it + 3, n_tiles - 1));  // for QK(it + 1); clamped into the piece
     sm_publish(it);
     MLA_FENCE();
   };
@@ -1021,6 +1034,7 @@ __device__ __forceinline__ void decode_paged_body(
     MLA_FENCE();
     sm_exp(8);             mm4(0, va[1], pf); va[0] = vfrag(ip, 1, 2); interleave<4>(); MLA_FENCE();
     sm_pack();             mm4(1, va[2], pf); va[1] = vfrag(ip, 1, 3); interleave<2>(); MLA_FENCE();
+    pref_id = load_id(tile0 + min(it + 3, n_tiles - 1));  // for QK(it + 1); clamped into the piece
     sm_publish(it);        mm4(2, va[0], pf); MLA_FENCE();
     // mm4(3, va[1], pf) of PV(ip) runs at the start of the next QK
   };
@@ -1215,6 +1229,7 @@ __device__ __forceinline__ void decode_paged_body(
             if (n_tiles > 1) issue(tile0 + 1, 1);
           }
           // tile 0: QK + softmax only
+          pref_id = load_id(tile0 + min(2, n_tiles - 1));
           if (n_tiles > 1) wait_vmcnt<F::dma>(); else wait_vmcnt<0>();
           tile_barrier();
           zero_tail(0);
