@@ -21,7 +21,10 @@ Prints one JSON line:
   value         whole-step throughput of the headline workload, algorithmic TFLOP/s
   roofline      mla_decode_paged on the headline workload against the roof its
                 arithmetic intensity selects (HBM below the ridge, bf16 MFMA above)
-  configs       every workload: decode and step times, intensity, binding roof, fraction
+  configs       every workload: decode and step times (mean, median, min of the timed
+                steps), intensity, binding roof, fraction; `warm` (the workloads whose
+                layer fits the 256 MB last-level cache): the scan alone on one layer at
+                every launch, labelled as warm (--no-warm skips it)
   cpu_baseline  the fp64 CPU oracle on a bounded sample of every workload
   next_rows     for the headline: cache append and query rotation, the scan over the
                 8-bit and 4-bit caches, the decompressed branch (chunks with s_q > 1)
@@ -37,6 +40,7 @@ import argparse
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -46,6 +50,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 RIDGE = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)   # 312.5 FLOP per byte
+LLC_BYTES = 256 * 10**6              # MI355X last-level (Infinity) cache, bytes
 FLOP_PER_PAIR = 128 * 2 * (576 + 512)  # all heads, one (query, key) pair: QK over 576 + PV over 512
 KV_BYTES_PER_TOKEN = 576 * 2
 # measurement order: the two short workloads are latency-bound and never reach
@@ -80,6 +85,8 @@ def parse():
     p.add_argument("--no-fp8", action="store_true", help="skip the 8-bit cache leg")
     p.add_argument("--no-mxfp4", action="store_true", help="skip the 4-bit cache leg")
     p.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay of the step")
+    p.add_argument("--no-warm", action="store_true",
+                   help="skip the warm-cache scan timing (the counter runs average over every dispatch)")
     p.add_argument("--no-ceilings", action="store_true",
                    help="skip the achievable streaming-read and sustained MFMA measurements")
     p.add_argument("--one-launch", action="store_true",
@@ -222,7 +229,32 @@ class Workload:
         per = [[e[j].elapsed_time(e[j + 1]) for e in ev] for j in range(len(self.names))]
         self.kernel_ms = {n: sum(x) / len(x) for n, x in zip(self.names, per)}
         self.kernel_min_ms = {n: min(x) for n, x in zip(self.names, per)}
+        self.kernel_median_ms = {n: statistics.median(x) for n, x in zip(self.names, per)}
         self.ms_step = wall / steps * 1e3
+        return self
+
+    def warm_decode(self, steps):
+        """The scan alone, on layer 0 at every launch (after 5 untimed ones), HIP events
+        between consecutive launches: the warm figure, taken where a layer's cache fits
+        the 256 MB last-level cache (single, uniform, prefill) and is served from there."""
+        torch, M = self.torch, self.M
+        stream = torch.cuda.current_stream()
+
+        def launch():
+            M.mla_decode_paged(self.q_abs, self.q_r, self.kv[0], self.tables[0], self.seqlens, self.S,
+                               o_part=self.o_part, lse_part=self.lse_part)
+        for _ in range(5):
+            launch()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record(stream)
+        for k in range(steps):
+            launch()
+            ev[k + 1].record(stream)
+        torch.cuda.synchronize()
+        t = [ev[k].elapsed_time(ev[k + 1]) * 1e3 for k in range(steps)]
+        self.warm = {"decode_median_us": round(statistics.median(t), 2), "decode_min_us": round(min(t), 2),
+                     "cache": f"warm: layer 0 ({self.layer_bytes / 1e6:.0f} MB of cache) at every launch, "
+                              f"inside the 256 MB last-level cache"}
         return self
 
     def graph_ms(self, steps):
@@ -251,6 +283,7 @@ class Workload:
         r.update({
             "decode_us": round(self.kernel_ms["mla_decode_paged"] * 1e3, 2),
             "decode_min_us": round(self.kernel_min_ms["mla_decode_paged"] * 1e3, 2),
+            "decode_median_us": round(self.kernel_median_ms["mla_decode_paged"] * 1e3, 2),
             "step_us": round(self.ms_step * 1e3, 2),
             "graph_step_us": None if math.isnan(self.graph_step_ms) else round(self.graph_step_ms * 1e3, 2),
             "kernels_us": {n: round(v * 1e3, 2) for n, v in self.kernel_ms.items()},
@@ -264,6 +297,7 @@ class Workload:
             "resident_layers": self.layers,
             "cache": f"cold: step k reads layer k mod {self.layers} ({self.layers * self.layer_bytes / 1e9:.1f} GB)",
             "traffic": measured_traffic(self.name, self.S),
+            "warm": getattr(self, "warm", None),
         })
         return r
 
@@ -608,6 +642,10 @@ def main():
               f"step {wls[n].ms_step * 1e3:.1f} us", file=sys.stderr, flush=True)
     for n in names:
         wls[n].graph_step_ms = float("nan") if args.no_graph else wls[n].graph_ms(args.steps)
+    if not args.no_warm:
+        for n in names:
+            if wls[n].layer_bytes <= LLC_BYTES:  # larger layers stream from HBM anyway
+                wls[n].warm_decode(args.steps)
 
     wl = wls[head]
     dec_s = wl.kernel_ms["mla_decode_paged"] * 1e-3
