@@ -298,8 +298,29 @@ class Workload:
             "cache": f"cold: step k reads layer k mod {self.layers} ({self.layers * self.layer_bytes / 1e9:.1f} GB)",
             "traffic": measured_traffic(self.name, self.S),
             "warm": getattr(self, "warm", None),
+            "projections": self.projection_roofs(),
         })
         return r
+
+    def projection_roofs(self):
+        """The absorb and the up-projection against their own roofs: each is
+        2 T H 128 512 FLOP over a 16 MiB weight. Absorb bytes: W_UK, bf16 q_c in,
+        bf16 q_abs out; up-projection bytes: W_UV, fp32 o_lat in, bf16 out. The
+        fused stage 2 also merges the splits, so its time covers both steps (its
+        o_lat never reaches HBM, its partials are the scan's overhead)."""
+        T, w = self.T, 128 * 128 * 512 * 2
+        flop = 2 * T * 128 * 128 * 512
+        out = {}
+        for name, kern, nbytes in (("absorb", "mla_absorb_q", w + T * 128 * 128 * 2 + T * 128 * 512 * 2),
+                                   ("up_proj", "mla_up_proj" if self.separate else "mla_combine_up_proj",
+                                    w + T * 128 * 512 * 4 + T * 128 * 128 * 2)):
+            sec = self.kernel_ms[kern] * 1e-3
+            r = roof(flop, nbytes, sec)
+            out[name] = {"kernel": kern, "us": round(sec * 1e6, 2), "bound": r["bound"], "frac": r["frac"],
+                         "algorithmic_bytes": nbytes, "flop": flop,
+                         "roofline_time_us": round(max(flop / (MFMA_BF16_PEAK_TFLOPS * 1e12),
+                                                       nbytes / (HBM_PEAK_GBS * 1e9)) * 1e6, 2)}
+        return out
 
 
 def time_next_rows(M, torch, wl, reps=200):

@@ -61,3 +61,20 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_projection_roofs_match_the_weight_bound():
+    """Absorb and up-projection roofs: 16 MiB of weight plus the activations at
+    8 TB/s (2.4 us at T = 16 and 23 us at T = 1024 for the absorb)."""
+    class W:
+        separate = False
+    w = W()
+    for T, absorb_us in ((16, 2.42), (1024, 23.07)):
+        w.T = T
+        w.kernel_ms = {"mla_absorb_q": 0.010, "mla_combine_up_proj": 0.020}
+        r = bench.Workload.projection_roofs(w)
+        assert r["absorb"]["roofline_time_us"] == absorb_us
+        assert r["absorb"]["bound"] == r["up_proj"]["bound"] == "hbm"
+        assert r["absorb"]["flop"] == 2 * T * 128 * 128 * 512
+        assert r["up_proj"]["algorithmic_bytes"] == 128 * 128 * 512 * 2 + T * 128 * 512 * 4 + T * 128 * 128 * 2
+        assert abs(r["absorb"]["frac"] - absorb_us / 10.0) < 1e-3
