@@ -155,11 +155,14 @@ __device__ __forceinline__ void mfma_qk_first(f32x16& d, const bf16x8& a, const 
 __device__ __forceinline__ void mfma_qk(f32x16& d, const bf16x8& a, const bf16x8& b) {
   asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
 }
-// VALU may read an MFMA result only after the MFMA has drained (at most
-// 16 passes + 2 on CDNA; 24 wait states here). Tied to the value so no read
-// of it can be scheduled above the wait.
+// The QK MFMAs are inline asm, so the compiler cannot see their hazards. A
+// VALU read of a v_mfma_f32_32x32x16_bf16 result (8 passes) needs 12 wait
+// states after the MFMA issues on gfx950: the count the compiler's own hazard
+// model inserts after the builtin. MFMAs that accumulate onto the same
+// registers (also a scaled f8f6f4 chain continued by bf16 MFMAs) need none.
+// Tied to the value so no read of it can be scheduled above the wait.
 __device__ __forceinline__ void mfma_result_fence(f32x16& d) {
-  asm("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(d));
+  asm("s_nop 11" : "+v"(d));
 }
 
 // scheduling hint: one MFMA followed by up to N VALU/transcendental ops, four times
@@ -806,8 +809,6 @@ __device__ __forceinline__ void decode_paged_body(
 #pragma unroll
         for (int j = 0; j < 8; ++j) *reinterpret_cast<bf16x8*>(vrow + (((8 * ds + j) ^ swz(dt)) << 4)) = bf16x8{};
       }
-      // the bf16 MFMAs below take S as srcC from a different MFMA shape: drain first
-      mfma_result_fence(S);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -864,8 +865,6 @@ __device__ __forceinline__ void decode_paged_body(
       }
       bf16x8 rf[2];
       rf[0] = *reinterpret_cast<const bf16x8*>(tb + rope8_off + (0 ^ rope8_x));
-      // the bf16 MFMAs below take S as srcC from a different MFMA shape: drain first
-      mfma_result_fence(S);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
