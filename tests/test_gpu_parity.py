@@ -331,6 +331,45 @@ def test_decode_rising_scores_within_headroom(M):
 # bit-exact invariances
 # ---------------------------------------------------------------------------
 
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "mxfp4"])
+def test_out_of_range_table_entries_are_clamped_into_the_pool(M, fmt):
+    """Table entries outside [0, num_pages) break the interface's contract; the
+    scan clamps them (below 0 -> page 0, from num_pages on -> the last page)
+    so that no entry addresses memory outside the pool. Both page lookups, for
+    a piece's first two tiles and the steady loop's one-tile-ahead prefetch,
+    clamp alike: a table with such entries gives bit for bit the result of its
+    clamped copy (pieces of ~32 tiles, so the steady loop runs)."""
+    lens = [700, 1500, 64, 2100]
+    q_abs, q_r, kv, bt, sl = _random_case(lens, 1, seed=91)
+    P = kv.shape[0]
+    bad = bt.clone()
+    kinds = [-7, P + 3, 2**31 - 1]
+    k = 0
+    for b, L in enumerate(lens):
+        for p in range(0, -(-L // 64), 3):  # every third live page of each row
+            bad[b, p] = kinds[k % 3]
+            k += 1
+    clamped = bad.clamp(0, P - 1)
+    kv_d = kv.to(DEV)
+    if fmt == "fp8":
+        kv_d, fn = M.mla_quantize_cache_fp8(kv_d), M.mla_decode_paged_fp8
+    elif fmt == "mxfp4":
+        kv_d, fn = M.mla_quantize_cache_mxfp4(kv_d), M.mla_decode_paged_mxfp4
+    else:
+        fn = M.mla_decode_paged
+    _say(f"out-of-range entries ({fmt}): pool {P} pages, {k} entries replaced, splits 3")
+    outs = []
+    for t in (bad, clamped):
+        o_part, lse_part = fn(q_abs.to(DEV), q_r.to(DEV), kv_d, t.to(DEV), sl.to(DEV), 3, SCALE)
+        torch.cuda.synchronize()
+        outs.append((o_part.cpu(), lse_part.cpu()))
+    (o1, l1), (o2, l2) = outs
+    live = torch.isfinite(l2)
+    assert bool(live.any())
+    assert torch.equal(l1, l2)
+    assert torch.equal(o1[live], o2[live])
+
+
 def test_page_placement_neighbour_values_and_rerun_bit_exact(M):
     q_abs, q_r, kv, bt, sl = _random_case([700, 64, 1500], 1, seed=13)
     S = 4
