@@ -751,7 +751,12 @@ __device__ __forceinline__ void decode_paged_body(
       const u32x4 dc0 = *reinterpret_cast<const u32x4*>(tb + dt * kFp4RowBytes + (((2 * ds) ^ (dt & 7)) << 4));
       const u32x4 dc1 = *reinterpret_cast<const u32x4*>(tb + dt * kFp4RowBytes + (((2 * ds + 1) ^ (dt & 7)) << 4));
       const unsigned de = *reinterpret_cast<const unsigned short*>(tb + kStage4Scale + dt * 16 + 2 * ds);
-      char* const vrow = vbuf + (it & 1) * kStageBytes + dt * kRowBytes;
+      // chunk 8 ds + j of the row sits at slot (8 ds + j) ^ swz(dt) = 8 ds + (j ^ swz(dt)) (swz < 8):
+      // from an offset whose bits 0-6 are zero but for the swizzle in bits 4-6, each chunk's
+      // address is one XOR (21 fewer VALU ops per wave and tile than recomputing the slot;
+      // long workload 245.8 -> 239.7 us, bit-identical)
+      static_assert(F::vbuf % 128 == 0 && kStageBytes % 128 == 0 && kRowBytes % 128 == 0, "128-byte aligned rows");
+      const int vrel = F::vbuf + (it & 1) * kStageBytes + dt * kRowBytes + 128 * ds + (swz(dt) << 4);
       auto dequant = [&](int j) {  // output chunk 8 ds + j (dims 64 ds + 8j .. +7)
         const unsigned w = (j < 4 ? dc0 : dc1)[j & 3];
         const float sc = __uint_as_float(((j < 4 ? de : de >> 8) & 255u) << 23);
@@ -759,7 +764,7 @@ __device__ __forceinline__ void decode_paged_body(
         const bf16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1);
         const bf16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2);
         const bf16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3);
-        *reinterpret_cast<bf16x8*>(vrow + (((8 * ds + j) ^ swz(dt)) << 4)) =
+        *reinterpret_cast<bf16x8*>(lds + (vrel ^ (j << 4))) =
             bf16x8{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
       };
       u32x4 ka[2];
@@ -807,7 +812,7 @@ __device__ __forceinline__ void decode_paged_body(
       // (written after its own chunks, and LDS writes of a wave land in order)
       if ((tile0 + it + 1) * kTok > t_end && (tile0 + it) * kTok + dt >= t_end) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) *reinterpret_cast<bf16x8*>(vrow + (((8 * ds + j) ^ swz(dt)) << 4)) = bf16x8{};
+        for (int j = 0; j < 8; ++j) *reinterpret_cast<bf16x8*>(lds + (vrel ^ (j << 4))) = bf16x8{};
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
