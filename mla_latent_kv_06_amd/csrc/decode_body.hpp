@@ -986,13 +986,6 @@ __device__ __forceinline__ void decode_paged_body(
       if constexpr (kFp8) xs[r] *= psc[(r - r0) >> 2][r & 3];
     }
   };
-  auto sm_exp2 = [&](int r) {  // scores r, r+1
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      xs[r + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(xs[r + e], c_log2, -m_ref));
-      l_run += xs[r + e];
-    }
-  };
   auto sm_pack = [&]() {
 #pragma unroll
     for (int r = 0; r < 16; ++r) pb[r >> 3][r & 7] = (__bf16)xs[r];

@@ -38,7 +38,6 @@ constexpr int kKRow = 256;       // bytes of a content-key or value row
 constexpr int kRRow = 128;       // bytes of a RoPE-key row
 constexpr int kMhaStage = kMhaTok * (2 * kKRow + kRRow);  // 40 KiB: K, V, k_R
 constexpr int kMhaStages = 2;
-constexpr int kMhaDmaPerWave = 10;                        // 1 KiB loads per wave per tile: 4 K, 4 V, 2 k_R
 constexpr float kRefSlack = 14.f;                         // log2 units: P <= 2^14 < 65504 (fp16)
 
 // 16-byte chunk positions: key rows (QK reads 16 consecutive rows at one
