@@ -122,6 +122,15 @@ int mla_plan_splits(const int32_t* seqlens_host, int B, int s_q, int max_pages, 
 mla_status mla_validate_block_table(const int32_t* block_table, int max_pages, const int32_t* seqlens, int B,
                                     int64_t num_pages, int* bad_seq, int* bad_page);
 
+/* Debug switch (environment variable, read at every call): with
+ * MLA_DEBUG_CHECKS set to anything but "" or "0", mla_decode_paged, its 8-bit
+ * and 4-bit forms and mla_decode_step* copy block_table and seqlens from the
+ * device after the caller's stream has drained, run the check above on them,
+ * and return its status (mla_last_error() prefixed "MLA_DEBUG_CHECKS:")
+ * without launching when the table is bad. The copy allocates host memory and
+ * synchronises the stream, so the switch is for debugging only and must stay
+ * off under graph capture; mla_decode_step_static never applies it. */
+
 /* Stage 1: split scan of the paged latent cache, absorbed scores, online
  * softmax, P . c_KV on matrix cores (teardown page, section 4 absorbed
  * scores; K3 study "Inside the blocks" stage 1).

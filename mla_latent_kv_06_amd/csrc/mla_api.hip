@@ -4,8 +4,10 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "../../include/mla.h"
 #include "append.hpp"
@@ -32,6 +34,33 @@ mla_status report_hip(hipError_t e, const char* what) {
 
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+// MLA_DEBUG_CHECKS set to anything but "" or "0": the paged scans and steps
+// copy the device block table and lengths to the host (synchronously, after
+// the caller's stream has drained) and validate them before launching, so a
+// bad table is reported instead of being clamped. Debug only: the copy
+// allocates host memory and synchronises, and is not capturable.
+bool debug_checks() {
+  const char* e = std::getenv("MLA_DEBUG_CHECKS");
+  return e != nullptr && e[0] != '\0' && !(e[0] == '0' && e[1] == '\0');
+}
+
+mla_status debug_table_check(const int32_t* block_table, int max_pages, const int32_t* seqlens, int B,
+                             int64_t num_pages, void* stream) {
+  std::vector<int32_t> bt((size_t)B * (size_t)max_pages), sl((size_t)B);
+  const hipStream_t s = as_stream(stream);
+  hipError_t e = hipMemcpyAsync(bt.data(), block_table, bt.size() * sizeof(int32_t), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(sl.data(), seqlens, sl.size() * sizeof(int32_t), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return report_hip(e, "MLA_DEBUG_CHECKS: block table copy");
+  const mla::Check c = mla::validate_block_table(bt.data(), max_pages, sl.data(), B, num_pages, nullptr, nullptr);
+  if (!c.ok()) {
+    mla::Check d = c;
+    d.detail = "MLA_DEBUG_CHECKS: " + c.detail;
+    return report(d);
+  }
+  return MLA_OK;
+}
+
 mla_status decode_paged_any(const void* q_abs, const void* q_r, const void* kv_cache, int64_t num_pages,
                             const int32_t* block_table, int max_pages, const int32_t* seqlens, int B, int s_q, int H,
                             float softmax_scale, int num_splits, float* o_part, float* lse_part, void* stream,
@@ -39,6 +68,10 @@ mla_status decode_paged_any(const void* q_abs, const void* q_r, const void* kv_c
   const mla::Check c = mla::check_decode(q_abs, q_r, kv_cache, num_pages, block_table, max_pages, seqlens, B, s_q, H,
                                          softmax_scale, num_splits, o_part, lse_part);
   if (!c.ok()) return report(c);
+  if (debug_checks()) {
+    const mla_status st = debug_table_check(block_table, max_pages, seqlens, B, num_pages, stream);
+    if (st != MLA_OK) return st;
+  }
   mla::DecodeParams p{};
   p.q_abs = static_cast<const __bf16*>(q_abs);
   p.q_r = static_cast<const __bf16*>(q_r);
@@ -68,6 +101,10 @@ mla_status decode_step_any(const void* q_c, const void* q_r, const void* kv_cach
   const mla::Check c = mla::check_step(q_c, q_r, kv_cache, num_pages, block_table, max_pages, seqlens, B, s_q, H, w_uk,
                                        w_uv, softmax_scale, num_splits, q_abs, o_part, lse_part, o_lat, out, lse);
   if (!c.ok()) return report(c);
+  if (debug_checks()) {
+    const mla_status st = debug_table_check(block_table, max_pages, seqlens, B, num_pages, stream);
+    if (st != MLA_OK) return st;
+  }
   mla::StepParams p{};
   p.d.q_abs = static_cast<const __bf16*>(q_abs);
   p.d.q_r = static_cast<const __bf16*>(q_r);

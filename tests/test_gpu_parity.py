@@ -331,6 +331,30 @@ def test_decode_rising_scores_within_headroom(M):
 # bit-exact invariances
 # ---------------------------------------------------------------------------
 
+def test_debug_checks_switch_reports_a_bad_table(M, monkeypatch):
+    """MLA_DEBUG_CHECKS=1: the scan validates the device block table on the
+    host before launching and reports a bad entry instead of clamping it; with
+    a good table it changes nothing (same partials, bit for bit)."""
+    q_abs, q_r, kv, bt, sl = _random_case([300, 130], 1, seed=93)
+    dev = [x.to(DEV) for x in (q_abs, q_r, kv, sl)]
+    run = lambda t: M.mla_decode_paged(dev[0], dev[1], dev[2], t.to(DEV), dev[3], 2, SCALE)
+    ref_o, ref_l = run(bt)
+    torch.cuda.synchronize()
+    monkeypatch.setenv("MLA_DEBUG_CHECKS", "1")
+    got_o, got_l = run(bt)
+    torch.cuda.synchronize()
+    live = torch.isfinite(ref_l)
+    assert torch.equal(got_l.cpu(), ref_l.cpu()) and torch.equal(got_o[live].cpu(), ref_o[live].cpu())
+    bad = bt.clone()
+    bad[1, 2] = kv.shape[0] + 4
+    with pytest.raises(M.MlaError) as e:
+        run(bad)
+    assert e.value.status == 2 and "MLA_DEBUG_CHECKS" in str(e.value) and "block_table[1, 2]" in str(e.value)
+    monkeypatch.setenv("MLA_DEBUG_CHECKS", "0")
+    run(bad)  # switched off: clamped, no error
+    torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("fmt", ["bf16", "fp8", "mxfp4"])
 def test_out_of_range_table_entries_are_clamped_into_the_pool(M, fmt):
     """Table entries outside [0, num_pages) break the interface's contract; the
